@@ -1,0 +1,169 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so: NVFP4 block quantization, the
+ * block-scaled 4-bit GEMM that consumes it, and the symmetric INT4
+ * per-group weight-only GEMM/GEMV, as hand-written HIP kernels for gfx950.
+ *
+ * Formats (pages cited by title and section):
+ *  - "Tu pipeline NVFP4: meter 62 GB de modelo en 24 GB de laptop",
+ *    section 2 ("Qué es realmente NVFP4"): each value is E2M1 (1 sign,
+ *    2 exponent, 1 mantissa bit, largest magnitude 6); 16 consecutive
+ *    values share one scale stored as FP8 E4M3; the scale is chosen from
+ *    the block's largest magnitude.
+ *  - "NVFP4 en difusión: la misma cuantización, un motor completamente
+ *    distinto", section 2 ("NVFP4 sin vLLM"): the weight is a uint8
+ *    tensor (out, in/2) holding two FP4 values per byte, the scale a
+ *    float8_e4m3fn tensor (out, in/16); the activation is quantized the
+ *    same way on every forward; the matmul multiplies the two decoded
+ *    operands (the weight transposed) and emits bfloat16.
+ *  - "Cuantización e inferencia local" (course class 085), formula block:
+ *    symmetric b-bit quantization s = max|x| / (2^(b-1) - 1),
+ *    q = clamp(round(x/s)), x ~ s*q, with one scale per group of weights.
+ *
+ * Layouts (all row-major, contiguous, no padding):
+ *  - bf16 matrices: [rows, cols] of IEEE bfloat16 bit patterns.
+ *  - NVFP4 codes:  uint8 [rows, cols/2]; element 2j of a row sits in bits
+ *    0-3 of byte j, element 2j+1 in bits 4-7.  A code is sign<<3 | E2M1
+ *    magnitude code (0..7 = 0, .5, 1, 1.5, 2, 3, 4, 6).
+ *  - NVFP4 scales: uint8 [rows, cols/16], E4M3 (OCP "fn") bit patterns.
+ *  - NVFP4 global scale: one fp32 in device memory.  The value of element
+ *    (r, c) is E2M1(code) * E4M3(scale[r][c/16]) * global_scale.
+ *  - INT4 codes: uint8 [N, K/2], two's-complement nibbles in [-7, 7],
+ *    element 2j in bits 0-3 of byte j; INT4 scales: fp16 [N, K/group].
+ *
+ * Ownership and streams: the caller allocates and frees every buffer.  All
+ * pointers except `stream` are device pointers.  The library allocates no
+ * memory, keeps no global state, never synchronizes the host and never
+ * reads device data back: every entry point only enqueues kernels on
+ * `stream` (a hipStream_t; NULL is the default stream) and returns.  All
+ * entry points are re-entrant; calls on different streams that share an
+ * output buffer race.
+ *
+ * Errors: arguments are validated on the host before any HIP call; a
+ * failed check returns an error status, enqueues nothing and records a
+ * message readable with nvfp4_last_error() (thread-local).  A kernel
+ * launch failure returns NVFP4_ERR_HIP.  Faults inside a kernel surface at
+ * the caller's next synchronization.  Empty outputs (M, N or rows == 0)
+ * return NVFP4_OK and enqueue nothing.  Alignment: every pointer must be
+ * 16-byte aligned (256-byte aligned allocations from HIP or torch satisfy
+ * this), except the fp32 global-scale pointers and the quantize workspace
+ * (4-byte).
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARG = 1, /* null pointer, negative size, aliasing */
+  NVFP4_ERR_SHAPE = 2,       /* a dimension that breaks the format's rules */
+  NVFP4_ERR_ALIGNMENT = 3,   /* a pointer below the required alignment */
+  NVFP4_ERR_UNSUPPORTED = 4, /* a valid request this build does not handle */
+  NVFP4_ERR_HIP = 5          /* the HIP runtime reported an error */
+} nvfp4_status;
+
+/* Version of this ABI; bumped on any incompatible change. */
+int nvfp4_abi_version(void);
+
+/* Device bytes of the workspace nvfp4_quantize needs (per-workgroup
+ * partial maxima of the global-amax pass).  The content needs no
+ * initialization and is overwritten by every call. */
+size_t nvfp4_quantize_workspace_bytes(void);
+
+/*
+ * NVFP4-quantize a bf16 matrix x [rows, cols] (cols % 16 == 0).
+ * Passages: the E2M1 / 16-value-block / E4M3-scale format and absmax scale
+ * choice ("Tu pipeline NVFP4", section 2); two codes per byte and the
+ * (out, in/2) / (out, in/16) layouts, with the activation quantized on
+ * every forward ("NVFP4 en difusión", section 2).
+ *
+ * Steps, each an fp32 operation with one round-to-nearest-even:
+ *   g   = amax(|x|) / 2688     (2688 = 6 * 448), computed on the device
+ *         and written to *global_scale, unless use_given_global_scale != 0,
+ *         in which case *global_scale is read (finite, >= 0) and not written;
+ *   per row and 16-block b: s = E4M3_RNE_saturating((amax_b / 6) / g),
+ *         or 0 when g == 0;
+ *   d = s * g;  per element: code = sign(x) | E2M1_RNE(|x| / d), ties to
+ *         the even code, saturating at 6; magnitude 0 when d == 0.
+ * Outputs: codes [rows, cols/2], scales [rows, cols/16], *global_scale.
+ * workspace: >= nvfp4_quantize_workspace_bytes() device bytes, not shared
+ * with a concurrent call.  Outputs must not overlap x or each other.
+ */
+nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols,
+                            uint8_t* codes, uint8_t* scales, float* global_scale,
+                            int use_given_global_scale, void* workspace, void* stream);
+
+/*
+ * out[M, N] (bf16) = bf16_RNE( g_a * g_w * sum_k A[m, k] * W[n, k] )
+ * where A[m, k] = E2M1(a code) * E4M3(a scale) and likewise for W: the
+ * decoded activation times the decoded weight, transposed.  Passage: the
+ * block-scaled matmul of "NVFP4 en difusión", section 2 (scale_a, scale_b,
+ * bfloat16 output).  Each decoded product is exact; sums are fp32.
+ * a_codes [M, K/2], a_scales [M, K/16], w_codes [N, K/2], w_scales
+ * [N, K/16]; a_gscale and w_gscale are device fp32 pointers (no host sync).
+ * K % 16 == 0.  M <= 16 runs the decode kernel that streams W once.
+ * K == 0 writes zeros (the packed operands may then be NULL).
+ * out must not overlap any input.
+ */
+nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                        void* out_bf16, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Kernel choice for nvfp4_gemm_ex / int4g_gemv_ex. */
+typedef enum nvfp4_algo {
+  NVFP4_ALGO_AUTO = 0,    /* what nvfp4_gemm / int4g_gemv pick */
+  NVFP4_ALGO_TILED = 1,   /* the LDS-staged MFMA tile kernel (any M) */
+  NVFP4_ALGO_DECODE = 2,  /* the weight-streaming kernel (M <= 16 only) */
+  NVFP4_ALGO_SIMPLE = 3   /* one output per thread, fp32 FMA (any shape) */
+} nvfp4_algo;
+
+/* nvfp4_gemm with an explicit kernel choice (tests and benchmarks). */
+nvfp4_status nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                           void* out_bf16, int64_t M, int64_t N, int64_t K, int algo, void* stream);
+
+/*
+ * Symmetric INT4 per-group quantization of a bf16 weight w [N, K], groups
+ * of `group` consecutive values along K (group == 128; K % 128 == 0).
+ * Passage: the symmetric formula of "Cuantización e inferencia local"
+ * (formula block) with b = 4 and one scale per group.
+ *   s16 = fp16_RNE( fl32(max|w_group| / 7) );
+ *   q   = clamp( rint_half_even( fl32(w / s16) ), -7, 7 ), 0 when s16 == 0.
+ * Outputs: q [N, K/2] two's-complement nibbles; scales_fp16 [N, K/group].
+ */
+nvfp4_status int4g_quantize(const void* w_bf16, int64_t N, int64_t K, int64_t group,
+                            uint8_t* q, void* scales_fp16, void* stream);
+
+/*
+ * W4A16: out[M, N] (bf16) = bf16_RNE( sum_g s16[n, g] * sum_{k in g}
+ * x[m, k] * q[n, k] ), x bf16 [M, K], q / scales as int4g_quantize writes
+ * them.  Passage: same formula block (x ~ s*q with a scale per group); the
+ * weight-only GPU kernels of the same page's method chart.  Each group's
+ * integer-weighted sum is taken in fp32, then scaled once by its s16.
+ * Any M >= 1: M <= 16 streams the weight once; larger M runs MFMA tiles.
+ */
+nvfp4_status int4g_gemv(const void* x_bf16, const uint8_t* q, const void* scales_fp16,
+                        void* out_bf16, int64_t M, int64_t N, int64_t K, int64_t group,
+                        void* stream);
+
+/* int4g_gemv with an explicit kernel choice (nvfp4_algo values). */
+nvfp4_status int4g_gemv_ex(const void* x_bf16, const uint8_t* q, const void* scales_fp16,
+                           void* out_bf16, int64_t M, int64_t N, int64_t K, int64_t group,
+                           int algo, void* stream);
+
+/* Static text of a status code. */
+const char* nvfp4_status_string(nvfp4_status s);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */

@@ -1,0 +1,189 @@
+"""Python binding of libnvfp4.so (C ABI in include/nvfp4.h).
+
+Argument marshalling only: every step of quantization and matmul runs in the
+library's HIP kernels.  Torch provides device memory and the current stream;
+nothing here computes on the data.  If the library is missing or the HIP
+runtime cannot load it, every call raises -- there is no CPU fallback.
+
+Function names follow the C ABI:
+
+* ``nvfp4_quantize(x)``               -> (codes, scales, global_scale)
+* ``nvfp4_gemm(a, w, algo=AUTO)``     -> bf16 [M, N]; a, w are the 3-tuples above
+* ``int4g_quantize(w, group=128)``    -> (q, scales_fp16)
+* ``int4g_gemv(x, q, scales, ...)``   -> bf16 [M, N]
+* ``nvfp4_linear(x, w)``              -> quantize x, then nvfp4_gemm (two calls)
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4.so")
+
+ALGO_AUTO, ALGO_TILED, ALGO_DECODE, ALGO_SIMPLE = 0, 1, 2, 3
+STATUS = {0: "NVFP4_OK", 1: "NVFP4_ERR_INVALID_ARG", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGNMENT",
+          4: "NVFP4_ERR_UNSUPPORTED", 5: "NVFP4_ERR_HIP"}
+
+# Every symbol include/nvfp4.h declares, with its ctypes signature.
+_P, _I64, _I, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, None
+SIGNATURES = {
+    "nvfp4_abi_version": ([], ctypes.c_int),
+    "nvfp4_quantize_workspace_bytes": ([], ctypes.c_size_t),
+    "nvfp4_quantize": ([_P, _I64, _I64, _P, _P, _P, _I, _P, _P], ctypes.c_int),
+    "nvfp4_gemm": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "nvfp4_gemm_ex": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P], ctypes.c_int),
+    "int4g_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "int4g_gemv": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
+    "int4g_gemv_ex": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P], ctypes.c_int),
+    "nvfp4_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "nvfp4_last_error": ([], ctypes.c_char_p),
+}
+
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib():
+    """The loaded library (ctypes.CDLL) with argument types set."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m quantized_gemm_nvfp4_amd.build` (or __graft_entry__.build())")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise Nvfp4Error(status, lib().nvfp4_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, shape, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda/hip) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def nvfp4_quantize(x, global_scale=None, out=None):
+    """NVFP4-quantize a bf16 [rows, cols] tensor (cols % 16 == 0).
+
+    global_scale: optional fp32 device tensor [1] to use instead of the
+    dynamic amax / 2688.  out: optional (codes, scales, global_scale) buffers.
+    Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/16],
+    global_scale fp32 [1]).
+    """
+    torch = _torch()
+    _need(x, torch.bfloat16, None, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+        g = global_scale if global_scale is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        codes, scales, g = out
+        if global_scale is not None and g is not global_scale:
+            raise ValueError("pass the given global scale as out[2]")
+    _need(codes, torch.uint8, (rows, cols // 2), "codes")
+    _need(scales, torch.uint8, (rows, cols // 16), "scales")
+    _need(g, torch.float32, (1,), "global_scale")
+    use_given = 1 if global_scale is not None else 0
+    ws = None
+    if not use_given:
+        ws = torch.empty(lib().nvfp4_quantize_workspace_bytes(), dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(g), use_given,
+                                _ptr(ws) if ws is not None else None, _stream(x)))
+    return codes, scales, g
+
+
+def nvfp4_gemm(a, w, algo=ALGO_AUTO, out=None):
+    """bf16 [M, N] = g_a g_w dequant(A) . dequant(W)^T.
+
+    a = (a_codes [M, K/2], a_scales [M, K/16], a_g [1]); w likewise with N rows.
+    """
+    torch = _torch()
+    ac, as_, ag = a
+    wc, ws, wg = w
+    M, N = ac.shape[0], wc.shape[0]
+    K = ac.shape[1] * 2
+    _need(ac, torch.uint8, (M, K // 2), "a_codes")
+    _need(as_, torch.uint8, (M, K // 16), "a_scales")
+    _need(ag, torch.float32, (1,), "a_gscale")
+    _need(wc, torch.uint8, (N, K // 2), "w_codes")
+    _need(ws, torch.uint8, (N, K // 16), "w_scales")
+    _need(wg, torch.float32, (1,), "w_gscale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=ac.device)
+    _need(out, torch.bfloat16, (M, N), "out")
+    _check(lib().nvfp4_gemm_ex(_ptr(ac), _ptr(as_), _ptr(ag), _ptr(wc), _ptr(ws), _ptr(wg), _ptr(out),
+                               M, N, K, int(algo), _stream(ac)))
+    return out
+
+
+def nvfp4_linear(x, w, algo=ALGO_AUTO):
+    """Dynamic activation quantization followed by the block-scaled GEMM."""
+    return nvfp4_gemm(nvfp4_quantize(x), w, algo=algo)
+
+
+def int4g_quantize(w, group=128, out=None):
+    """Symmetric INT4 per-group quantization of a bf16 [N, K] weight.
+    Returns (q uint8 [N, K/2], scales fp16 [N, K/group])."""
+    torch = _torch()
+    _need(w, torch.bfloat16, None, "w")
+    N, K = w.shape
+    if out is None:
+        q = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+        s = torch.empty((N, K // group if group else 0), dtype=torch.float16, device=w.device)
+    else:
+        q, s = out
+    _check(lib().int4g_quantize(_ptr(w), N, K, group, _ptr(q), _ptr(s), _stream(w)))
+    return q, s
+
+
+def int4g_gemv(x, q, scales, group=128, algo=ALGO_AUTO, out=None):
+    """W4A16: bf16 [M, N] = x . dequant(q, scales)^T."""
+    torch = _torch()
+    M, K = x.shape
+    N = q.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(q, torch.uint8, (N, K // 2), "q")
+    _need(scales, torch.float16, (N, K // group), "scales")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, (M, N), "out")
+    _check(lib().int4g_gemv_ex(_ptr(x), _ptr(q), _ptr(scales), _ptr(out), M, N, K, group, int(algo),
+                               _stream(x)))
+    return out

@@ -1,0 +1,250 @@
+// C ABI of libnvfp4.so (declared in include/nvfp4.h): argument validation,
+// kernel choice and error reporting.  Every check runs on the host before
+// any HIP call, so a rejected call enqueues nothing and touches no device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/nvfp4.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+nvfp4_status fail(nvfp4_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+nvfp4_status ok() {
+  g_last_error[0] = '\0';
+  return NVFP4_OK;
+}
+
+nvfp4_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  const void* p;
+  int64_t bytes;
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+// Checks that no output range overlaps any other listed range.
+nvfp4_status check_disjoint(const Range* outs, int nout, const Range* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j]))
+        return fail(NVFP4_ERR_INVALID_ARG, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(NVFP4_ERR_INVALID_ARG, "output %s overlaps output %s", outs[i].name, outs[j].name);
+  }
+  return NVFP4_OK;
+}
+
+constexpr int64_t kMaxDim = 0x7FFFFFFF;
+
+#define REQUIRE_PTR(p)                                                               \
+  do {                                                                               \
+    if ((p) == nullptr) return fail(NVFP4_ERR_INVALID_ARG, "%s is a null pointer", #p); \
+  } while (0)
+#define REQUIRE_ALIGN(p, a)                                                                  \
+  do {                                                                                       \
+    if (!aligned((p), (a))) return fail(NVFP4_ERR_ALIGNMENT, "%s is not %d-byte aligned", #p, (int)(a)); \
+  } while (0)
+
+nvfp4_status check_dims(int64_t a, const char* an, int64_t b, const char* bn, int64_t c, const char* cn) {
+  if (a < 0 || b < 0 || c < 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "negative size (%s=%lld, %s=%lld, %s=%lld)", an, (long long)a, bn,
+                (long long)b, cn, (long long)c);
+  if (a > kMaxDim || b > kMaxDim || c > kMaxDim)
+    return fail(NVFP4_ERR_UNSUPPORTED, "a dimension exceeds 2^31-1 (%s=%lld, %s=%lld, %s=%lld)", an,
+                (long long)a, bn, (long long)b, cn, (long long)c);
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return 1; }
+
+size_t nvfp4_quantize_workspace_bytes(void) { return sizeof(uint32_t) * nvfp4k::kAmaxPartials; }
+
+const char* nvfp4_status_string(nvfp4_status s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID_ARG: return "invalid argument";
+    case NVFP4_ERR_SHAPE: return "shape violates the format";
+    case NVFP4_ERR_ALIGNMENT: return "misaligned pointer";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported request";
+    case NVFP4_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* nvfp4_last_error(void) { return g_last_error; }
+
+nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                            float* global_scale, int use_given_global_scale, void* workspace, void* stream) {
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  REQUIRE_PTR(global_scale);
+  if (!use_given_global_scale) REQUIRE_PTR(workspace);
+  if (nvfp4_status s = check_dims(rows, "rows", cols, "cols", 0, "-")) return s;
+  if (cols % 16 != 0) return fail(NVFP4_ERR_SHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  if (rows > 0 && cols > INT64_MAX / 2 / rows) return fail(NVFP4_ERR_UNSUPPORTED, "rows*cols overflows");
+  REQUIRE_ALIGN(x_bf16, 16);
+  REQUIRE_ALIGN(codes, 16);
+  REQUIRE_ALIGN(scales, 16);
+  REQUIRE_ALIGN(global_scale, 4);
+  if (!use_given_global_scale) REQUIRE_ALIGN(workspace, 4);
+  const int64_t n = rows * cols;
+  const Range outs[3] = {{codes, n / 2, "codes"}, {scales, n / 16, "scales"}, {global_scale, 4, "global_scale"}};
+  const Range ins[2] = {{x_bf16, n * 2, "x"},
+                        {workspace, use_given_global_scale ? 0 : (int64_t)nvfp4_quantize_workspace_bytes(),
+                         "workspace"}};
+  if (n == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 3, ins, 2)) return s;
+  return hip_status(nvfp4k::launch_nvfp4_quantize(x_bf16, rows, cols, codes, scales, global_scale,
+                                                  use_given_global_scale, (uint32_t*)workspace,
+                                                  (hipStream_t)stream),
+                    "nvfp4_quantize launch");
+}
+
+nvfp4_status nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale, void* out_bf16,
+                           int64_t M, int64_t N, int64_t K, int algo, void* stream) {
+  if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
+  if (K > 0) {  // with K == 0 the packed operands are empty and never read
+    REQUIRE_PTR(a_codes);
+    REQUIRE_PTR(a_scales);
+    REQUIRE_PTR(w_codes);
+    REQUIRE_PTR(w_scales);
+  }
+  REQUIRE_PTR(a_gscale);
+  REQUIRE_PTR(w_gscale);
+  REQUIRE_PTR(out_bf16);
+  if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
+  if (algo < NVFP4_ALGO_AUTO || algo > NVFP4_ALGO_SIMPLE) return fail(NVFP4_ERR_INVALID_ARG, "unknown algo %d", algo);
+  REQUIRE_ALIGN(a_codes, 16);
+  REQUIRE_ALIGN(a_scales, 16);
+  REQUIRE_ALIGN(w_codes, 16);
+  REQUIRE_ALIGN(w_scales, 16);
+  REQUIRE_ALIGN(out_bf16, 16);
+  REQUIRE_ALIGN(a_gscale, 4);
+  REQUIRE_ALIGN(w_gscale, 4);
+  const Range outs[1] = {{out_bf16, M * N * 2, "out"}};
+  const Range ins[6] = {{a_codes, M * K / 2, "a_codes"}, {a_scales, M * K / 16, "a_scales"},
+                        {a_gscale, 4, "a_gscale"},       {w_codes, N * K / 2, "w_codes"},
+                        {w_scales, N * K / 16, "w_scales"}, {w_gscale, 4, "w_gscale"}};
+  if (M == 0 || N == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 1, ins, 6)) return s;
+  const bool k128 = (K % 128) == 0 && K > 0;
+  if (algo == NVFP4_ALGO_AUTO) algo = !k128 ? NVFP4_ALGO_SIMPLE : (M <= 16 ? NVFP4_ALGO_DECODE : NVFP4_ALGO_TILED);
+  hipStream_t st = (hipStream_t)stream;
+  switch (algo) {
+    case NVFP4_ALGO_TILED:
+      if (!k128) return fail(NVFP4_ERR_UNSUPPORTED, "tiled kernel needs K %% 128 == 0 and K > 0 (K=%lld)", (long long)K);
+      return hip_status(nvfp4k::launch_nvfp4_gemm_tiled(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale,
+                                                        out_bf16, M, N, K, st),
+                        "nvfp4_gemm tiled launch");
+    case NVFP4_ALGO_DECODE:
+      if (!k128 || M > 16)
+        return fail(NVFP4_ERR_UNSUPPORTED, "decode kernel needs M <= 16 and K %% 128 == 0 (M=%lld, K=%lld)",
+                    (long long)M, (long long)K);
+      return hip_status(nvfp4k::launch_nvfp4_gemm_decode(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale,
+                                                         out_bf16, M, N, K, st),
+                        "nvfp4_gemm decode launch");
+    default:
+      return hip_status(nvfp4k::launch_nvfp4_gemm_simple(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale,
+                                                         out_bf16, M, N, K, st),
+                        "nvfp4_gemm simple launch");
+  }
+}
+
+nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale, void* out_bf16,
+                        int64_t M, int64_t N, int64_t K, void* stream) {
+  return nvfp4_gemm_ex(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_bf16, M, N, K,
+                       NVFP4_ALGO_AUTO, stream);
+}
+
+nvfp4_status int4g_quantize(const void* w_bf16, int64_t N, int64_t K, int64_t group, uint8_t* q, void* scales_fp16,
+                            void* stream) {
+  REQUIRE_PTR(w_bf16);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(scales_fp16);
+  if (nvfp4_status s = check_dims(N, "N", K, "K", group, "group")) return s;
+  if (group != 128) return fail(NVFP4_ERR_UNSUPPORTED, "group=%lld; only 128 is supported", (long long)group);
+  if (K % 128 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of the group (128)", (long long)K);
+  REQUIRE_ALIGN(w_bf16, 16);
+  REQUIRE_ALIGN(q, 16);
+  REQUIRE_ALIGN(scales_fp16, 16);
+  const Range outs[2] = {{q, N * K / 2, "q"}, {scales_fp16, N * (K / 128) * 2, "scales"}};
+  const Range ins[1] = {{w_bf16, N * K * 2, "w"}};
+  if (N == 0 || K == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 2, ins, 1)) return s;
+  return hip_status(nvfp4k::launch_int4g_quantize(w_bf16, N, K, q, scales_fp16, (hipStream_t)stream),
+                    "int4g_quantize launch");
+}
+
+nvfp4_status int4g_gemv_ex(const void* x_bf16, const uint8_t* q, const void* scales_fp16, void* out_bf16, int64_t M,
+                           int64_t N, int64_t K, int64_t group, int algo, void* stream) {
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(scales_fp16);
+  REQUIRE_PTR(out_bf16);
+  if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
+  if (group != 128) return fail(NVFP4_ERR_UNSUPPORTED, "group=%lld; only 128 is supported", (long long)group);
+  if (K % 128 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of the group (128)", (long long)K);
+  if (algo < NVFP4_ALGO_AUTO || algo > NVFP4_ALGO_SIMPLE) return fail(NVFP4_ERR_INVALID_ARG, "unknown algo %d", algo);
+  REQUIRE_ALIGN(x_bf16, 16);
+  REQUIRE_ALIGN(q, 16);
+  REQUIRE_ALIGN(scales_fp16, 16);
+  REQUIRE_ALIGN(out_bf16, 16);
+  const Range outs[1] = {{out_bf16, M * N * 2, "out"}};
+  const Range ins[3] = {{x_bf16, M * K * 2, "x"}, {q, N * K / 2, "q"}, {scales_fp16, N * (K / 128) * 2, "scales"}};
+  if (M == 0 || N == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 1, ins, 3)) return s;
+  if (algo == NVFP4_ALGO_AUTO) algo = (K == 0) ? NVFP4_ALGO_SIMPLE : (M <= 16 ? NVFP4_ALGO_DECODE : NVFP4_ALGO_TILED);
+  hipStream_t st = (hipStream_t)stream;
+  switch (algo) {
+    case NVFP4_ALGO_TILED:
+      if (K == 0) return fail(NVFP4_ERR_UNSUPPORTED, "tiled kernel needs K > 0");
+      return hip_status(nvfp4k::launch_int4g_gemm_tiled(x_bf16, q, scales_fp16, out_bf16, M, N, K, st),
+                        "int4g_gemv tiled launch");
+    case NVFP4_ALGO_DECODE:
+      if (M > 16 || K == 0) return fail(NVFP4_ERR_UNSUPPORTED, "decode kernel needs M <= 16 and K > 0 (M=%lld)", (long long)M);
+      return hip_status(nvfp4k::launch_int4g_gemm_decode(x_bf16, q, scales_fp16, out_bf16, M, N, K, st),
+                        "int4g_gemv decode launch");
+    default:
+      return hip_status(nvfp4k::launch_int4g_gemm_simple(x_bf16, q, scales_fp16, out_bf16, M, N, K, st),
+                        "int4g_gemv simple launch");
+  }
+}
+
+nvfp4_status int4g_gemv(const void* x_bf16, const uint8_t* q, const void* scales_fp16, void* out_bf16, int64_t M,
+                        int64_t N, int64_t K, int64_t group, void* stream) {
+  return int4g_gemv_ex(x_bf16, q, scales_fp16, out_bf16, M, N, K, group, NVFP4_ALGO_AUTO, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+// Device helpers shared by the NVFP4 / INT4 kernels (gfx950, wave64).
+//
+// Number formats (pages cited by title and section):
+//  - "Tu pipeline NVFP4 ...", section 2: E2M1 elements (1 sign, 2 exponent,
+//    1 mantissa bit, largest magnitude 6), one FP8 E4M3 scale per 16 values.
+//  - "NVFP4 en difusión ...", section 2: the scale type is float8_e4m3fn
+//    (OCP "finite" variant: bias 7, largest finite 448, no infinities).
+//
+// The conversions below work on IEEE bit patterns: a round-to-nearest-even
+// to n mantissa bits is "add half an ulp minus one, plus the kept LSB, then
+// truncate", which also carries into the exponent when the mantissa
+// overflows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace nvfp4k {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef short short2v __attribute__((ext_vector_type(2)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 16;        // values per NVFP4 scale block
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; overflow -> inf).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// E4M3 (fn) byte of a non-negative fp32, RNE, saturating to 448 (0x7E)
+// above the largest finite value (and for +inf).
+__device__ __forceinline__ uint32_t e4m3_from_f32_sat(float v) {
+  if (!(v <= 448.0f)) return 0x7Eu;
+  if (v < 0.015625f) {                       // below 2^-6: quantum 2^-9
+    return (uint32_t)__builtin_rintf(v * 512.0f);   // 0..8; 8 is 2^-6
+  }
+  uint32_t b = __float_as_uint(v);
+  uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;   // exp8:3 | man3
+  return r - (120u << 3);                   // rebias 127 -> 7
+}
+
+// Value of a non-negative E4M3 byte (0x00..0x7E) as fp32, exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t e = c >> 3, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;          // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 magnitude code (0..7) of y >= 0, RNE with ties to the even code,
+// saturating at 6.  Below 1 the grid is the subnormal step 0.5, so the code
+// is rint(2y); from 1 up, E2M1 keeps one mantissa bit, so the fp32 pattern is
+// rounded to one mantissa bit and rebased from exponent bias 127 to 1.
+__device__ __forceinline__ uint32_t e2m1_code_from_f32(float y) {
+  if (y < 1.0f) return (uint32_t)__builtin_rintf(y * 2.0f);    // 0, 1, 2
+  uint32_t b = __float_as_uint(y);
+  uint32_t r = (b + 0x1FFFFFu + ((b >> 22) & 1u)) >> 22;        // exp8:1 | man1
+  r -= (126u << 1);
+  return r < 7u ? r : 7u;
+}
+
+// fp32 -> fp16 bits, RNE, gradual underflow, overflow -> inf.
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t sign = (u >> 16) & 0x8000u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x477FF000u) return sign | 0x7C00u;              // >= 65520
+  if (a < 0x38800000u) {                                     // below 2^-14
+    float t = __uint_as_float(a) * 16777216.0f;              // units of 2^-24
+    return sign | (uint32_t)__builtin_rintf(t);
+  }
+  uint32_t r = (a + 0xFFFu + ((a >> 13) & 1u)) >> 13;
+  return sign | (r - (112u << 10));
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  _Float16 x = __builtin_bit_cast(_Float16, (unsigned short)h);
+  return (float)x;
+}
+
+// Largest bf16 magnitude pattern among the two bf16 in a dword.
+__device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
+  uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+  return lo > hi ? lo : hi;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t t = __shfl_xor(v, o, 64);
+    v = v > t ? v : t;
+  }
+  return v;
+}
+
+// Two E2M1 codes of byte `sel` of `w` -> two fp16 (element 2j low nibble in
+// .x), exact.  The hardware conversion applies only the exponent of its fp32
+// scale operand; with 1.0 it is a plain decode.
+template <int sel>
+__device__ __forceinline__ half2v e2m1x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, sel);
+}
+
+// Dequantize the 8 E2M1 codes in dword `w` and multiply by the block scale
+// `s2` (the scale in both halves): every product has at most 6 significant
+// bits and lies in [2^-10, 2688], so it is exact in fp16.
+__device__ __forceinline__ half8v dequant8_f16(uint32_t w, half2v s2) {
+  half2v p0 = e2m1x2_to_f16<0>(w) * s2;
+  half2v p1 = e2m1x2_to_f16<1>(w) * s2;
+  half2v p2 = e2m1x2_to_f16<2>(w) * s2;
+  half2v p3 = e2m1x2_to_f16<3>(w) * s2;
+  return half8v{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// E4M3 byte -> fp16 scale in both halves (exact: E4M3 values are fp16 normals).
+__device__ __forceinline__ half2v e4m3_to_f16x2(uint32_t byte) {
+  float f = __builtin_amdgcn_cvt_f32_fp8(byte, 0);
+  _Float16 h = (_Float16)f;
+  return half2v{h, h};
+}
+
+// Signed INT4 nibble pair of byte `sel` -> two bf16 bit patterns in a dword
+// (exact: |q| <= 8).
+__device__ __forceinline__ uint32_t int4x2_to_bf16x2(uint32_t w, int sel) {
+  int lo = (int)(w << (28 - 8 * sel)) >> 28;
+  int hi = (int)(w << (24 - 8 * sel)) >> 28;
+  uint32_t blo = __float_as_uint((float)lo) >> 16;
+  uint32_t bhi = __float_as_uint((float)hi) & 0xFFFF0000u;
+  return bhi | blo;
+}
+
+}  // namespace nvfp4k

@@ -1,0 +1,279 @@
+// INT4 per-group W4A16 GEMM / GEMV for gfx950.
+//
+// out[m, n] = bf16_RNE( sum_g s16[n, g] * sum_{k in g} x[m, k] * q[n, k] ),
+// the symmetric per-group scheme of "Cuantización e inferencia local"
+// (formula block, b = 4, one fp16 scale per group of 128 along K).
+//
+// Exact decode of the weight on the matrix cores:
+//  - A two's-complement nibble u holds q in [-7, 7]; u ^ 8 = q + 8 in
+//    [1, 15].  An E4M3 byte 0x00..0x0F is exactly (its value) * 2^-9 (the
+//    subnormals continue linearly into the first normal binade), and
+//    v_cvt_scalef32_pk_bf16_fp8 with scale 2^9 (the instruction uses only the
+//    scale's exponent) returns q + 8 exactly as bf16.  Spreading 8 nibbles to
+//    bytes takes 5 integer ops, so the decode costs about one op per value.
+//  - The offset is removed with one more MFMA per step against a constant
+//    -8 operand: sum x (q + 8) + sum x (-8) = sum x q, both sides exact
+//    products, summed in fp32 (the offset is small, so the two sums do not
+//    cancel catastrophically).
+//  - Each 128-value group is accumulated in its own fp32 tile, then scaled
+//    once by its fp16 scale: q * s16 is not exact in bf16, so the scale is
+//    kept out of the MFMA operands.
+#include "common.h"
+#include "launch.h"
+
+namespace nvfp4k {
+
+namespace {
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(1))) void* gbl_void_t;
+
+// 8 int4 codes (dword w, element 2j in the low nibble of byte j) -> 8 bf16
+// values q + 8 in element order.
+__device__ __forceinline__ short8v int4x8_offset_bf16(uint32_t w) {
+  const uint32_t t = w ^ 0x88888888u;
+  const uint32_t ev = t & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
+  const uint32_t od = (t >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+  const uint32_t lo = __builtin_amdgcn_perm(od, ev, 0x05010400u);   // e0 e1 e2 e3
+  const uint32_t hi = __builtin_amdgcn_perm(od, ev, 0x07030602u);   // e4 e5 e6 e7
+  const bf16x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false);
+  const bf16x2v p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true);
+  const bf16x2v p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false);
+  const bf16x2v p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true);
+  const short2v s0 = __builtin_bit_cast(short2v, p0), s1 = __builtin_bit_cast(short2v, p1);
+  const short2v s2 = __builtin_bit_cast(short2v, p2), s3 = __builtin_bit_cast(short2v, p3);
+  return short8v{s0.x, s0.y, s1.x, s1.y, s2.x, s2.y, s3.x, s3.y};
+}
+
+constexpr short kMinus8Bf16 = (short)0xC100;    // -8.0 in bf16
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+__device__ __forceinline__ short8v as_short8(const uint4& v) { return __builtin_bit_cast(short8v, v); }
+}  // namespace
+
+// ---- M <= 16: stream the weight once -------------------------------------
+// One workgroup per 16 weight rows; 4 waves split the 128-value groups
+// (group g goes to wave g % 4).  v_mfma_f32_16x16x32_bf16 with x as the first
+// operand (rows m, padded to 16) and the weight as the second (columns n), so
+// each lane's accumulators share one column n and one group scale.
+__global__ __launch_bounds__(256) void int4g_gemm_decode_kernel(const uint16_t* __restrict__ x,
+                                                                const uint8_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ s,
+                                                                uint16_t* __restrict__ out, int M, int N, int K) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int r = lane & 15, grp = lane >> 4;
+  const int ng = K / 128;
+  const int nrow = min(n0 + r, N - 1);
+  const uint8_t* qrow = q + (int64_t)nrow * (K / 2) + 16 * grp;
+  const uint16_t* srow = s + (int64_t)nrow * ng;
+  const bool x_on = r < M;
+  const uint16_t* xrow = x + (int64_t)(x_on ? r : 0) * K + 32 * grp;
+  const short8v c8 = {kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16,
+                      kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16};
+
+  float4v acc = {0.f, 0.f, 0.f, 0.f};
+  for (int g = wave; g < ng; g += 4) {
+    const uint4 wq = *(const uint4*)(qrow + (int64_t)g * 64);
+    const float sc = f16_bits_to_f32(srow[g]);
+    uint4 xv[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      xv[jj] = x_on ? *(const uint4*)(xrow + (int64_t)g * 128 + 8 * jj) : make_uint4(0, 0, 0, 0);
+    float4v tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const short8v xa = as_short8(xv[jj]);
+      tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, int4x8_offset_bf16(word_of(wq, jj)), tmp, 0, 0, 0);
+      tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, c8, tmp, 0, 0, 0);
+    }
+    acc += sc * tmp;
+  }
+
+  __shared__ float4v red[4][64];
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  const float4v sum = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+  // D[m][n] (16 x 16): lane n + 16 (m / 4), register m % 4.
+  const int n = n0 + (lane & 15);
+  if (n >= N) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * (lane >> 4) + i;
+    if (m < M) out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(sum[i]);
+  }
+}
+
+// ---- any M: LDS-staged MFMA tiles -----------------------------------------
+// Workgroup tile 128 (m) x 256 (n), K stage = one 128-value group; 4 waves of
+// 64 x 128 (2 x 4 tiles of 32 x 32).  x fragments are stored in LDS in lane
+// order (one 1 KB region per MFMA step), the packed weight as in the NVFP4
+// kernel; both are copied with global_load_lds (16-byte transfers, which
+// land at lane * 16 in LDS).  Per group: tmp tiles start
+// from zero, collect 8 steps, and are added to the accumulators times the
+// lane's column scale.
+namespace {
+constexpr int IT_M = 128, IT_N = 256, IT_K = 128;
+constexpr int kXBytes = IT_M * IT_K * 2;        // 32 KB
+constexpr int kQBytes = IT_N * IT_K / 2;        // 16 KB
+constexpr int kIStage = kXBytes + kQBytes;
+constexpr int kISmem = 2 * kIStage;
+}  // namespace
+
+__global__ __launch_bounds__(256, 1) void int4g_gemm_tiled_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint8_t* __restrict__ q,
+                                                                  const uint16_t* __restrict__ s,
+                                                                  uint16_t* __restrict__ out, int M, int N, int K,
+                                                                  int tiles_m, int tiles_n) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // XCD-aware order: each XCD gets a contiguous run of tiles, n fastest.
+  const int total = tiles_m * tiles_n;
+  int id = blockIdx.x;
+  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+  const int tile_m = id / tiles_n, tile_n = id % tiles_n;
+  const int m0 = tile_m * IT_M, n0 = tile_n * IT_N;
+  const int ng = K / 128;
+
+  // x: 4 fragments x 8 steps; wave w copies steps 2w, 2w+1 of every fragment.
+  // Lane l of region (f, jj): row 32f + l%32, values 64(l/32) + 8jj .. +8.
+  const uint16_t* gx[8];
+  int lds_x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int f = i >> 1, jj = 2 * wave + (i & 1);
+    const int row = min(m0 + 32 * f + (lane & 31), M - 1);
+    gx[i] = x + (int64_t)row * K + 64 * (lane >> 5) + 8 * jj;
+    lds_x[i] = (f * 8 + jj) * 1024;
+  }
+  const uint8_t* gq[4];
+  int lds_q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qd = 4 * wave + i, f = qd >> 1, hs = qd & 1;
+    const int row = min(n0 + 32 * f + (lane & 31), N - 1);
+    gq[i] = q + (int64_t)row * (K / 2) + 32 * (lane >> 5) + 16 * hs;
+    lds_q[i] = kXBytes + qd * 1024;
+  }
+  // Group scales of this lane's 4 output columns, read straight from global
+  // memory one group ahead (they are 1/64 of the weight bytes).
+  const uint16_t* gsc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) gsc[j] = s + (int64_t)min(n0 + 128 * (wave & 1) + 32 * j + (lane & 31), N - 1) * ng;
+
+  auto issue = [&](int g, int buf) {
+    uint8_t* base = smem + buf * kIStage;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void_t)(gx[i] + (int64_t)g * 128), (lds_void_t)(base + lds_x[i]), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void_t)(gq[i] + (int64_t)g * 64), (lds_void_t)(base + lds_q[i]), 16, 0, 0);
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+  const short8v c8 = {kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16,
+                      kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16};
+  float16v acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = float16v{};
+
+  uint32_t sc_next[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sc_next[j] = gsc[j][0];
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int g = 0; g < ng; ++g) {
+    const int buf = g & 1;
+    float sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc[j] = f16_bits_to_f32(sc_next[j]);
+    if (g + 1 < ng) {
+      issue(g + 1, buf ^ 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc_next[j] = gsc[j][g + 1];
+    }
+    const uint8_t* base = smem + buf * kIStage;
+    uint4 cq[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+        cq[j][hs] = *(const uint4*)(base + kXBytes + ((4 * wn + j) * 2 + hs) * 1024 + lane * 16);
+    float16v tmp[2][4], corr[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      corr[i] = float16v{};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tmp[i][j] = float16v{};
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      short8v xa[2], wb[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) xa[i] = as_short8(*(const uint4*)(base + ((2 * wm + i) * 8 + jj) * 1024 + lane * 16));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wb[j] = int4x8_offset_bf16(word_of(cq[j][jj >> 2], jj & 3));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], c8, corr[i], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          tmp[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], wb[j], tmp[i][j], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += sc[j] * (tmp[i][j] + corr[i]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // D[m][n] of each 32 x 32 tile: lane n + 32((m/4)%2), register (m%4) + 4(m/8).
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 128 * wn + 32 * j + r32;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int m = m0 + 64 * wm + 32 * i + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        if (m < M) out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(acc[i][j][rr]);
+      }
+    }
+  }
+}
+
+hipError_t launch_int4g_gemm_decode(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,
+                                    int64_t N, int64_t K, hipStream_t stream) {
+  hipLaunchKernelGGL(int4g_gemm_decode_kernel, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream,
+                     (const uint16_t*)x, q, (const uint16_t*)s, (uint16_t*)out, (int)M, (int)N, (int)K);
+  return hipGetLastError();
+}
+
+hipError_t launch_int4g_gemm_tiled(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,
+                                   int64_t N, int64_t K, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)int4g_gemm_tiled_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kISmem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles_m = (int)((M + IT_M - 1) / IT_M), tiles_n = (int)((N + IT_N - 1) / IT_N);
+  hipLaunchKernelGGL(int4g_gemm_tiled_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), kISmem, stream,
+                     (const uint16_t*)x, q, (const uint16_t*)s, (uint16_t*)out, (int)M, (int)N, (int)K, tiles_m,
+                     tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4k

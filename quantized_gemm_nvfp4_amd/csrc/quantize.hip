@@ -1,0 +1,179 @@
+// NVFP4 and INT4 per-group quantization kernels for gfx950.
+//
+// NVFP4 ("Tu pipeline NVFP4 ...", section 2; "NVFP4 en difusión ...",
+// section 2): each 16-value block along a row gets an E4M3 scale chosen from
+// the block's largest magnitude, each value an E2M1 code, two codes per
+// byte.  A per-tensor fp32 scale g = amax / (6 * 448) sits above the block
+// scales.  The activation is quantized on every call, so g is computed on
+// the device and never read back by the host.
+//
+// Two passes: (1) a grid of at most kAmaxPartials workgroups writes the
+// largest bf16 magnitude each one saw (the max is order-independent, so the
+// result is exact and deterministic); (2) every workgroup of the quantize
+// kernel reduces those partials itself, derives g, and quantizes one 16-value
+// block per thread.  No atomics, no memset, no host sync.
+//
+// INT4 ("Cuantización e inferencia local", formula block, b = 4): per row
+// and group of 128 values, s = max|w| / 7 stored as fp16, q = clamp(rint(w /
+// s), -7, 7) stored as two's-complement nibbles.
+#include "common.h"
+#include "launch.h"
+
+namespace nvfp4k {
+
+// ---- pass 1: partial maxima of |x| over a bf16 tensor ---------------------
+// x is read as 16-byte vectors (8 bf16); n_vec = elements / 8.
+__global__ __launch_bounds__(256) void amax_partial_kernel(const uint4* __restrict__ x, int64_t n_vec,
+                                                           uint32_t* __restrict__ partial) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n_vec; i += 4 * stride) {
+    uint4 v0 = x[i], v1 = x[i + stride], v2 = x[i + 2 * stride], v3 = x[i + 3 * stride];
+    uint32_t a = bf16x2_absmax_bits(v0.x), b = bf16x2_absmax_bits(v0.y);
+    a = max(a, bf16x2_absmax_bits(v0.z)); b = max(b, bf16x2_absmax_bits(v0.w));
+    a = max(a, bf16x2_absmax_bits(v1.x)); b = max(b, bf16x2_absmax_bits(v1.y));
+    a = max(a, bf16x2_absmax_bits(v1.z)); b = max(b, bf16x2_absmax_bits(v1.w));
+    a = max(a, bf16x2_absmax_bits(v2.x)); b = max(b, bf16x2_absmax_bits(v2.y));
+    a = max(a, bf16x2_absmax_bits(v2.z)); b = max(b, bf16x2_absmax_bits(v2.w));
+    a = max(a, bf16x2_absmax_bits(v3.x)); b = max(b, bf16x2_absmax_bits(v3.y));
+    a = max(a, bf16x2_absmax_bits(v3.z)); b = max(b, bf16x2_absmax_bits(v3.w));
+    m = max(m, max(a, b));
+  }
+  for (; i < n_vec; i += stride) {
+    uint4 v = x[i];
+    m = max(m, max(max(bf16x2_absmax_bits(v.x), bf16x2_absmax_bits(v.y)),
+                   max(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w))));
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t red[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// ---- pass 2: one 16-value block per thread ---------------------------------
+// x: bf16 [nblocks * 16]; codes: 8 bytes per block; scales: 1 byte per block.
+__global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restrict__ x, int64_t nblocks,
+                                                          uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                          float* __restrict__ gscale,
+                                                          const uint32_t* __restrict__ partial, int npartial,
+                                                          int use_given) {
+  __shared__ float s_g;
+  if (threadIdx.x < 64) {
+    float g;
+    if (use_given) {
+      g = *gscale;
+    } else {
+      uint32_t m = 0;
+      for (int i = threadIdx.x; i < npartial; i += 64) m = max(m, partial[i]);
+      m = wave_max_u32(m);
+      g = bf16_bits_to_f32(m) / 2688.0f;               // amax / (6 * 448)
+      if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = g;
+    }
+    if (threadIdx.x == 0) s_g = g;
+  }
+  __syncthreads();
+  const float g = s_g;
+
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
+    const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t amax_bits = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, bf16x2_absmax_bits(w[i]));
+    const float amax_b = bf16_bits_to_f32(amax_bits);
+    const float s_raw = (g == 0.0f) ? 0.0f : (amax_b / 6.0f) / g;
+    const uint32_t sc = e4m3_from_f32_sat(s_raw);
+    const float d = e4m3_to_f32(sc) * g;
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = w[i] & 0xFFFFu, hi = w[i] >> 16;
+      const float ylo = (d != 0.0f) ? bf16_bits_to_f32(lo & 0x7FFFu) / d : 0.0f;
+      const float yhi = (d != 0.0f) ? bf16_bits_to_f32(hi & 0x7FFFu) / d : 0.0f;
+      const uint32_t clo = e2m1_code_from_f32(ylo) | ((lo >> 12) & 8u);
+      const uint32_t chi = e2m1_code_from_f32(yhi) | ((hi >> 12) & 8u);
+      packed[i >> 2] |= (clo | (chi << 4)) << (8 * (i & 3));
+    }
+    codes[b] = make_uint2(packed[0], packed[1]);
+    scales[b] = (uint8_t)sc;
+  }
+}
+
+// ---- INT4 per-group (128) quantization ------------------------------------
+// 16 lanes per group, 8 values (16 bytes) per lane; a wave covers 4 groups.
+__global__ __launch_bounds__(256) void int4g_quant_kernel(const uint4* __restrict__ w, int64_t ngroups,
+                                                          uint32_t* __restrict__ q,
+                                                          uint16_t* __restrict__ scales) {
+  const int64_t gthreads = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < ngroups * 16;
+       t += gthreads) {
+    // t / 16 is the group; every lane of a 16-lane group runs the same trip
+    // count (blockDim and the grid stride are multiples of 16), so the
+    // shuffles below see full groups.
+    const uint4 v = w[t];
+    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t m = max(max(bf16x2_absmax_bits(x[0]), bf16x2_absmax_bits(x[1])),
+                     max(bf16x2_absmax_bits(x[2]), bf16x2_absmax_bits(x[3])));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      uint32_t u = __shfl_xor(m, o, 16);
+      m = max(m, u);
+    }
+    const float s32 = bf16_bits_to_f32(m) / 7.0f;
+    const uint32_t s16 = f32_to_f16_rne(s32);
+    const float s = f16_bits_to_f32(s16);
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = (x[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      int qi = 0;
+      if (s != 0.0f) {
+        float y = __builtin_rintf(bf16_bits_to_f32(h) / s);
+        y = y > 7.0f ? 7.0f : (y < -7.0f ? -7.0f : y);
+        qi = (int)y;
+      }
+      out |= ((uint32_t)qi & 0xFu) << (4 * i);
+    }
+    q[t] = out;
+    if ((t & 15) == 0) scales[t >> 4] = (uint16_t)s16;
+  }
+}
+
+// ---- launchers -------------------------------------------------------------
+hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                 float* gscale, int use_given, uint32_t* workspace, hipStream_t stream) {
+  const int64_t n = rows * cols;
+  const int64_t nblocks = n / kBlock;
+  int npartial = 0;
+  if (!use_given) {
+    const int64_t n_vec = n / 8;
+    int64_t grid = (n_vec + 255) / 256;
+    if (grid > kAmaxPartials) grid = kAmaxPartials;
+    npartial = (int)grid;
+    hipLaunchKernelGGL(amax_partial_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint4*)x, n_vec, workspace);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  int64_t grid = (nblocks + 255) / 256;
+  if (grid > 2048) grid = 2048;
+  hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint4*)x, nblocks,
+                     (uint2*)codes, scales, gscale, (const uint32_t*)workspace, npartial, use_given);
+  return hipGetLastError();
+}
+
+hipError_t launch_int4g_quantize(const void* w, int64_t N, int64_t K, uint8_t* q, void* scales,
+                                 hipStream_t stream) {
+  const int64_t ngroups = N * (K / 128);
+  int64_t grid = (ngroups * 16 + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(int4g_quant_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint4*)w, ngroups,
+                     (uint32_t*)q, (uint16_t*)scales);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4k

@@ -1,0 +1,127 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device.
+
+The pointers passed here are never dereferenced: validation runs on the host
+before any HIP call, so fake (but suitably aligned) addresses are safe."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_gemm_nvfp4_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+OK, INVALID, SHAPE, ALIGN, UNSUP = 0, 1, 2, 3, 4
+P = ctypes.c_void_p
+A = P(0x10000)      # fake, 16-byte aligned, distinct addresses
+B = P(0x20000)
+C = P(0x30000)
+D = P(0x40000)
+E = P(0x50000)
+F = P(0x60000)
+G = P(0x70000)
+ODD = P(0x10008)    # 8-byte aligned only
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z0-9_]+)\s*\(", text)) - {"defined"})
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert "nvfp4_quantize" in names and "nvfp4_gemm" in names and "int4g_gemv" in names
+    lib = q.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in nvfp4.h but not exported"
+    assert set(names) == set(q.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_version_and_strings():
+    lib = q.lib()
+    assert lib.nvfp4_abi_version() == 1
+    assert lib.nvfp4_quantize_workspace_bytes() == 4096
+    assert lib.nvfp4_status_string(0) == b"ok"
+    assert lib.nvfp4_status_string(3) == b"misaligned pointer"
+
+
+def _err():
+    return q.lib().nvfp4_last_error().decode()
+
+
+def test_quantize_validation():
+    lib = q.lib()
+    f = lib.nvfp4_quantize
+    assert f(None, 4, 32, B, C, D, 0, E, None) == INVALID and "x_bf16" in _err()
+    assert f(A, 4, 32, B, C, D, 0, None, None) == INVALID and "workspace" in _err()
+    assert f(A, -1, 32, B, C, D, 0, E, None) == INVALID
+    assert f(A, 4, 24, B, C, D, 0, E, None) == SHAPE and "16" in _err()
+    assert f(ODD, 4, 32, B, C, D, 0, E, None) == ALIGN
+    assert f(A, 4, 32, ODD, C, D, 0, E, None) == ALIGN
+    assert f(A, 4, 32, A, C, D, 0, E, None) == INVALID and "overlap" in _err()
+    assert f(A, 4, 32, B, B, D, 0, E, None) == INVALID and "overlap" in _err()
+    assert f(A, 1 << 40, 32, B, C, D, 0, E, None) == UNSUP
+    # empty tensors: nothing to do, nothing enqueued
+    assert f(A, 0, 32, B, C, D, 0, E, None) == OK
+    assert f(A, 5, 0, B, C, D, 0, E, None) == OK
+    assert _err() == ""
+    # a given global scale needs no workspace
+    assert f(A, 0, 32, B, C, D, 1, None, None) == OK
+
+
+def test_gemm_validation():
+    f = q.lib().nvfp4_gemm_ex
+    good = [A, B, C, D, E, F, G]
+    assert f(*good, 32, 64, 120, 0, None) == SHAPE                 # K % 16
+    assert f(*good, -3, 64, 128, 0, None) == INVALID
+    assert f(None, *good[1:], 32, 64, 128, 0, None) == INVALID
+    assert f(A, B, C, D, E, F, A, 32, 64, 128, 0, None) == INVALID  # out aliases a_codes
+    assert f(A, B, C, D, E, F, ODD, 32, 64, 128, 0, None) == ALIGN
+    assert f(A, B, P(0x30002), D, E, F, G, 32, 64, 128, 0, None) == ALIGN   # gscale 4-byte
+    assert f(*good, 32, 64, 128, 9, None) == INVALID                # unknown algo
+    assert f(*good, 32, 64, 144, q.ALGO_TILED, None) == UNSUP       # tiled needs K % 128
+    assert f(*good, 17, 64, 128, q.ALGO_DECODE, None) == UNSUP      # decode needs M <= 16
+    assert f(*good, 0, 64, 128, 0, None) == OK
+    assert f(*good, 32, 0, 128, 0, None) == OK
+    assert q.lib().nvfp4_gemm(*good, 32, 64, 120, None) == SHAPE
+
+
+def test_int4_validation():
+    lib = q.lib()
+    assert lib.int4g_quantize(A, 8, 256, 64, B, C, None) == UNSUP      # group must be 128
+    assert lib.int4g_quantize(A, 8, 192, 128, B, C, None) == SHAPE     # K % group
+    assert lib.int4g_quantize(A, 8, 256, 128, A, C, None) == INVALID   # q aliases w
+    assert lib.int4g_quantize(A, 0, 256, 128, B, C, None) == OK
+    g = lib.int4g_gemv_ex
+    assert g(A, B, C, D, 4, 8, 256, 32, 0, None) == UNSUP
+    assert g(A, B, C, D, 4, 8, 200, 128, 0, None) == SHAPE
+    assert g(A, B, C, D, 17, 8, 256, 128, q.ALGO_DECODE, None) == UNSUP
+    assert g(A, B, C, ODD, 4, 8, 256, 128, 0, None) == ALIGN
+    assert g(A, B, C, D, 0, 8, 256, 128, 0, None) == OK
+    assert lib.int4g_gemv(A, B, C, D, 4, 8, 256, 64, None) == UNSUP
+
+
+def test_error_text_is_thread_local():
+    import threading
+    lib = q.lib()
+    assert lib.nvfp4_quantize(A, 4, 24, B, C, D, 0, E, None) == SHAPE
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.nvfp4_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "16" in _err()
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        q.nvfp4_quantize(torch.zeros((2, 32), dtype=torch.bfloat16))

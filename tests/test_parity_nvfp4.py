@@ -1,0 +1,208 @@
+"""GPU parity of nvfp4_quantize and nvfp4_gemm against the CPU oracle.
+
+Codes, scales and the global scale must match byte for byte; GEMM outputs
+must satisfy rel-L2 <= 1e-3 and per-row max-abs <= 2e-2 * max|row| against
+the oracle's fp64 result rounded to bf16.  Full-size configurations compare
+sampled output rows (the oracle evaluates the same definition on those rows
+only); codes are compared in full."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import formats as F
+from oracle import metrics as Mx
+from oracle import nvfp4 as O
+from tests.gpu_util import Guarded, dev_bf16, host_bits, host_u8, log, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = {"tiled": 1, "decode": 2, "simple": 3}
+
+
+def _q():
+    need_gpu()
+    import quantized_gemm_nvfp4_amd as q
+    return q
+
+
+def gpu_quantize(bits, g=None):
+    q = _q()
+    import torch
+    x = dev_bf16(bits)
+    R, C = bits.shape
+    codes = Guarded((R, C // 2), torch.uint8)
+    scales = Guarded((R, C // 16), torch.uint8)
+    gt = torch.tensor([g], dtype=torch.float32, device="cuda:0") if g is not None else None
+    out_g = gt if gt is not None else torch.empty(1, dtype=torch.float32, device="cuda:0")
+    q.nvfp4_quantize(x, global_scale=gt, out=(codes.t, scales.t, out_g))
+    torch.cuda.synchronize()
+    assert codes.intact() and scales.intact(), "quantize wrote outside its outputs"
+    return codes.t, scales.t, out_g
+
+
+def assert_quant_equal(bits, g=None, label=""):
+    c, s, gg = gpu_quantize(bits, g)
+    oc, os_, og = O.quantize(bits, g=g)
+    gc, gs, ggv = host_u8(c), host_u8(s), np.float32(gg.cpu().numpy()[0])
+    assert ggv.view(np.uint32) == np.float32(og).view(np.uint32), f"{label}: global scale {ggv} != {og}"
+    bad_s = np.argwhere(gs != os_)
+    assert bad_s.size == 0, f"{label}: {len(bad_s)} scale bytes differ, first at {bad_s[0]}"
+    bad_c = np.argwhere(gc != oc)
+    assert bad_c.size == 0, f"{label}: {len(bad_c)} code bytes differ, first at {bad_c[0]}"
+    return c, s, gg
+
+
+# ------------------------------------------------------------------ quantize
+def test_quantize_worked_row(golden):
+    g = golden("nvfp4_worked_row.txt")
+    vals = np.array([float(v) for v in g["values"]], dtype=np.float32)[None, :]
+    bits = F.bf16_bits(vals)
+    c, s, gg = assert_quant_equal(bits, label="worked row")
+    assert [int(h, 16) for h in g["codes_hex"]] == list(host_u8(c)[0])
+
+
+@pytest.mark.parametrize("seed,shape,kw", [
+    (1, (1, 16), {}),
+    (2, (3, 48), {}),
+    (3, (37, 272), dict(sigma=0.02, outlier_frac=0.01, outlier_mul=50)),
+    (4, (129, 1040), dict(zero_frac=0.2)),
+    (5, (64, 4096), dict(sigma=1e-3, outlier_frac=0.001, outlier_mul=1e4)),   # subnormal E4M3 scales
+    (6, (7, 160), dict(sigma=1e-36)),                                            # denormal fp32 g
+    (7, (2, 2000 * 16), dict(sigma=3e4)),
+])
+def test_quantize_random(seed, shape, kw):
+    log(f"quantize seed={seed} shape={shape}")
+    assert_quant_equal(workloads.random_bf16(seed, shape, **kw), label=f"seed {seed}")
+
+
+def test_quantize_degenerate():
+    z = np.zeros((4, 64), np.uint16)
+    z[1, 3] = 0x8000                                   # -0.0
+    assert_quant_equal(z, label="all zero")
+    one = np.zeros((3, 32), np.uint16)
+    one[2, 31] = F.bf16_bits(np.float32([-2.5]))[0]
+    assert_quant_equal(one, label="single value")
+
+
+def test_quantize_given_global_scale():
+    bits = workloads.random_bf16(8, (33, 128))
+    for g in (1.0, 0.003, 1e-30, 0.0):
+        assert_quant_equal(bits, g=g, label=f"given g={g}")
+
+
+def test_quantize_full_size_tensors():
+    x_up, w_up, w_down = workloads.prefill()
+    for name, bits in [("prefill x_up", x_up), ("decode/prefill W_up", w_up), ("prefill W_down", w_down),
+                       ("decode x", workloads.decode_x()[0]), ("dit x_0", workloads.dit_x(0))]:
+        log(f"quantize full {name} {bits.shape}")
+        assert_quant_equal(bits, label=name)
+
+
+def test_quantize_deterministic():
+    bits = workloads.random_bf16(9, (300, 512))
+    a = gpu_quantize(bits)
+    b = gpu_quantize(bits)
+    for u, v in zip(a, b):
+        assert bool((u == v).all())
+
+
+# ---------------------------------------------------------------------- gemm
+def gpu_gemm(a, w, algo=0):
+    q = _q()
+    import torch
+    M, N = a[0].shape[0], w[0].shape[0]
+    out = Guarded((M, N), torch.bfloat16)
+    q.nvfp4_gemm(a, w, algo=algo, out=out.t)
+    torch.cuda.synchronize()
+    assert out.intact(), "gemm wrote outside its output"
+    return F.bf16_from_bits(host_bits(out.t)).astype(np.float64)
+
+
+def check_gemm(a_bits, w_bits, algos=(0,), rows=None, label=""):
+    a = assert_quant_equal(a_bits, label=label + " A")
+    w = assert_quant_equal(w_bits, label=label + " W")
+    oa, ow = O.quantize(a_bits), O.quantize(w_bits)
+    ref = O.gemm_rows(*oa, *ow, rows) if rows is not None else O.gemm(*oa, *ow)
+    for algo in algos:
+        y = gpu_gemm(a, w, algo)
+        ys = y[rows] if rows is not None else y
+        ok, rl, rr = Mx.check_output(ys, ref)
+        log(f"{label} algo={algo}: rel_l2={rl:.3e} row_ratio={rr:.3e}")
+        assert ok, f"{label} algo={algo}: rel_l2={rl:.3e} row_ratio={rr:.3e}"
+    return a, w
+
+
+def test_gemm_tiny_config_all_kernels():
+    a_bits, w_bits = workloads.tiny()
+    check_gemm(a_bits, w_bits, algos=(0, 1, 2, 3), label="tiny 16x256x256")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 1, 128), (5, 37, 256), (16, 300, 384), (17, 33, 128), (100, 250, 640),
+    (257, 513, 1024), (300, 260, 128 * 9), (64, 16, 2048)])
+def test_gemm_ragged_tiled_and_simple(M, N, K):
+    a_bits = workloads.random_bf16(M * 7 + 1, (M, K))
+    w_bits = workloads.random_bf16(N * 11 + 2, (N, K), sigma=0.02, outlier_frac=0.005, outlier_mul=20)
+    algos = (0, 1, 3) + ((2,) if M <= 16 else ())
+    check_gemm(a_bits, w_bits, algos=algos, label=f"ragged {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("K", [16, 48, 80, 272])
+def test_gemm_k_not_multiple_of_128_uses_simple(K):
+    a_bits = workloads.random_bf16(K + 3, (9, K))
+    w_bits = workloads.random_bf16(K + 4, (21, K), sigma=0.02)
+    check_gemm(a_bits, w_bits, algos=(0, 3), label=f"K={K}")
+
+
+def test_gemm_decode_config():
+    x_bits, _ = workloads.decode_x()
+    w_bits = workloads.decode_w()
+    for M in (1, 4, 16):
+        check_gemm(x_bits[:M], w_bits, algos=(0,), label=f"decode M={M}")
+
+
+def test_gemm_prefill_config_chained():
+    x_up, w_up, w_down = workloads.prefill()
+    rows = np.random.default_rng(0).choice(4096, 48, replace=False)
+    rows.sort()
+    q = _q()
+    a, w = check_gemm(x_up, w_up, algos=(0,), rows=rows, label="prefill up")
+    # teacher-forced: the down projection quantizes the GPU's own up output
+    h = q.nvfp4_gemm(a, w)
+    h_bits = host_bits(h)
+    check_gemm(h_bits, w_down, algos=(0,), rows=rows, label="prefill down")
+
+
+def test_gemm_dit_config_one_step():
+    wq, wu, wd = workloads.dit_weights()
+    x = workloads.dit_x(0)
+    rows = np.random.default_rng(1).choice(4096, 48, replace=False)
+    q = _q()
+    check_gemm(x, wq, rows=rows, label="dit qkv")
+    a, w = check_gemm(x, wu, rows=rows, label="dit up")
+    h_bits = host_bits(q.nvfp4_gemm(a, w))
+    check_gemm(h_bits, wd, rows=rows, label="dit down")
+
+
+def test_gemm_deterministic():
+    a_bits = workloads.random_bf16(61, (512, 1024))
+    w_bits = workloads.random_bf16(62, (768, 1024), sigma=0.02)
+    a, w = gpu_quantize(a_bits), gpu_quantize(w_bits)
+    for algo in (1, 3):
+        y1, y2 = gpu_gemm(a, w, algo), gpu_gemm(a, w, algo)
+        assert np.array_equal(y1, y2)
+    d1, d2 = gpu_gemm((a[0][:16], a[1][:16], a[2]), w, 2), gpu_gemm((a[0][:16], a[1][:16], a[2]), w, 2)
+    assert np.array_equal(d1, d2)
+
+
+def test_gemm_zero_k_writes_zeros():
+    q = _q()
+    import torch
+    a = (torch.empty((3, 0), dtype=torch.uint8, device="cuda:0"), torch.empty((3, 0), dtype=torch.uint8, device="cuda:0"),
+         torch.ones(1, device="cuda:0"))
+    w = (torch.empty((5, 0), dtype=torch.uint8, device="cuda:0"), torch.empty((5, 0), dtype=torch.uint8, device="cuda:0"),
+         torch.ones(1, device="cuda:0"))
+    out = torch.full((3, 5), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    q.nvfp4_gemm(a, w, out=out)
+    torch.cuda.synchronize()
+    assert bool((out == 0).all())
