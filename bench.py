@@ -1,0 +1,397 @@
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+One step = the prefill chain on the M = 4096 dense-decoder MLP:
+    quantize x_up [4096, 5376]  ->  GEMM up   (x W_up^T,   W_up   [21504, 5376])
+    quantize h    [4096, 21504] ->  GEMM down (h W_down^T, W_down [5376, 21504])
+with dynamic per-call activation quantization (the weights are quantized once,
+before timing).  `value` is 2 * (M*N*K for both GEMMs) / step time, in TFLOP/s,
+activation quantization included.
+
+The same run also measures, on their own timed loops, the decode GEMV at
+M = 1 (GB/s of algorithmic bytes, rotating 16 weight copies so every call
+misses the 256 MB last-level cache), the DiT linear stack over 4 steps, and
+the INT4 per-group W4A16 path (M = 1 and 16 in GB/s, M = 2048 in TFLOP/s).
+
+`roofline` reports the tiled GEMM kernel: algorithmic FLOPs per launch over
+its average launch time, measured with events on the launch stream inside
+the timed region, against the fp16/bf16 dense MFMA peak (2.5 PFLOP/s).
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+                       [--no-cpu-baseline] [--copy-calibration]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 GEMM TFLOP/s incl. act quant (M=4096) + decode GB/s (M=1); % roofline"
+PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_tiled_prefill.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def dev_bf16(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+
+
+class Timer:
+    """Events on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def ms(self):
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm_tiled.hip", "common.h"):
+        with open(os.path.join(ROOT, "quantized_gemm_nvfp4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per tiled-GEMM launch from committed rocprofv3 counters, or
+    None if they were taken on a different version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def run_prefill(torch, q, steps, warmup):
+    import workloads
+    x_bits, wu_bits, wd_bits = workloads.prefill()
+    M, N1, K1 = 4096, 21504, 5376
+    N2, K2 = 5376, 21504
+    x = dev_bf16(torch, x_bits)
+    wu = q.nvfp4_quantize(dev_bf16(torch, wu_bits))
+    wd = q.nvfp4_quantize(dev_bf16(torch, wd_bits))
+    # preallocated buffers: the step allocates nothing
+    a1 = (torch.empty((M, K1 // 2), dtype=torch.uint8, device="cuda:0"),
+          torch.empty((M, K1 // 16), dtype=torch.uint8, device="cuda:0"),
+          torch.empty(1, dtype=torch.float32, device="cuda:0"))
+    a2 = (torch.empty((M, K2 // 2), dtype=torch.uint8, device="cuda:0"),
+          torch.empty((M, K2 // 16), dtype=torch.uint8, device="cuda:0"),
+          torch.empty(1, dtype=torch.float32, device="cuda:0"))
+    h = torch.empty((M, N1), dtype=torch.bfloat16, device="cuda:0")
+    y = torch.empty((M, N2), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.empty(q.lib().nvfp4_quantize_workspace_bytes(), dtype=torch.uint8, device="cuda:0")
+    del x_bits
+
+    lib = q.lib()
+    stream = q._stream(x)
+    P = q._ptr
+
+    def quant(inp, a):
+        q._check(lib.nvfp4_quantize(P(inp), inp.shape[0], inp.shape[1], P(a[0]), P(a[1]), P(a[2]), 0, P(ws), stream))
+
+    def gemm(a, w, out):
+        q._check(lib.nvfp4_gemm_ex(P(a[0]), P(a[1]), P(a[2]), P(w[0]), P(w[1]), P(w[2]), P(out),
+                                   out.shape[0], out.shape[1], a[0].shape[1] * 2, q.ALGO_TILED, stream))
+
+    gemm_timer = Timer(torch)
+    quant_timer = Timer(torch)
+
+    def step(timed):
+        t = quant_timer.start() if timed else None
+        quant(x, a1)
+        if timed:
+            quant_timer.stop(t)
+            t = gemm_timer.start()
+        gemm(a1, wu, h)
+        if timed:
+            gemm_timer.stop(t)
+            t = quant_timer.start()
+        quant(h, a2)
+        if timed:
+            quant_timer.stop(t)
+            t = gemm_timer.start()
+        gemm(a2, wd, y)
+        if timed:
+            gemm_timer.stop(t)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(True)
+        if (i + 1) % max(1, steps // 4) == 0:
+            log(f"prefill step {i + 1}/{steps} enqueued")
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    flops = 2.0 * M * N1 * K1 + 2.0 * M * N2 * K2
+    gemm_ms = gemm_timer.ms()
+    quant_ms = quant_timer.ms()
+    gemm_avg = float(np.mean(gemm_ms))
+    return {
+        "ms_per_step": ms_step,
+        "tflops": flops / (ms_step * 1e-3) / 1e12,
+        "gemm_avg_ms": gemm_avg,
+        "gemm_flops_per_launch": 2.0 * M * N1 * K1,
+        "gemm_tflops": (2.0 * M * N1 * K1) / (gemm_avg * 1e-3) / 1e12,
+        "quant_avg_ms": float(np.mean(quant_ms)),
+        "gemm_ms_up_down": [float(np.mean(gemm_ms[0::2])), float(np.mean(gemm_ms[1::2]))],
+        "quant_ms_x_h": [float(np.mean(quant_ms[0::2])), float(np.mean(quant_ms[1::2]))],
+    }
+
+
+def run_decode(torch, q, iters=200, copies=16):
+    """M = 1 decode on the 21504 x 5376 weight; GB/s of algorithmic bytes."""
+    import workloads
+    x_bits, _ = workloads.decode_x()
+    w = q.nvfp4_quantize(dev_bf16(torch, workloads.decode_w()))
+    ws = [(w[0].clone(), w[1].clone(), w[2].clone()) for _ in range(copies)]   # ~1.04 GB rotated
+    N, K = 21504, 5376
+    out = {}
+    for M in (1, 4, 16):
+        x = dev_bf16(torch, x_bits[:M])
+        a = q.nvfp4_quantize(x)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+        alg_bytes = N * K // 2 + N * K // 16 + 4 + M * K // 2 + M * K // 16 + 4 + M * N * 2
+        for i in range(20):
+            q.nvfp4_gemm(a, ws[i % copies], out=y)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(iters):
+            q.nvfp4_gemm(a, ws[i % copies], out=y)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / iters
+        # including the per-call activation quantization
+        t0.record()
+        for i in range(iters):
+            q.nvfp4_quantize(x, out=a)
+            q.nvfp4_gemm(a, ws[i % copies], out=y)
+        t1.record()
+        torch.cuda.synchronize()
+        us_q = t0.elapsed_time(t1) * 1e3 / iters
+        out[f"M{M}"] = {"us": us, "GBps": alg_bytes / (us * 1e-6) / 1e9,
+                        "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                        "us_incl_act_quant": us_q, "alg_bytes": alg_bytes}
+        log(f"decode M={M}: {us:.2f} us, {out[f'M{M}']['GBps']:.0f} GB/s")
+    del ws
+    return out
+
+
+def run_dit(torch, q, reps=3):
+    """4 denoising steps x (qkv, up, down) with fresh activations; TFLOP/s incl. act quant."""
+    import workloads
+    wq, wu, wd = [q.nvfp4_quantize(dev_bf16(torch, b)) for b in workloads.dit_weights()]
+    xs = [dev_bf16(torch, workloads.dit_x(t)) for t in range(4)]
+    flops = 4 * 2.0 * 4096 * 3072 * (9216 + 12288 + 12288)
+
+    def run():
+        for t in range(4):
+            a = q.nvfp4_quantize(xs[t])
+            q.nvfp4_gemm(a, wq)
+            hh = q.nvfp4_gemm(a, wu)
+            q.nvfp4_gemm(q.nvfp4_quantize(hh), wd)
+
+    run()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    log(f"dit 4 steps: {ms:.3f} ms")
+    return {"ms_4_steps": ms, "tflops": flops / (ms * 1e-3) / 1e12}
+
+
+def run_int4(torch, q, iters=100, copies=8):
+    import workloads
+    w_bits = workloads.int4_w()
+    x_bits = workloads.int4_x()
+    N, K = 28672, 8192
+    qq, ss = q.int4g_quantize(dev_bf16(torch, w_bits))
+    del w_bits
+    rot = [(qq.clone(), ss.clone()) for _ in range(copies)]      # ~0.97 GB rotated
+    out = {}
+    for M in (1, 16):
+        x = dev_bf16(torch, x_bits[:M])
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+        alg_bytes = N * K // 2 + N * (K // 128) * 2 + M * K * 2 + M * N * 2
+        for i in range(10):
+            q.int4g_gemv(x, *rot[i % copies], out=y)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(iters):
+            q.int4g_gemv(x, *rot[i % copies], out=y)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / iters
+        out[f"M{M}"] = {"us": us, "GBps": alg_bytes / (us * 1e-6) / 1e9,
+                        "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+        log(f"int4 M={M}: {us:.2f} us, {out[f'M{M}']['GBps']:.0f} GB/s")
+    x = dev_bf16(torch, x_bits)
+    y = torch.empty((2048, N), dtype=torch.bfloat16, device="cuda:0")
+    q.int4g_gemv(x, qq, ss, out=y)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(5):
+        q.int4g_gemv(x, qq, ss, out=y)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / 5
+    out["M2048"] = {"ms": ms, "tflops": 2.0 * 2048 * N * K / (ms * 1e-3) / 1e12}
+    log(f"int4 M=2048: {ms:.3f} ms")
+    return out
+
+
+def run_copy_calibration(torch, nbytes=1 << 30):
+    """A plain device copy of known size, for scaling rocprofv3 byte counters."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 copies of {nbytes} bytes")
+
+
+def cpu_baseline(rows=256):
+    """The CPU oracle on a bounded sample of the prefill workload: quantize a
+    row sample of x_up (global scale over the whole tensor, as the method
+    defines it) and evaluate the up-projection GEMM for those rows in fp64."""
+    import threadpoolctl
+    import workloads
+    from oracle import nvfp4 as O
+    x_bits, wu_bits, _ = workloads.prefill()
+    wq = O.quantize(wu_bits)                      # offline weight quantization, not timed
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    sample = np.asarray(x_bits[:rows])
+    g = O.global_scale(x_bits)
+    t0 = time.perf_counter()
+    a = O.quantize(sample, g=g)
+    O.gemm(*a, *wq)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * 21504 * 5376
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} of 4096 rows of the up projection (quantize + fp64 GEMM incl. weight decode), "
+                      f"{dt:.1f} s", "seconds": dt,
+            "cpu": _cpu_model(), "host_cores": len(os.sched_getaffinity(0))}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true", help="only the prefill step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a "
+              f"single GPU; see the sharding notes in the design document)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_gemm_nvfp4_amd as q
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    q.lib()
+    log(f"device {torch.cuda.get_device_name(0)}")
+
+    pre = run_prefill(torch, q, args.steps, args.warmup)
+    log(f"prefill: {pre['ms_per_step']:.3f} ms/step, {pre['tflops']:.1f} TFLOP/s incl. act quant; "
+        f"tiled GEMM {pre['gemm_avg_ms']:.3f} ms ({pre['gemm_tflops']:.1f} TFLOP/s)")
+    extras = {}
+    if not args.no_extras:
+        extras["decode"] = run_decode(torch, q)
+        extras["dit"] = run_dit(torch, q)
+        extras["int4"] = run_int4(torch, q)
+    if args.copy_calibration:
+        run_copy_calibration(torch)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline()
+        log(f"cpu baseline: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    achieved = pre["gemm_tflops"]
+    line = {
+        "metric": METRIC,
+        "value": round(pre["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "prefill MLP M=4096: quantize x[4096,5376] + NVFP4 GEMM vs W_up[21504,5376], "
+                               "quantize h[4096,21504] + NVFP4 GEMM vs W_down[5376,21504]",
+                   "M": 4096, "N_up": 21504, "K_up": 5376, "N_down": 5376, "K_down": 21504,
+                   "format": "E2M1 codes, E4M3 scale per 16, fp32 per-tensor scale"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": load_traffic(), "kernel": "nvfp4_gemm_tiled_kernel",
+                     "avg_launch_ms": round(pre["gemm_avg_ms"], 4)},
+        "cpu_baseline": cpu,
+        "prefill": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in pre.items()},
+    }
+    if extras:
+        d1 = extras["decode"]["M1"]
+        line["decode_m1"] = {"value": round(d1["GBps"], 1), "unit": "GB/s", "frac_hbm": round(d1["frac_hbm"], 4),
+                             "us": round(d1["us"], 2), "us_incl_act_quant": round(d1["us_incl_act_quant"], 2)}
+        line["extras"] = extras
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
