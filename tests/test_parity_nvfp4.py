@@ -206,3 +206,21 @@ def test_gemm_zero_k_writes_zeros():
     q.nvfp4_gemm(a, w, out=out)
     torch.cuda.synchronize()
     assert bool((out == 0).all())
+
+
+def test_gemm_subnormal_and_zero_scales():
+    """Rows spanning 2^-25 in magnitude give subnormal and zero E4M3 block
+    scales next to normal ones, in both operands."""
+    rng = np.random.default_rng(71)
+    a = rng.standard_normal((40, 512)).astype(np.float32)
+    a *= (2.0 ** -np.arange(40, dtype=np.float32) * 0.7)[:, None]
+    w = rng.standard_normal((72, 512)).astype(np.float32) * 0.02
+    w *= (2.0 ** -(np.arange(72, dtype=np.float32) % 25))[:, None]
+    w[5, 100] = 3.0
+    a_bits = F.bf16_bits(F.bf16_round(a).astype(np.float32))
+    w_bits = F.bf16_bits(F.bf16_round(w).astype(np.float32))
+    oa, ow = O.quantize(a_bits), O.quantize(w_bits)
+    sub = lambda s: np.count_nonzero((s > 0) & (s < 8))
+    assert sub(oa[1]) > 0 and sub(ow[1]) > 0, "case must contain subnormal scales"
+    check_gemm(a_bits, w_bits, algos=(0, 1, 2, 3) if a_bits.shape[0] <= 16 else (0, 1, 3), label="subnormal scales")
+    check_gemm(a_bits[:16], w_bits, algos=(2,), label="subnormal scales decode")
