@@ -169,12 +169,41 @@ def run_prefill(torch, q, steps, warmup):
     }
 
 
-def run_decode(torch, q, iters=200, copies=16):
-    """M = 1 decode on the 21504 x 5376 weight; GB/s of algorithmic bytes."""
+def graph_time_us(torch, fn, iters, reps=5):
+    """Per-call GPU time of `fn(i)` for i in range(iters), captured once into
+    a HIP graph (so host launch overhead does not pace the GPU) and replayed
+    `reps` times between events."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / (reps * iters)
+
+
+def run_decode(torch, q, iters=64, copies=16):
+    """Decode on the 21504 x 5376 weight at M = 1, 4, 16; GB/s of algorithmic
+    bytes.  16 weight copies (~1.04 GB) are rotated so every call misses the
+    256 MB last-level cache; calls are replayed from a HIP graph."""
     import workloads
     x_bits, _ = workloads.decode_x()
     w = q.nvfp4_quantize(dev_bf16(torch, workloads.decode_w()))
-    ws = [(w[0].clone(), w[1].clone(), w[2].clone()) for _ in range(copies)]   # ~1.04 GB rotated
+    ws = [(w[0].clone(), w[1].clone(), w[2].clone()) for _ in range(copies)]
     N, K = 21504, 5376
     out = {}
     for M in (1, 4, 16):
@@ -182,29 +211,18 @@ def run_decode(torch, q, iters=200, copies=16):
         a = q.nvfp4_quantize(x)
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
         alg_bytes = N * K // 2 + N * K // 16 + 4 + M * K // 2 + M * K // 16 + 4 + M * N * 2
-        for i in range(20):
-            q.nvfp4_gemm(a, ws[i % copies], out=y)
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for i in range(iters):
-            q.nvfp4_gemm(a, ws[i % copies], out=y)
-        t1.record()
-        torch.cuda.synchronize()
-        us = t0.elapsed_time(t1) * 1e3 / iters
-        # including the per-call activation quantization
-        t0.record()
-        for i in range(iters):
+        ref = q.nvfp4_gemm(a, ws[(iters - 1) % copies]).clone()
+        us = graph_time_us(torch, lambda i: q.nvfp4_gemm(a, ws[i % copies], out=y), iters)
+        assert torch.equal(y, ref), "graph replay differs from the eager call"
+
+        def with_quant(i):
             q.nvfp4_quantize(x, out=a)
             q.nvfp4_gemm(a, ws[i % copies], out=y)
-        t1.record()
-        torch.cuda.synchronize()
-        us_q = t0.elapsed_time(t1) * 1e3 / iters
+        us_q = graph_time_us(torch, with_quant, iters)
         out[f"M{M}"] = {"us": us, "GBps": alg_bytes / (us * 1e-6) / 1e9,
                         "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                         "us_incl_act_quant": us_q, "alg_bytes": alg_bytes}
-        log(f"decode M={M}: {us:.2f} us, {out[f'M{M}']['GBps']:.0f} GB/s")
+        log(f"decode M={M}: {us:.2f} us, {out[f'M{M}']['GBps']:.0f} GB/s; incl. act quant {us_q:.2f} us")
     del ws
     return out
 
@@ -237,7 +255,7 @@ def run_dit(torch, q, reps=3):
     return {"ms_4_steps": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
-def run_int4(torch, q, iters=100, copies=8):
+def run_int4(torch, q, iters=64, copies=8):
     import workloads
     w_bits = workloads.int4_w()
     x_bits = workloads.int4_x()
@@ -250,17 +268,9 @@ def run_int4(torch, q, iters=100, copies=8):
         x = dev_bf16(torch, x_bits[:M])
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
         alg_bytes = N * K // 2 + N * (K // 128) * 2 + M * K * 2 + M * N * 2
-        for i in range(10):
-            q.int4g_gemv(x, *rot[i % copies], out=y)
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for i in range(iters):
-            q.int4g_gemv(x, *rot[i % copies], out=y)
-        t1.record()
-        torch.cuda.synchronize()
-        us = t0.elapsed_time(t1) * 1e3 / iters
+        ref = q.int4g_gemv(x, *rot[(iters - 1) % copies]).clone()
+        us = graph_time_us(torch, lambda i: q.int4g_gemv(x, *rot[i % copies], out=y), iters)
+        assert torch.equal(y, ref), "graph replay differs from the eager call"
         out[f"M{M}"] = {"us": us, "GBps": alg_bytes / (us * 1e-6) / 1e9,
                         "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
         log(f"int4 M={M}: {us:.2f} us, {out[f'M{M}']['GBps']:.0f} GB/s")
@@ -332,6 +342,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the prefill step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--only", choices=["decode", "dit", "int4"], help="time only this extra workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a "
@@ -344,6 +355,10 @@ def main():
     q.lib()
     log(f"device {torch.cuda.get_device_name(0)}")
 
+    if args.only:
+        res = {"decode": run_decode, "dit": run_dit, "int4": run_int4}[args.only](torch, q)
+        print(json.dumps({"only": args.only, "result": res}))
+        return
     pre = run_prefill(torch, q, args.steps, args.warmup)
     log(f"prefill: {pre['ms_per_step']:.3f} ms/step, {pre['tflops']:.1f} TFLOP/s incl. act quant; "
         f"tiled GEMM {pre['gemm_avg_ms']:.3f} ms ({pre['gemm_tflops']:.1f} TFLOP/s)")
