@@ -130,6 +130,26 @@ __device__ __forceinline__ half2v e4m3_to_f16x2(uint32_t byte) {
   return half2v{h, h};
 }
 
+// Two E4M3 scale bytes (low half of `pair`) -> fp16 in both halves, each
+// equal to the scale times 2^-8, exact: the E4M3 bit pattern shifted left by
+// 7 is an fp16 pattern with the same mantissa and exponent bits, and the bias
+// difference (15 - 7) divides by 2^8 (subnormal scales included).
+__device__ __forceinline__ half2v e4m3x2_to_f16x2_div256(uint32_t pair) {
+  const uint32_t spread = __builtin_amdgcn_perm(0u, pair, 0x0C010C00u);   // [b0, 0, b1, 0]
+  return __builtin_bit_cast(half2v, spread << 7);
+}
+
+// Eight E2M1 codes of `w` times a block scale given as scale * 2^-8 (see
+// e4m3x2_to_f16x2_div256): the conversion multiplies by 2^8 (a power of two,
+// applied exactly), so every product equals code value * scale exactly.
+__device__ __forceinline__ half8v dequant8_f16_div256(uint32_t w, half2v s2) {
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s2;
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s2;
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s2;
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * s2;
+  return half8v{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
 // Signed INT4 nibble pair of byte `sel` -> two bf16 bit patterns in a dword
 // (exact: |q| <= 8).
 __device__ __forceinline__ uint32_t int4x2_to_bf16x2(uint32_t w, int sel) {

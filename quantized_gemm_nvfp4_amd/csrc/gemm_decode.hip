@@ -3,44 +3,175 @@
 // Same product as the tiled kernel (the block-scaled matmul of "NVFP4 en
 // difusión ...", section 2), shaped for the bandwidth-bound case: decode
 // moves the whole packed weight once per call and does 2*M flops per weight,
-// so the kernel's job is to stream W at HBM speed and keep the decoding
-// (one VALU op per weight value) off the critical path.
+// so the kernels' job is to stream W at HBM speed and to keep the decoding
+// (about one VALU op per weight value: the E2M1 conversion and the block
+// scale multiply, two values per instruction each) from becoming the limit.
 //
-//  - One workgroup per 16 weight rows; its 4 waves split K in 128-value
-//    chunks (chunk c goes to wave c % 4) and are summed in LDS in a fixed
-//    order, so results are deterministic.
-//  - Per chunk a lane loads 16 bytes of codes (32 values) of one W row and
-//    the 2 scale bytes of those values; each wave issues four chunks' loads
-//    before decoding any of them.
-//  - v_mfma_f32_16x16x32_f16 with W as the first operand: M <= 16 is padded
-//    to the MFMA's 16 columns; the decoded fp16 operands are exact, as in the
-//    tiled kernel.
-//  - The activation operand: for M <= 2 the workgroup decodes the whole
-//    activation once into LDS as fp16 (at most 2 x K x 2 bytes) and lanes of
-//    rows >= M feed zeros, so per chunk only W is decoded.  For larger M each
-//    wave decodes its chunk of the activation codes next to W's (the cost is
-//    then shared by M useful columns).
+// Two kernels:
+//  - row-slot GEMV (M <= 2): W is read in storage order, one contiguous
+//    1 KB per load instruction; the MFMA reduces along each lane's own data
+//    (diagonal trick below).
+//  - row-block GEMM (M <= 16): 16 rows of W per workgroup, the activation
+//    rows in the MFMA's columns; each load instruction reads 64 bytes of 16
+//    rows, which HBM serves less efficiently, but M useful columns per MFMA.
 #include "common.h"
 #include "launch.h"
 
 namespace nvfp4k {
 
 namespace {
-constexpr int kBatch = 4;            // chunks in flight per wave
-constexpr int kLdsActRows = 2;       // activation rows decoded into LDS
-constexpr int kLdsActMaxK = 16384;   // K limit of the LDS activation (64 KB)
+constexpr int kBatch = 4;                       // row-block kernel: chunks in flight per wave
+constexpr uint32_t kOob = 0x80000000u;          // an offset past every buffer's end
+constexpr int kRawBufferWord3 = 0x00020000;     // raw (untyped) buffer, gfx9 encoding
+constexpr int kCachePolicyNT = 2;               // streamed once: non-temporal
+constexpr int kMaxSlots = 16;                   // row-slot kernel: K <= 16 * 2048
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+
+template <int kAux = 0>
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int kAux = 0>
+__device__ __forceinline__ uint32_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kAux);
+}
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 }  // namespace
 
-template <bool kActInLds>
-__global__ __launch_bounds__(256) void nvfp4_gemm_decode_kernel(
+// ---------------------------------------------------------------------------
+// Row-slot GEMV (M <= 2).
+//
+// A row of W is cut into 1 KB slots (2048 values); wave s of a workgroup owns
+// slot s of each of the workgroup's kR consecutive rows, so every load
+// instruction reads 1 KB of contiguous memory and a workgroup reads kR whole
+// rows (one contiguous region).  HBM serves this pattern markedly faster than
+// 16 rows x 64 bytes per instruction.
+//
+// The product still runs on v_mfma_f32_16x16x32_f16 although the MFMA's row
+// structure does not match the load pattern: lane L = i + 16 g feeds A with
+// 8 of the W values at its own slot position and B with the activation values
+// at the same position, so D[i][i] = sum over g of <W(i + 16 g), x(i + 16 g)>:
+// the diagonal holds the slot's dot product in 16 pieces.  Each (row,
+// activation row) pair has its own accumulator and only its diagonal is read;
+// the matrix cores do 16x the useful work, which at M <= 2 still leaves them
+// mostly idle.
+//
+// All of a wave's loads (its activation slot, then its slot of each of the
+// kR rows) are issued before any decoding; the activation slot is decoded
+// once into registers.  Block scales are converted with the exact 2^-8 bit
+// trick of e4m3x2_to_f16x2_div256 (the E2M1 conversion multiplies by 2^8).
+template <int kM, int kR>
+__global__ __launch_bounds__(1024) void nvfp4_gemv_rowslot_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
     uint16_t* __restrict__ out, int M, int N, int K) {
-  extern __shared__ __attribute__((aligned(16))) _Float16 s_act[];   // [M][K] fp16 when kActInLds
+  extern __shared__ __attribute__((aligned(16))) float4v s_diag[];   // [slots][kR][kM][16]
+  const int lane = threadIdx.x & 63;
+  const int slot = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nslots = blockDim.x >> 6;
+  const uint32_t row_bytes = (uint32_t)K / 2, row_scales = (uint32_t)K / 16;
+  const int n0 = blockIdx.x * kR;
+  const uint32_t nrows = (uint32_t)min(kR, N - n0);
+  const auto wr = buffer_of(w_codes + (int64_t)n0 * row_bytes, nrows * row_bytes);
+  const auto wsr = buffer_of(w_scales + (int64_t)n0 * row_scales, nrows * row_scales);
+  const auto ar = buffer_of(a_codes, (uint32_t)M * row_bytes);      // rows >= M read as zero
+  const auto asr = buffer_of(a_scales, (uint32_t)M * row_scales);
+
+  // This lane's 32 values of a row: 16 code bytes and 2 scale bytes.
+  const uint32_t off = 1024u * slot + 16u * lane;
+  const bool in = off < row_bytes;
+  const uint32_t coff = in ? off : kOob;
+  const uint32_t soff = in ? 128u * slot + 2u * lane : kOob;
+  uint4 xc[kM];
+  uint32_t xs[kM];
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    xc[m] = load16(ar, coff + m * row_bytes);
+    xs[m] = load2(asr, soff + m * row_scales);
+  }
+  uint4 wc[kR];
+  uint32_t ws[kR];
+#pragma unroll
+  for (int rho = 0; rho < kR; ++rho) {
+    wc[rho] = load16<kCachePolicyNT>(wr, coff + rho * row_bytes);
+    ws[rho] = load2<kCachePolicyNT>(wsr, soff + rho * row_scales);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  half8v xv[kM][4];
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    const half2v s = e4m3x2_to_f16x2_div256(xs[m]);
+    const half2v s0 = {s.x, s.x}, s1 = {s.y, s.y};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) xv[m][jj] = dequant8_f16_div256(word_of(xc[m], jj), jj < 2 ? s0 : s1);
+  }
+  float4v acc[kR][kM];
+#pragma unroll
+  for (int rho = 0; rho < kR; ++rho) {
+    const half2v s = e4m3x2_to_f16x2_div256(ws[rho]);
+    const half2v s0 = {s.x, s.x}, s1 = {s.y, s.y};
+#pragma unroll
+    for (int m = 0; m < kM; ++m) acc[rho][m] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const half8v wv = dequant8_f16_div256(word_of(wc[rho], jj), jj < 2 ? s0 : s1);
+#pragma unroll
+      for (int m = 0; m < kM; ++m)
+        acc[rho][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, xv[m][jj], acc[rho][m], 0, 0, 0);
+    }
+  }
+
+  // D[i][i] sits at lane i + 16 (i / 4), register i % 4: those 16 lanes store
+  // their whole float4 and the reduction picks component i % 4.
+  const int i = lane & 15;
+  if ((i >> 2) == (lane >> 4)) {
+#pragma unroll
+    for (int rho = 0; rho < kR; ++rho)
+#pragma unroll
+      for (int m = 0; m < kM; ++m) s_diag[((slot * kR + rho) * kM + m) * 16 + i] = acc[rho][m];
+  }
+  __syncthreads();
+  // Thread t < 16 kR kM: output (rho, m) = t / 16, diagonal entry t % 16;
+  // the slots are summed in order, then the 16 entries by a fixed butterfly.
+  const int t = threadIdx.x;
+  if (t >= 16 * kR * kM) return;
+  const int pair = t >> 4, ii = t & 15;
+  float v = 0.f;
+  for (int w = 0; w < nslots; ++w) v += s_diag[(w * kR * kM + pair) * 16 + ii][ii & 3];
+  v += __shfl_xor(v, 1, 16);
+  v += __shfl_xor(v, 2, 16);
+  v += __shfl_xor(v, 4, 16);
+  v += __shfl_xor(v, 8, 16);
+  const int rho = pair / kM, m = pair % kM;
+  if (ii == 0 && m < M && n0 + rho < N)
+    out[(int64_t)m * N + n0 + rho] = (uint16_t)f32_to_bf16_rne(v * ((*a_g) * (*w_g)));
+}
+
+// ---------------------------------------------------------------------------
+// Row-block GEMM (M <= 16).
+//
+//  - One workgroup per 16 weight rows; its 4 waves split K in 128-value
+//    chunks (chunk c goes to wave c % 4) and are summed in LDS in a fixed
+//    order, so results are deterministic.
+//  - Per chunk a lane loads 16 bytes of codes (32 values) of one W row and
+//    the 2 scale bytes of those values, and the same for one activation row;
+//    each wave issues kBatch chunks' loads before decoding any of them.
+//  - v_mfma_f32_16x16x32_f16 with W as the first operand: M <= 16 is padded
+//    to the MFMA's 16 columns (lanes of rows >= M feed zeros); the decoded
+//    fp16 operands are exact, as in the tiled kernel.
+__global__ __launch_bounds__(256) void nvfp4_gemm_rowblock_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
+    uint16_t* __restrict__ out, int M, int N, int K) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16;
   const int r = lane & 15, grp = lane >> 4;
@@ -52,23 +183,7 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_decode_kernel(
   const uint8_t* asrow = a_scales + (int64_t)(a_on ? r : 0) * row_scales + 2 * grp;
   const int nchunks = K / 128;
 
-  if (kActInLds) {
-    // Decode the activation (M <= 2 rows) once: one 16-value block per
-    // thread and iteration, written as 16 fp16 at [m][16 b].
-    const int nblk = M * (K / 16);
-    for (int b = threadIdx.x; b < nblk; b += 256) {
-      const int m = b / (K / 16), kb = b - m * (K / 16);
-      const uint2 c2 = *(const uint2*)(a_codes + (int64_t)m * row_bytes + 8 * kb);
-      const half2v s2 = e4m3_to_f16x2(a_scales[(int64_t)m * row_scales + kb]);
-      half8v* dst = (half8v*)(s_act + (int64_t)m * K + 16 * kb);
-      dst[0] = dequant8_f16(c2.x, s2);
-      dst[1] = dequant8_f16(c2.y, s2);
-    }
-    __syncthreads();
-  }
-
   float4v acc = {0.f, 0.f, 0.f, 0.f};
-  const half8v zero8 = {};
   for (int c0 = wave; c0 < nchunks; c0 += 4 * kBatch) {
     uint4 wc[kBatch], ac[kBatch];
     uint32_t ws[kBatch], as[kBatch];
@@ -82,7 +197,7 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_decode_kernel(
       if (c < nchunks) {
         wc[u] = *(const uint4*)(wrow + (int64_t)c * 64);
         ws[u] = *(const uint16_t*)(wsrow + (int64_t)c * 8);
-        if (!kActInLds && a_on) {
+        if (a_on) {
           ac[u] = *(const uint4*)(arow + (int64_t)c * 64);
           as[u] = *(const uint16_t*)(asrow + (int64_t)c * 8);
         }
@@ -100,12 +215,7 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_decode_kernel(
         for (int t = 0; t < 2; ++t) {
           const int jj = 2 * blk + t;
           const half8v wv = dequant8_f16(word_of(wc[u], jj), sw2);
-          half8v av;
-          if (kActInLds) {
-            av = a_on ? *(const half8v*)(s_act + (int64_t)r * K + 128 * c + 32 * grp + 8 * jj) : zero8;
-          } else {
-            av = dequant8_f16(word_of(ac[u], jj), sa2);
-          }
+          const half8v av = dequant8_f16(word_of(ac[u], jj), sa2);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, av, acc, 0, 0, 0);
         }
       }
@@ -135,17 +245,28 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_decode_kernel(
   }
 }
 
+namespace {
+template <int kM, int kR>
+void launch_rowslot(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc, const uint8_t* ws,
+                    const float* wg, void* out, int M, int N, int K, hipStream_t stream) {
+  const int nslots = (K / 2 + 1023) / 1024;
+  const size_t lds = (size_t)nslots * kR * kM * 16 * sizeof(float4v);
+  hipLaunchKernelGGL((nvfp4_gemv_rowslot_kernel<kM, kR>), dim3((unsigned)((N + kR - 1) / kR)), dim3(64 * nslots),
+                     lds, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, M, N, K);
+}
+}  // namespace
+
 hipError_t launch_nvfp4_gemm_decode(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
                                     const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
                                     int64_t K, hipStream_t stream) {
-  const unsigned grid = (unsigned)((N + 15) / 16);
-  if (M <= kLdsActRows && K <= kLdsActMaxK) {
-    const size_t lds = (size_t)M * K * 2;
-    hipLaunchKernelGGL(nvfp4_gemm_decode_kernel<true>, dim3(grid), dim3(256), lds, stream, ac, as, ag, wc, ws, wg,
-                       (uint16_t*)out, (int)M, (int)N, (int)K);
+  const bool rowslot_k = K <= (int64_t)kMaxSlots * 2048;
+  if (M == 1 && rowslot_k) {
+    launch_rowslot<1, 4>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
+  } else if (M == 2 && rowslot_k) {
+    launch_rowslot<2, 4>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
   } else {
-    hipLaunchKernelGGL(nvfp4_gemm_decode_kernel<false>, dim3(grid), dim3(256), 0, stream, ac, as, ag, wc, ws, wg,
-                       (uint16_t*)out, (int)M, (int)N, (int)K);
+    hipLaunchKernelGGL(nvfp4_gemm_rowblock_kernel, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream, ac, as,
+                       ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K);
   }
   return hipGetLastError();
 }
