@@ -89,6 +89,29 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)x;
 }
 
+// Raw buffer resources (gfx9 descriptor word 3 for an untyped buffer): the
+// hardware range-checks every access against `bytes`, and loads past the end
+// return zero, so callers can map tails to an offset past the end instead of
+// branching (and keep every wave's load count the same).
+constexpr uint32_t kBufferOob = 0x80000000u;     // an offset past every buffer's end
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kCachePolicyNT = 2;                // streamed once: non-temporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+
+template <int kAux = 0>
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int kAux = 0>
+__device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kAux);
+}
+
 // Largest bf16 magnitude pattern among the two bf16 in a dword.
 __device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
   uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;

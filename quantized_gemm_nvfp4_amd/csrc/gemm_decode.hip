@@ -21,25 +21,8 @@ namespace nvfp4k {
 
 namespace {
 constexpr int kBatch = 4;                       // row-block kernel: chunks in flight per wave
-constexpr uint32_t kOob = 0x80000000u;          // an offset past every buffer's end
-constexpr int kRawBufferWord3 = 0x00020000;     // raw (untyped) buffer, gfx9 encoding
-constexpr int kCachePolicyNT = 2;               // streamed once: non-temporal
 constexpr int kMaxSlots = 16;                   // row-slot kernel: K <= 16 * 2048
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
-}
-
-template <int kAux = 0>
-__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-template <int kAux = 0>
-__device__ __forceinline__ uint32_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kAux);
-}
+constexpr uint32_t kOob = kBufferOob;
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
@@ -94,15 +77,15 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_rowslot_kernel(
   uint32_t xs[kM];
 #pragma unroll
   for (int m = 0; m < kM; ++m) {
-    xc[m] = load16(ar, coff + m * row_bytes);
-    xs[m] = load2(asr, soff + m * row_scales);
+    xc[m] = buffer_load16(ar, coff + m * row_bytes);
+    xs[m] = buffer_load2(asr, soff + m * row_scales);
   }
   uint4 wc[kR];
   uint32_t ws[kR];
 #pragma unroll
   for (int rho = 0; rho < kR; ++rho) {
-    wc[rho] = load16<kCachePolicyNT>(wr, coff + rho * row_bytes);
-    ws[rho] = load2<kCachePolicyNT>(wsr, soff + rho * row_scales);
+    wc[rho] = buffer_load16<kCachePolicyNT>(wr, coff + rho * row_bytes);
+    ws[rho] = buffer_load2<kCachePolicyNT>(wsr, soff + rho * row_scales);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -140,20 +123,23 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_rowslot_kernel(
       for (int m = 0; m < kM; ++m) s_diag[((slot * kR + rho) * kM + m) * 16 + i] = acc[rho][m];
   }
   __syncthreads();
-  // Thread t < 16 kR kM: output (rho, m) = t / 16, diagonal entry t % 16;
-  // the slots are summed in order, then the 16 entries by a fixed butterfly.
-  const int t = threadIdx.x;
-  if (t >= 16 * kR * kM) return;
-  const int pair = t >> 4, ii = t & 15;
-  float v = 0.f;
-  for (int w = 0; w < nslots; ++w) v += s_diag[(w * kR * kM + pair) * 16 + ii][ii & 3];
-  v += __shfl_xor(v, 1, 16);
-  v += __shfl_xor(v, 2, 16);
-  v += __shfl_xor(v, 4, 16);
-  v += __shfl_xor(v, 8, 16);
-  const int rho = pair / kM, m = pair % kM;
-  if (ii == 0 && m < M && n0 + rho < N)
-    out[(int64_t)m * N + n0 + rho] = (uint16_t)f32_to_bf16_rne(v * ((*a_g) * (*w_g)));
+  const float gg = (*a_g) * (*w_g);
+  // Item t (< 16 kR kM, in strides of the block size): output (rho, m) =
+  // t / 16, diagonal entry t % 16.  The slots are summed in order, then the
+  // 16 entries by a fixed butterfly within each aligned group of 16 lanes
+  // (the item count is a multiple of 16 and the block size of 64, so every
+  // group is whole).
+  for (int t = threadIdx.x; t < 16 * kR * kM; t += blockDim.x) {
+    const int pair = t >> 4, ii = t & 15;
+    float v = 0.f;
+    for (int w = 0; w < nslots; ++w) v += s_diag[(w * kR * kM + pair) * 16 + ii][ii & 3];
+    v += __shfl_xor(v, 1, 16);
+    v += __shfl_xor(v, 2, 16);
+    v += __shfl_xor(v, 4, 16);
+    v += __shfl_xor(v, 8, 16);
+    const int rho = pair / kM, m = pair % kM;
+    if (ii == 0 && m < M && n0 + rho < N) out[(int64_t)m * N + n0 + rho] = (uint16_t)f32_to_bf16_rne(v * gg);
+  }
 }
 
 // ---------------------------------------------------------------------------

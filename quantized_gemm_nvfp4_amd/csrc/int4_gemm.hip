@@ -107,6 +107,108 @@ __global__ __launch_bounds__(256) void int4g_gemm_decode_kernel(const uint16_t* 
   }
 }
 
+// ---- M <= 2: row-slot GEMV (the weight read in storage order) --------------
+// As in the NVFP4 row-slot kernel: a weight row is cut into 1 KB slots (16
+// groups of 128 values) and wave s of a workgroup owns slot s of the
+// workgroup's kR consecutive rows, so each load instruction reads 1 KB of
+// contiguous memory.  Within a slot, lane i + 16 g loads the 16-byte piece
+// 4 i + g: the four lanes i, i + 16, i + 32, i + 48 hold the four quarters
+// of group i.  With the weight (q + 8) as the MFMA's A operand and x at the
+// same positions as B, D[i][i] = sum over group i of x (q + 8); the
+// accumulator starts from D[i][i] = -8 sum over group i of x, computed once
+// per wave, which removes the offset.  The diagonal lane of group i then
+// multiplies by the group's fp16 scale (fp32 arithmetic), and the epilogue
+// sums the diagonals over groups and slots in a fixed order.
+template <int kM, int kR>
+__global__ __launch_bounds__(1024) void int4g_gemv_rowslot_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint8_t* __restrict__ q,
+                                                                  const uint16_t* __restrict__ s,
+                                                                  uint16_t* __restrict__ out, int M, int N, int K) {
+  extern __shared__ __attribute__((aligned(16))) float4v s_diag[];   // [slots][kR][kM][16]
+  const int lane = threadIdx.x & 63;
+  const int slot = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nslots = blockDim.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const uint32_t row_bytes = (uint32_t)K / 2, row_groups = (uint32_t)K / 128;
+  const int n0 = blockIdx.x * kR;
+  const uint32_t nrows = (uint32_t)min(kR, N - n0);
+  const auto qr = buffer_of(q + (int64_t)n0 * row_bytes, nrows * row_bytes);
+  const auto sr = buffer_of(s + (int64_t)n0 * row_groups, nrows * row_groups * 2);
+  const auto xr = buffer_of(x, (uint32_t)M * K * 2);                // rows >= M read as zero
+
+  // Piece 4 i + g of the slot: 32 values starting at k0; group 16 slot + i.
+  const uint32_t piece = 1024u * slot + 16u * (4 * i + g);
+  const bool in = piece < row_bytes;
+  const uint32_t qoff = in ? piece : kBufferOob;
+  const uint32_t k0 = 2u * piece;
+  const uint32_t soff = (16u * slot + i < row_groups) ? 2u * (16u * slot + i) : kBufferOob;
+  uint4 xv[kM][4];
+#pragma unroll
+  for (int m = 0; m < kM; ++m)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) xv[m][jj] = buffer_load16(xr, in ? 2u * (m * (uint32_t)K + k0 + 8u * jj) : kBufferOob);
+  uint4 wq[kR];
+  uint32_t ws[kR];
+#pragma unroll
+  for (int rho = 0; rho < kR; ++rho) {
+    wq[rho] = buffer_load16<kCachePolicyNT>(qr, qoff + rho * row_bytes);
+    ws[rho] = buffer_load2<kCachePolicyNT>(sr, soff + rho * row_groups * 2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const short8v c8 = {kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16,
+                      kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16};
+  float4v off8[kM];                     // D[i][i] = -8 * sum of x over group i
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    off8[m] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      off8[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c8, as_short8(xv[m][jj]), off8[m], 0, 0, 0);
+  }
+  float4v tot[kR][kM];
+#pragma unroll
+  for (int rho = 0; rho < kR; ++rho) {
+    const float sc = f16_bits_to_f32(ws[rho] & 0xFFFFu);
+#pragma unroll
+    for (int m = 0; m < kM; ++m) tot[rho][m] = off8[m];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const short8v wv = int4x8_offset_bf16(word_of(wq[rho], jj));
+#pragma unroll
+      for (int m = 0; m < kM; ++m)
+        tot[rho][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, as_short8(xv[m][jj]), tot[rho][m], 0, 0, 0);
+    }
+#pragma unroll
+    for (int m = 0; m < kM; ++m) tot[rho][m] *= sc;
+  }
+
+  // D[i][i] sits at lane i + 16 (i / 4), register i % 4.
+  if ((i >> 2) == g) {
+#pragma unroll
+    for (int rho = 0; rho < kR; ++rho)
+#pragma unroll
+      for (int m = 0; m < kM; ++m) s_diag[((slot * kR + rho) * kM + m) * 16 + i] = tot[rho][m];
+  }
+  __syncthreads();
+  // Item t (< 16 kR kM, in strides of the block size): output (rho, m) =
+  // t / 16, diagonal entry t % 16.  The slots are summed in order, then the
+  // 16 entries by a fixed butterfly within each aligned group of 16 lanes
+  // (the item count is a multiple of 16 and the block size of 64, so every
+  // group is whole).
+  for (int t = threadIdx.x; t < 16 * kR * kM; t += blockDim.x) {
+    const int pair = t >> 4, ii = t & 15;
+    float v = 0.f;
+    for (int w = 0; w < nslots; ++w) v += s_diag[(w * kR * kM + pair) * 16 + ii][ii & 3];
+    v += __shfl_xor(v, 1, 16);
+    v += __shfl_xor(v, 2, 16);
+    v += __shfl_xor(v, 4, 16);
+    v += __shfl_xor(v, 8, 16);
+    const int rho = pair / kM, m = pair % kM;
+    if (ii == 0 && m < M && n0 + rho < N) out[(int64_t)m * N + n0 + rho] = (uint16_t)f32_to_bf16_rne(v);
+  }
+}
+
 // ---- any M: LDS-staged MFMA tiles -----------------------------------------
 // Workgroup tile 128 (m) x 256 (n), K stage = one 128-value group; 4 waves of
 // 64 x 128 (2 x 4 tiles of 32 x 32).  x fragments are stored in LDS in lane
@@ -253,8 +355,29 @@ __global__ __launch_bounds__(256, 1) void int4g_gemm_tiled_kernel(const uint16_t
   }
 }
 
+namespace {
+template <int kM, int kR>
+void launch_int4_rowslot(const void* x, const uint8_t* q, const void* s, void* out, int M, int N, int K,
+                         hipStream_t stream) {
+  const int nslots = (K / 2 + 1023) / 1024;
+  const size_t lds = (size_t)nslots * kR * kM * 16 * sizeof(float4v);
+  hipLaunchKernelGGL((int4g_gemv_rowslot_kernel<kM, kR>), dim3((unsigned)((N + kR - 1) / kR)), dim3(64 * nslots),
+                     lds, stream, (const uint16_t*)x, q, (const uint16_t*)s, (uint16_t*)out, M, N, K);
+}
+}  // namespace
+
 hipError_t launch_int4g_gemm_decode(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,
                                     int64_t N, int64_t K, hipStream_t stream) {
+  if (K <= 16 * 2048 && (int64_t)M * K * 2 < (1ll << 31)) {
+    if (M == 1) {
+      launch_int4_rowslot<1, 8>(x, q, s, out, (int)M, (int)N, (int)K, stream);
+      return hipGetLastError();
+    }
+    if (M == 2) {
+      launch_int4_rowslot<2, 4>(x, q, s, out, (int)M, (int)N, (int)K, stream);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL(int4g_gemm_decode_kernel, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream,
                      (const uint16_t*)x, q, (const uint16_t*)s, (uint16_t*)out, (int)M, (int)N, (int)K);
   return hipGetLastError();

@@ -147,6 +147,17 @@ def test_gemm_ragged_tiled_and_simple(M, N, K):
     check_gemm(a_bits, w_bits, algos=algos, label=f"ragged {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (1, 1, 128), (2, 3, 128), (1, 9, 2048), (2, 37, 2176), (1, 33, 4224), (2, 8, 6144), (1, 5, 32768 + 128)])
+def test_gemm_decode_shapes(M, N, K):
+    # M <= 2 runs the row-slot GEMV: one 1 KB slot per 2048 values of K (the
+    # last one partial), 4 rows per workgroup (N ragged); K > 32768 falls back
+    # to the row-block kernel.
+    a_bits = workloads.random_bf16(M * 13 + K, (M, K), outlier_frac=0.01, outlier_mul=30)
+    w_bits = workloads.random_bf16(N * 17 + K, (N, K), sigma=0.02, zero_frac=0.05)
+    check_gemm(a_bits, w_bits, algos=(0, 2), label=f"decode {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("K", [16, 48, 80, 272])
 def test_gemm_k_not_multiple_of_128_uses_simple(K):
     a_bits = workloads.random_bf16(K + 3, (9, K))
