@@ -13,6 +13,7 @@ Everything is plain numpy, written from the pages' definitions:
 * ``formats``  -- the element and scale number formats: E2M1 (4-bit float),
   FP8 E4M3 ("float8_e4m3fn"), and the bf16 / fp16 round-to-nearest-even casts.
 * ``nvfp4``    -- NVFP4 quantize / dequantize and the block-scaled GEMM.
+* ``scale_rules`` -- block-scale selection: absmax, four-over-six, MSE.
 * ``intq``     -- the symmetric integer formula and its INT4 per-group form.
 * ``metrics``  -- the parity metrics (relative L2, per-row max-abs).
 
