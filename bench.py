@@ -227,6 +227,30 @@ def run_decode(torch, q, iters=64, copies=16):
     return out
 
 
+def run_weight_quant(torch, q, reps=5):
+    """Offline weight quantization of W_up [21504, 5376] under each block-scale
+    rule (absmax, four-over-six, MSE): time per call and GB/s of algorithmic
+    bytes (2 B read + 0.5625 B written per element)."""
+    import workloads
+    w = dev_bf16(torch, workloads.decode_w())
+    n = w.numel()
+    out = {}
+    for rule in ("absmax", "four_over_six", "mse"):
+        q.nvfp4_quantize(w, rule=rule)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            q.nvfp4_quantize(w, rule=rule)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / reps
+        out[rule] = {"us": us, "GBps": n * 2.5625 / (us * 1e-6) / 1e9}
+        log(f"weight quant {rule}: {us:.1f} us, {out[rule]['GBps']:.0f} GB/s")
+    return out
+
+
 def run_dit(torch, q, reps=3):
     """4 denoising steps x (qkv, up, down) with fresh activations; TFLOP/s incl. act quant."""
     import workloads
@@ -342,7 +366,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the prefill step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["decode", "dit", "int4"], help="time only this extra workload")
+    ap.add_argument("--only", choices=["decode", "dit", "int4", "weight_quant"],
+                    help="time only this extra workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a "
@@ -356,7 +381,8 @@ def main():
     log(f"device {torch.cuda.get_device_name(0)}")
 
     if args.only:
-        res = {"decode": run_decode, "dit": run_dit, "int4": run_int4}[args.only](torch, q)
+        res = {"decode": run_decode, "dit": run_dit, "int4": run_int4,
+               "weight_quant": run_weight_quant}[args.only](torch, q)
         print(json.dumps({"only": args.only, "result": res}))
         return
     pre = run_prefill(torch, q, args.steps, args.warmup)
@@ -367,6 +393,7 @@ def main():
         extras["decode"] = run_decode(torch, q)
         extras["dit"] = run_dit(torch, q)
         extras["int4"] = run_int4(torch, q)
+        extras["weight_quant"] = run_weight_quant(torch, q)
     if args.copy_calibration:
         run_copy_calibration(torch)
     cpu = None

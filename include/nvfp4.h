@@ -98,6 +98,40 @@ nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols,
                             uint8_t* codes, uint8_t* scales, float* global_scale,
                             int use_given_global_scale, void* workspace, void* stream);
 
+/* Block-scale selection rules for nvfp4_quantize_ex. */
+typedef enum nvfp4_scale_rule {
+  NVFP4_SCALE_ABSMAX = 0,        /* the block max maps to 6 (nvfp4_quantize) */
+  NVFP4_SCALE_FOUR_OVER_SIX = 1, /* max -> 6 or max -> 4, the lower error */
+  NVFP4_SCALE_MSE = 2            /* least error over a one-binade window */
+} nvfp4_scale_rule;
+
+/*
+ * nvfp4_quantize with a choice of block-scale rule.  Passage: the table of
+ * scale algorithms in "Tu pipeline NVFP4", section 2 (absmax; MSE, which
+ * tries several scales and keeps the one with the least reconstruction
+ * error of the block; four-over-six, which lets each block map its largest
+ * magnitude to 4 or to 6, whichever errs less).  Meant for weights, which
+ * are quantized once; the GEMM consumes the result unchanged.
+ *
+ * g, the candidate arithmetic and the codes are exactly those of
+ * nvfp4_quantize; only the stored scale byte of a block may differ:
+ *   error(s) = sum over the block, in element order, of (x - v * d)^2 with
+ *     d = s * g and v the signed E2M1 value of each code, every step an fp32
+ *     operation with one rounding (no fused multiply-add);
+ *   FOUR_OVER_SIX: candidates s6 = E4M3(fl32(fl32(amax_b / 6) / g)) and
+ *     s4 = E4M3(fl32(fl32(amax_b / 4) / g)); s4 only if strictly better;
+ *   MSE: the E4M3 codes c6, c6 - 1, c6 + 1, ..., c6 - 8, c6 + 8 (within
+ *     1..0x7E), c6 being the absmax code; a later candidate only if
+ *     strictly better.
+ * The error under MSE is never above four-over-six's, which is never above
+ * absmax's.  Unknown rules return NVFP4_ERR_INVALID_ARG.  All other
+ * arguments and errors as nvfp4_quantize.
+ */
+nvfp4_status nvfp4_quantize_ex(const void* x_bf16, int64_t rows, int64_t cols,
+                               uint8_t* codes, uint8_t* scales, float* global_scale,
+                               int use_given_global_scale, int scale_rule, void* workspace,
+                               void* stream);
+
 /*
  * out[M, N] (bf16) = bf16_RNE( g_a * g_w * sum_k A[m, k] * W[n, k] )
  * where A[m, k] = E2M1(a code) * E4M3(a scale) and likewise for W: the

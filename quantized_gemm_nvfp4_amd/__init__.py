@@ -29,6 +29,7 @@ SIGNATURES = {
     "nvfp4_abi_version": ([], ctypes.c_int),
     "nvfp4_quantize_workspace_bytes": ([], ctypes.c_size_t),
     "nvfp4_quantize": ([_P, _I64, _I64, _P, _P, _P, _I, _P, _P], ctypes.c_int),
+    "nvfp4_quantize_ex": ([_P, _I64, _I64, _P, _P, _P, _I, _I, _P, _P], ctypes.c_int),
     "nvfp4_gemm": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "nvfp4_gemm_ex": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P], ctypes.c_int),
     "int4g_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
@@ -96,11 +97,15 @@ def _need(t, dtype, shape, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def nvfp4_quantize(x, global_scale=None, out=None):
+SCALE_RULES = {"absmax": 0, "four_over_six": 1, "mse": 2}
+
+
+def nvfp4_quantize(x, global_scale=None, out=None, rule="absmax"):
     """NVFP4-quantize a bf16 [rows, cols] tensor (cols % 16 == 0).
 
     global_scale: optional fp32 device tensor [1] to use instead of the
     dynamic amax / 2688.  out: optional (codes, scales, global_scale) buffers.
+    rule: block-scale selection, "absmax" (default), "four_over_six" or "mse".
     Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/16],
     global_scale fp32 [1]).
     """
@@ -124,8 +129,10 @@ def nvfp4_quantize(x, global_scale=None, out=None):
     ws = None
     if not use_given:
         ws = torch.empty(lib().nvfp4_quantize_workspace_bytes(), dtype=torch.uint8, device=x.device)
-    _check(lib().nvfp4_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(g), use_given,
-                                _ptr(ws) if ws is not None else None, _stream(x)))
+    if rule not in SCALE_RULES:
+        raise ValueError(f"unknown scale rule {rule!r}; one of {sorted(SCALE_RULES)}")
+    _check(lib().nvfp4_quantize_ex(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(g), use_given,
+                                   SCALE_RULES[rule], _ptr(ws) if ws is not None else None, _stream(x)))
     return codes, scales, g
 
 

@@ -102,13 +102,16 @@ const char* nvfp4_status_string(nvfp4_status s) {
 
 const char* nvfp4_last_error(void) { return g_last_error; }
 
-nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                            float* global_scale, int use_given_global_scale, void* workspace, void* stream) {
+nvfp4_status nvfp4_quantize_ex(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                               float* global_scale, int use_given_global_scale, int scale_rule, void* workspace,
+                               void* stream) {
   REQUIRE_PTR(x_bf16);
   REQUIRE_PTR(codes);
   REQUIRE_PTR(scales);
   REQUIRE_PTR(global_scale);
   if (!use_given_global_scale) REQUIRE_PTR(workspace);
+  if (scale_rule < NVFP4_SCALE_ABSMAX || scale_rule > NVFP4_SCALE_MSE)
+    return fail(NVFP4_ERR_INVALID_ARG, "unknown scale rule %d", scale_rule);
   if (nvfp4_status s = check_dims(rows, "rows", cols, "cols", 0, "-")) return s;
   if (cols % 16 != 0) return fail(NVFP4_ERR_SHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
   if (rows > 0 && cols > INT64_MAX / 2 / rows) return fail(NVFP4_ERR_UNSUPPORTED, "rows*cols overflows");
@@ -125,9 +128,15 @@ nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint
   if (n == 0) return ok();
   if (nvfp4_status s = check_disjoint(outs, 3, ins, 2)) return s;
   return hip_status(nvfp4k::launch_nvfp4_quantize(x_bf16, rows, cols, codes, scales, global_scale,
-                                                  use_given_global_scale, (uint32_t*)workspace,
+                                                  use_given_global_scale, scale_rule, (uint32_t*)workspace,
                                                   (hipStream_t)stream),
                     "nvfp4_quantize launch");
+}
+
+nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                            float* global_scale, int use_given_global_scale, void* workspace, void* stream) {
+  return nvfp4_quantize_ex(x_bf16, rows, cols, codes, scales, global_scale, use_given_global_scale,
+                           NVFP4_SCALE_ABSMAX, workspace, stream);
 }
 
 nvfp4_status nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,

@@ -12,8 +12,9 @@ namespace nvfp4k {
 // workspace holds this many uint32).
 constexpr int kAmaxPartials = 1024;
 
+// rule: 0 absmax, 1 four-over-six, 2 MSE (block-scale selection).
 hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                                 float* gscale, int use_given, uint32_t* workspace, hipStream_t stream);
+                                 float* gscale, int use_given, int rule, uint32_t* workspace, hipStream_t stream);
 
 hipError_t launch_int4g_quantize(const void* w, int64_t N, int64_t K, uint8_t* q, void* scales,
                                  hipStream_t stream);

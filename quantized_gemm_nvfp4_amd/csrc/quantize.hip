@@ -54,7 +54,56 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const uint4* __restri
 }
 
 // ---- pass 2: one 16-value block per thread ---------------------------------
+// Block-scale rules ("Tu pipeline NVFP4 ...", section 2, table of scale
+// algorithms): absmax maps the block's largest magnitude to 6; four-over-six
+// also tries mapping it to 4 and keeps whichever reconstructs the block with
+// less error; MSE tries the E4M3 scales within one binade (8 codes) of the
+// absmax scale, visited c6, c6 - 1, c6 + 1, ..., c6 + 8, and keeps the
+// least error (a later candidate must be strictly better).  The error of a
+// block under scale s is, in fp32 with one rounding per step and no fused
+// multiply-add: d = s * g, x_hat = v * d (v the signed E2M1 value of the
+// element's code), e = x - x_hat, err = sum of e * e in element order.
+enum ScaleRule { kRuleAbsmax = 0, kRuleFourOverSix = 1, kRuleMse = 2 };
+
+namespace {
+// Signed E2M1 value of code c (0..15), exact: codes 0/1 are 0 and 0.5, then
+// (1 + m/2) * 2^(e - 1) with e = c >> 1, m = c & 1.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t mag = c & 7u;
+  const float v = mag < 2u ? 0.5f * (float)mag : __uint_as_float((((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22));
+  return (c & 8u) ? -v : v;
+}
+
+// Element code of the bf16 pattern h under d (the quantizer's rule).
+__device__ __forceinline__ uint32_t element_code(uint32_t h, float d) {
+  const float y = (d != 0.0f) ? bf16_bits_to_f32(h & 0x7FFFu) / d : 0.0f;
+  return e2m1_code_from_f32(y) | ((h >> 12) & 8u);
+}
+
+__device__ __forceinline__ float block_error(const uint32_t (&w)[8], uint32_t sc, float g) {
+#pragma clang fp contract(off)
+  const float d = e4m3_to_f32(sc) * g;
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    const float x = bf16_bits_to_f32(h);
+    const float xhat = e2m1_value(element_code(h, d)) * d;
+    const float e = x - xhat;
+    const float sq = e * e;
+    acc = acc + sq;
+  }
+  return acc;
+}
+
+__device__ __forceinline__ uint32_t scale_code(float amax_b, float top, float g) {
+  const float s_raw = (g == 0.0f) ? 0.0f : (amax_b / top) / g;
+  return e4m3_from_f32_sat(s_raw);
+}
+}  // namespace
+
 // x: bf16 [nblocks * 16]; codes: 8 bytes per block; scales: 1 byte per block.
+template <int kRule>
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restrict__ x, int64_t nblocks,
                                                           uint2* __restrict__ codes, uint8_t* __restrict__ scales,
                                                           float* __restrict__ gscale,
@@ -85,17 +134,34 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, bf16x2_absmax_bits(w[i]));
     const float amax_b = bf16_bits_to_f32(amax_bits);
-    const float s_raw = (g == 0.0f) ? 0.0f : (amax_b / 6.0f) / g;
-    const uint32_t sc = e4m3_from_f32_sat(s_raw);
+    uint32_t sc = scale_code(amax_b, 6.0f, g);
+    if (kRule != kRuleAbsmax) {
+      float best = block_error(w, sc, g);
+      if (kRule == kRuleFourOverSix) {
+        const uint32_t c4 = scale_code(amax_b, 4.0f, g);
+        if (block_error(w, c4, g) < best) sc = c4;
+      } else {
+        const int c6 = (int)sc;
+        for (int step = 1; step <= 8; ++step) {
+#pragma unroll
+          for (int sgn = 0; sgn < 2; ++sgn) {
+            const int c = sgn ? c6 + step : c6 - step;
+            if (c < 1 || c > 0x7E) continue;
+            const float e = block_error(w, (uint32_t)c, g);
+            if (e < best) {
+              best = e;
+              sc = (uint32_t)c;
+            }
+          }
+        }
+      }
+    }
     const float d = e4m3_to_f32(sc) * g;
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t lo = w[i] & 0xFFFFu, hi = w[i] >> 16;
-      const float ylo = (d != 0.0f) ? bf16_bits_to_f32(lo & 0x7FFFu) / d : 0.0f;
-      const float yhi = (d != 0.0f) ? bf16_bits_to_f32(hi & 0x7FFFu) / d : 0.0f;
-      const uint32_t clo = e2m1_code_from_f32(ylo) | ((lo >> 12) & 8u);
-      const uint32_t chi = e2m1_code_from_f32(yhi) | ((hi >> 12) & 8u);
+      const uint32_t clo = element_code(w[i] & 0xFFFFu, d);
+      const uint32_t chi = element_code(w[i] >> 16, d);
       packed[i >> 2] |= (clo | (chi << 4)) << (8 * (i & 3));
     }
     codes[b] = make_uint2(packed[0], packed[1]);
@@ -145,7 +211,7 @@ __global__ __launch_bounds__(256) void int4g_quant_kernel(const uint4* __restric
 
 // ---- launchers -------------------------------------------------------------
 hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                                 float* gscale, int use_given, uint32_t* workspace, hipStream_t stream) {
+                                 float* gscale, int use_given, int rule, uint32_t* workspace, hipStream_t stream) {
   const int64_t n = rows * cols;
   const int64_t nblocks = n / kBlock;
   int npartial = 0;
@@ -161,8 +227,18 @@ hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint
   }
   int64_t grid = (nblocks + 255) / 256;
   if (grid > 2048) grid = 2048;
-  hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint4*)x, nblocks,
-                     (uint2*)codes, scales, gscale, (const uint32_t*)workspace, npartial, use_given);
+  if (rule == kRuleFourOverSix) {
+    hipLaunchKernelGGL(nvfp4_quant_kernel<kRuleFourOverSix>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint4*)x, nblocks, (uint2*)codes, scales, gscale, (const uint32_t*)workspace, npartial,
+                       use_given);
+  } else if (rule == kRuleMse) {
+    hipLaunchKernelGGL(nvfp4_quant_kernel<kRuleMse>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint4*)x,
+                       nblocks, (uint2*)codes, scales, gscale, (const uint32_t*)workspace, npartial, use_given);
+  } else {
+    hipLaunchKernelGGL(nvfp4_quant_kernel<kRuleAbsmax>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint4*)x, nblocks, (uint2*)codes, scales, gscale, (const uint32_t*)workspace, npartial,
+                       use_given);
+  }
   return hipGetLastError();
 }
 

@@ -73,6 +73,15 @@ def test_quantize_validation():
     assert f(A, 0, 32, B, C, D, 1, None, None) == OK
 
 
+def test_quantize_ex_rule_validation():
+    f = q.lib().nvfp4_quantize_ex
+    assert f(A, 4, 32, B, C, D, 0, 3, E, None) == INVALID and "rule" in _err()
+    assert f(A, 4, 32, B, C, D, 0, -1, E, None) == INVALID
+    assert f(A, 4, 24, B, C, D, 0, 2, E, None) == SHAPE
+    for rule in (0, 1, 2):
+        assert f(A, 0, 32, B, C, D, 0, rule, E, None) == OK
+
+
 def test_gemm_validation():
     f = q.lib().nvfp4_gemm_ex
     good = [A, B, C, D, E, F, G]
