@@ -35,6 +35,9 @@ Parity: pinned by tests/test_oracle_nvfp4.py -- a hand-worked three-block
 row (tests/golden/nvfp4_worked_row.txt), the per-element error bound, a
 pure-Python triple loop on tiny shapes, the unit-scale special case (plain
 matmul of grid values), and W = diag(grid) reproducing dequant(A) exactly.
+The weight-only product ``gemm_w4a16`` is pinned by a triple loop and by
+equality with ``gemm`` when the bf16 activation is itself a dequantized
+NVFP4 tensor with g = 1.
 """
 import numpy as np
 
@@ -137,6 +140,24 @@ def gemm(a_codes, a_scales, a_g, w_codes, w_scales, w_g):
     Returns float64 holding bf16 values, [M, N].
     """
     return F.bf16_round(gemm_fp64(a_codes, a_scales, a_g, w_codes, w_scales, w_g))
+
+
+def gemm_w4a16_fp64(x, w_codes, w_scales, w_g):
+    """Unrounded fp64 g_w * X @ dequant(W)^T with X a bf16 activation [M, K]
+    (weight-only NVFP4: the activation is not quantized)."""
+    X = _as_bf16_values(x).astype(np.float64)
+    W = dequantize_blockscaled(w_codes, w_scales)
+    return np.float64(np.float32(w_g)) * (X @ W.T)
+
+
+def gemm_w4a16(x, w_codes, w_scales, w_g):
+    """Y_ref = bf16_RNE(g_w * sum_k X[m,k] * W_hat[n,k]) in fp64, [M, N].
+
+    The weight-only mode: "Cuantización e inferencia local" (section on
+    activation outliers) notes that weight-only methods keep the activations
+    in 16-bit; here the weight is NVFP4 exactly as for ``gemm`` and the
+    activation stays bf16."""
+    return F.bf16_round(gemm_w4a16_fp64(x, w_codes, w_scales, w_g))
 
 
 def gemm_rows(a_codes, a_scales, a_g, w_codes, w_scales, w_g, rows):

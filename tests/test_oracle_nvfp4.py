@@ -194,3 +194,29 @@ def test_quantize_accepts_bits_and_values_equally():
     r1 = Q.quantize(bits)
     r2 = Q.quantize(F.bf16_from_bits(bits))
     assert all(np.array_equal(u, v) for u, v in zip(r1, r2))
+
+
+def test_w4a16_vs_triple_loop():
+    rng = np.random.default_rng(7)
+    x = F.bf16_round(rng.normal(size=(3, 32)).astype(np.float32)).astype(np.float32)
+    w = F.bf16_round((0.02 * rng.normal(size=(5, 32))).astype(np.float32)).astype(np.float32)
+    wc, ws, wg = Q.quantize(w)
+    codes = Q.unpack_codes(wc)
+    y = Q.gemm_w4a16_fp64(x, wc, ws, wg)
+    for m in range(3):
+        for n in range(5):
+            tot = 0.0
+            for k in range(32):
+                wv = float(F.e2m1_decode(codes[n, k])) * float(F.e4m3_decode(ws[n, k // 16]))
+                tot += float(x[m, k]) * wv
+            assert abs(y[m, n] - float(np.float32(wg)) * tot) <= 1e-12 * (1 + abs(y[m, n]))
+
+
+def test_w4a16_equals_w4a4_when_x_is_dequantized_nvfp4():
+    a_bits = workloads.random_bf16(71, (7, 256), outlier_frac=0.02, outlier_mul=10)
+    w_bits = workloads.random_bf16(72, (9, 256), sigma=0.02)
+    a = Q.quantize(a_bits, g=1.0)
+    w = Q.quantize(w_bits)
+    x = Q.dequantize_blockscaled(a[0], a[1]).astype(np.float32)     # bf16-exact values
+    assert np.array_equal(F.bf16_round(x), x)
+    np.testing.assert_array_equal(Q.gemm_w4a16(x, *w), Q.gemm(*a, *w))
