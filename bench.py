@@ -223,6 +223,17 @@ def run_decode(torch, q, iters=64, copies=16):
                         "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                         "us_incl_act_quant": us_q, "alg_bytes": alg_bytes}
         log(f"decode M={M}: {us:.2f} us, {out[f'M{M}']['GBps']:.0f} GB/s; incl. act quant {us_q:.2f} us")
+    # weight-only mode: bf16 activation straight into the GEMV (no quantization)
+    for M in (1, 2):
+        x = dev_bf16(torch, x_bits[:M])
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+        alg_bytes = N * K // 2 + N * K // 16 + 4 + M * K * 2 + M * N * 2
+        ref = q.nvfp4_gemm_w4a16(x, ws[(iters - 1) % copies]).clone()
+        us = graph_time_us(torch, lambda i: q.nvfp4_gemm_w4a16(x, ws[i % copies], out=y), iters)
+        assert torch.equal(y, ref), "graph replay differs from the eager call"
+        out[f"w4a16_M{M}"] = {"us": us, "GBps": alg_bytes / (us * 1e-6) / 1e9,
+                              "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "alg_bytes": alg_bytes}
+        log(f"decode W4A16 M={M}: {us:.2f} us, {out[f'w4a16_M{M}']['GBps']:.0f} GB/s")
     del ws
     return out
 

@@ -162,6 +162,31 @@ nvfp4_status nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            void* out_bf16, int64_t M, int64_t N, int64_t K, int algo, void* stream);
 
 /*
+ * Weight-only NVFP4 GEMM: out[M, N] (bf16) = bf16_RNE( g_w * sum_k x[m, k] *
+ * W[n, k] ) with x a bf16 activation that is not quantized and W the NVFP4
+ * weight of nvfp4_gemm.  Passages: the weight format of "NVFP4 en
+ * difusión", section 2, and the remark in "Cuantización e inferencia
+ * local" that weight-only methods keep activations in 16-bit to avoid
+ * their outliers.
+ * x [M, K] bf16 row-major; w_codes [N, K/2]; w_scales [N, K/16]; w_gscale
+ * a device fp32 pointer.  K % 16 == 0; K == 0 writes zeros.
+ * Exactness: W's decoded values are exact; the decode kernel (M <= 2,
+ * K % 128 == 0, K <= 32768) feeds the matrix cores fp16, converting each
+ * 2048-value slice of x after a power-of-two rescale that puts the slice's
+ * largest magnitude in [2^15, 2^16): elements within 2^32 of that maximum
+ * are exact, smaller ones are truncated to the fp16 subnormal grid.  Other
+ * shapes run a one-output-per-thread kernel in fp32.
+ * algo: NVFP4_ALGO_AUTO, _DECODE or _SIMPLE; others return
+ * NVFP4_ERR_INVALID_ARG.  out must not overlap any input.
+ */
+nvfp4_status nvfp4_gemm_w4a16(const void* x_bf16, const uint8_t* w_codes, const uint8_t* w_scales,
+                              const float* w_gscale, void* out_bf16, int64_t M, int64_t N, int64_t K,
+                              void* stream);
+nvfp4_status nvfp4_gemm_w4a16_ex(const void* x_bf16, const uint8_t* w_codes, const uint8_t* w_scales,
+                                 const float* w_gscale, void* out_bf16, int64_t M, int64_t N, int64_t K,
+                                 int algo, void* stream);
+
+/*
  * Symmetric INT4 per-group quantization of a bf16 weight w [N, K], groups
  * of `group` consecutive values along K (group == 128; K % 128 == 0).
  * Passage: the symmetric formula of "Cuantización e inferencia local"

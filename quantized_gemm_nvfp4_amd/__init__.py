@@ -7,8 +7,10 @@ runtime cannot load it, every call raises -- there is no CPU fallback.
 
 Function names follow the C ABI:
 
-* ``nvfp4_quantize(x)``               -> (codes, scales, global_scale)
+* ``nvfp4_quantize(x, rule=...)``     -> (codes, scales, global_scale); rule absmax /
+  four_over_six / mse
 * ``nvfp4_gemm(a, w, algo=AUTO)``     -> bf16 [M, N]; a, w are the 3-tuples above
+* ``nvfp4_gemm_w4a16(x, w)``          -> bf16 [M, N]; x bf16 (weight-only NVFP4)
 * ``int4g_quantize(w, group=128)``    -> (q, scales_fp16)
 * ``int4g_gemv(x, q, scales, ...)``   -> bf16 [M, N]
 * ``nvfp4_linear(x, w)``              -> quantize x, then nvfp4_gemm (two calls)
@@ -32,6 +34,8 @@ SIGNATURES = {
     "nvfp4_quantize_ex": ([_P, _I64, _I64, _P, _P, _P, _I, _I, _P, _P], ctypes.c_int),
     "nvfp4_gemm": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "nvfp4_gemm_ex": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P], ctypes.c_int),
+    "nvfp4_gemm_w4a16": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "nvfp4_gemm_w4a16_ex": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P], ctypes.c_int),
     "int4g_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "int4g_gemv": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "int4g_gemv_ex": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P], ctypes.c_int),
@@ -157,6 +161,25 @@ def nvfp4_gemm(a, w, algo=ALGO_AUTO, out=None):
     _need(out, torch.bfloat16, (M, N), "out")
     _check(lib().nvfp4_gemm_ex(_ptr(ac), _ptr(as_), _ptr(ag), _ptr(wc), _ptr(ws), _ptr(wg), _ptr(out),
                                M, N, K, int(algo), _stream(ac)))
+    return out
+
+
+def nvfp4_gemm_w4a16(x, w, algo=ALGO_AUTO, out=None):
+    """bf16 [M, N] = g_w x . dequant(W)^T with x bf16 [M, K] (weight-only)."""
+    torch = _torch()
+    wc, ws, wg = w
+    _need(x, torch.bfloat16, None, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    N = wc.shape[0]
+    _need(wc, torch.uint8, (N, K // 2), "w_codes")
+    _need(ws, torch.uint8, (N, K // 16), "w_scales")
+    _need(wg, torch.float32, (1,), "w_gscale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, (M, N), "out")
+    _check(lib().nvfp4_gemm_w4a16_ex(_ptr(x), _ptr(wc), _ptr(ws), _ptr(wg), _ptr(out), M, N, K, algo, _stream(x)))
     return out
 
 

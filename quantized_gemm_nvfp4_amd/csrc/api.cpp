@@ -197,6 +197,49 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
                        NVFP4_ALGO_AUTO, stream);
 }
 
+nvfp4_status nvfp4_gemm_w4a16_ex(const void* x_bf16, const uint8_t* w_codes, const uint8_t* w_scales,
+                                 const float* w_gscale, void* out_bf16, int64_t M, int64_t N, int64_t K, int algo,
+                                 void* stream) {
+  if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
+  if (K > 0) {
+    REQUIRE_PTR(x_bf16);
+    REQUIRE_PTR(w_codes);
+    REQUIRE_PTR(w_scales);
+  }
+  REQUIRE_PTR(w_gscale);
+  REQUIRE_PTR(out_bf16);
+  if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
+  if (algo != NVFP4_ALGO_AUTO && algo != NVFP4_ALGO_DECODE && algo != NVFP4_ALGO_SIMPLE)
+    return fail(NVFP4_ERR_INVALID_ARG, "algo %d is not available for the weight-only GEMM", algo);
+  REQUIRE_ALIGN(x_bf16, 16);
+  REQUIRE_ALIGN(w_codes, 16);
+  REQUIRE_ALIGN(w_scales, 16);
+  REQUIRE_ALIGN(out_bf16, 16);
+  REQUIRE_ALIGN(w_gscale, 4);
+  const Range outs[1] = {{out_bf16, M * N * 2, "out"}};
+  const Range ins[4] = {{x_bf16, M * K * 2, "x"}, {w_codes, N * K / 2, "w_codes"},
+                        {w_scales, N * K / 16, "w_scales"}, {w_gscale, 4, "w_gscale"}};
+  if (M == 0 || N == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 1, ins, 4)) return s;
+  const bool decode_ok = nvfp4k::nvfp4_w4a16_decode_supported(M, K);
+  if (algo == NVFP4_ALGO_AUTO) algo = decode_ok ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE;
+  hipStream_t st = (hipStream_t)stream;
+  if (algo == NVFP4_ALGO_DECODE) {
+    if (!decode_ok)
+      return fail(NVFP4_ERR_UNSUPPORTED, "weight-only decode kernel needs M <= 2, K %% 128 == 0 and K <= 32768 "
+                  "(M=%lld, K=%lld)", (long long)M, (long long)K);
+    return hip_status(nvfp4k::launch_nvfp4_w4a16_decode(x_bf16, w_codes, w_scales, w_gscale, out_bf16, M, N, K, st),
+                      "nvfp4_gemm_w4a16 decode launch");
+  }
+  return hip_status(nvfp4k::launch_nvfp4_w4a16_simple(x_bf16, w_codes, w_scales, w_gscale, out_bf16, M, N, K, st),
+                    "nvfp4_gemm_w4a16 simple launch");
+}
+
+nvfp4_status nvfp4_gemm_w4a16(const void* x_bf16, const uint8_t* w_codes, const uint8_t* w_scales,
+                              const float* w_gscale, void* out_bf16, int64_t M, int64_t N, int64_t K, void* stream) {
+  return nvfp4_gemm_w4a16_ex(x_bf16, w_codes, w_scales, w_gscale, out_bf16, M, N, K, NVFP4_ALGO_AUTO, stream);
+}
+
 nvfp4_status int4g_quantize(const void* w_bf16, int64_t N, int64_t K, int64_t group, uint8_t* q, void* scales_fp16,
                             void* stream) {
   REQUIRE_PTR(w_bf16);

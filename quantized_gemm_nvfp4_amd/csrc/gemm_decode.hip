@@ -143,6 +143,121 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_rowslot_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Weight-only row-slot GEMV (M <= 2): bf16 activation x NVFP4 weight.
+//
+// The weight side is the row-slot GEMV above.  The activation is bf16 and is
+// not quantized; the MFMA takes fp16, so each wave converts its slot of x to
+// fp16 after multiplying by a power of two 2^-k chosen from the slot's
+// largest magnitude (which lands in [2^15, 2^16)): every element within 2^32
+// of that maximum converts exactly (bf16's 8 significant bits fit fp16's
+// normal and upper subnormal range), smaller ones are truncated to the fp16
+// subnormal grid.  The slot's partial sums are multiplied back by 2^k
+// (exact) before the slots are added.
+template <int kM, int kR>
+__global__ __launch_bounds__(1024) void nvfp4_gemv_w4a16_rowslot_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
+    const float* __restrict__ w_g, uint16_t* __restrict__ out, int M, int N, int K) {
+  extern __shared__ __attribute__((aligned(16))) float4v s_diag[];   // [slots][kR][kM][16]
+  const int lane = threadIdx.x & 63;
+  const int slot = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nslots = blockDim.x >> 6;
+  const uint32_t row_bytes = (uint32_t)K / 2, row_scales = (uint32_t)K / 16;
+  const int n0 = blockIdx.x * kR;
+  const uint32_t nrows = (uint32_t)min(kR, N - n0);
+  const auto wr = buffer_of(w_codes + (int64_t)n0 * row_bytes, nrows * row_bytes);
+  const auto wsr = buffer_of(w_scales + (int64_t)n0 * row_scales, nrows * row_scales);
+  const auto xr = buffer_of(x, (uint32_t)M * (uint32_t)K * 2u);   // rows >= M read as zero
+
+  // This lane's 32 values of a row: 16 code bytes, 2 scale bytes, and the
+  // 32 bf16 activation values at the same K positions (64 bytes).
+  const uint32_t off = 1024u * slot + 16u * lane;
+  const bool in = off < row_bytes;
+  const uint32_t coff = in ? off : kOob;
+  const uint32_t soff = in ? 128u * slot + 2u * lane : kOob;
+  uint4 xb[kM][4];
+#pragma unroll
+  for (int m = 0; m < kM; ++m)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      xb[m][jj] = buffer_load16(xr, in ? 2u * ((uint32_t)m * K + 2u * off + 8u * jj) : kOob);
+  uint4 wc[kR];
+  uint32_t ws[kR];
+#pragma unroll
+  for (int rho = 0; rho < kR; ++rho) {
+    wc[rho] = buffer_load16<kCachePolicyNT>(wr, coff + rho * row_bytes);
+    ws[rho] = buffer_load2<kCachePolicyNT>(wsr, soff + rho * row_scales);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  half8v xv[kM][4];
+  float unscale[kM];
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      mx = max(max(max(mx, bf16x2_absmax_bits(xb[m][jj].x)), bf16x2_absmax_bits(xb[m][jj].y)),
+               max(bf16x2_absmax_bits(xb[m][jj].z), bf16x2_absmax_bits(xb[m][jj].w)));
+    mx = wave_max_u32(mx);
+    // k = (biased exponent of the max) - 127 - 15, kept where 2^-k and 2^k
+    // are normal fp32 numbers.
+    const int k = min(max((int)(mx >> 7) - 142, -126), 126);
+    const float pre = __uint_as_float((uint32_t)(127 - k) << 23);
+    unscale[m] = __uint_as_float((uint32_t)(127 + k) << 23);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t wv[4] = {xb[m][jj].x, xb[m][jj].y, xb[m][jj].z, xb[m][jj].w};
+      half8v h;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float lo = __uint_as_float(wv[t] << 16) * pre;
+        const float hi = __uint_as_float(wv[t] & 0xFFFF0000u) * pre;
+        const half2v p = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+        h[2 * t] = p.x;
+        h[2 * t + 1] = p.y;
+      }
+      xv[m][jj] = h;
+    }
+  }
+  float4v acc[kR][kM];
+#pragma unroll
+  for (int rho = 0; rho < kR; ++rho) {
+    const half2v s = e4m3x2_to_f16x2_div256(ws[rho]);
+    const half2v s0 = {s.x, s.x}, s1 = {s.y, s.y};
+#pragma unroll
+    for (int m = 0; m < kM; ++m) acc[rho][m] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const half8v wv = dequant8_f16_div256(word_of(wc[rho], jj), jj < 2 ? s0 : s1);
+#pragma unroll
+      for (int m = 0; m < kM; ++m)
+        acc[rho][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, xv[m][jj], acc[rho][m], 0, 0, 0);
+    }
+  }
+
+  const int i = lane & 15;
+  if ((i >> 2) == (lane >> 4)) {
+#pragma unroll
+    for (int rho = 0; rho < kR; ++rho)
+#pragma unroll
+      for (int m = 0; m < kM; ++m) s_diag[((slot * kR + rho) * kM + m) * 16 + i] = acc[rho][m] * unscale[m];
+  }
+  __syncthreads();
+  const float gw = *w_g;
+  for (int t = threadIdx.x; t < 16 * kR * kM; t += blockDim.x) {
+    const int pair = t >> 4, ii = t & 15;
+    float v = 0.f;
+    for (int w = 0; w < nslots; ++w) v += s_diag[(w * kR * kM + pair) * 16 + ii][ii & 3];
+    v += __shfl_xor(v, 1, 16);
+    v += __shfl_xor(v, 2, 16);
+    v += __shfl_xor(v, 4, 16);
+    v += __shfl_xor(v, 8, 16);
+    const int rho = pair / kM, m = pair % kM;
+    if (ii == 0 && m < M && n0 + rho < N) out[(int64_t)m * N + n0 + rho] = (uint16_t)f32_to_bf16_rne(v * gw);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Row-block GEMM (M <= 16).
 //
 //  - One workgroup per 16 weight rows; its 4 waves split K in 128-value
@@ -240,7 +355,29 @@ void launch_rowslot(const uint8_t* ac, const uint8_t* as, const float* ag, const
   hipLaunchKernelGGL((nvfp4_gemv_rowslot_kernel<kM, kR>), dim3((unsigned)((N + kR - 1) / kR)), dim3(64 * nslots),
                      lds, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, M, N, K);
 }
+template <int kM, int kR>
+void launch_w4a16_rowslot(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out, int M,
+                          int N, int K, hipStream_t stream) {
+  const int nslots = (K / 2 + 1023) / 1024;
+  const size_t lds = (size_t)nslots * kR * kM * 16 * sizeof(float4v);
+  hipLaunchKernelGGL((nvfp4_gemv_w4a16_rowslot_kernel<kM, kR>), dim3((unsigned)((N + kR - 1) / kR)),
+                     dim3(64 * nslots), lds, stream, (const uint16_t*)x, wc, ws, wg, (uint16_t*)out, M, N, K);
+}
 }  // namespace
+
+bool nvfp4_w4a16_decode_supported(int64_t M, int64_t K) {
+  return M >= 1 && M <= 2 && K > 0 && K % 128 == 0 && K <= (int64_t)kMaxSlots * 2048;
+}
+
+hipError_t launch_nvfp4_w4a16_decode(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
+                                     int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (M == 1) {
+    launch_w4a16_rowslot<1, 8>(x, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
+  } else {
+    launch_w4a16_rowslot<2, 4>(x, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_nvfp4_gemm_decode(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
                                     const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,

@@ -49,6 +49,35 @@ __global__ __launch_bounds__(64) void nvfp4_gemm_simple_kernel(
   }
 }
 
+// Weight-only NVFP4: out = bf16_RNE(g_w sum_b s_w sum_{k in b} x e_w); each
+// x * e_w is exact in fp32 (8 x 2 significant bits), the block sums round.
+__global__ __launch_bounds__(64) void nvfp4_w4a16_simple_kernel(const uint16_t* __restrict__ x,
+                                                                const uint8_t* __restrict__ w_codes,
+                                                                const uint8_t* __restrict__ w_scales,
+                                                                const float* __restrict__ w_g,
+                                                                uint16_t* __restrict__ out, int M, int N, int K) {
+  const int n = blockIdx.x * 64 + threadIdx.x;
+  if (n >= N) return;
+  const int nb = K / 16;
+  for (int m = blockIdx.y; m < M; m += gridDim.y) {
+    const uint16_t* xr = x + (int64_t)m * K;
+    const uint2* wr = (const uint2*)(w_codes + (int64_t)n * (K / 2));
+    const uint8_t* wsr = w_scales + (int64_t)n * nb;
+    float acc = 0.0f;
+    for (int b = 0; b < nb; ++b) {
+      const uint2 wv = wr[b];
+      float bs = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t ww = e < 8 ? wv.x : wv.y;
+        bs += bf16_bits_to_f32(xr[16 * b + e]) * e2m1_value((ww >> (4 * (e & 7))) & 15u);
+      }
+      acc += e4m3_to_f32(wsr[b]) * bs;
+    }
+    out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(acc * (*w_g));
+  }
+}
+
 __global__ __launch_bounds__(64) void int4g_gemm_simple_kernel(const uint16_t* __restrict__ x,
                                                                const uint8_t* __restrict__ q,
                                                                const uint16_t* __restrict__ s,
@@ -74,6 +103,13 @@ __global__ __launch_bounds__(64) void int4g_gemm_simple_kernel(const uint16_t* _
   }
   out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(acc);
   }
+}
+
+hipError_t launch_nvfp4_w4a16_simple(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
+                                     int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  hipLaunchKernelGGL(nvfp4_w4a16_simple_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)(M < 65535 ? M : 65535)),
+                     dim3(64), 0, stream, (const uint16_t*)x, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K);
+  return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_gemm_simple(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,

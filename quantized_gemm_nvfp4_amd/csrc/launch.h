@@ -31,6 +31,14 @@ hipError_t launch_nvfp4_gemm_simple(const uint8_t* ac, const uint8_t* as, const 
                                     const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
                                     int64_t K, hipStream_t stream);
 
+// Weight-only NVFP4: out[M, N] bf16 = g_w * x . dequant(W)^T, x bf16.
+// decode: nvfp4_w4a16_decode_supported(M, K).  simple: K % 16 == 0.
+bool nvfp4_w4a16_decode_supported(int64_t M, int64_t K);
+hipError_t launch_nvfp4_w4a16_decode(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
+                                     int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_nvfp4_w4a16_simple(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
+                                     int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 // INT4 per-group (128) W4A16 kernels; out[M, N] bf16 = x . dequant(q, s)^T.
 // decode: M <= 16.  tiled: any M.  simple: any M.  All need K % 128 == 0.
 hipError_t launch_int4g_gemm_decode(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,
