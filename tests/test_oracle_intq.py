@@ -97,3 +97,71 @@ def test_int4_gemm_vs_triple_loop():
             ref[i, j] = acc
     assert np.allclose(I.int4g_gemm_fp64(x, packed, sbits), ref, rtol=1e-12, atol=1e-15)
     assert np.array_equal(I.int4g_gemm(x, packed, sbits), F.bf16_round(I.int4g_gemm_fp64(x, packed, sbits)))
+
+
+# ------------------------------------------------------------- asymmetric --
+def test_asym_page_formula_worked_group(golden):
+    g = golden("int4_asym_worked_example.txt")
+    x = np.array([float(t) for t in g["page_values"]])
+    s, z, q, xh = I.asymmetric_quantize(x, 4)
+    assert s == 5.0 / 15.0 and z == int(g["page_z"][0])
+    assert list(q) == [int(t) for t in g["page_q"]]
+    assert np.max(np.abs(x - xh)) <= s / 2 + 1e-15
+
+
+def test_asym_stored_int4_worked_group(golden):
+    g = golden("int4_asym_worked_example.txt")
+    row = np.zeros((1, 128), dtype=np.float32)
+    row[0, :8] = [float(t) for t in g["page_values"]]
+    packed, sb, z, q = I.int4g_asym_quantize(F.bf16_bits(row))
+    assert sb[0, 0] == int(g["stored_scale_bits"][0], 16)
+    assert z[0, 0] == int(g["stored_z"][0])
+    assert list(q[0, :8]) == [int(t) for t in g["stored_q8"]]
+    assert np.all(q[0, 8:] == 3)
+    assert list(packed[0, :4]) == [int(t, 16) for t in g["stored_bytes8"]]
+    assert np.all(packed[0, 4:] == 0x33)
+
+
+def test_asym_bounds_brute_force_and_exact_zero():
+    bits = workloads.random_bf16(81, (24, 512), sigma=0.02, outlier_frac=0.01, outlier_mul=10, zero_frac=0.1)
+    w = F.bf16_from_bits(bits).astype(np.float64)
+    packed, sb, z, q = I.int4g_asym_quantize(bits)
+    s = np.repeat(F.fp16_from_bits(sb), 128, axis=1)
+    zz = np.repeat(z.astype(np.float64), 128, axis=1)
+    xh = I.int4g_asym_dequantize(packed, sb, z)
+    err = np.abs(w - xh)
+    # zero is exactly representable
+    assert np.all(xh[w == 0] == 0)
+    # elements whose level was not clamped: within s/2, and at the nearest level
+    unclamped = (q > 0) & (q < 15)
+    assert np.all(err[unclamped] <= s[unclamped] / 2 * (1 + 1e-6))
+    lv = np.arange(16)[None, None, :]
+    levels = s[..., None] * (lv - zz[..., None])
+    best = np.min(np.abs(w[..., None] - levels), axis=-1)
+    assert np.all(err <= best + 1e-12 * np.abs(w).max())
+    # everything: within 1.5 s (a clamp at the ends of the widened range)
+    assert np.all(err <= 1.5 * s + 1e-12)
+
+
+def test_asym_zero_group_and_constant_group():
+    w = np.zeros((2, 256), dtype=np.float32)
+    w[1, 128:] = 0.25                           # one constant positive group
+    packed, sb, z, q = I.int4g_asym_quantize(F.bf16_bits(w))
+    xh = I.int4g_asym_dequantize(packed, sb, z)
+    assert np.all(xh[0] == 0) and np.all(xh[1, :128] == 0)
+    np.testing.assert_allclose(xh[1, 128:], 0.25, rtol=2e-3)
+
+
+def test_asym_gemm_vs_triple_loop():
+    rng = np.random.default_rng(9)
+    x = F.bf16_round(rng.normal(size=(2, 256)).astype(np.float32)).astype(np.float32)
+    w = F.bf16_round((0.02 * rng.normal(size=(3, 256)) + 0.01).astype(np.float32)).astype(np.float32)
+    packed, sb, z, q = I.int4g_asym_quantize(F.bf16_bits(w))
+    y = I.int4g_asym_gemm_fp64(F.bf16_bits(x), packed, sb, z)
+    s = F.fp16_from_bits(sb)
+    for m in range(2):
+        for n in range(3):
+            tot = 0.0
+            for k in range(256):
+                tot += float(x[m, k]) * float(s[n, k // 128]) * (int(q[n, k]) - int(z[n, k // 128]))
+            assert abs(y[m, n] - tot) <= 1e-12 * (1 + abs(tot))
