@@ -323,7 +323,24 @@ def run_int4(torch, q, iters=64, copies=8):
     ms = t0.elapsed_time(t1) / 5
     out["M2048"] = {"ms": ms, "tflops": 2.0 * 2048 * N * K / (ms * 1e-3) / 1e12}
     log(f"int4 M=2048: {ms:.3f} ms")
+    del rot
+    # asymmetric (zero-point) variant of the same weight, M = 1
+    import workloads
+    qa, sa, za = q.int4g_asym_quantize(dev_bf16(torch, workloads.int4_w()))
+    rot = [(qa.clone(), sa.clone(), za.clone()) for _ in range(copies)]
+    del qa, sa, za
+    x = dev_bf16(torch, x_bits[:1])
+    y = torch.empty((1, N), dtype=torch.bfloat16, device="cuda:0")
+    alg_bytes = N * K // 2 + N * (K // 128) * 3 + K * 2 + N * 2
+    ref = q.int4g_asym_gemv(x, *rot[(iters - 1) % copies]).clone()
+    us = graph_time_us(torch, lambda i: q.int4g_asym_gemv(x, *rot[i % copies], out=y), iters)
+    assert torch.equal(y, ref), "graph replay differs from the eager call"
+    out["asym_M1"] = {"us": us, "GBps": alg_bytes / (us * 1e-6) / 1e9,
+                      "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    log(f"int4 asym M=1: {us:.2f} us, {out['asym_M1']['GBps']:.0f} GB/s")
+    del rot
     return out
+
 
 
 def run_copy_calibration(torch, nbytes=1 << 30):

@@ -221,6 +221,35 @@ const char* nvfp4_status_string(nvfp4_status s);
 /* Detail of the last error raised on the calling thread ("" if none). */
 const char* nvfp4_last_error(void);
 
+/*
+ * Asymmetric (zero-point) INT4 per-group quantization of a bf16 weight
+ * W [N, K] (group 128 along K, K % 128 == 0).  Passage: the asymmetric map
+ * of "Cuantización e inferencia local", formula block: s = (x_max - x_min) /
+ * (2^b - 1), z = round(-x_min / s), q = clamp(round(x / s) + z, 0, 2^b - 1),
+ * x_hat = s (q - z), with b = 4 and one (s, z) per group.
+ * The range is widened to contain 0 (lo = min(0, min w), hi = max(0, max w)),
+ * so z is in [0, 15] and 0 is exact; s16 = fp16_RNE(fl32(fl32(hi - lo) /
+ * 15)), z = clamp(rint(fl32(-lo / s16)), 0, 15), q = clamp(rint(fl32(w /
+ * s16)) + z, 0, 15); q = z = 0 where s16 == 0.
+ * Outputs: q [N, K/2] unsigned nibbles (element 2j in bits 0-3 of byte j),
+ * scales [N, K/128] fp16, zeros [N, K/128] uint8.  group must be 128.
+ */
+nvfp4_status int4g_asym_quantize(const void* w_bf16, int64_t N, int64_t K, int64_t group,
+                                 uint8_t* q, void* scales_fp16, uint8_t* zeros, void* stream);
+
+/*
+ * out[M, N] (bf16) = bf16_RNE( sum_k x[m, k] * s16[n, k/128] * (q[n, k] -
+ * z[n, k/128]) ), x bf16 [M, K] (the same passage; weight-only).  M <= 2
+ * (K <= 32768) runs the row-slot GEMV that streams q once; other shapes a
+ * one-output-per-thread kernel.  algo: NVFP4_ALGO_AUTO, _DECODE or _SIMPLE.
+ */
+nvfp4_status int4g_asym_gemv(const void* x_bf16, const uint8_t* q, const void* scales_fp16,
+                             const uint8_t* zeros, void* out_bf16, int64_t M, int64_t N, int64_t K,
+                             int64_t group, void* stream);
+nvfp4_status int4g_asym_gemv_ex(const void* x_bf16, const uint8_t* q, const void* scales_fp16,
+                                const uint8_t* zeros, void* out_bf16, int64_t M, int64_t N, int64_t K,
+                                int64_t group, int algo, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,8 @@ Function names follow the C ABI:
 * ``nvfp4_gemm_w4a16(x, w)``          -> bf16 [M, N]; x bf16 (weight-only NVFP4)
 * ``int4g_quantize(w, group=128)``    -> (q, scales_fp16)
 * ``int4g_gemv(x, q, scales, ...)``   -> bf16 [M, N]
+* ``int4g_asym_quantize(w)``          -> (q, scales_fp16, zeros_u8), zero-point INT4
+* ``int4g_asym_gemv(x, q, s, z)``     -> bf16 [M, N]
 * ``nvfp4_linear(x, w)``              -> quantize x, then nvfp4_gemm (two calls)
 """
 import ctypes
@@ -39,6 +41,9 @@ SIGNATURES = {
     "int4g_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "int4g_gemv": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "int4g_gemv_ex": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P], ctypes.c_int),
+    "int4g_asym_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
+    "int4g_asym_gemv": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
+    "int4g_asym_gemv_ex": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P], ctypes.c_int),
     "nvfp4_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "nvfp4_last_error": ([], ctypes.c_char_p),
 }
@@ -216,4 +221,41 @@ def int4g_gemv(x, q, scales, group=128, algo=ALGO_AUTO, out=None):
     _need(out, torch.bfloat16, (M, N), "out")
     _check(lib().int4g_gemv_ex(_ptr(x), _ptr(q), _ptr(scales), _ptr(out), M, N, K, group, int(algo),
                                _stream(x)))
+    return out
+
+
+def int4g_asym_quantize(w, group=128, out=None):
+    """Asymmetric (zero-point) INT4 per-group quantization of a bf16 [N, K]
+    weight.  Returns (q uint8 [N, K/2], scales fp16 [N, K/128], zeros uint8
+    [N, K/128])."""
+    torch = _torch()
+    _need(w, torch.bfloat16, None, "w")
+    N, K = w.shape
+    if out is None:
+        q = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+        s = torch.empty((N, K // group), dtype=torch.float16, device=w.device)
+        z = torch.empty((N, K // group), dtype=torch.uint8, device=w.device)
+    else:
+        q, s, z = out
+    _need(q, torch.uint8, (N, K // 2), "q")
+    _need(s, torch.float16, (N, K // group), "scales")
+    _need(z, torch.uint8, (N, K // group), "zeros")
+    _check(lib().int4g_asym_quantize(_ptr(w), N, K, group, _ptr(q), _ptr(s), _ptr(z), _stream(w)))
+    return q, s, z
+
+
+def int4g_asym_gemv(x, q, scales, zeros, group=128, algo=ALGO_AUTO, out=None):
+    """bf16 [M, N] = x . (s16 (q - z))^T for the asymmetric INT4 weight."""
+    torch = _torch()
+    _need(x, torch.bfloat16, None, "x")
+    M, K = x.shape
+    N = q.shape[0]
+    _need(q, torch.uint8, (N, K // 2), "q")
+    _need(scales, torch.float16, (N, K // group), "scales")
+    _need(zeros, torch.uint8, (N, K // group), "zeros")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, (M, N), "out")
+    _check(lib().int4g_asym_gemv_ex(_ptr(x), _ptr(q), _ptr(scales), _ptr(zeros), _ptr(out), M, N, K, group, algo,
+                                    _stream(x)))
     return out

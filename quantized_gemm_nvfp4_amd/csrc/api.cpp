@@ -299,4 +299,66 @@ nvfp4_status int4g_gemv(const void* x_bf16, const uint8_t* q, const void* scales
   return int4g_gemv_ex(x_bf16, q, scales_fp16, out_bf16, M, N, K, group, NVFP4_ALGO_AUTO, stream);
 }
 
+nvfp4_status int4g_asym_quantize(const void* w_bf16, int64_t N, int64_t K, int64_t group, uint8_t* q,
+                                 void* scales_fp16, uint8_t* zeros, void* stream) {
+  REQUIRE_PTR(w_bf16);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(scales_fp16);
+  REQUIRE_PTR(zeros);
+  if (nvfp4_status s = check_dims(N, "N", K, "K", group, "group")) return s;
+  if (group != 128) return fail(NVFP4_ERR_UNSUPPORTED, "group=%lld; only 128 is supported", (long long)group);
+  if (K % 128 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of the group (128)", (long long)K);
+  REQUIRE_ALIGN(w_bf16, 16);
+  REQUIRE_ALIGN(q, 16);
+  REQUIRE_ALIGN(scales_fp16, 16);
+  const Range outs[3] = {{q, N * K / 2, "q"}, {scales_fp16, N * (K / 128) * 2, "scales"},
+                         {zeros, N * (K / 128), "zeros"}};
+  const Range ins[1] = {{w_bf16, N * K * 2, "w"}};
+  if (N == 0 || K == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 3, ins, 1)) return s;
+  return hip_status(nvfp4k::launch_int4g_asym_quantize(w_bf16, N, K, q, scales_fp16, zeros, (hipStream_t)stream),
+                    "int4g_asym_quantize launch");
+}
+
+nvfp4_status int4g_asym_gemv_ex(const void* x_bf16, const uint8_t* q, const void* scales_fp16, const uint8_t* zeros,
+                                void* out_bf16, int64_t M, int64_t N, int64_t K, int64_t group, int algo,
+                                void* stream) {
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(scales_fp16);
+  REQUIRE_PTR(zeros);
+  REQUIRE_PTR(out_bf16);
+  if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
+  if (group != 128) return fail(NVFP4_ERR_UNSUPPORTED, "group=%lld; only 128 is supported", (long long)group);
+  if (K % 128 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of the group (128)", (long long)K);
+  if (algo != NVFP4_ALGO_AUTO && algo != NVFP4_ALGO_DECODE && algo != NVFP4_ALGO_SIMPLE)
+    return fail(NVFP4_ERR_INVALID_ARG, "algo %d is not available for the asymmetric INT4 GEMV", algo);
+  REQUIRE_ALIGN(x_bf16, 16);
+  REQUIRE_ALIGN(q, 16);
+  REQUIRE_ALIGN(scales_fp16, 16);
+  REQUIRE_ALIGN(out_bf16, 16);
+  const Range outs[1] = {{out_bf16, M * N * 2, "out"}};
+  const Range ins[4] = {{x_bf16, M * K * 2, "x"}, {q, N * K / 2, "q"}, {scales_fp16, N * (K / 128) * 2, "scales"},
+                        {zeros, N * (K / 128), "zeros"}};
+  if (M == 0 || N == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 1, ins, 4)) return s;
+  const bool decode_ok = nvfp4k::int4g_asym_decode_supported(M, K);
+  if (algo == NVFP4_ALGO_AUTO) algo = decode_ok ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE;
+  hipStream_t st = (hipStream_t)stream;
+  if (algo == NVFP4_ALGO_DECODE) {
+    if (!decode_ok)
+      return fail(NVFP4_ERR_UNSUPPORTED, "asymmetric decode kernel needs M <= 2 and 0 < K <= 32768 (M=%lld, K=%lld)",
+                  (long long)M, (long long)K);
+    return hip_status(nvfp4k::launch_int4g_asym_decode(x_bf16, q, scales_fp16, zeros, out_bf16, M, N, K, st),
+                      "int4g_asym_gemv decode launch");
+  }
+  return hip_status(nvfp4k::launch_int4g_asym_simple(x_bf16, q, scales_fp16, zeros, out_bf16, M, N, K, st),
+                    "int4g_asym_gemv simple launch");
+}
+
+nvfp4_status int4g_asym_gemv(const void* x_bf16, const uint8_t* q, const void* scales_fp16, const uint8_t* zeros,
+                             void* out_bf16, int64_t M, int64_t N, int64_t K, int64_t group, void* stream) {
+  return int4g_asym_gemv_ex(x_bf16, q, scales_fp16, zeros, out_bf16, M, N, K, group, NVFP4_ALGO_AUTO, stream);
+}
+
 }  // extern "C"

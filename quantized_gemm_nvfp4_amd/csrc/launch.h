@@ -48,4 +48,14 @@ hipError_t launch_int4g_gemm_tiled(const void* x, const uint8_t* q, const void* 
 hipError_t launch_int4g_gemm_simple(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,
                                     int64_t N, int64_t K, hipStream_t stream);
 
+// Asymmetric (zero-point) INT4 per-group (128): unsigned nibbles, fp16
+// scales and uint8 zero points per group; out = x . (s16 (q - z))^T.
+hipError_t launch_int4g_asym_quantize(const void* w, int64_t N, int64_t K, uint8_t* q, void* scales, uint8_t* zeros,
+                                      hipStream_t stream);
+bool int4g_asym_decode_supported(int64_t M, int64_t K);
+hipError_t launch_int4g_asym_decode(const void* x, const uint8_t* q, const void* s, const uint8_t* z, void* out,
+                                    int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_int4g_asym_simple(const void* x, const uint8_t* q, const void* s, const uint8_t* z, void* out,
+                                    int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 }  // namespace nvfp4k
