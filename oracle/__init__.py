@@ -14,6 +14,7 @@ Everything is plain numpy, written from the pages' definitions:
   FP8 E4M3 ("float8_e4m3fn"), and the bf16 / fp16 round-to-nearest-even casts.
 * ``nvfp4``    -- NVFP4 quantize / dequantize and the block-scaled GEMM.
 * ``scale_rules`` -- block-scale selection: absmax, four-over-six, MSE.
+* ``lora``     -- the run-time low-rank branch next to the NVFP4 product.
 * ``intq``     -- the symmetric integer formula and its INT4 per-group form.
 * ``metrics``  -- the parity metrics (relative L2, per-row max-abs).
 
