@@ -290,6 +290,84 @@ def run_dit(torch, q, reps=3):
     return {"ms_4_steps": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
+def _event_ms(torch, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / reps
+
+
+def run_lora(torch, q, reps=10, rank=32):
+    """Run-time low-rank branch next to the NVFP4 product: the diffusion qkv
+    layer [4096 x 3072] x [9216 x 3072] with a rank-32 adapter (quantize with
+    the fused down projection, then the GEMM with the branch in its epilogue)
+    against the same layer without it; and decode M=1 on the 21504 x 5376
+    weight with a rank-32 adapter."""
+    import workloads
+    x = dev_bf16(torch, workloads.dit_x(0))
+    w = q.nvfp4_quantize(dev_bf16(torch, workloads.dit_weights()[0]))
+    down, up = [dev_bf16(torch, b) for b in workloads.dit_lora(rank)]
+    M, N, K = 4096, 9216, 3072
+    a = q.nvfp4_quantize(x)
+    t = torch.empty((M, rank), dtype=torch.float32, device="cuda:0")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    g = torch.empty(1, dtype=torch.float32, device="cuda:0")
+    a_l = (torch.empty_like(a[0]), torch.empty_like(a[1]), g)
+
+    def plain():
+        q.nvfp4_quantize(x, out=a)
+        q.nvfp4_gemm(a, w, out=y)
+
+    def lora():
+        q.nvfp4_quantize_lora(x, down, out=(a_l[0], a_l[1], g, t))
+        q.nvfp4_gemm_lora(a_l, w, t, up, out=y)
+
+    out = {"rank": rank}
+    out["dit_qkv_ms"] = _event_ms(torch, plain, reps)
+    out["dit_qkv_lora_ms"] = _event_ms(torch, lora, reps)
+    out["dit_qkv_quant_ms"] = _event_ms(torch, lambda: q.nvfp4_quantize(x, out=a), reps)
+    out["dit_qkv_quant_lora_ms"] = _event_ms(torch, lambda: q.nvfp4_quantize_lora(x, down, out=(a_l[0], a_l[1], g, t)),
+                                             reps)
+    out["dit_qkv_gemm_ms"] = _event_ms(torch, lambda: q.nvfp4_gemm(a, w, out=y), reps)
+    out["dit_qkv_gemm_lora_ms"] = _event_ms(torch, lambda: q.nvfp4_gemm_lora(a_l, w, t, up, out=y), reps)
+    flops = 2.0 * M * N * K
+    out["dit_qkv_tflops"] = flops / (out["dit_qkv_ms"] * 1e-3) / 1e12
+    out["overhead_frac"] = out["dit_qkv_lora_ms"] / out["dit_qkv_ms"] - 1.0
+    log(f"lora r={rank} dit qkv: {out['dit_qkv_ms']:.3f} ms plain, {out['dit_qkv_lora_ms']:.3f} ms with the branch "
+        f"(quant {out['dit_qkv_quant_ms']:.3f} -> {out['dit_qkv_quant_lora_ms']:.3f}, "
+        f"gemm {out['dit_qkv_gemm_ms']:.3f} -> {out['dit_qkv_gemm_lora_ms']:.3f})")
+    # decode M = 1 with the branch (weights rotated past the last-level cache)
+    xd, _ = workloads.decode_x()
+    wd = q.nvfp4_quantize(dev_bf16(torch, workloads.decode_w()))
+    copies, iters = 16, 64
+    ws = [(wd[0].clone(), wd[1].clone(), wd[2].clone()) for _ in range(copies)]
+    Nd, Kd = 21504, 5376
+    x1 = dev_bf16(torch, xd[:1])
+    dn1 = dev_bf16(torch, workloads.random_bf16(77, (rank, Kd), sigma=0.02))
+    up1 = dev_bf16(torch, workloads.random_bf16(78, (Nd, rank), sigma=0.02))
+    a1 = q.nvfp4_quantize(x1)
+    t1 = torch.empty((1, rank), dtype=torch.float32, device="cuda:0")
+    y1 = torch.empty((1, Nd), dtype=torch.bfloat16, device="cuda:0")
+    out["decode_m1_us"] = graph_time_us(torch, lambda i: q.nvfp4_gemm(a1, ws[i % copies], out=y1), iters)
+    out["decode_m1_lora_us"] = graph_time_us(torch, lambda i: q.nvfp4_gemm_lora(a1, ws[i % copies], t1, up1, out=y1),
+                                             iters)
+
+    def dec_full(i):
+        q.nvfp4_quantize_lora(x1, dn1, out=(a1[0], a1[1], a1[2], t1))
+        q.nvfp4_gemm_lora(a1, ws[i % copies], t1, up1, out=y1)
+    out["decode_m1_lora_incl_quant_us"] = graph_time_us(torch, dec_full, iters)
+    log(f"lora r={rank} decode M=1: {out['decode_m1_us']:.2f} us plain, {out['decode_m1_lora_us']:.2f} us with the "
+        f"branch, {out['decode_m1_lora_incl_quant_us']:.2f} us incl. quantize + down projection")
+    del ws
+    return out
+
+
 def run_int4(torch, q, iters=64, copies=8):
     import workloads
     w_bits = workloads.int4_w()
@@ -394,7 +472,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the prefill step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["decode", "dit", "int4", "weight_quant"],
+    ap.add_argument("--only", choices=["decode", "dit", "int4", "weight_quant", "lora"],
                     help="time only this extra workload")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -410,7 +488,7 @@ def main():
 
     if args.only:
         res = {"decode": run_decode, "dit": run_dit, "int4": run_int4,
-               "weight_quant": run_weight_quant}[args.only](torch, q)
+               "weight_quant": run_weight_quant, "lora": run_lora}[args.only](torch, q)
         print(json.dumps({"only": args.only, "result": res}))
         return
     pre = run_prefill(torch, q, args.steps, args.warmup)
@@ -422,6 +500,7 @@ def main():
         extras["dit"] = run_dit(torch, q)
         extras["int4"] = run_int4(torch, q)
         extras["weight_quant"] = run_weight_quant(torch, q)
+        extras["lora"] = run_lora(torch, q)
     if args.copy_calibration:
         run_copy_calibration(torch)
     cpu = None

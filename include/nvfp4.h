@@ -250,6 +250,52 @@ nvfp4_status int4g_asym_gemv_ex(const void* x_bf16, const uint8_t* q, const void
                                 const uint8_t* zeros, void* out_bf16, int64_t M, int64_t N, int64_t K,
                                 int64_t group, int algo, void* stream);
 
+/*
+ * Low-rank (LoRA) branch next to an NVFP4 layer.  Passage: "NVFP4 en
+ * difusión", section 3 (fine-tuning a model already in 4 bits): a low-rank
+ * correction cannot be folded into NVFP4 weights, so it runs at run time
+ * beside the quantized product, and its down projection is computed in the
+ * same pass that quantizes the activation.  The layer is
+ *   y = bf16_RNE( g_a g_w A_hat W_hat^T + T L_up^T ),  T = X L_down^T,
+ * with X the bf16 activation before quantization, L_down bf16 [r, cols]
+ * and L_up bf16 [N, r] (nn.Linear layouts; a LoRA scale alpha / r is
+ * folded into L_up by the caller).  Rank r: a multiple of 8 in [8, 128];
+ * other values return NVFP4_ERR_UNSUPPORTED.
+ *
+ * nvfp4_quantize_lora: nvfp4_quantize (absmax rule) of x [rows, cols] plus
+ * lora_t [rows, r] fp32 = X L_down^T, with X read once for the global
+ * amax and the down projection.  Each bf16 product is exact in fp32, the
+ * sums are fp32 in a fixed order (the same for every call with the same
+ * shapes).  The workspace is always required, also with
+ * use_given_global_scale: nvfp4_quantize_lora_workspace_bytes(rows, cols,
+ * r) bytes, 4-byte aligned, no initialization (it holds partial maxima and,
+ * when the down projection is split along K, partial products).  lora_down_bf16 and lora_t are 16-byte aligned
+ * and must not overlap the outputs.  Other arguments and errors as
+ * nvfp4_quantize.
+ */
+size_t nvfp4_quantize_lora_workspace_bytes(int64_t rows, int64_t cols, int64_t r);
+nvfp4_status nvfp4_quantize_lora(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes,
+                                 uint8_t* scales, float* global_scale, int use_given_global_scale,
+                                 const void* lora_down_bf16, int64_t r, float* lora_t, void* workspace,
+                                 void* stream);
+
+/*
+ * nvfp4_gemm_lora: out[M, N] (bf16) = bf16_RNE( g_a g_w sum_k A[m, k] W[n, k]
+ * + sum_j lora_t[m, j] L_up[n, j] ), A and W as nvfp4_gemm, lora_t fp32
+ * [M, r] (as nvfp4_quantize_lora writes it), lora_up_bf16 [N, r].  The
+ * branch is added in the GEMM epilogue before the single rounding (in the
+ * tiled kernel on the matrix cores with T split into two bf16 parts, which
+ * keeps about 16 bits of T).  Kernel choice as nvfp4_gemm(_ex).
+ */
+nvfp4_status nvfp4_gemm_lora(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                             const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                             const float* lora_t, const void* lora_up_bf16, int64_t r, void* out_bf16,
+                             int64_t M, int64_t N, int64_t K, void* stream);
+nvfp4_status nvfp4_gemm_lora_ex(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                                const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                                const float* lora_t, const void* lora_up_bf16, int64_t r, void* out_bf16,
+                                int64_t M, int64_t N, int64_t K, int algo, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,10 @@ SIGNATURES = {
     "int4g_asym_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "int4g_asym_gemv": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "int4g_asym_gemv_ex": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P], ctypes.c_int),
+    "nvfp4_quantize_lora_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),
+    "nvfp4_quantize_lora": ([_P, _I64, _I64, _P, _P, _P, _I, _P, _I64, _P, _P, _P], ctypes.c_int),
+    "nvfp4_gemm_lora": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "nvfp4_gemm_lora_ex": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _P, _I64, _I64, _I64, _I, _P], ctypes.c_int),
     "nvfp4_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "nvfp4_last_error": ([], ctypes.c_char_p),
 }
@@ -191,6 +195,74 @@ def nvfp4_gemm_w4a16(x, w, algo=ALGO_AUTO, out=None):
 def nvfp4_linear(x, w, algo=ALGO_AUTO):
     """Dynamic activation quantization followed by the block-scaled GEMM."""
     return nvfp4_gemm(nvfp4_quantize(x), w, algo=algo)
+
+
+def nvfp4_quantize_lora(x, lora_down, global_scale=None, out=None):
+    """nvfp4_quantize (absmax) of x [rows, cols] plus T = x . lora_down^T.
+
+    lora_down: bf16 [r, cols].  out: optional (codes, scales, global_scale,
+    t) buffers.  Returns (codes, scales, global_scale, t fp32 [rows, r]).
+    """
+    torch = _torch()
+    _need(x, torch.bfloat16, None, "x")
+    if x.dim() != 2 or lora_down.dim() != 2:
+        raise ValueError("x and lora_down must be 2-D")
+    rows, cols = x.shape
+    r = lora_down.shape[0]
+    _need(lora_down, torch.bfloat16, (r, cols), "lora_down")
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+        g = global_scale if global_scale is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+        t = torch.empty((rows, r), dtype=torch.float32, device=x.device)
+    else:
+        codes, scales, g, t = out
+        if global_scale is not None and g is not global_scale:
+            raise ValueError("pass the given global scale as out[2]")
+    _need(codes, torch.uint8, (rows, cols // 2), "codes")
+    _need(scales, torch.uint8, (rows, cols // 16), "scales")
+    _need(g, torch.float32, (1,), "global_scale")
+    _need(t, torch.float32, (rows, r), "t")
+    ws = torch.empty(lib().nvfp4_quantize_lora_workspace_bytes(rows, cols, r), dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_quantize_lora(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(g),
+                                     1 if global_scale is not None else 0, _ptr(lora_down), r, _ptr(t), _ptr(ws),
+                                     _stream(x)))
+    return codes, scales, g, t
+
+
+def nvfp4_gemm_lora(a, w, t, lora_up, algo=ALGO_AUTO, out=None):
+    """nvfp4_gemm(a, w) + t . lora_up^T, rounded once to bf16.
+
+    t: fp32 [M, r] (from nvfp4_quantize_lora); lora_up: bf16 [N, r].
+    """
+    torch = _torch()
+    ac, as_, ag = a
+    wc, ws, wg = w
+    M, N = ac.shape[0], wc.shape[0]
+    K = ac.shape[1] * 2
+    r = t.shape[1] if t.dim() == 2 else -1
+    _need(ac, torch.uint8, (M, K // 2), "a_codes")
+    _need(as_, torch.uint8, (M, K // 16), "a_scales")
+    _need(ag, torch.float32, (1,), "a_gscale")
+    _need(wc, torch.uint8, (N, K // 2), "w_codes")
+    _need(ws, torch.uint8, (N, K // 16), "w_scales")
+    _need(wg, torch.float32, (1,), "w_gscale")
+    _need(t, torch.float32, (M, r), "t")
+    _need(lora_up, torch.bfloat16, (N, r), "lora_up")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=ac.device)
+    _need(out, torch.bfloat16, (M, N), "out")
+    _check(lib().nvfp4_gemm_lora_ex(_ptr(ac), _ptr(as_), _ptr(ag), _ptr(wc), _ptr(ws), _ptr(wg), _ptr(t),
+                                    _ptr(lora_up), r, _ptr(out), M, N, K, int(algo), _stream(ac)))
+    return out
+
+
+def nvfp4_linear_lora(x, w, lora_down, lora_up, algo=ALGO_AUTO):
+    """NVFP4 layer with a run-time low-rank branch: quantize x (computing
+    T = x . lora_down^T in the same pass), then the GEMM with T . lora_up^T
+    added before the bf16 rounding."""
+    codes, scales, g, t = nvfp4_quantize_lora(x, lora_down)
+    return nvfp4_gemm_lora((codes, scales, g), w, t, lora_up, algo=algo)
 
 
 def int4g_quantize(w, group=128, out=None):

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libnvfp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["quantize.hip", "gemm_tiled.hip", "gemm_decode.hip", "gemm_simple.hip", "int4_gemm.hip", "int4_asym.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm_tiled.hip", "gemm_decode.hip", "gemm_simple.hip", "int4_gemm.hip", "int4_asym.hip", "lora.hip", "api.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -80,6 +80,73 @@ nvfp4_status check_dims(int64_t a, const char* an, int64_t b, const char* bn, in
   return NVFP4_OK;
 }
 
+// Shared by nvfp4_gemm_ex and nvfp4_gemm_lora_ex; lora_t == nullptr means
+// no low-rank branch (its arguments were validated by the caller).
+nvfp4_status gemm_impl(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale, void* out_bf16,
+                       int64_t M, int64_t N, int64_t K, int algo, const float* lora_t, const void* lora_up,
+                       int64_t r, void* stream) {
+  if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
+  if (K > 0) {  // with K == 0 the packed operands are empty and never read
+    REQUIRE_PTR(a_codes);
+    REQUIRE_PTR(a_scales);
+    REQUIRE_PTR(w_codes);
+    REQUIRE_PTR(w_scales);
+  }
+  REQUIRE_PTR(a_gscale);
+  REQUIRE_PTR(w_gscale);
+  REQUIRE_PTR(out_bf16);
+  if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
+  if (algo < NVFP4_ALGO_AUTO || algo > NVFP4_ALGO_SIMPLE) return fail(NVFP4_ERR_INVALID_ARG, "unknown algo %d", algo);
+  REQUIRE_ALIGN(a_codes, 16);
+  REQUIRE_ALIGN(a_scales, 16);
+  REQUIRE_ALIGN(w_codes, 16);
+  REQUIRE_ALIGN(w_scales, 16);
+  REQUIRE_ALIGN(out_bf16, 16);
+  REQUIRE_ALIGN(a_gscale, 4);
+  REQUIRE_ALIGN(w_gscale, 4);
+  const Range outs[1] = {{out_bf16, M * N * 2, "out"}};
+  const Range ins[8] = {{a_codes, M * K / 2, "a_codes"}, {a_scales, M * K / 16, "a_scales"},
+                        {a_gscale, 4, "a_gscale"},       {w_codes, N * K / 2, "w_codes"},
+                        {w_scales, N * K / 16, "w_scales"}, {w_gscale, 4, "w_gscale"},
+                        {lora_t, lora_t ? M * r * 4 : 0, "lora_t"}, {lora_up, lora_t ? N * r * 2 : 0, "lora_up"}};
+  if (M == 0 || N == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 1, ins, 8)) return s;
+  const bool k128 = (K % 128) == 0 && K > 0;
+  if (algo == NVFP4_ALGO_AUTO) algo = !k128 ? NVFP4_ALGO_SIMPLE : (M <= 16 ? NVFP4_ALGO_DECODE : NVFP4_ALGO_TILED);
+  hipStream_t st = (hipStream_t)stream;
+  switch (algo) {
+    case NVFP4_ALGO_TILED:
+      if (!k128) return fail(NVFP4_ERR_UNSUPPORTED, "tiled kernel needs K %% 128 == 0 and K > 0 (K=%lld)", (long long)K);
+      if (lora_t)
+        return hip_status(nvfp4k::launch_nvfp4_gemm_tiled_lora(a_codes, a_scales, a_gscale, w_codes, w_scales,
+                                                               w_gscale, out_bf16, M, N, K, lora_t, lora_up, r, st),
+                          "nvfp4_gemm_lora tiled launch");
+      return hip_status(nvfp4k::launch_nvfp4_gemm_tiled(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale,
+                                                        out_bf16, M, N, K, st),
+                        "nvfp4_gemm tiled launch");
+    case NVFP4_ALGO_DECODE:
+      if (!k128 || M > 16)
+        return fail(NVFP4_ERR_UNSUPPORTED, "decode kernel needs M <= 16 and K %% 128 == 0 (M=%lld, K=%lld)",
+                    (long long)M, (long long)K);
+      return hip_status(nvfp4k::launch_nvfp4_gemm_decode_lora(a_codes, a_scales, a_gscale, w_codes, w_scales,
+                                                              w_gscale, out_bf16, M, N, K, lora_t, lora_up, r, st),
+                        "nvfp4_gemm decode launch");
+    default:
+      return hip_status(nvfp4k::launch_nvfp4_gemm_simple_lora(a_codes, a_scales, a_gscale, w_codes, w_scales,
+                                                              w_gscale, out_bf16, M, N, K, lora_t, lora_up, r, st),
+                        "nvfp4_gemm simple launch");
+  }
+}
+
+// Rank limits shared by the two low-rank entry points.
+nvfp4_status check_rank(int64_t r) {
+  if (r < 8 || r > nvfp4k::kLoraMaxRank || r % 8 != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED, "rank r=%lld; supported ranks are multiples of 8 in [8, %d]", (long long)r,
+                nvfp4k::kLoraMaxRank);
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -87,6 +154,11 @@ extern "C" {
 int nvfp4_abi_version(void) { return 1; }
 
 size_t nvfp4_quantize_workspace_bytes(void) { return sizeof(uint32_t) * nvfp4k::kAmaxPartials; }
+
+size_t nvfp4_quantize_lora_workspace_bytes(int64_t rows, int64_t cols, int64_t r) {
+  if (rows < 0 || cols < 0 || r < 0 || rows > kMaxDim || cols > kMaxDim || r > nvfp4k::kLoraMaxRank) return 0;
+  return (size_t)nvfp4k::lora_workspace_bytes(rows, cols, r);
+}
 
 const char* nvfp4_status_string(nvfp4_status s) {
   switch (s) {
@@ -142,52 +214,8 @@ nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint
 nvfp4_status nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
                            const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale, void* out_bf16,
                            int64_t M, int64_t N, int64_t K, int algo, void* stream) {
-  if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
-  if (K > 0) {  // with K == 0 the packed operands are empty and never read
-    REQUIRE_PTR(a_codes);
-    REQUIRE_PTR(a_scales);
-    REQUIRE_PTR(w_codes);
-    REQUIRE_PTR(w_scales);
-  }
-  REQUIRE_PTR(a_gscale);
-  REQUIRE_PTR(w_gscale);
-  REQUIRE_PTR(out_bf16);
-  if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
-  if (algo < NVFP4_ALGO_AUTO || algo > NVFP4_ALGO_SIMPLE) return fail(NVFP4_ERR_INVALID_ARG, "unknown algo %d", algo);
-  REQUIRE_ALIGN(a_codes, 16);
-  REQUIRE_ALIGN(a_scales, 16);
-  REQUIRE_ALIGN(w_codes, 16);
-  REQUIRE_ALIGN(w_scales, 16);
-  REQUIRE_ALIGN(out_bf16, 16);
-  REQUIRE_ALIGN(a_gscale, 4);
-  REQUIRE_ALIGN(w_gscale, 4);
-  const Range outs[1] = {{out_bf16, M * N * 2, "out"}};
-  const Range ins[6] = {{a_codes, M * K / 2, "a_codes"}, {a_scales, M * K / 16, "a_scales"},
-                        {a_gscale, 4, "a_gscale"},       {w_codes, N * K / 2, "w_codes"},
-                        {w_scales, N * K / 16, "w_scales"}, {w_gscale, 4, "w_gscale"}};
-  if (M == 0 || N == 0) return ok();
-  if (nvfp4_status s = check_disjoint(outs, 1, ins, 6)) return s;
-  const bool k128 = (K % 128) == 0 && K > 0;
-  if (algo == NVFP4_ALGO_AUTO) algo = !k128 ? NVFP4_ALGO_SIMPLE : (M <= 16 ? NVFP4_ALGO_DECODE : NVFP4_ALGO_TILED);
-  hipStream_t st = (hipStream_t)stream;
-  switch (algo) {
-    case NVFP4_ALGO_TILED:
-      if (!k128) return fail(NVFP4_ERR_UNSUPPORTED, "tiled kernel needs K %% 128 == 0 and K > 0 (K=%lld)", (long long)K);
-      return hip_status(nvfp4k::launch_nvfp4_gemm_tiled(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale,
-                                                        out_bf16, M, N, K, st),
-                        "nvfp4_gemm tiled launch");
-    case NVFP4_ALGO_DECODE:
-      if (!k128 || M > 16)
-        return fail(NVFP4_ERR_UNSUPPORTED, "decode kernel needs M <= 16 and K %% 128 == 0 (M=%lld, K=%lld)",
-                    (long long)M, (long long)K);
-      return hip_status(nvfp4k::launch_nvfp4_gemm_decode(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale,
-                                                         out_bf16, M, N, K, st),
-                        "nvfp4_gemm decode launch");
-    default:
-      return hip_status(nvfp4k::launch_nvfp4_gemm_simple(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale,
-                                                         out_bf16, M, N, K, st),
-                        "nvfp4_gemm simple launch");
-  }
+  return gemm_impl(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_bf16, M, N, K, algo, nullptr,
+                   nullptr, 0, stream);
 }
 
 nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
@@ -359,6 +387,68 @@ nvfp4_status int4g_asym_gemv_ex(const void* x_bf16, const uint8_t* q, const void
 nvfp4_status int4g_asym_gemv(const void* x_bf16, const uint8_t* q, const void* scales_fp16, const uint8_t* zeros,
                              void* out_bf16, int64_t M, int64_t N, int64_t K, int64_t group, void* stream) {
   return int4g_asym_gemv_ex(x_bf16, q, scales_fp16, zeros, out_bf16, M, N, K, group, NVFP4_ALGO_AUTO, stream);
+}
+
+nvfp4_status nvfp4_quantize_lora(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                 float* global_scale, int use_given_global_scale, const void* lora_down_bf16,
+                                 int64_t r, float* lora_t, void* workspace, void* stream) {
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  REQUIRE_PTR(global_scale);
+  REQUIRE_PTR(lora_down_bf16);
+  REQUIRE_PTR(lora_t);
+  REQUIRE_PTR(workspace);
+  if (nvfp4_status s = check_dims(rows, "rows", cols, "cols", r, "r")) return s;
+  if (nvfp4_status s = check_rank(r)) return s;
+  if (cols % 16 != 0) return fail(NVFP4_ERR_SHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  if (rows > 0 && cols > INT64_MAX / 2 / rows) return fail(NVFP4_ERR_UNSUPPORTED, "rows*cols overflows");
+  if (r * cols * 2 > (int64_t)INT32_MAX || 16 * cols * 2 > (int64_t)INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "r*cols or 16*cols exceeds 2^30 values (r=%lld, cols=%lld)", (long long)r,
+                (long long)cols);
+  REQUIRE_ALIGN(x_bf16, 16);
+  REQUIRE_ALIGN(codes, 16);
+  REQUIRE_ALIGN(scales, 16);
+  REQUIRE_ALIGN(global_scale, 4);
+  REQUIRE_ALIGN(lora_down_bf16, 16);
+  REQUIRE_ALIGN(lora_t, 16);
+  REQUIRE_ALIGN(workspace, 4);
+  const int64_t n = rows * cols;
+  const Range outs[4] = {{codes, n / 2, "codes"}, {scales, n / 16, "scales"}, {global_scale, 4, "global_scale"},
+                         {lora_t, rows * r * 4, "lora_t"}};
+  const Range ins[3] = {{x_bf16, n * 2, "x"}, {lora_down_bf16, r * cols * 2, "lora_down"},
+                        {workspace, nvfp4k::lora_workspace_bytes(rows, cols, r), "workspace"}};
+  if (rows == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 4, ins, 3)) return s;
+  return hip_status(nvfp4k::launch_nvfp4_quantize_lora(x_bf16, rows, cols, codes, scales, global_scale,
+                                                       use_given_global_scale, lora_down_bf16, r, lora_t,
+                                                       (uint32_t*)workspace, (hipStream_t)stream),
+                    "nvfp4_quantize_lora launch");
+}
+
+nvfp4_status nvfp4_gemm_lora_ex(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                                const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                                const float* lora_t, const void* lora_up_bf16, int64_t r, void* out_bf16, int64_t M,
+                                int64_t N, int64_t K, int algo, void* stream) {
+  REQUIRE_PTR(lora_t);
+  REQUIRE_PTR(lora_up_bf16);
+  if (nvfp4_status s = check_dims(M, "M", N, "N", r, "r")) return s;
+  if (nvfp4_status s = check_rank(r)) return s;
+  if (M * r * 4 > (int64_t)INT32_MAX || N * r * 2 > (int64_t)INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "lora_t or lora_up exceeds 2 GiB (M=%lld, N=%lld, r=%lld)", (long long)M,
+                (long long)N, (long long)r);
+  REQUIRE_ALIGN(lora_t, 16);
+  REQUIRE_ALIGN(lora_up_bf16, 16);
+  return gemm_impl(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_bf16, M, N, K, algo, lora_t,
+                   lora_up_bf16, r, stream);
+}
+
+nvfp4_status nvfp4_gemm_lora(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                             const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                             const float* lora_t, const void* lora_up_bf16, int64_t r, void* out_bf16, int64_t M,
+                             int64_t N, int64_t K, void* stream) {
+  return nvfp4_gemm_lora_ex(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, lora_t, lora_up_bf16, r,
+                            out_bf16, M, N, K, NVFP4_ALGO_AUTO, stream);
 }
 
 }  // extern "C"

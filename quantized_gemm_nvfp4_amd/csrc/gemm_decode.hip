@@ -51,11 +51,12 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
 // kR rows) are issued before any decoding; the activation slot is decoded
 // once into registers.  Block scales are converted with the exact 2^-8 bit
 // trick of e4m3x2_to_f16x2_div256 (the E2M1 conversion multiplies by 2^8).
-template <int kM, int kR>
+template <int kM, int kR, bool kLora>
 __global__ __launch_bounds__(1024) void nvfp4_gemv_rowslot_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
-    uint16_t* __restrict__ out, int M, int N, int K) {
+    uint16_t* __restrict__ out, int M, int N, int K, const float* __restrict__ lora_t,
+    const uint16_t* __restrict__ lora_up, int r) {
   extern __shared__ __attribute__((aligned(16))) float4v s_diag[];   // [slots][kR][kM][16]
   const int lane = threadIdx.x & 63;
   const int slot = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -128,17 +129,25 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_rowslot_kernel(
   // t / 16, diagonal entry t % 16.  The slots are summed in order, then the
   // 16 entries by a fixed butterfly within each aligned group of 16 lanes
   // (the item count is a multiple of 16 and the block size of 64, so every
-  // group is whole).
+  // group is whole).  With the low-rank branch, entry ii also carries the
+  // terms j = ii, ii + 16, ... of sum_j T[m][j] L_up[n][j] (not scaled by
+  // g_a g_w).
   for (int t = threadIdx.x; t < 16 * kR * kM; t += blockDim.x) {
     const int pair = t >> 4, ii = t & 15;
     float v = 0.f;
     for (int w = 0; w < nslots; ++w) v += s_diag[(w * kR * kM + pair) * 16 + ii][ii & 3];
+    if (kLora) {
+      v *= gg;
+      const int rho = pair / kM, m = pair % kM, n = n0 + rho;
+      if (m < M && n < N)
+        for (int j = ii; j < r; j += 16) v += lora_t[(int64_t)m * r + j] * bf16_bits_to_f32(lora_up[(int64_t)n * r + j]);
+    }
     v += __shfl_xor(v, 1, 16);
     v += __shfl_xor(v, 2, 16);
     v += __shfl_xor(v, 4, 16);
     v += __shfl_xor(v, 8, 16);
     const int rho = pair / kM, m = pair % kM;
-    if (ii == 0 && m < M && n0 + rho < N) out[(int64_t)m * N + n0 + rho] = (uint16_t)f32_to_bf16_rne(v * gg);
+    if (ii == 0 && m < M && n0 + rho < N) out[(int64_t)m * N + n0 + rho] = (uint16_t)f32_to_bf16_rne(kLora ? v : v * gg);
   }
 }
 
@@ -272,7 +281,8 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_w4a16_rowslot_kernel(
 __global__ __launch_bounds__(256) void nvfp4_gemm_rowblock_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
-    uint16_t* __restrict__ out, int M, int N, int K) {
+    uint16_t* __restrict__ out, int M, int N, int K, const float* __restrict__ lora_t,
+    const uint16_t* __restrict__ lora_up, int rank) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16;
   const int r = lane & 15, grp = lane >> 4;
@@ -334,8 +344,18 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_rowblock_kernel(
   const int n = n0 + 4 * (lane >> 4);
   if (m >= M) return;
   uint16_t* orow = out + (int64_t)m * N;
-  const uint32_t b0 = f32_to_bf16_rne(s[0] * gg), b1 = f32_to_bf16_rne(s[1] * gg);
-  const uint32_t b2 = f32_to_bf16_rne(s[2] * gg), b3 = f32_to_bf16_rne(s[3] * gg);
+  float v[4] = {s[0] * gg, s[1] * gg, s[2] * gg, s[3] * gg};
+  if (lora_t != nullptr) {      // low-rank branch: + sum_j T[m][j] L_up[n][j]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (n + q >= N) continue;
+      float l = 0.f;
+      for (int j = 0; j < rank; ++j) l += lora_t[(int64_t)m * rank + j] * bf16_bits_to_f32(lora_up[(int64_t)(n + q) * rank + j]);
+      v[q] += l;
+    }
+  }
+  const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
+  const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
   if ((N & 3) == 0 && n + 3 < N) {
     *(uint2*)(orow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
   } else {
@@ -347,13 +367,15 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_rowblock_kernel(
 }
 
 namespace {
-template <int kM, int kR>
+template <int kM, int kR, bool kLora = false>
 void launch_rowslot(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc, const uint8_t* ws,
-                    const float* wg, void* out, int M, int N, int K, hipStream_t stream) {
+                    const float* wg, void* out, int M, int N, int K, hipStream_t stream, const float* lora_t = nullptr,
+                    const void* lora_up = nullptr, int r = 0) {
   const int nslots = (K / 2 + 1023) / 1024;
   const size_t lds = (size_t)nslots * kR * kM * 16 * sizeof(float4v);
-  hipLaunchKernelGGL((nvfp4_gemv_rowslot_kernel<kM, kR>), dim3((unsigned)((N + kR - 1) / kR)), dim3(64 * nslots),
-                     lds, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, M, N, K);
+  hipLaunchKernelGGL((nvfp4_gemv_rowslot_kernel<kM, kR, kLora>), dim3((unsigned)((N + kR - 1) / kR)),
+                     dim3(64 * nslots), lds, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, M, N, K, lora_t,
+                     (const uint16_t*)lora_up, r);
 }
 template <int kM, int kR>
 void launch_w4a16_rowslot(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out, int M,
@@ -379,19 +401,34 @@ hipError_t launch_nvfp4_w4a16_decode(const void* x, const uint8_t* wc, const uin
   return hipGetLastError();
 }
 
+hipError_t launch_nvfp4_gemm_decode_lora(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
+                                         const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
+                                         int64_t K, const float* lora_t, const void* lora_up, int64_t r,
+                                         hipStream_t stream) {
+  const bool rowslot_k = K <= (int64_t)kMaxSlots * 2048;
+  const bool lora = lora_t != nullptr;
+  if (M == 1 && rowslot_k) {
+    if (lora)
+      launch_rowslot<1, 4, true>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream, lora_t, lora_up, (int)r);
+    else
+      launch_rowslot<1, 4>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
+  } else if (M == 2 && rowslot_k) {
+    if (lora)
+      launch_rowslot<2, 4, true>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream, lora_t, lora_up, (int)r);
+    else
+      launch_rowslot<2, 4>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
+  } else {
+    hipLaunchKernelGGL(nvfp4_gemm_rowblock_kernel, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream, ac, as,
+                       ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, (const uint16_t*)lora_up,
+                       (int)r);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_nvfp4_gemm_decode(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
                                     const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
                                     int64_t K, hipStream_t stream) {
-  const bool rowslot_k = K <= (int64_t)kMaxSlots * 2048;
-  if (M == 1 && rowslot_k) {
-    launch_rowslot<1, 4>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
-  } else if (M == 2 && rowslot_k) {
-    launch_rowslot<2, 4>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
-  } else {
-    hipLaunchKernelGGL(nvfp4_gemm_rowblock_kernel, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream, ac, as,
-                       ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K);
-  }
-  return hipGetLastError();
+  return launch_nvfp4_gemm_decode_lora(ac, as, ag, wc, ws, wg, out, M, N, K, nullptr, nullptr, 0, stream);
 }
 
 }  // namespace nvfp4k

@@ -24,7 +24,8 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
 __global__ __launch_bounds__(64) void nvfp4_gemm_simple_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
-    uint16_t* __restrict__ out, int M, int N, int K) {
+    uint16_t* __restrict__ out, int M, int N, int K, const float* __restrict__ lora_t,
+    const uint16_t* __restrict__ lora_up, int r) {
   const int n = blockIdx.x * 64 + threadIdx.x;
   if (n >= N) return;
   const int nb = K / 16;
@@ -45,7 +46,10 @@ __global__ __launch_bounds__(64) void nvfp4_gemm_simple_kernel(
     }
     acc += (e4m3_to_f32(asr[b]) * e4m3_to_f32(wsr[b])) * bs;
   }
-  out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(acc * ((*a_g) * (*w_g)));
+  float v = acc * ((*a_g) * (*w_g));
+  if (lora_t != nullptr)        // low-rank branch: + sum_j T[m][j] L_up[n][j]
+    for (int j = 0; j < r; ++j) v += lora_t[(int64_t)m * r + j] * bf16_bits_to_f32(lora_up[(int64_t)n * r + j]);
+  out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v);
   }
 }
 
@@ -112,12 +116,20 @@ hipError_t launch_nvfp4_w4a16_simple(const void* x, const uint8_t* wc, const uin
   return hipGetLastError();
 }
 
+hipError_t launch_nvfp4_gemm_simple_lora(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
+                                         const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
+                                         int64_t K, const float* lora_t, const void* lora_up, int64_t r,
+                                         hipStream_t stream) {
+  hipLaunchKernelGGL(nvfp4_gemm_simple_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)(M < 65535 ? M : 65535)),
+                     dim3(64), 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t,
+                     (const uint16_t*)lora_up, (int)r);
+  return hipGetLastError();
+}
+
 hipError_t launch_nvfp4_gemm_simple(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
                                     const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
                                     int64_t K, hipStream_t stream) {
-  hipLaunchKernelGGL(nvfp4_gemm_simple_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)(M < 65535 ? M : 65535)), dim3(64), 0, stream,
-                     ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K);
-  return hipGetLastError();
+  return launch_nvfp4_gemm_simple_lora(ac, as, ag, wc, ws, wg, out, M, N, K, nullptr, nullptr, 0, stream);
 }
 
 hipError_t launch_int4g_gemm_simple(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,

@@ -254,10 +254,14 @@ __device__ __forceinline__ void tiled_stage(const TiledCtx& c, int st, float16v 
   }
 }
 
+// kLora: add the low-rank branch T L_up^T (T fp32 [M, r], L_up bf16 [N, r])
+// to each output before the bf16 rounding (see the epilogue).
+template <bool kLora>
 __global__ __launch_bounds__(512, 1) void nvfp4_gemm_tiled_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
-    uint16_t* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n) {
+    uint16_t* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, const float* __restrict__ lora_t,
+    const uint16_t* __restrict__ lora_up, int r) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tile_m, tile_n;
   map_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
@@ -318,6 +322,86 @@ __global__ __launch_bounds__(512, 1) void nvfp4_gemm_tiled_kernel(
   // register (n%4) + 4(n/8): four consecutive n per register quad.
   const float gg = (*a_g) * (*w_g);
   const bool vec_ok = (N & 3) == 0;
+  if (kLora) {
+    // Low-rank branch: D = L_up T^T on the same 32 x 32 fragments (L_up rows
+    // n as the first operand, T rows m as the second), accumulated straight
+    // into acc after acc is scaled by gg; the store below then multiplies by
+    // 1.  T is split into bf16 hi + lo parts (T - hi is exact in fp32 and
+    // its bf16 rounding leaves ~2^-17 of T), so the branch keeps near-fp32
+    // precision.  Ranks go 32 at a time through LDS (the decoded-A buffers,
+    // free once the main loop is done): all 512 threads load the tile's T
+    // rows and L_up rows for the chunk at once, so the epilogue pays one
+    // memory latency per chunk.  LDS rows hold 16-byte pieces, XOR-swizzled
+    // by the row: T row (128 B) piece (2 kk + h) * 2 + {hi, lo}, L_up row
+    // (64 B) piece 2 kk + h, where lane half h covers ranks 8h..8h+7 of the
+    // 16-rank step kk.
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = acc[j][i] * gg;
+    const auto tr = buffer_of(lora_t, (uint32_t)M * (uint32_t)r * 4u);
+    const auto ur = buffer_of(lora_up, (uint32_t)N * (uint32_t)r * 2u);
+    uint4* st = (uint4*)g_af0;      // [256 rows][8 pieces]
+    uint4* su = (uint4*)g_af1;      // [256 rows][4 pieces]
+    const int srow = tid >> 1, shalf = tid & 1;
+    for (int c0 = 0; c0 < r; c0 += 32) {
+      __syncthreads();              // previous users of the buffers are done
+      {
+        const uint32_t m = (uint32_t)(m0 + srow), n = (uint32_t)(n0 + srow);
+        uint4 tv[4], uv[2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t k = (uint32_t)(c0 + 16 * shalf + 4 * q);
+          tv[q] = buffer_load16(tr, m < (uint32_t)M && k < (uint32_t)r ? 4u * (m * r + k) : kBufferOob);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t k = (uint32_t)(c0 + 16 * shalf + 8 * q);
+          uv[q] = buffer_load16(ur, n < (uint32_t)N && k < (uint32_t)r ? 2u * (n * r + k) : kBufferOob);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint4 t0 = tv[2 * hh], t1 = tv[2 * hh + 1];
+          const float f[8] = {__uint_as_float(t0.x), __uint_as_float(t0.y), __uint_as_float(t0.z),
+                              __uint_as_float(t0.w), __uint_as_float(t1.x), __uint_as_float(t1.y),
+                              __uint_as_float(t1.z), __uint_as_float(t1.w)};
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t h0 = f32_to_bf16_rne(f[2 * e]), h1 = f32_to_bf16_rne(f[2 * e + 1]);
+            const uint32_t l0 = f32_to_bf16_rne(f[2 * e] - bf16_bits_to_f32(h0));
+            const uint32_t l1 = f32_to_bf16_rne(f[2 * e + 1] - bf16_bits_to_f32(h1));
+            hi[e] = h0 | (h1 << 16);
+            lo[e] = l0 | (l1 << 16);
+          }
+          const int p = (2 * shalf + hh) * 2;
+          st[srow * 8 + (p ^ (srow & 7))] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+          st[srow * 8 + ((p + 1) ^ (srow & 7))] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+          su[srow * 4 + ((2 * shalf + hh) ^ (srow & 3))] = uv[hh];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if (c0 + 16 * kk >= r) break;
+        const int pt = (2 * kk + h) * 2, pu = 2 * kk + h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 128 * wm + 32 * i + r32;
+          const short8v hi = __builtin_bit_cast(short8v, st[row * 8 + (pt ^ (row & 7))]);
+          const short8v lo = __builtin_bit_cast(short8v, st[row * 8 + ((pt + 1) ^ (row & 7))]);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = 64 * wn + 32 * j + r32;
+            const short8v up = __builtin_bit_cast(short8v, su[col * 4 + (pu ^ (col & 3))]);
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(up, hi, acc[j][i], 0, 0, 0);
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(up, lo, acc[j][i], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  const float gmul = kLora ? 1.0f : gg;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + 128 * wm + 32 * i + r32;
@@ -328,10 +412,10 @@ __global__ __launch_bounds__(512, 1) void nvfp4_gemm_tiled_kernel(
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int n = n0 + 64 * wn + 32 * j + 8 * rq + 4 * h;
-        const uint32_t b0 = f32_to_bf16_rne(acc[j][i][4 * rq + 0] * gg);
-        const uint32_t b1 = f32_to_bf16_rne(acc[j][i][4 * rq + 1] * gg);
-        const uint32_t b2 = f32_to_bf16_rne(acc[j][i][4 * rq + 2] * gg);
-        const uint32_t b3 = f32_to_bf16_rne(acc[j][i][4 * rq + 3] * gg);
+        const uint32_t b0 = f32_to_bf16_rne(acc[j][i][4 * rq + 0] * gmul);
+        const uint32_t b1 = f32_to_bf16_rne(acc[j][i][4 * rq + 1] * gmul);
+        const uint32_t b2 = f32_to_bf16_rne(acc[j][i][4 * rq + 2] * gmul);
+        const uint32_t b3 = f32_to_bf16_rne(acc[j][i][4 * rq + 3] * gmul);
         if (vec_ok && n + 3 < N) {
           *(uint2*)(orow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
         } else {
@@ -349,8 +433,20 @@ hipError_t launch_nvfp4_gemm_tiled(const uint8_t* ac, const uint8_t* as, const f
                                    const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N, int64_t K,
                                    hipStream_t stream) {
   const int tiles_m = (int)((M + TM - 1) / TM), tiles_n = (int)((N + TN - 1) / TN);
-  hipLaunchKernelGGL(nvfp4_gemm_tiled_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream,
-                     ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, tiles_m, tiles_n);
+  hipLaunchKernelGGL(nvfp4_gemm_tiled_kernel<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream,
+                     ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, tiles_m, tiles_n, nullptr,
+                     nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_gemm_tiled_lora(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
+                                        const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
+                                        int64_t K, const float* lora_t, const void* lora_up, int64_t r,
+                                        hipStream_t stream) {
+  const int tiles_m = (int)((M + TM - 1) / TM), tiles_n = (int)((N + TN - 1) / TN);
+  hipLaunchKernelGGL(nvfp4_gemm_tiled_kernel<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream,
+                     ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, tiles_m, tiles_n, lora_t,
+                     (const uint16_t*)lora_up, (int)r);
   return hipGetLastError();
 }
 

@@ -12,9 +12,45 @@ namespace nvfp4k {
 // workspace holds this many uint32).
 constexpr int kAmaxPartials = 1024;
 
-// rule: 0 absmax, 1 four-over-six, 2 MSE (block-scale selection).
+// Block-scale selection rules of the quantizer.
+enum ScaleRule { kRuleAbsmax = 0, kRuleFourOverSix = 1, kRuleMse = 2 };
+
 hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                                  float* gscale, int use_given, int rule, uint32_t* workspace, hipStream_t stream);
+// The second pass alone (codes and scales), reducing `npartial` partial
+// maxima from workspace unless use_given.  With t_splits > 1 it also sums
+// t_splits partial products t_part[s][t_n] into t_out[t_n], in order of s.
+hipError_t launch_nvfp4_quantize_pass2(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                       float* gscale, int use_given, int rule, int npartial, uint32_t* workspace,
+                                       hipStream_t stream, const float* t_part = nullptr, int t_splits = 0,
+                                       float* t_out = nullptr, int64_t t_n = 0);
+
+// Low-rank branch: the quantizer with T = X L_down^T [rows, r] (fp32)
+// computed in its first pass; r <= kLoraMaxRank.
+constexpr int kLoraMaxRank = 128;
+// The first pass runs on (row groups of 16) x (K slices) workgroups, at most
+// kAmaxPartials in all; with more than one slice the slices' partial T go to
+// the workspace after the partial maxima and the second pass sums them.
+constexpr int kLoraSliceSteps = 8;        // at least 8 K steps of 32 per slice
+inline int lora_row_blocks(int64_t rows) {
+  const int64_t g = (rows + 15) / 16;
+  return (int)(g < kAmaxPartials ? g : kAmaxPartials);
+}
+inline int lora_k_slices(int64_t rows, int64_t cols) {
+  const int gx = lora_row_blocks(rows);
+  const int64_t steps = (cols + 31) / 32;
+  int64_t s = kAmaxPartials / (gx > 0 ? gx : 1);
+  const int64_t smax = steps / kLoraSliceSteps;
+  if (s > smax) s = smax;
+  return (int)(s < 1 ? 1 : s);
+}
+inline int64_t lora_workspace_bytes(int64_t rows, int64_t cols, int64_t r) {
+  const int s = lora_k_slices(rows, cols);
+  return (int64_t)sizeof(uint32_t) * kAmaxPartials + (s > 1 ? (int64_t)s * rows * r * 4 : 0);
+}
+hipError_t launch_nvfp4_quantize_lora(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                      float* gscale, int use_given, const void* l_down, int64_t r, float* t,
+                                      uint32_t* workspace, hipStream_t stream);
 
 hipError_t launch_int4g_quantize(const void* w, int64_t N, int64_t K, uint8_t* q, void* scales,
                                  hipStream_t stream);
@@ -38,6 +74,21 @@ hipError_t launch_nvfp4_w4a16_decode(const void* x, const uint8_t* wc, const uin
                                      int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_nvfp4_w4a16_simple(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
                                      int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// The same NVFP4 GEMMs plus the low-rank branch T L_up^T (T fp32 [M, r],
+// L_up bf16 [N, r]) added before the bf16 rounding.
+hipError_t launch_nvfp4_gemm_tiled_lora(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
+                                        const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
+                                        int64_t K, const float* lora_t, const void* lora_up, int64_t r,
+                                        hipStream_t stream);
+hipError_t launch_nvfp4_gemm_decode_lora(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
+                                         const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
+                                         int64_t K, const float* lora_t, const void* lora_up, int64_t r,
+                                         hipStream_t stream);
+hipError_t launch_nvfp4_gemm_simple_lora(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
+                                         const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
+                                         int64_t K, const float* lora_t, const void* lora_up, int64_t r,
+                                         hipStream_t stream);
 
 // INT4 per-group (128) W4A16 kernels; out[M, N] bf16 = x . dequant(q, s)^T.
 // decode: M <= 16.  tiled: any M.  simple: any M.  All need K % 128 == 0.

@@ -63,8 +63,6 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const uint4* __restri
 // block under scale s is, in fp32 with one rounding per step and no fused
 // multiply-add: d = s * g, x_hat = v * d (v the signed E2M1 value of the
 // element's code), e = x - x_hat, err = sum of e * e in element order.
-enum ScaleRule { kRuleAbsmax = 0, kRuleFourOverSix = 1, kRuleMse = 2 };
-
 namespace {
 // Signed E2M1 value of code c (0..15), exact: codes 0/1 are 0 and 0.5, then
 // (1 + m/2) * 2^(e - 1) with e = c >> 1, m = c & 1.
@@ -108,7 +106,8 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
                                                           uint2* __restrict__ codes, uint8_t* __restrict__ scales,
                                                           float* __restrict__ gscale,
                                                           const uint32_t* __restrict__ partial, int npartial,
-                                                          int use_given) {
+                                                          int use_given, const float* __restrict__ t_part,
+                                                          int t_splits, float* __restrict__ t_out, int64_t t_n) {
   __shared__ float s_g;
   if (threadIdx.x < 64) {
     float g;
@@ -127,6 +126,13 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
   const float g = s_g;
 
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // Side job for a split low-rank down projection: T = the sum of its K
+  // slices' partial products, in slice order.
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t_splits > 1 && e < t_n; e += stride) {
+    float v = t_part[e];
+    for (int sp = 1; sp < t_splits; ++sp) v += t_part[(int64_t)sp * t_n + e];
+    t_out[e] = v;
+  }
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
     const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
     const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -210,10 +216,32 @@ __global__ __launch_bounds__(256) void int4g_quant_kernel(const uint4* __restric
 }
 
 // ---- launchers -------------------------------------------------------------
+hipError_t launch_nvfp4_quantize_pass2(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                       float* gscale, int use_given, int rule, int npartial, uint32_t* workspace,
+                                       hipStream_t stream, const float* t_part, int t_splits, float* t_out,
+                                       int64_t t_n) {
+  const int64_t nblocks = rows * cols / kBlock;
+  int64_t grid = (nblocks + 255) / 256;
+  if (grid > 2048) grid = 2048;
+  if (rule == kRuleFourOverSix) {
+    hipLaunchKernelGGL(nvfp4_quant_kernel<kRuleFourOverSix>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint4*)x, nblocks, (uint2*)codes, scales, gscale, (const uint32_t*)workspace, npartial,
+                       use_given, t_part, t_splits, t_out, t_n);
+  } else if (rule == kRuleMse) {
+    hipLaunchKernelGGL(nvfp4_quant_kernel<kRuleMse>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint4*)x,
+                       nblocks, (uint2*)codes, scales, gscale, (const uint32_t*)workspace, npartial, use_given,
+                       t_part, t_splits, t_out, t_n);
+  } else {
+    hipLaunchKernelGGL(nvfp4_quant_kernel<kRuleAbsmax>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint4*)x, nblocks, (uint2*)codes, scales, gscale, (const uint32_t*)workspace, npartial,
+                       use_given, t_part, t_splits, t_out, t_n);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                                  float* gscale, int use_given, int rule, uint32_t* workspace, hipStream_t stream) {
   const int64_t n = rows * cols;
-  const int64_t nblocks = n / kBlock;
   int npartial = 0;
   if (!use_given) {
     const int64_t n_vec = n / 8;
@@ -225,21 +253,8 @@ hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  int64_t grid = (nblocks + 255) / 256;
-  if (grid > 2048) grid = 2048;
-  if (rule == kRuleFourOverSix) {
-    hipLaunchKernelGGL(nvfp4_quant_kernel<kRuleFourOverSix>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       (const uint4*)x, nblocks, (uint2*)codes, scales, gscale, (const uint32_t*)workspace, npartial,
-                       use_given);
-  } else if (rule == kRuleMse) {
-    hipLaunchKernelGGL(nvfp4_quant_kernel<kRuleMse>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint4*)x,
-                       nblocks, (uint2*)codes, scales, gscale, (const uint32_t*)workspace, npartial, use_given);
-  } else {
-    hipLaunchKernelGGL(nvfp4_quant_kernel<kRuleAbsmax>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       (const uint4*)x, nblocks, (uint2*)codes, scales, gscale, (const uint32_t*)workspace, npartial,
-                       use_given);
-  }
-  return hipGetLastError();
+  return launch_nvfp4_quantize_pass2(x, rows, cols, codes, scales, gscale, use_given, rule, npartial, workspace,
+                                     stream);
 }
 
 hipError_t launch_int4g_quantize(const void* w, int64_t N, int64_t K, uint8_t* q, void* scales,

@@ -114,6 +114,45 @@ def test_int4_validation():
     assert lib.int4g_gemv(A, B, C, D, 4, 8, 256, 64, None) == UNSUP
 
 
+def test_lora_workspace_size():
+    f = q.lib().nvfp4_quantize_lora_workspace_bytes
+    # one K slice: only the 1024 partial maxima
+    assert f(20000, 3072, 32) == 4096
+    assert f(8, 128, 32) == 4096
+    # decode row (1 row group): min(1024, 168 steps / 8) = 21 slices of partial T
+    assert f(1, 5376, 32) == 4096 + 21 * 1 * 32 * 4
+    # 256 row groups: 1024 / 256 = 4 slices
+    assert f(4096, 3072, 32) == 4096 + 4 * 4096 * 32 * 4
+    assert f(-1, 128, 8) == 0 and f(4, 128, 256) == 0
+
+
+def test_lora_validation():
+    lib = q.lib()
+    f = lib.nvfp4_quantize_lora
+    # x, rows, cols, codes, scales, g, use_given, lora_down, r, t, workspace, stream
+    assert f(A, 4, 32, B, C, D, 0, E, 12, F, G, None) == UNSUP and "rank" in _err()     # r % 8
+    assert f(A, 4, 32, B, C, D, 0, E, 0, F, G, None) == UNSUP
+    assert f(A, 4, 32, B, C, D, 0, E, 136, F, G, None) == UNSUP                         # r > 128
+    assert f(A, 4, 24, B, C, D, 0, E, 16, F, G, None) == SHAPE
+    assert f(A, 4, 32, B, C, D, 0, E, 16, F, None, None) == INVALID and "workspace" in _err()
+    assert f(A, 4, 32, B, C, D, 1, E, 16, F, None, None) == INVALID   # always needs the workspace
+    assert f(A, 4, 32, B, C, D, 0, None, 16, F, G, None) == INVALID
+    assert f(A, 4, 32, B, C, D, 0, E, 16, ODD, G, None) == ALIGN
+    assert f(A, 4, 32, B, C, D, 0, E, 16, A, G, None) == INVALID and "overlap" in _err()  # t aliases x
+    assert f(A, 0, 32, B, C, D, 0, E, 16, F, G, None) == OK
+    g = lib.nvfp4_gemm_lora_ex
+    # a_codes, a_scales, a_g, w_codes, w_scales, w_g, t, up, r, out, M, N, K, algo, stream
+    T, U, O = P(0x80000), P(0x90000), P(0xA0000)
+    assert g(A, B, C, D, E, F, T, U, 20, O, 4, 8, 128, 0, None) == UNSUP                 # r % 8
+    assert g(A, B, C, D, E, F, None, U, 16, O, 4, 8, 128, 0, None) == INVALID
+    assert g(A, B, C, D, E, F, T, U, 16, O, 4, 8, 120, 0, None) == SHAPE
+    assert g(A, B, C, D, E, F, T, U, 16, T, 4, 8, 128, 0, None) == INVALID and "overlap" in _err()
+    assert g(A, B, C, D, E, F, ODD, U, 16, O, 4, 8, 128, 0, None) == ALIGN
+    assert g(A, B, C, D, E, F, T, U, 16, O, 17, 8, 128, q.ALGO_DECODE, None) == UNSUP
+    assert g(A, B, C, D, E, F, T, U, 16, O, 0, 8, 128, 0, None) == OK
+    assert lib.nvfp4_gemm_lora(A, B, C, D, E, F, T, U, 4, O, 4, 8, 128, None) == UNSUP
+
+
 def test_error_text_is_thread_local():
     import threading
     lib = q.lib()

@@ -29,7 +29,7 @@ import functools
 
 import numpy as np
 
-WORKLOAD_IDS = {"tiny": 0, "decode": 2, "prefill": 3, "dit": 4, "int4": 5}
+WORKLOAD_IDS = {"tiny": 0, "decode": 2, "prefill": 3, "dit": 4, "int4": 5, "lora": 6}
 
 SHAPES = {
     "tiny": {"M": 16, "N": 256, "K": 256},
@@ -37,6 +37,7 @@ SHAPES = {
     "prefill": {"M": 4096, "up": (21504, 5376), "down": (5376, 21504)},
     "dit": {"M": 4096, "qkv": (9216, 3072), "up": (12288, 3072), "down": (3072, 12288), "steps": 4},
     "int4": {"M": (1, 16, 2048), "N": 28672, "K": 8192, "group": 128},
+    "lora": {"M": 4096, "qkv": (9216, 3072), "rank": 32},
 }
 
 
@@ -112,6 +113,21 @@ def int4_w():
 @functools.lru_cache(maxsize=None)
 def int4_x():
     return normal_bf16("int4", 2, (2048, 8192))
+
+
+@functools.lru_cache(maxsize=None)
+def dit_lora(rank=32):
+    """Low-rank factors on the qkv projection [9216, 3072] of the diffusion
+    stack: L_down bf16 [rank, 3072] and L_up bf16 [9216, rank], both
+    ~ N(0, 0.02) (a trained adapter: L_up is not the zero initialization)."""
+    return (normal_bf16("lora", rank, (rank, 3072), 0.02),
+            normal_bf16("lora", 1000 + rank, (9216, rank), 0.02))
+
+
+def random_f32(seed, shape, sigma=1.0):
+    """Seeded fp32 tensor ~ N(0, sigma^2) with full 24-bit mantissas."""
+    rng = np.random.default_rng([101, seed])
+    return (rng.standard_normal(shape) * sigma).astype(np.float32)
 
 
 def random_bf16(seed, shape, sigma=1.0, outlier_frac=0.0, outlier_mul=1.0, zero_frac=0.0):
