@@ -106,6 +106,8 @@ def run_prefill(torch, q, steps, warmup):
     h = torch.empty((M, N1), dtype=torch.bfloat16, device="cuda:0")
     y = torch.empty((M, N2), dtype=torch.bfloat16, device="cuda:0")
     ws = torch.empty(q.lib().nvfp4_quantize_workspace_bytes(), dtype=torch.uint8, device="cuda:0")
+    gws = [torch.empty(max(1, q.lib().nvfp4_gemm_workspace_bytes(M, n, k)), dtype=torch.uint8, device="cuda:0")
+           for n, k in ((N1, K1), (N2, K2))]
     del x_bits
 
     lib = q.lib()
@@ -115,9 +117,10 @@ def run_prefill(torch, q, steps, warmup):
     def quant(inp, a):
         q._check(lib.nvfp4_quantize(P(inp), inp.shape[0], inp.shape[1], P(a[0]), P(a[1]), P(a[2]), 0, P(ws), stream))
 
-    def gemm(a, w, out):
-        q._check(lib.nvfp4_gemm_ex(P(a[0]), P(a[1]), P(a[2]), P(w[0]), P(w[1]), P(w[2]), P(out),
-                                   out.shape[0], out.shape[1], a[0].shape[1] * 2, q.ALGO_TILED, stream))
+    def gemm(a, w, out, gw):
+        q._check(lib.nvfp4_gemm_ws(P(a[0]), P(a[1]), P(a[2]), P(w[0]), P(w[1]), P(w[2]), P(out),
+                                   out.shape[0], out.shape[1], a[0].shape[1] * 2, q.ALGO_TILED, P(gw), gw.numel(),
+                                   stream))
 
     gemm_timer = Timer(torch)
     quant_timer = Timer(torch)
@@ -128,7 +131,7 @@ def run_prefill(torch, q, steps, warmup):
         if timed:
             quant_timer.stop(t)
             t = gemm_timer.start()
-        gemm(a1, wu, h)
+        gemm(a1, wu, h, gws[0])
         if timed:
             gemm_timer.stop(t)
             t = quant_timer.start()
@@ -136,7 +139,7 @@ def run_prefill(torch, q, steps, warmup):
         if timed:
             quant_timer.stop(t)
             t = gemm_timer.start()
-        gemm(a2, wd, y)
+        gemm(a2, wd, y, gws[1])
         if timed:
             gemm_timer.stop(t)
 

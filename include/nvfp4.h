@@ -162,6 +162,27 @@ nvfp4_status nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            void* out_bf16, int64_t M, int64_t N, int64_t K, int algo, void* stream);
 
 /*
+ * nvfp4_gemm_ex with a workspace.  The tiled kernel runs one 256 x 256
+ * output tile per compute unit at a time; when the tile count is not a
+ * multiple of the compute units, the leftover tiles of the last, partial
+ * round are split along K into up to 8 parts that run side by side, and a
+ * second kernel sums each tile's parts in order and rounds.  Only the
+ * summation order of those tiles changes (the same fp32 products, the same
+ * tolerance); the split depends only on M, N, K and the device's compute
+ * unit count, so repeated calls give identical bits.
+ * workspace: >= nvfp4_gemm_workspace_bytes(M, N, K) bytes of device memory
+ * for the current device, 256-byte aligned, no initialization, not shared
+ * with a concurrent call, not overlapping any argument.  The size is 0 when
+ * no split applies (M <= 16, K % 128 != 0, whole rounds); with workspace
+ * NULL or workspace_bytes below the size, the call runs as nvfp4_gemm_ex.
+ */
+size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+nvfp4_status nvfp4_gemm_ws(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                           void* out_bf16, int64_t M, int64_t N, int64_t K, int algo, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * Weight-only NVFP4 GEMM: out[M, N] (bf16) = bf16_RNE( g_w * sum_k x[m, k] *
  * W[n, k] ) with x a bf16 activation that is not quantized and W the NVFP4
  * weight of nvfp4_gemm.  Passages: the weight format of "NVFP4 en

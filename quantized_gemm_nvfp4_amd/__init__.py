@@ -36,6 +36,8 @@ SIGNATURES = {
     "nvfp4_quantize_ex": ([_P, _I64, _I64, _P, _P, _P, _I, _I, _P, _P], ctypes.c_int),
     "nvfp4_gemm": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "nvfp4_gemm_ex": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P], ctypes.c_int),
+    "nvfp4_gemm_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),
+    "nvfp4_gemm_ws": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "nvfp4_gemm_w4a16": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "nvfp4_gemm_w4a16_ex": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P], ctypes.c_int),
     "int4g_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
@@ -149,10 +151,13 @@ def nvfp4_quantize(x, global_scale=None, out=None, rule="absmax"):
     return codes, scales, g
 
 
-def nvfp4_gemm(a, w, algo=ALGO_AUTO, out=None):
+def nvfp4_gemm(a, w, algo=ALGO_AUTO, out=None, workspace=None):
     """bf16 [M, N] = g_a g_w dequant(A) . dequant(W)^T.
 
     a = (a_codes [M, K/2], a_scales [M, K/16], a_g [1]); w likewise with N rows.
+    workspace: optional uint8 device tensor for the K split of the leftover
+    tiles (nvfp4_gemm_workspace_bytes); when None one is taken from torch's
+    allocator if the shape needs it.
     """
     torch = _torch()
     ac, as_, ag = a
@@ -168,8 +173,15 @@ def nvfp4_gemm(a, w, algo=ALGO_AUTO, out=None):
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=ac.device)
     _need(out, torch.bfloat16, (M, N), "out")
-    _check(lib().nvfp4_gemm_ex(_ptr(ac), _ptr(as_), _ptr(ag), _ptr(wc), _ptr(ws), _ptr(wg), _ptr(out),
-                               M, N, K, int(algo), _stream(ac)))
+    if workspace is None:
+        nbytes = lib().nvfp4_gemm_workspace_bytes(M, N, K)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=ac.device)
+    if workspace is not None:
+        _need(workspace, torch.uint8, None, "workspace")
+    _check(lib().nvfp4_gemm_ws(_ptr(ac), _ptr(as_), _ptr(ag), _ptr(wc), _ptr(ws), _ptr(wg), _ptr(out),
+                               M, N, K, int(algo), _ptr(workspace) if workspace is not None else None,
+                               workspace.numel() if workspace is not None else 0, _stream(ac)))
     return out
 
 

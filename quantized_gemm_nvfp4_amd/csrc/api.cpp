@@ -85,7 +85,7 @@ nvfp4_status check_dims(int64_t a, const char* an, int64_t b, const char* bn, in
 nvfp4_status gemm_impl(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale, void* out_bf16,
                        int64_t M, int64_t N, int64_t K, int algo, const float* lora_t, const void* lora_up,
-                       int64_t r, void* stream) {
+                       int64_t r, void* workspace, size_t workspace_bytes, void* stream) {
   if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
   if (K > 0) {  // with K == 0 the packed operands are empty and never read
     REQUIRE_PTR(a_codes);
@@ -105,13 +105,18 @@ nvfp4_status gemm_impl(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   REQUIRE_ALIGN(out_bf16, 16);
   REQUIRE_ALIGN(a_gscale, 4);
   REQUIRE_ALIGN(w_gscale, 4);
-  const Range outs[1] = {{out_bf16, M * N * 2, "out"}};
+  if (workspace != nullptr) {
+    REQUIRE_ALIGN(workspace, 256);
+    if (workspace_bytes > (size_t)INT64_MAX) return fail(NVFP4_ERR_INVALID_ARG, "workspace_bytes is too large");
+  }
+  const Range outs[2] = {{out_bf16, M * N * 2, "out"},
+                         {workspace, workspace ? (int64_t)workspace_bytes : 0, "workspace"}};
   const Range ins[8] = {{a_codes, M * K / 2, "a_codes"}, {a_scales, M * K / 16, "a_scales"},
                         {a_gscale, 4, "a_gscale"},       {w_codes, N * K / 2, "w_codes"},
                         {w_scales, N * K / 16, "w_scales"}, {w_gscale, 4, "w_gscale"},
                         {lora_t, lora_t ? M * r * 4 : 0, "lora_t"}, {lora_up, lora_t ? N * r * 2 : 0, "lora_up"}};
   if (M == 0 || N == 0) return ok();
-  if (nvfp4_status s = check_disjoint(outs, 1, ins, 8)) return s;
+  if (nvfp4_status s = check_disjoint(outs, 2, ins, 8)) return s;
   const bool k128 = (K % 128) == 0 && K > 0;
   if (algo == NVFP4_ALGO_AUTO) algo = !k128 ? NVFP4_ALGO_SIMPLE : (M <= 16 ? NVFP4_ALGO_DECODE : NVFP4_ALGO_TILED);
   hipStream_t st = (hipStream_t)stream;
@@ -122,8 +127,9 @@ nvfp4_status gemm_impl(const uint8_t* a_codes, const uint8_t* a_scales, const fl
         return hip_status(nvfp4k::launch_nvfp4_gemm_tiled_lora(a_codes, a_scales, a_gscale, w_codes, w_scales,
                                                                w_gscale, out_bf16, M, N, K, lora_t, lora_up, r, st),
                           "nvfp4_gemm_lora tiled launch");
-      return hip_status(nvfp4k::launch_nvfp4_gemm_tiled(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale,
-                                                        out_bf16, M, N, K, st),
+      return hip_status(nvfp4k::launch_nvfp4_gemm_tiled_ws(a_codes, a_scales, a_gscale, w_codes, w_scales,
+                                                           w_gscale, out_bf16, M, N, K, workspace,
+                                                           (int64_t)workspace_bytes, st),
                         "nvfp4_gemm tiled launch");
     case NVFP4_ALGO_DECODE:
       if (!k128 || M > 16)
@@ -215,7 +221,20 @@ nvfp4_status nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale, void* out_bf16,
                            int64_t M, int64_t N, int64_t K, int algo, void* stream) {
   return gemm_impl(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_bf16, M, N, K, algo, nullptr,
-                   nullptr, 0, stream);
+                   nullptr, 0, nullptr, 0, stream);
+}
+
+size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 16 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  return (size_t)nvfp4k::nvfp4_gemm_tiled_workspace_bytes(M, N, K);
+}
+
+nvfp4_status nvfp4_gemm_ws(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale, void* out_bf16,
+                           int64_t M, int64_t N, int64_t K, int algo, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return gemm_impl(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_bf16, M, N, K, algo, nullptr,
+                   nullptr, 0, workspace, workspace_bytes, stream);
 }
 
 nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
@@ -440,7 +459,7 @@ nvfp4_status nvfp4_gemm_lora_ex(const uint8_t* a_codes, const uint8_t* a_scales,
   REQUIRE_ALIGN(lora_t, 16);
   REQUIRE_ALIGN(lora_up_bf16, 16);
   return gemm_impl(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_bf16, M, N, K, algo, lora_t,
-                   lora_up_bf16, r, stream);
+                   lora_up_bf16, r, nullptr, 0, stream);
 }
 
 nvfp4_status nvfp4_gemm_lora(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,

@@ -12,35 +12,45 @@
 // it is given 1.0) and one packed fp16 multiply by the block scale.
 //
 // Design for CDNA4:
-//  - Workgroup tile 256 x 256, K stage of 64 values, 8 waves of 128 (m) x 64
-//    (n); two waves share each SIMD so one wave's decoding (VALU) issues
-//    while the other's MFMAs run.
+//  - Workgroup tile 256 x 256, K stage of 64 values, 4 waves of 128 (m) x
+//    128 (n), one wave per SIMD; a wave's 16 accumulator fragments (256
+//    registers) live in the accumulation register file.  Each A fragment
+//    read from LDS feeds 4 MFMAs.  The variant with the low-rank epilogue
+//    uses 8 waves of 128 x 64 (two per SIMD, accumulators in ordinary
+//    registers), because its epilogue scales and extends the accumulators
+//    with vector instructions, which cannot read the accumulation file.
 //  - The packed operands (codes and scale bytes) are copied global -> LDS with
 //    global_load_lds into a ring of four stage slots, three stages ahead of
 //    the MFMAs.  Each code copy instruction reads 32 rows x 32 contiguous
 //    bytes.  The slots are distinct LDS objects and the stage loop is
 //    unrolled by four, so the compiler sees that copies in flight never alias
-//    what is being read; every stage issues exactly three copies per wave and
-//    one wait per stage leaves the newest stage's copies in flight.
+//    what is being read; every stage issues the same copies (24 instructions
+//    per workgroup) and one wait per stage leaves the newest stage's copies
+//    in flight.
 //  - With copies in flight the compiler waits for all outstanding LDS reads
 //    before consuming any, so within a step single MFMAs are interleaved with
 //    the next step's LDS reads and the decoding (explicit scheduling groups):
 //    the reads are issued early and have completed by the next step.
 //  - A is decoded once per workgroup, one stage ahead, into a double-buffered
-//    fp16 tile in LDS (32 values per thread per stage); the MFMA reads it
-//    with one ds_read_b128 per fragment and step.  W stays packed in LDS and
-//    each wave decodes its two W fragments in registers.  Decoding A per wave
-//    instead would repeat it for all four waves that share an A fragment.
+//    fp16 tile in LDS (16384 values per stage); the MFMA reads it with one
+//    ds_read_b128 per fragment and step.  W stays packed in LDS and each
+//    wave decodes its W fragments in registers.
 //  - The MFMA sums 16 values of K per lane-half; which physical K a lane
 //    feeds does not change the sum as long as both operands use the same
 //    assignment.  Lane-half h takes K [32h, 32h + 32) of the stage, 8 per
 //    step, so a lane's W codes for the whole stage are one 16-byte piece.
 //    In LDS the two 16-byte pieces of a row's stage segment sit at slot
-//    2*row + (piece ^ ((row >> 3) & 1)): the copy writes them in order, and
-//    16 readers of 16 consecutive rows hit 16 distinct bank groups.  The
-//    fp16 A tile is stored in MFMA lane order (conflict-free reads).
+//    2*row + (piece ^ swz(row)): the copy writes them in order, and 16
+//    readers of 16 consecutive rows hit 16 distinct bank groups.  The fp16 A
+//    tile is stored in MFMA lane order (conflict-free reads).
 //  - The W fragment is the MFMA's first operand, so each lane's accumulators
 //    hold 4 consecutive output columns n: 8-byte bf16 stores.
+//  - One workgroup fills a CU (LDS), so a grid of T tiles runs in
+//    ceil(T / CUs) rounds.  With a workspace, the tiles of the last, partial
+//    round are split along K into S parts (S = CUs / leftover tiles, at most
+//    8) that run side by side; each part stores its fp32 accumulators and a
+//    second kernel sums the parts in order and rounds.  The split depends
+//    only on the shape and the CU count, so results are reproducible.
 //  - Workgroups are dispatched round-robin over the 8 XCDs; the tile order
 //    gives each XCD a contiguous range of tiles, grouped 4 tile-rows at a
 //    time, so tiles running together on one XCD share A and W in its L2.
@@ -57,8 +67,10 @@ constexpr int kScaleRow = TK / 16;                   // 4 scale bytes per row pe
 constexpr int kScaleBytes = TM * kScaleRow;          // 1 KB per operand per stage
 constexpr int kAf16Bytes = TM * TK * 2;              // 32 KB decoded A per stage
 constexpr int kRing = 4;                             // packed stage slots
-constexpr int kCopies = 3;                           // copy instructions per wave per stage
 constexpr int kGroupM = 4;
+constexpr int kMaxSplit = 8;
+constexpr int kMinPartStages = 4;
+constexpr int64_t kPartFloats = (int64_t)TM * TN;    // one tile's fp32 accumulators
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* gbl_void_t;
@@ -70,11 +82,9 @@ __device__ __forceinline__ void g2lds4(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((gbl_void_t)g, (lds_void_t)l, 4, 0, 0);
 }
 
-
-__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  int id = bid;
-  if ((total & 7) == 0) id = (bid & 7) * (total >> 3) + (bid >> 3);
+// Tile (tm, tn) of tile index id: groups of kGroupM tile-rows, column-major
+// within a group.
+__device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = kGroupM * tiles_n;
   const int grp = id / per_group;
   const int first_m = grp * kGroupM;
@@ -137,27 +147,42 @@ template <int B> __device__ __forceinline__ uint8_t* s_slot() {
 }
 template <int F> __device__ __forceinline__ uint8_t* af_buf() { return F == 0 ? g_af0 : g_af1; }
 
-// Per-thread state of the tiled kernel.
+// Per-thread state of the tiled kernel with kW waves.  The stage copies are
+// 8 "copy slots" of 32 code rows of each operand and 64 scale rows of one
+// operand; wave w moves slots kFr w .. kFr w + kFr - 1 (kFr = 8 / kW).
+template <int kW>
 struct TiledCtx {
-  const uint8_t* ga;    // A code copy source (row, piece) of this lane
-  const uint8_t* gw;    // W code copy source
-  const uint8_t* gs;    // scale copy source (A for waves 0-3, W for 4-7)
-  int wave, lane, wm, wn, h, r32, nst;
+  static constexpr int kFr = 8 / kW;       // copy slots and A fragments per wave
+  static constexpr int kJ = kW == 4 ? 4 : 2;  // W fragments per wave
+  static constexpr int kCopies = 3 * kFr;  // copy instructions per wave per stage
+  const uint8_t* ga[kFr];  // A code copy sources (row, piece) of this lane
+  const uint8_t* gw[kFr];  // W code copy sources
+  const uint8_t* gs[kFr];  // scale copy sources (A for copy slots 0-3, W for 4-7)
+  int wave, lane, wm, wn, h, r32;
+  int st0, nst;            // first K stage and number of stages of this workgroup
 };
 
-// Copies of stage `st` into ring slot B: 3 load instructions per wave.
-template <int B>
-__device__ __forceinline__ void tiled_issue(const TiledCtx& c, int st) {
-  g2lds16(c.ga + st * kRowBytes, a_slot<B>() + c.wave * 1024);
-  g2lds16(c.gw + st * kRowBytes, w_slot<B>() + c.wave * 1024);
-  g2lds4(c.gs + st * kScaleRow, s_slot<B>() + (c.wave >> 2) * kScaleBytes + (c.wave & 3) * 256);
+// Copies of local stage ls into ring slot B.  Past the last stage the
+// copies repeat the last stage, so every stage issues the same number of
+// copies.
+template <int B, int kW>
+__device__ __forceinline__ void tiled_issue(const TiledCtx<kW>& c, int ls) {
+  constexpr int kFr = TiledCtx<kW>::kFr;
+  const int st = c.st0 + min(ls, c.nst - 1);
+#pragma unroll
+  for (int q = 0; q < kFr; ++q) {
+    const int vw = kFr * c.wave + q;
+    g2lds16(c.ga[q] + st * kRowBytes, a_slot<B>() + vw * 1024);
+    g2lds16(c.gw[q] + st * kRowBytes, w_slot<B>() + vw * 1024);
+    g2lds4(c.gs[q] + st * kScaleRow, s_slot<B>() + (vw >> 2) * kScaleBytes + (vw & 3) * 256);
+  }
 }
 
-// The 32 A values a thread decodes per stage: wave w handles fragment w;
-// lane l takes row 32w + l%32 and K [32 (l/32), +32) of the stage in slot B
-// (one 16-byte code piece and the scale bytes of its two blocks), and
-// writes them to the fp16 tile in MFMA lane order: region (w, step jj) of
-// 1 KB, lane slot l (so a wave's writes are one contiguous 1 KB).
+// The 32 A values of fragment f (32 rows) a thread decodes per stage: lane
+// l takes row 32f + l%32 and K [32 (l/32), +32) of the stage in slot B (one
+// 16-byte code piece and the scale bytes of its two blocks), and writes them
+// to the fp16 tile in MFMA lane order: region (f, step jj) of 1 KB, lane
+// slot l.  Wave w decodes fragments kFr w .. kFr w + kFr - 1.
 struct ADecode {
   uint4 codes;
   half2v s2;
@@ -165,13 +190,13 @@ struct ADecode {
 };
 
 template <int B>
-__device__ __forceinline__ ADecode decode_a_load(int wave, int lane) {
-  const int r = 32 * wave + (lane & 31), hh = lane >> 5;
+__device__ __forceinline__ ADecode decode_a_load(int f, int lane) {
+  const int r = 32 * f + (lane & 31), hh = lane >> 5;
   ADecode d;
   d.codes = *(const uint4*)(a_slot<B>() + piece_slot(r, hh) * 16);
   const uint32_t sb = *(const uint16_t*)(s_slot<B>() + r * kScaleRow + 2 * hh);
   d.s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
-  d.dst = wave * 4096 + lane * 16;
+  d.dst = f * 4096 + lane * 16;
   return d;
 }
 
@@ -181,49 +206,51 @@ __device__ __forceinline__ void decode_a_step(const ADecode& d, int jj) {
   *(half8v*)(af_buf<F>() + d.dst + jj * 1024) = dequant8_f16(word_of(d.codes, jj), jj < 2 ? d.s2.xx : d.s2.yy);
 }
 
-// One K stage: B = st % 4 (ring slot), st % 2 = B % 2 (decoded A buffer).
-// Wait for stage st + 1's copies, barrier, start the copies of stage st + 3
-// into slot (B + 3) % 4 (free since the barrier), then multiply stage st
-// while decoding A of stage st + 1.  Past the last stage the copies repeat
-// the last stage (every stage issues the same number of copies) and the
-// stage does nothing else; at the last stage the decode writes a tile
-// nobody reads.
-template <int B>
-__device__ __forceinline__ void tiled_stage(const TiledCtx& c, int st, float16v (&acc)[2][4]) {
-  NVFP4_WAIT_VMCNT(kCopies);
+// One K stage: B = ls % 4 (ring slot), ls % 2 = B % 2 (decoded A buffer).
+// Wait for stage ls + 1's copies, barrier, start the copies of stage ls + 3
+// into slot (B + 3) % 4 (free since the barrier), then multiply stage ls
+// while decoding A of stage ls + 1.  Past the last stage the stage does
+// nothing but its copies; at the last stage the decode writes a tile nobody
+// reads.
+template <int B, int kW>
+__device__ __forceinline__ void tiled_stage(const TiledCtx<kW>& c, int ls, float16v (&acc)[TiledCtx<kW>::kJ][4]) {
+  constexpr int kFr = TiledCtx<kW>::kFr, kJ = TiledCtx<kW>::kJ;
+  NVFP4_WAIT_VMCNT(TiledCtx<kW>::kCopies);
   stage_barrier();
-  tiled_issue<(B + 3) % kRing>(c, min(st + 3, c.nst - 1));
-  if (st >= c.nst) return;
+  tiled_issue<(B + 3) % kRing>(c, ls + 3);
+  if (ls >= c.nst) return;
 
   const int h = c.h, r32 = c.r32, lane = c.lane, wm = c.wm, wn = c.wn;
-  const ADecode dec = decode_a_load<(B + 1) % kRing>(c.wave, lane);
-  const uint8_t* af = af_buf<B & 1>();
-  // W: this lane's code piece h of rows 32 (2 wn + j) + r32, and the two
-  // scale bytes of its blocks 2h, 2h + 1.
-  uint4 cw[2];
-  half2v sw[2];
+  ADecode dec[kFr];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 32 * (2 * wn + j) + r32;
+  for (int q = 0; q < kFr; ++q) dec[q] = decode_a_load<(B + 1) % kRing>(kFr * c.wave + q, lane);
+  const uint8_t* af = af_buf<B & 1>();
+  // W: this lane's code piece h of rows 32 (kJ wn + j) + r32, and the two
+  // scale bytes of its blocks 2h, 2h + 1.
+  uint4 cw[kJ];
+  half2v sw[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int row = 32 * (kJ * wn + j) + r32;
     cw[j] = *(const uint4*)(w_slot<B>() + piece_slot(row, h) * 16);
     const uint32_t sb = *(const uint16_t*)(s_slot<B>() + kScaleBytes + row * kScaleRow + 2 * h);
     sw[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
   }
-  // Step jj's 8 MFMAs are interleaved one at a time with the LDS reads and W
-  // decoding of step jj + 1 and step jj's share of the A decode; each MFMA
-  // occupies the matrix core for several cycles, during which the wave
+  // Step jj's 4 kJ MFMAs are interleaved one at a time with the LDS reads
+  // and W decoding of step jj + 1 and step jj's share of the A decode; each
+  // MFMA occupies the matrix core for several cycles, during which the wave
   // issues the other work.
-  half8v av[2][4], wv[2][2];
+  half8v av[2][4], wv[2][kJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i) av[0][i] = *(const half8v*)(af + ((4 * wm + i) * 4 + 0) * 1024 + lane * 16);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) wv[0][j] = dequant8_f16(word_of(cw[j], 0), sw[j].xx);
+  for (int j = 0; j < kJ; ++j) wv[0][j] = dequant8_f16(word_of(cw[j], 0), sw[j].xx);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int cur = jj & 1, nxt = cur ^ 1;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kJ; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[cur][j], av[cur][i], acc[j][i], 0, 0, 0);
@@ -232,221 +259,386 @@ __device__ __forceinline__ void tiled_stage(const TiledCtx& c, int st, float16v 
       for (int i = 0; i < 4; ++i)
         av[nxt][i] = *(const half8v*)(af + ((4 * wm + i) * 4 + jj + 1) * 1024 + lane * 16);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < kJ; ++j)
         wv[nxt][j] = dequant8_f16(word_of(cw[j], jj + 1), jj + 1 < 2 ? sw[j].xx : sw[j].yy);
     }
-    decode_a_step<(B + 1) & 1>(dec, jj);
-    // MFMA, read, 2 VALU (x4); MFMA, 4 VALU (x3); MFMA, write
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
+    for (int q = 0; q < kFr; ++q) decode_a_step<(B + 1) & 1>(dec[q], jj);
+    if (kW == 4) {
+      // MFMA, read, 3 VALU (x4); MFMA, 3 VALU (x10); MFMA, write (x2)
 #pragma unroll
-    for (int g = 0; g < 3; ++g) {
+      for (int g = 0; g < 4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+#pragma unroll
+      for (int g = 0; g < 10; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+    } else {
+      // MFMA, read, 2 VALU (x4); MFMA, 4 VALU (x3); MFMA, write
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+#pragma unroll
+      for (int g = 0; g < 3; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// kLora: add the low-rank branch T L_up^T (T fp32 [M, r], L_up bf16 [N, r])
-// to each output before the bf16 rounding (see the epilogue).
-template <bool kLora>
-__global__ __launch_bounds__(512, 1) void nvfp4_gemm_tiled_kernel(
+// bf16 stores of one 32 x 32 fragment times gmul: rows m, columns
+// nb + 8 rq + 4 h + (0..3) from registers 4 rq .. 4 rq + 3.  D[n][m] of a
+// fragment sits at lane m + 32((n/4)%2), register (n%4) + 4(n/8): four
+// consecutive n per register quad.
+__device__ __forceinline__ void store_frag(const float16v& a, float gmul, uint16_t* __restrict__ out, int M, int N,
+                                           int m, int nb, int h) {
+  if (m >= M) return;
+  uint16_t* orow = out + (int64_t)m * N;
+  const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+  for (int rq = 0; rq < 4; ++rq) {
+    const int n = nb + 8 * rq + 4 * h;
+    const uint32_t b0 = f32_to_bf16_rne(a[4 * rq + 0] * gmul);
+    const uint32_t b1 = f32_to_bf16_rne(a[4 * rq + 1] * gmul);
+    const uint32_t b2 = f32_to_bf16_rne(a[4 * rq + 2] * gmul);
+    const uint32_t b3 = f32_to_bf16_rne(a[4 * rq + 3] * gmul);
+    if (vec_ok && n + 3 < N) {
+      *(uint2*)(orow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    } else {
+      if (n + 0 < N) orow[n + 0] = (uint16_t)b0;
+      if (n + 1 < N) orow[n + 1] = (uint16_t)b1;
+      if (n + 2 < N) orow[n + 2] = (uint16_t)b2;
+      if (n + 3 < N) orow[n + 3] = (uint16_t)b3;
+    }
+  }
+}
+
+// A wave's 4 kJ fragments: fragment (j, i) covers rows m0 + 128 wm + 32 i
+// and columns n0 + 32 kJ wn + 32 j.
+template <int kJ>
+__device__ __forceinline__ void store_tile(const float16v (&acc)[kJ][4], float gmul, uint16_t* __restrict__ out,
+                                           int M, int N, int m0, int n0, int wm, int wn, int h, int r32) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      store_frag(acc[j][i], gmul, out, M, N, m0 + 128 * wm + 32 * i + r32, n0 + 32 * kJ * wn + 32 * j, h);
+}
+
+// Low-rank branch: D = L_up T^T on the same 32 x 32 fragments (L_up rows n
+// as the first operand, T rows m as the second), accumulated straight into
+// acc after acc is scaled by g_a g_w.  T is split into bf16 hi + lo parts
+// (T - hi is exact in fp32 and its bf16 rounding leaves ~2^-17 of T), so
+// the branch keeps near-fp32 precision.  Ranks go 32 at a time through LDS
+// (the decoded-A buffers, free once the main loop is done): the threads
+// load the tile's T rows and L_up rows of the chunk together (kW / 4
+// threads per row), so the epilogue pays one memory latency per chunk.  LDS
+// rows hold 16-byte pieces, XOR-swizzled by the row: T row (128 B) piece
+// 2q + {hi, lo} and L_up row (64 B) piece q for the ranks 8q .. 8q + 7 of
+// the chunk (q = 2 kk + h: lane half h of 16-rank step kk).
+template <int kW>
+__device__ __forceinline__ void lora_epilogue(float16v (&acc)[TiledCtx<kW>::kJ][4], float gg,
+                                              const float* __restrict__ lora_t, const uint16_t* __restrict__ lora_up,
+                                              int r, int M, int N, int m0, int n0, int wm, int wn, int h, int r32) {
+  constexpr int kJ = TiledCtx<kW>::kJ;
+  constexpr int kTpr = kW / 4;            // threads per staged row
+  constexpr int kNq = 4 / kTpr;           // 8-rank groups per thread
+#pragma unroll
+  for (int j = 0; j < kJ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = acc[j][i] * gg;
+  const auto tr = buffer_of(lora_t, (uint32_t)M * (uint32_t)r * 4u);
+  const auto ur = buffer_of(lora_up, (uint32_t)N * (uint32_t)r * 2u);
+  uint4* st = (uint4*)g_af0;      // [256 rows][8 pieces]
+  uint4* su = (uint4*)g_af1;      // [256 rows][4 pieces]
+  const int srow = threadIdx.x / kTpr, q0 = (threadIdx.x % kTpr) * kNq;
+  for (int c0 = 0; c0 < r; c0 += 32) {
+    __syncthreads();              // previous users of the buffers are done
+    {
+      const uint32_t m = (uint32_t)(m0 + srow), n = (uint32_t)(n0 + srow);
+      uint4 tv[2 * kNq], uv[kNq];
+#pragma unroll
+      for (int e = 0; e < 2 * kNq; ++e) {
+        const uint32_t k = (uint32_t)(c0 + 8 * q0 + 4 * e);
+        tv[e] = buffer_load16(tr, m < (uint32_t)M && k < (uint32_t)r ? 4u * (m * r + k) : kBufferOob);
+      }
+#pragma unroll
+      for (int e = 0; e < kNq; ++e) {
+        const uint32_t k = (uint32_t)(c0 + 8 * (q0 + e));
+        uv[e] = buffer_load16(ur, n < (uint32_t)N && k < (uint32_t)r ? 2u * (n * r + k) : kBufferOob);
+      }
+#pragma unroll
+      for (int e = 0; e < kNq; ++e) {
+        const int q = q0 + e;
+        const uint4 t0 = tv[2 * e], t1 = tv[2 * e + 1];
+        const float f[8] = {__uint_as_float(t0.x), __uint_as_float(t0.y), __uint_as_float(t0.z),
+                            __uint_as_float(t0.w), __uint_as_float(t1.x), __uint_as_float(t1.y),
+                            __uint_as_float(t1.z), __uint_as_float(t1.w)};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const uint32_t h0 = f32_to_bf16_rne(f[2 * x]), h1 = f32_to_bf16_rne(f[2 * x + 1]);
+          const uint32_t l0 = f32_to_bf16_rne(f[2 * x] - bf16_bits_to_f32(h0));
+          const uint32_t l1 = f32_to_bf16_rne(f[2 * x + 1] - bf16_bits_to_f32(h1));
+          hi[x] = h0 | (h1 << 16);
+          lo[x] = l0 | (l1 << 16);
+        }
+        st[srow * 8 + ((2 * q) ^ (srow & 7))] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        st[srow * 8 + ((2 * q + 1) ^ (srow & 7))] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        su[srow * 4 + (q ^ (srow & 3))] = uv[e];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (c0 + 16 * kk >= r) break;
+      const int q = 2 * kk + h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 128 * wm + 32 * i + r32;
+        const short8v hi = __builtin_bit_cast(short8v, st[row * 8 + ((2 * q) ^ (row & 7))]);
+        const short8v lo = __builtin_bit_cast(short8v, st[row * 8 + ((2 * q + 1) ^ (row & 7))]);
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+          const int col = 32 * kJ * wn + 32 * j + r32;
+          const short8v up = __builtin_bit_cast(short8v, su[col * 4 + (q ^ (col & 3))]);
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(up, hi, acc[j][i], 0, 0, 0);
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(up, lo, acc[j][i], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// Grid: full_tiles whole tiles, then (tiles - full_tiles) x splits K parts.
+// Whole tiles are visited in an XCD-aware order when full_tiles % 8 == 0.
+// Part p of leftover tile t takes stages [p nst / S, (p + 1) nst / S) and
+// stores its unscaled fp32 accumulators to part[(t S + p)] in lane order
+// (kW == 4 only).  kLora: add the low-rank branch T L_up^T (T fp32 [M, r],
+// L_up bf16 [N, r]) to each output before the bf16 rounding (launched
+// with kW == 8 and without splits).
+template <int kW, bool kLora>
+__global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
-    uint16_t* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, const float* __restrict__ lora_t,
-    const uint16_t* __restrict__ lora_up, int r) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint16_t* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int full_tiles, int splits,
+    float* __restrict__ part, const float* __restrict__ lora_t, const uint16_t* __restrict__ lora_up, int r) {
+  using Ctx = TiledCtx<kW>;
+  constexpr int kFr = Ctx::kFr, kJ = Ctx::kJ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bid = blockIdx.x;
+  const int nst_all = K / TK;
+  int tile_id, st0 = 0, st1 = nst_all, unit = -1;
+  if (bid < full_tiles) {
+    tile_id = (full_tiles & 7) == 0 ? (bid & 7) * (full_tiles >> 3) + (bid >> 3) : bid;
+  } else {
+    unit = bid - full_tiles;
+    const int p = unit % splits;
+    tile_id = full_tiles + unit / splits;
+    st0 = p * nst_all / splits;
+    st1 = (p + 1) * nst_all / splits;
+  }
   int tile_m, tile_n;
-  map_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+  tile_of(tile_id, tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * TM, n0 = tile_n * TN;
   const int64_t row_bytes = K / 2, row_scales = K / 16;
 
-  TiledCtx c;
+  Ctx c;
   c.wave = wave;
   c.lane = lane;
-  c.wm = wave >> 2;                 // wave's A rows 128 wm ..
-  c.wn = wave & 3;                  // wave's W rows 64 wn ..
+  c.wm = wave / (kW / 2);           // wave's A rows 128 wm ..
+  c.wn = wave % (kW / 2);           // wave's W rows 32 kJ wn ..
   c.h = lane >> 5;
   c.r32 = lane & 31;
-  c.nst = K / TK;
-  {
-    // Code copies: wave w copies rows 32w..32w+31 of each operand's stage;
-    // lane l holds row 32w + l/2 and piece (l%2) ^ piece_swz(row), so it
-    // lands at piece_slot(row, piece).  Rows past M or N re-read the last
-    // row: those results are never stored.
-    const int r = 32 * wave + (lane >> 1);
-    const int piece = (lane & 1) ^ piece_swz(r);
-    c.ga = a_codes + (int64_t)min(m0 + r, M - 1) * row_bytes + 16 * piece;
-    c.gw = w_codes + (int64_t)min(n0 + r, N - 1) * row_bytes + 16 * piece;
-    // Scale copies: waves 0-3 copy A's rows 64 (w%4) + lane, 4-7 W's; laid
+  c.st0 = st0;
+  c.nst = st1 - st0;
+#pragma unroll
+  for (int q = 0; q < kFr; ++q) {
+    // Code copies of copy slot vw: lane l holds row 32 vw + l/2 and piece
+    // (l%2) ^ piece_swz(row), so it lands at piece_slot(row, piece).  Rows
+    // past M or N re-read the last row: those results are never stored.
+    // Scale copies: slots 0-3 copy A's rows 64 (vw%4) + lane, 4-7 W's; laid
     // out [operand][row][4 bytes].
-    const int sr = 64 * (wave & 3) + lane;
-    c.gs = wave < 4 ? a_scales + (int64_t)min(m0 + sr, M - 1) * row_scales
-                    : w_scales + (int64_t)min(n0 + sr, N - 1) * row_scales;
+    const int vw = kFr * wave + q;
+    const int rr = 32 * vw + (lane >> 1);
+    const int piece = (lane & 1) ^ piece_swz(rr);
+    c.ga[q] = a_codes + (int64_t)min(m0 + rr, M - 1) * row_bytes + 16 * piece;
+    c.gw[q] = w_codes + (int64_t)min(n0 + rr, N - 1) * row_bytes + 16 * piece;
+    const int sr = 64 * (vw & 3) + lane;
+    c.gs[q] = vw < 4 ? a_scales + (int64_t)min(m0 + sr, M - 1) * row_scales
+                     : w_scales + (int64_t)min(n0 + sr, N - 1) * row_scales;
   }
 
-  float16v acc[2][4];
+  float16v acc[kJ][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < kJ; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = float16v{};
 
   // Prologue: stages 0-2 in flight, stage 0's A decoded.
   tiled_issue<0>(c, 0);
-  tiled_issue<1>(c, min(1, c.nst - 1));
-  tiled_issue<2>(c, min(2, c.nst - 1));
-  NVFP4_WAIT_VMCNT(2 * kCopies);
+  tiled_issue<1>(c, 1);
+  tiled_issue<2>(c, 2);
+  NVFP4_WAIT_VMCNT(2 * Ctx::kCopies);
   stage_barrier();
-  {
-    const ADecode d = decode_a_load<0>(wave, lane);
+#pragma unroll
+  for (int q = 0; q < kFr; ++q) {
+    const ADecode d = decode_a_load<0>(kFr * wave + q, lane);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) decode_a_step<0>(d, jj);
   }
-  for (int st = 0; st < c.nst; st += 4) {
-    tiled_stage<0>(c, st, acc);
-    tiled_stage<1>(c, st + 1, acc);
-    tiled_stage<2>(c, st + 2, acc);
-    tiled_stage<3>(c, st + 3, acc);
+  for (int ls = 0; ls < c.nst; ls += 4) {
+    tiled_stage<0>(c, ls, acc);
+    tiled_stage<1>(c, ls + 1, acc);
+    tiled_stage<2>(c, ls + 2, acc);
+    tiled_stage<3>(c, ls + 3, acc);
   }
   NVFP4_WAIT_VMCNT(0);      // no copy may land in LDS after the workgroup ends
 
   const int h = c.h, r32 = c.r32, wm = c.wm, wn = c.wn;
-  // Epilogue: D[n][m] of each 32 x 32 tile sits at lane m + 32((n/4)%2),
-  // register (n%4) + 4(n/8): four consecutive n per register quad.
+  if (kW == 4 && unit >= 0) {
+    // K part of a split tile: fragment (j, i) of wave w at
+    // part[unit][(w * 16 + j * 4 + i) * 64 + lane][16].
+    float* dst = part + (int64_t)unit * kPartFloats + (int64_t)wave * 16 * 64 * 16 + lane * 16;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4* d4 = (float4*)(dst + (j * 4 + i) * 64 * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          d4[e] = make_float4(acc[j][i][4 * e], acc[j][i][4 * e + 1], acc[j][i][4 * e + 2], acc[j][i][4 * e + 3]);
+      }
+    return;
+  }
   const float gg = (*a_g) * (*w_g);
-  const bool vec_ok = (N & 3) == 0;
-  if (kLora) {
-    // Low-rank branch: D = L_up T^T on the same 32 x 32 fragments (L_up rows
-    // n as the first operand, T rows m as the second), accumulated straight
-    // into acc after acc is scaled by gg; the store below then multiplies by
-    // 1.  T is split into bf16 hi + lo parts (T - hi is exact in fp32 and
-    // its bf16 rounding leaves ~2^-17 of T), so the branch keeps near-fp32
-    // precision.  Ranks go 32 at a time through LDS (the decoded-A buffers,
-    // free once the main loop is done): all 512 threads load the tile's T
-    // rows and L_up rows for the chunk at once, so the epilogue pays one
-    // memory latency per chunk.  LDS rows hold 16-byte pieces, XOR-swizzled
-    // by the row: T row (128 B) piece (2 kk + h) * 2 + {hi, lo}, L_up row
-    // (64 B) piece 2 kk + h, where lane half h covers ranks 8h..8h+7 of the
-    // 16-rank step kk.
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[j][i] = acc[j][i] * gg;
-    const auto tr = buffer_of(lora_t, (uint32_t)M * (uint32_t)r * 4u);
-    const auto ur = buffer_of(lora_up, (uint32_t)N * (uint32_t)r * 2u);
-    uint4* st = (uint4*)g_af0;      // [256 rows][8 pieces]
-    uint4* su = (uint4*)g_af1;      // [256 rows][4 pieces]
-    const int srow = tid >> 1, shalf = tid & 1;
-    for (int c0 = 0; c0 < r; c0 += 32) {
-      __syncthreads();              // previous users of the buffers are done
-      {
-        const uint32_t m = (uint32_t)(m0 + srow), n = (uint32_t)(n0 + srow);
-        uint4 tv[4], uv[2];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t k = (uint32_t)(c0 + 16 * shalf + 4 * q);
-          tv[q] = buffer_load16(tr, m < (uint32_t)M && k < (uint32_t)r ? 4u * (m * r + k) : kBufferOob);
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const uint32_t k = (uint32_t)(c0 + 16 * shalf + 8 * q);
-          uv[q] = buffer_load16(ur, n < (uint32_t)N && k < (uint32_t)r ? 2u * (n * r + k) : kBufferOob);
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const uint4 t0 = tv[2 * hh], t1 = tv[2 * hh + 1];
-          const float f[8] = {__uint_as_float(t0.x), __uint_as_float(t0.y), __uint_as_float(t0.z),
-                              __uint_as_float(t0.w), __uint_as_float(t1.x), __uint_as_float(t1.y),
-                              __uint_as_float(t1.z), __uint_as_float(t1.w)};
-          uint32_t hi[4], lo[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t h0 = f32_to_bf16_rne(f[2 * e]), h1 = f32_to_bf16_rne(f[2 * e + 1]);
-            const uint32_t l0 = f32_to_bf16_rne(f[2 * e] - bf16_bits_to_f32(h0));
-            const uint32_t l1 = f32_to_bf16_rne(f[2 * e + 1] - bf16_bits_to_f32(h1));
-            hi[e] = h0 | (h1 << 16);
-            lo[e] = l0 | (l1 << 16);
-          }
-          const int p = (2 * shalf + hh) * 2;
-          st[srow * 8 + (p ^ (srow & 7))] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-          st[srow * 8 + ((p + 1) ^ (srow & 7))] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-          su[srow * 4 + ((2 * shalf + hh) ^ (srow & 3))] = uv[hh];
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (c0 + 16 * kk >= r) break;
-        const int pt = (2 * kk + h) * 2, pu = 2 * kk + h;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 128 * wm + 32 * i + r32;
-          const short8v hi = __builtin_bit_cast(short8v, st[row * 8 + (pt ^ (row & 7))]);
-          const short8v lo = __builtin_bit_cast(short8v, st[row * 8 + ((pt + 1) ^ (row & 7))]);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = 64 * wn + 32 * j + r32;
-            const short8v up = __builtin_bit_cast(short8v, su[col * 4 + (pu ^ (col & 3))]);
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(up, hi, acc[j][i], 0, 0, 0);
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(up, lo, acc[j][i], 0, 0, 0);
-          }
-        }
-      }
-    }
+  if (kLora) lora_epilogue<kW>(acc, gg, lora_t, lora_up, r, M, N, m0, n0, wm, wn, h, r32);
+  store_tile<kJ>(acc, kLora ? 1.0f : gg, out, M, N, m0, n0, wm, wn, h, r32);
+}
+
+// Leftover tile t: workgroup (t, g) sums, for fragments 4g .. 4g + 3 of
+// the tile (one per wave; fragment f = 16 w + 4 j + i of the GEMM's wave w),
+// the `splits` K parts in order, scales by g_a g_w, rounds to bf16 and
+// stores.
+__global__ __launch_bounds__(256) void nvfp4_gemm_tiled_reduce_kernel(const float* __restrict__ part,
+                                                                      const float* __restrict__ a_g,
+                                                                      const float* __restrict__ w_g,
+                                                                      uint16_t* __restrict__ out, int M, int N,
+                                                                      int tiles_m, int tiles_n, int full_tiles,
+                                                                      int splits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x >> 4;
+  const int f = 4 * (blockIdx.x & 15) + (threadIdx.x >> 6);
+  const int w = f >> 4, j = (f >> 2) & 3, i = f & 3;
+  int tile_m, tile_n;
+  tile_of(full_tiles + t, tiles_m, tiles_n, tile_m, tile_n);
+  const float* src = part + (int64_t)t * splits * kPartFloats + ((int64_t)f * 64 + lane) * 16;
+  float16v s = *(const float16v*)src;
+  for (int p = 1; p < splits; ++p) s += *(const float16v*)(src + p * kPartFloats);
+  const int wm = w >> 1, wn = w & 1;
+  store_frag(s, (*a_g) * (*w_g), out, M, N, tile_m * TM + 128 * wm + 32 * i + (lane & 31),
+             tile_n * TN + 128 * wn + 32 * j, lane >> 5);
+}
+
+namespace {
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
   }
-  const float gmul = kLora ? 1.0f : gg;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 128 * wm + 32 * i + r32;
-    if (m >= M) continue;
-    uint16_t* orow = out + (int64_t)m * N;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int n = n0 + 64 * wn + 32 * j + 8 * rq + 4 * h;
-        const uint32_t b0 = f32_to_bf16_rne(acc[j][i][4 * rq + 0] * gmul);
-        const uint32_t b1 = f32_to_bf16_rne(acc[j][i][4 * rq + 1] * gmul);
-        const uint32_t b2 = f32_to_bf16_rne(acc[j][i][4 * rq + 2] * gmul);
-        const uint32_t b3 = f32_to_bf16_rne(acc[j][i][4 * rq + 3] * gmul);
-        if (vec_ok && n + 3 < N) {
-          *(uint2*)(orow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-        } else {
-          if (n + 0 < N) orow[n + 0] = (uint16_t)b0;
-          if (n + 1 < N) orow[n + 1] = (uint16_t)b1;
-          if (n + 2 < N) orow[n + 2] = (uint16_t)b2;
-          if (n + 3 < N) orow[n + 3] = (uint16_t)b3;
-        }
-      }
-    }
-  }
+  return cached[dev];
+}
+
+struct TiledPlan {
+  int tiles_m, tiles_n, full_tiles, splits;
+  int64_t part_bytes;
+};
+
+// Whole tiles for every full round; the leftover tiles of a partial round
+// are split along K so that they fill the CUs (no split without leftovers
+// or when the parts would be shorter than kMinPartStages stages).
+TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K, bool allow_split) {
+  TiledPlan p;
+  p.tiles_m = (int)((M + TM - 1) / TM);
+  p.tiles_n = (int)((N + TN - 1) / TN);
+  const int tiles = p.tiles_m * p.tiles_n;
+  p.full_tiles = tiles;
+  p.splits = 1;
+  p.part_bytes = 0;
+  if (!allow_split) return p;
+  const int cus = device_cus();
+  const int left = tiles % cus;
+  if (left == 0) return p;
+  int s = cus / left;
+  const int nst = (int)(K / TK);
+  if (s > kMaxSplit) s = kMaxSplit;
+  if (s > nst / kMinPartStages) s = nst / kMinPartStages;
+  if (s < 2) return p;
+  p.full_tiles = tiles - left;
+  p.splits = s;
+  p.part_bytes = (int64_t)left * s * kPartFloats * 4;
+  return p;
+}
+}  // namespace
+
+int64_t nvfp4_gemm_tiled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0) return 0;
+  return plan_tiled(M, N, K, true).part_bytes;
+}
+
+hipError_t launch_nvfp4_gemm_tiled_ws(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
+                                      const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
+                                      int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  TiledPlan p = plan_tiled(M, N, K, workspace != nullptr);
+  if (p.part_bytes > workspace_bytes) p = plan_tiled(M, N, K, false);
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int grid = p.full_tiles + (tiles - p.full_tiles) * p.splits;
+  hipLaunchKernelGGL((nvfp4_gemm_tiled_kernel<4, false>), dim3((unsigned)grid), dim3(256), 0, stream, ac, as, ag, wc, ws,
+                     wg, (uint16_t*)out, (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n, p.full_tiles, p.splits,
+                     (float*)workspace, nullptr, nullptr, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.full_tiles == tiles) return e;
+  hipLaunchKernelGGL(nvfp4_gemm_tiled_reduce_kernel, dim3((unsigned)(16 * (tiles - p.full_tiles))), dim3(256), 0,
+                     stream,
+                     (const float*)workspace, ag, wg, (uint16_t*)out, (int)M, (int)N, p.tiles_m, p.tiles_n,
+                     p.full_tiles, p.splits);
+  return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_gemm_tiled(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
                                    const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N, int64_t K,
                                    hipStream_t stream) {
-  const int tiles_m = (int)((M + TM - 1) / TM), tiles_n = (int)((N + TN - 1) / TN);
-  hipLaunchKernelGGL(nvfp4_gemm_tiled_kernel<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream,
-                     ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, tiles_m, tiles_n, nullptr,
-                     nullptr, 0);
-  return hipGetLastError();
+  return launch_nvfp4_gemm_tiled_ws(ac, as, ag, wc, ws, wg, out, M, N, K, nullptr, 0, stream);
 }
 
 hipError_t launch_nvfp4_gemm_tiled_lora(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
                                         const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
                                         int64_t K, const float* lora_t, const void* lora_up, int64_t r,
                                         hipStream_t stream) {
-  const int tiles_m = (int)((M + TM - 1) / TM), tiles_n = (int)((N + TN - 1) / TN);
-  hipLaunchKernelGGL(nvfp4_gemm_tiled_kernel<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream,
-                     ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, tiles_m, tiles_n, lora_t,
-                     (const uint16_t*)lora_up, (int)r);
+  const TiledPlan p = plan_tiled(M, N, K, false);
+  hipLaunchKernelGGL((nvfp4_gemm_tiled_kernel<8, true>), dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(512), 0, stream,
+                     ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n,
+                     p.tiles_m * p.tiles_n, 1, nullptr, lora_t, (const uint16_t*)lora_up, (int)r);
   return hipGetLastError();
 }
 

@@ -57,6 +57,13 @@ hipError_t launch_int4g_quantize(const void* w, int64_t N, int64_t K, uint8_t* q
 
 // NVFP4 GEMM kernels; out[M, N] bf16 = g_a g_w * A . W^T.
 // tiled: K % 128 == 0.  decode: M <= 16, K % 128 == 0.  simple: K % 16 == 0.
+// Tiled GEMM with the leftover tiles of a partial last round split along K
+// (fp32 parts in `workspace`, summed by a second kernel); without a large
+// enough workspace every tile runs whole.
+int64_t nvfp4_gemm_tiled_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_nvfp4_gemm_tiled_ws(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
+                                      const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
+                                      int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t stream);
 hipError_t launch_nvfp4_gemm_tiled(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
                                    const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N, int64_t K,
                                    hipStream_t stream);

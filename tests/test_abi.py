@@ -97,6 +97,13 @@ def test_gemm_validation():
     assert f(*good, 0, 64, 128, 0, None) == OK
     assert f(*good, 32, 0, 128, 0, None) == OK
     assert q.lib().nvfp4_gemm(*good, 32, 64, 120, None) == SHAPE
+    ws = q.lib().nvfp4_gemm_ws
+    W = P(0x100000)
+    assert ws(*good, 32, 64, 128, 0, P(0x100010), 4096, None) == ALIGN         # workspace 256-byte aligned
+    assert ws(*good, 32, 64, 128, 0, P(0x70000), 4096, None) == INVALID         # overlaps out
+    assert ws(*good, 0, 64, 128, 0, W, 4096, None) == OK
+    assert q.lib().nvfp4_gemm_workspace_bytes(16, 4096, 4096) == 0               # decode sizes never split
+    assert q.lib().nvfp4_gemm_workspace_bytes(4096, 4096, 120) == 0              # K % 128
 
 
 def test_int4_validation():

@@ -147,6 +147,37 @@ def test_gemm_ragged_tiled_and_simple(M, N, K):
     check_gemm(a_bits, w_bits, algos=algos, label=f"ragged {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,split", [
+    (512, 512, 1024, True), (300, 260, 128 * 9, True), (1000, 700, 2048, True), (600, 1300, 256, False)])
+def test_gemm_tiled_split_and_whole(M, N, K, split):
+    # With a workspace the leftover tiles of the last round are split along
+    # K (parts of 4..5 stages, up to 8 parts) and summed by a second kernel;
+    # without one every tile runs whole.  Both must meet the bar; the split
+    # only changes the fp32 summation order.
+    q = _q()
+    import torch
+    a_bits = workloads.random_bf16(M + 5, (M, K))
+    w_bits = workloads.random_bf16(N + 6, (N, K), sigma=0.02, outlier_frac=0.005, outlier_mul=20)
+    a = assert_quant_equal(a_bits, label="split A")
+    w = assert_quant_equal(w_bits, label="split W")
+    ref = O.gemm(*O.quantize(a_bits), *O.quantize(w_bits))
+    nbytes = q.lib().nvfp4_gemm_workspace_bytes(M, N, K)
+    assert (nbytes > 0) == split
+    outs = {}
+    for name, ws in (("split", None), ("whole", torch.empty(0, dtype=torch.uint8, device="cuda:0"))):
+        out = Guarded((M, N), torch.bfloat16)
+        q.nvfp4_gemm(a, w, algo=q.ALGO_TILED, out=out.t, workspace=ws)
+        torch.cuda.synchronize()
+        assert out.intact(), "wrote outside its output"
+        y = F.bf16_from_bits(host_bits(out.t)).astype(np.float64)
+        ok, rl, rr = Mx.check_output(y, ref)
+        log(f"tiled {name} {M}x{N}x{K}: rel_l2={rl:.3e} row_ratio={rr:.3e}")
+        assert ok, f"{name}: rel_l2={rl:.3e} row_ratio={rr:.3e}"
+        outs[name] = y
+    if not split:
+        assert np.array_equal(outs["split"], outs["whole"])
+
+
 @pytest.mark.parametrize("M,N,K", [
     (1, 1, 128), (2, 3, 128), (1, 9, 2048), (2, 37, 2176), (1, 33, 4224), (2, 8, 6144), (1, 5, 32768 + 128)])
 def test_gemm_decode_shapes(M, N, K):
