@@ -302,6 +302,124 @@ __device__ __forceinline__ void tiled_stage(const TiledCtx<kW>& c, int ls, float
   }
 }
 
+// Four-wave stage with the work spread over the MFMAs.  A single wave per
+// SIMD stalls its MFMA stream whenever an instruction cannot issue, so
+// (a) the six copy instructions of stage ls + 3 are issued two per step in
+// steps 0-2, between MFMAs, instead of back to back after the barrier, and
+// (b) the W codes and scale bytes of stage ls + 1 are read into registers
+// during step 3 (slot (B + 1) % 4 is complete and visible since this
+// stage's barrier), so after the next barrier only the A fragment reads
+// stand before the first MFMA.
+struct WPre {
+  uint4 cw[4];
+  uint32_t sb[4];
+};
+
+template <int B>
+__device__ __forceinline__ void w_prefetch(const TiledCtx<4>& c, WPre& p) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 32 * (4 * c.wn + j) + c.r32;
+    p.cw[j] = *(const uint4*)(w_slot<B>() + piece_slot(row, c.h) * 16);
+    p.sb[j] = *(const uint16_t*)(s_slot<B>() + kScaleBytes + row * kScaleRow + 2 * c.h);
+  }
+}
+
+// Copy instructions 2 part, 2 part + 1 of the list (A, W, scales of copy
+// slot 2w, then of slot 2w + 1) for local stage ls into ring slot B.
+template <int B>
+__device__ __forceinline__ void tiled_copy_part(const TiledCtx<4>& c, int ls, int part) {
+  const int st = c.st0 + min(ls, c.nst - 1);
+#pragma unroll
+  for (int e = 2 * part; e < 2 * part + 2; ++e) {
+    const int q = e / 3, kind = e % 3, vw = 2 * c.wave + q;
+    if (kind == 0) g2lds16(c.ga[q] + st * kRowBytes, a_slot<B>() + vw * 1024);
+    else if (kind == 1) g2lds16(c.gw[q] + st * kRowBytes, w_slot<B>() + vw * 1024);
+    else g2lds4(c.gs[q] + st * kScaleRow, s_slot<B>() + (vw >> 2) * kScaleBytes + (vw & 3) * 256);
+  }
+}
+
+// kChecked: the stage may lie past the last one (then it only issues its
+// copies).  Whole groups of four stages run unchecked, with no branch in
+// the stage, so the compiler's tracking of which LDS slots the copies in
+// flight write stays exact and it does not wait for all of them before
+// the next stage's LDS reads.
+template <int B, bool kChecked>
+__device__ __forceinline__ void tiled_stage4(const TiledCtx<4>& c, int ls, float16v (&acc)[4][4], WPre (&pw)[2]) {
+  NVFP4_WAIT_VMCNT(TiledCtx<4>::kCopies);
+  stage_barrier();
+  if (kChecked && ls >= c.nst) {
+    tiled_issue<(B + 3) % kRing>(c, ls + 3);
+    return;
+  }
+  const int lane = c.lane, wm = c.wm;
+  // The step-0 A fragments are the only LDS reads the first MFMA waits for:
+  // issue them first (LDS reads complete in order), then the A-decode reads,
+  // while the step-0 W fragments are decoded from registers.
+  const uint8_t* af = af_buf<B & 1>();
+  half8v av[2][4], wv[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) av[0][i] = *(const half8v*)(af + ((4 * wm + i) * 4 + 0) * 1024 + lane * 16);
+  __builtin_amdgcn_sched_barrier(0);
+  const ADecode dec0 = decode_a_load<(B + 1) % kRing>(2 * c.wave, lane);
+  const ADecode dec1 = decode_a_load<(B + 1) % kRing>(2 * c.wave + 1, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  const WPre& cur = pw[B & 1];
+  half2v sw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sw[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.sb[j], 1.0f, false);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wv[0][j] = dequant8_f16(word_of(cur.cw[j], 0), sw[j].xx);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int cu = jj & 1, nx = cu ^ 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[cu][j], av[cu][i], acc[j][i], 0, 0, 0);
+    if (jj < 3) tiled_copy_part<(B + 3) % kRing>(c, ls + 3, jj);
+    if (jj + 1 < 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        av[nx][i] = *(const half8v*)(af + ((4 * wm + i) * 4 + jj + 1) * 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wv[nx][j] = dequant8_f16(word_of(cur.cw[j], jj + 1), jj + 1 < 2 ? sw[j].xx : sw[j].yy);
+    } else {
+      w_prefetch<(B + 1) % kRing>(c, pw[(B + 1) & 1]);
+    }
+    decode_a_step<(B + 1) & 1>(dec0, jj);
+    decode_a_step<(B + 1) & 1>(dec1, jj);
+    // MFMA, copy, 2 VALU (x2); MFMA, read, 3 VALU (x8); MFMA, 3 VALU (x4);
+    // MFMA, write (x2)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // bf16 stores of one 32 x 32 fragment times gmul: rows m, columns
 // nb + 8 rq + 4 h + (0..3) from registers 4 rq .. 4 rq + 3.  D[n][m] of a
 // fragment sits at lane m + 32((n/4)%2), register (n%4) + 4(n/8): four
@@ -503,11 +621,29 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) decode_a_step<0>(d, jj);
   }
-  for (int ls = 0; ls < c.nst; ls += 4) {
-    tiled_stage<0>(c, ls, acc);
-    tiled_stage<1>(c, ls + 1, acc);
-    tiled_stage<2>(c, ls + 2, acc);
-    tiled_stage<3>(c, ls + 3, acc);
+  if constexpr (kW == 4) {
+    WPre pw[2];
+    w_prefetch<0>(c, pw[0]);
+    int ls = 0;
+    for (; ls + 4 <= c.nst; ls += 4) {
+      tiled_stage4<0, false>(c, ls, acc, pw);
+      tiled_stage4<1, false>(c, ls + 1, acc, pw);
+      tiled_stage4<2, false>(c, ls + 2, acc, pw);
+      tiled_stage4<3, false>(c, ls + 3, acc, pw);
+    }
+    if (ls < c.nst) {
+      tiled_stage4<0, true>(c, ls, acc, pw);
+      tiled_stage4<1, true>(c, ls + 1, acc, pw);
+      tiled_stage4<2, true>(c, ls + 2, acc, pw);
+      tiled_stage4<3, true>(c, ls + 3, acc, pw);
+    }
+  } else {
+    for (int ls = 0; ls < c.nst; ls += 4) {
+      tiled_stage<0>(c, ls, acc);
+      tiled_stage<1>(c, ls + 1, acc);
+      tiled_stage<2>(c, ls + 2, acc);
+      tiled_stage<3>(c, ls + 3, acc);
+    }
   }
   NVFP4_WAIT_VMCNT(0);      // no copy may land in LDS after the workgroup ends
 
