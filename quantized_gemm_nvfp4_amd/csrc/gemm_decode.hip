@@ -7,13 +7,17 @@
 // (about one VALU op per weight value: the E2M1 conversion and the block
 // scale multiply, two values per instruction each) from becoming the limit.
 //
-// Two kernels:
+// Three kernels:
 //  - row-slot GEMV (M <= 2): W is read in storage order, one contiguous
 //    1 KB per load instruction; the MFMA reduces along each lane's own data
 //    (diagonal trick below).
-//  - row-block GEMM (M <= 16): 16 rows of W per workgroup, the activation
-//    rows in the MFMA's columns; each load instruction reads 64 bytes of 16
-//    rows, which HBM serves less efficiently, but M useful columns per MFMA.
+//  - packed row-block GEMM (3 <= M <= 8): 16 rows of W per workgroup, the
+//    MFMA's columns shared by P = 16 / Mp K-chunks of Mp activation rows, so
+//    the activation decode is shared and each load reads R = 16 / P rows x
+//    1024 / R contiguous bytes;
+//  - row-block GEMM (9 <= M <= 16): 16 rows of W per workgroup, the
+//    activation rows in the MFMA's columns; each load instruction reads 64
+//    bytes of 16 rows, which HBM serves less efficiently.
 #include "common.h"
 #include "launch.h"
 
@@ -148,6 +152,118 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_rowslot_kernel(
     v += __shfl_xor(v, 8, 16);
     const int rho = pair / kM, m = pair % kM;
     if (ii == 0 && m < M && n0 + rho < N) out[(int64_t)m * N + n0 + rho] = (uint16_t)f32_to_bf16_rne(kLora ? v : v * gg);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Packed row-block GEMM (3 <= M <= 8).
+//
+// A workgroup owns 16 rows of W; its 4 waves split K.  The product runs on
+// v_mfma_f32_16x16x32_f16 with W in the rows and the activation in the
+// columns, but the 16 columns carry P = 16 / Mp K-chunks of Mp activation
+// rows (Mp >= M): A row c R + w holds W row rg R + w (R = 16 / P, row group
+// rg) at chunk c, B column c Mp + m holds activation row m at the same
+// chunk, so the useful outputs are the P diagonal blocks D[c R + w][c Mp + m],
+// summed at the end.  Every W value enters exactly one MFMA, as with P = 1,
+// but each decoded activation fragment serves all P row groups, so the
+// activation decode (at P = 1 as much VALU work as the weight decode) drops
+// by P; and one load instruction covers R rows x 1024 / R contiguous bytes
+// (4 rows x 256 B at P = 4) instead of 16 rows x 64 B.  (P = 16 would be the
+// diagonal trick of the row-slot GEMV.)
+//
+// Lane (i, g) = i + 16 g handles 16-byte piece p = g + 4 (c + P t) of its
+// rows in iteration t (any assignment of K positions to lanes gives the same
+// dot products as long as both operands use it).  Every wave issues the same
+// unconditional buffer loads (pieces past K and rows past N or M read as
+// zero), kU iterations at a time, before decoding them.  (With P = 1, i.e.
+// 9 <= M <= 16, this layout measured slower than the row-block kernel
+// below, which is used there.)
+template <int P, bool kLora, int kU>
+__global__ __launch_bounds__(256) void nvfp4_gemm_rowpack_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
+    uint16_t* __restrict__ out, int M, int N, int K, const float* __restrict__ lora_t,
+    const uint16_t* __restrict__ lora_up, int rank) {
+  constexpr int R = 16 / P;     // W rows per row group = A rows per chunk = activation rows per chunk
+  // kU: iterations in flight per wave (P W loads each)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t row_bytes = (uint32_t)K / 2, row_scales = (uint32_t)K / 16;
+  const int n0 = blockIdx.x * 16;
+  const uint32_t nrows = (uint32_t)min(16, N - n0);
+  const auto wr = buffer_of(w_codes + (int64_t)n0 * row_bytes, nrows * row_bytes);
+  const auto wsr = buffer_of(w_scales + (int64_t)n0 * row_scales, nrows * row_scales);
+  const auto ar = buffer_of(a_codes, (uint32_t)M * row_bytes);      // rows >= M read as zero
+  const auto asr = buffer_of(a_scales, (uint32_t)M * row_scales);
+  const int i = lane & 15, g = lane >> 4, w = i % R, c = i / R;
+  const uint32_t pbase = (uint32_t)(g + 4 * c);                    // piece in iteration 0
+  const uint32_t niter = (row_bytes + 64u * P - 1) / (64u * P);
+
+  float4v acc[P];
+#pragma unroll
+  for (int rg = 0; rg < P; ++rg) acc[rg] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (uint32_t t0 = wave; t0 < niter; t0 += 4 * kU) {
+    uint4 wc[kU][P], xc[kU];
+    uint32_t ws[kU][P], xs[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t p = pbase + 4u * P * (t0 + 4u * u);
+      const bool in = 16u * p < row_bytes && t0 + 4u * u < niter;
+#pragma unroll
+      for (int rg = 0; rg < P; ++rg) {
+        const uint32_t row = (uint32_t)(rg * R + w);
+        wc[u][rg] = buffer_load16<kCachePolicyNT>(wr, in ? row * row_bytes + 16u * p : kOob);
+        ws[u][rg] = buffer_load2<kCachePolicyNT>(wsr, in ? row * row_scales + 2u * p : kOob);
+      }
+      xc[u] = buffer_load16(ar, in ? (uint32_t)w * row_bytes + 16u * p : kOob);
+      xs[u] = buffer_load2(asr, in ? (uint32_t)w * row_scales + 2u * p : kOob);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const half2v xs2 = e4m3x2_to_f16x2_div256(xs[u]);
+      const half2v x0 = {xs2.x, xs2.x}, x1 = {xs2.y, xs2.y};
+      half8v xv[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) xv[jj] = dequant8_f16_div256(word_of(xc[u], jj), jj < 2 ? x0 : x1);
+#pragma unroll
+      for (int rg = 0; rg < P; ++rg) {
+        const half2v ws2 = e4m3x2_to_f16x2_div256(ws[u][rg]);
+        const half2v w0 = {ws2.x, ws2.x}, w1 = {ws2.y, ws2.y};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16_div256(word_of(wc[u][rg], jj), jj < 2 ? w0 : w1),
+                                                           xv[jj], acc[rg], 0, 0, 0);
+      }
+    }
+  }
+
+  // D[ii][jj] (16 x 16) sits at lane jj + 16 (ii / 4), register ii % 4.
+  // Output (W row rg R + w, activation row m) sums, over the waves in order
+  // and then the chunks c, D[c R + w][c R + m].
+  __shared__ float4v red[4][P][64];
+#pragma unroll
+  for (int rg = 0; rg < P; ++rg) red[wave][rg][lane] = acc[rg];
+  __syncthreads();
+  const float gg = (*a_g) * (*w_g);
+  for (int t = threadIdx.x; t < 16 * R; t += blockDim.x) {
+    const int nrow = t / R, mm = t % R;
+    const int n = n0 + nrow;
+    if (mm >= M || n >= N) continue;
+    const int rg = nrow / R, wr_ = nrow % R;
+    float v = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv)
+#pragma unroll
+      for (int cc = 0; cc < P; ++cc) {
+        const int ii = cc * R + wr_, jj = cc * R + mm;
+        v += red[wv][rg][jj + 16 * (ii >> 2)][ii & 3];
+      }
+    v *= gg;
+    if (kLora)      // low-rank branch: + sum_j T[mm][j] L_up[n][j]
+      for (int q = 0; q < rank; ++q)
+        v += lora_t[(int64_t)mm * rank + q] * bf16_bits_to_f32(lora_up[(int64_t)n * rank + q]);
+    out[(int64_t)mm * N + n] = (uint16_t)f32_to_bf16_rne(v);
   }
 }
 
@@ -417,6 +533,20 @@ hipError_t launch_nvfp4_gemm_decode_lora(const uint8_t* ac, const uint8_t* as, c
       launch_rowslot<2, 4, true>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream, lora_t, lora_up, (int)r);
     else
       launch_rowslot<2, 4>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
+  } else if (M <= 8) {
+    // packed row-block kernel: P = 4 chunks for M <= 4 (2 iterations in
+    // flight per wave), P = 2 for M <= 8 (8 in flight); the fastest settings
+    // measured on the 21504 x 5376 decode weight
+    const dim3 grid((unsigned)((N + 15) / 16)), block(256);
+    const uint16_t* up = (const uint16_t*)lora_up;
+    const int ri = (int)r;
+    if (M <= 4) {
+      if (lora) hipLaunchKernelGGL((nvfp4_gemm_rowpack_kernel<4, true, 2>), grid, block, 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, up, ri);
+      else hipLaunchKernelGGL((nvfp4_gemm_rowpack_kernel<4, false, 2>), grid, block, 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, up, ri);
+    } else {
+      if (lora) hipLaunchKernelGGL((nvfp4_gemm_rowpack_kernel<2, true, 8>), grid, block, 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, up, ri);
+      else hipLaunchKernelGGL((nvfp4_gemm_rowpack_kernel<2, false, 8>), grid, block, 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, up, ri);
+    }
   } else {
     hipLaunchKernelGGL(nvfp4_gemm_rowblock_kernel, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream, ac, as,
                        ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, (const uint16_t*)lora_up,
