@@ -84,6 +84,32 @@ def test_quantize_degenerate():
     assert_quant_equal(one, label="single value")
 
 
+def test_quantize_rounding_boundaries():
+    # Quotients |x| / d swept in single-ulp steps across every E2M1 rounding
+    # boundary (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5): with the given global
+    # scale g_j = 2^-7 (1 + j 2^-23), the block maximum 6 * 2^-7 gives scale
+    # 1.0, d = g_j, and x = t * 2^-7 lands at t (1 - j 2^-23).  Codes must
+    # equal the oracle's (exact fl32 division, ties to even) for every j.
+    q = _q()
+    import torch
+    ts = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    vals = [6.0 * 2.0 ** -7] + [t * 2.0 ** -7 for t in ts] + [-t * 2.0 ** -7 for t in ts] + [0.0]
+    bits = F.bf16_bits(np.array([vals], dtype=np.float32))
+    assert np.array_equal(F.bf16_from_bits(bits)[0].astype(np.float64), np.array(vals)), "inputs not bf16-exact"
+    g0 = np.float32(2.0 ** -7)
+    for j in range(-40, 41):
+        gj = g0
+        step = np.float32(np.inf) if j > 0 else np.float32(-np.inf)
+        for _ in range(abs(j)):
+            gj = np.nextafter(gj, step, dtype=np.float32)
+        gt = torch.tensor([float(gj)], dtype=torch.float32, device="cuda:0")
+        codes, scales, _ = q.nvfp4_quantize(dev_bf16(bits), global_scale=gt)
+        torch.cuda.synchronize()
+        oc, osc, _ = O.quantize(bits, g=gj)
+        assert host_u8(scales)[0, 0] == osc[0, 0] == 0x38, f"j={j}: scale {host_u8(scales)[0, 0]:#x}"
+        assert np.array_equal(host_u8(codes), oc), f"j={j}: codes {host_u8(codes)} vs {oc}"
+
+
 def test_quantize_given_global_scale():
     bits = workloads.random_bf16(8, (33, 128))
     for g in (1.0, 0.003, 1e-30, 0.0):
