@@ -172,10 +172,12 @@ def run_prefill(torch, q, steps, warmup):
     }
 
 
-def graph_time_us(torch, fn, iters, reps=5):
+def graph_time_us(torch, fn, iters, reps=9):
     """Per-call GPU time of `fn(i)` for i in range(iters), captured once into
-    a HIP graph (so host launch overhead does not pace the GPU) and replayed
-    `reps` times between events."""
+    a HIP graph (so host launch overhead does not pace the GPU); the graph is
+    replayed `reps` times after two warm-up replays, each replay timed
+    between events, and the median replay is reported (clocks and the other
+    tenants of the memory system make single replays vary)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -188,15 +190,19 @@ def graph_time_us(torch, fn, iters, reps=5):
         for i in range(iters):
             fn(i)
     g.replay()
+    g.replay()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
+    times = []
     for _ in range(reps):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
         g.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) * 1e3 / (reps * iters)
+        t1.record()
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1) * 1e3 / iters)
+    times.sort()
+    return times[len(times) // 2]
 
 
 def run_decode(torch, q, iters=64, copies=16):
