@@ -712,7 +712,12 @@ struct TiledPlan {
 
 // Whole tiles for every full round; the leftover tiles of a partial round
 // are split along K so that they fill the CUs (no split without leftovers
-// or when the parts would be shorter than kMinPartStages stages).
+// or when the parts would be shorter than kMinPartStages stages).  Only a
+// last round at most half full is split (S = CUs / leftover >= 2): the chip
+// is power bound, so when fewer CUs run they clock higher, and a round 3/4
+// full (192 of 256 tiles, the DiT down GEMM) measured as fast unsplit as
+// split into 4 parts was slow (0.27 vs 0.34 ms, the parts' traffic
+// included).
 TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K, bool allow_split) {
   TiledPlan p;
   p.tiles_m = (int)((M + TM - 1) / TM);
