@@ -67,11 +67,17 @@ class Timer:
 
 
 def kernel_source_hash():
+    """Hash of the tiled GEMM's source with comments and whitespace removed,
+    so that counters taken on a build stay valid across comment-only edits."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("gemm_tiled.hip", "common.h"):
-        with open(os.path.join(ROOT, "quantized_gemm_nvfp4_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_gemm_nvfp4_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"//[^\n]*", "", src)
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        h.update(re.sub(r"\s+", " ", src).strip().encode())
     return h.hexdigest()[:16]
 
 
