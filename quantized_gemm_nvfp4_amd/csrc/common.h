@@ -39,6 +39,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Two fp32 -> two bf16 (round to nearest even) in one dword, a in the low
+// half: v_cvt_pk_bf16_f32, bit-identical to f32_to_bf16_rne for every
+// non-NaN input (checked on gfx950 over all 2^32 patterns).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{a, b}, bf16x2v));
+}
+
 // E4M3 (fn) byte of a non-negative fp32, RNE, saturating to 448 (0x7E)
 // above the largest finite value (and for +inf).
 __device__ __forceinline__ uint32_t e4m3_from_f32_sat(float v) {

@@ -432,17 +432,15 @@ __device__ __forceinline__ void store_frag(const float16v& a, float gmul, uint16
 #pragma unroll
   for (int rq = 0; rq < 4; ++rq) {
     const int n = nb + 8 * rq + 4 * h;
-    const uint32_t b0 = f32_to_bf16_rne(a[4 * rq + 0] * gmul);
-    const uint32_t b1 = f32_to_bf16_rne(a[4 * rq + 1] * gmul);
-    const uint32_t b2 = f32_to_bf16_rne(a[4 * rq + 2] * gmul);
-    const uint32_t b3 = f32_to_bf16_rne(a[4 * rq + 3] * gmul);
+    const uint32_t b01 = f32x2_to_bf16x2_rne(a[4 * rq + 0] * gmul, a[4 * rq + 1] * gmul);
+    const uint32_t b23 = f32x2_to_bf16x2_rne(a[4 * rq + 2] * gmul, a[4 * rq + 3] * gmul);
     if (vec_ok && n + 3 < N) {
-      *(uint2*)(orow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      *(uint2*)(orow + n) = make_uint2(b01, b23);
     } else {
-      if (n + 0 < N) orow[n + 0] = (uint16_t)b0;
-      if (n + 1 < N) orow[n + 1] = (uint16_t)b1;
-      if (n + 2 < N) orow[n + 2] = (uint16_t)b2;
-      if (n + 3 < N) orow[n + 3] = (uint16_t)b3;
+      if (n + 0 < N) orow[n + 0] = (uint16_t)b01;
+      if (n + 1 < N) orow[n + 1] = (uint16_t)(b01 >> 16);
+      if (n + 2 < N) orow[n + 2] = (uint16_t)b23;
+      if (n + 3 < N) orow[n + 3] = (uint16_t)(b23 >> 16);
     }
   }
 }

@@ -24,7 +24,6 @@
 namespace nvfp4k {
 
 namespace {
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* gbl_void_t;
 
@@ -55,41 +54,60 @@ __device__ __forceinline__ short8v as_short8(const uint4& v) { return __builtin_
 
 // ---- M <= 16: stream the weight once -------------------------------------
 // One workgroup per 16 weight rows; 4 waves split the 128-value groups
-// (group g goes to wave g % 4).  v_mfma_f32_16x16x32_bf16 with x as the first
-// operand (rows m, padded to 16) and the weight as the second (columns n), so
-// each lane's accumulators share one column n and one group scale.
+// (group g goes to wave g % 4), kI4Batch groups' loads in flight per wave.
+// v_mfma_f32_16x16x32_bf16 with x as the first operand (rows m, padded to
+// 16) and the weight as the second (columns n), so each lane's accumulators
+// share one column n and one group scale.  All loads are unconditional
+// buffer loads: rows past N or M and groups past K read as zero.
+namespace {
+constexpr int kI4Batch = 4;
+}  // namespace
+
 __global__ __launch_bounds__(256) void int4g_gemm_decode_kernel(const uint16_t* __restrict__ x,
                                                                 const uint8_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ s,
                                                                 uint16_t* __restrict__ out, int M, int N, int K) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16;
   const int r = lane & 15, grp = lane >> 4;
   const int ng = K / 128;
-  const int nrow = min(n0 + r, N - 1);
-  const uint8_t* qrow = q + (int64_t)nrow * (K / 2) + 16 * grp;
-  const uint16_t* srow = s + (int64_t)nrow * ng;
-  const bool x_on = r < M;
-  const uint16_t* xrow = x + (int64_t)(x_on ? r : 0) * K + 32 * grp;
+  const uint32_t row_bytes = (uint32_t)K / 2;
+  const uint32_t nrows = (uint32_t)min(16, N - n0);
+  const auto qr = buffer_of(q + (int64_t)n0 * row_bytes, nrows * row_bytes);
+  const auto sr = buffer_of(s + (int64_t)n0 * ng, nrows * (uint32_t)ng * 2u);
+  const auto xr = buffer_of(x, (uint32_t)M * (uint32_t)K * 2u);
+  const uint32_t qoff = (uint32_t)r * row_bytes + 16u * grp;
+  const uint32_t soff = (uint32_t)r * (uint32_t)ng * 2u;
+  const uint32_t xoff = ((uint32_t)r * (uint32_t)K + 32u * grp) * 2u;
   const short8v c8 = {kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16,
                       kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16};
 
   float4v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int g = wave; g < ng; g += 4) {
-    const uint4 wq = *(const uint4*)(qrow + (int64_t)g * 64);
-    const float sc = f16_bits_to_f32(srow[g]);
-    uint4 xv[4];
+  for (int g0 = wave; g0 < ng; g0 += 4 * kI4Batch) {
+    uint4 wq[kI4Batch], xv[kI4Batch][4];
+    uint32_t sb[kI4Batch];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      xv[jj] = x_on ? *(const uint4*)(xrow + (int64_t)g * 128 + 8 * jj) : make_uint4(0, 0, 0, 0);
-    float4v tmp = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < kI4Batch; ++u) {
+      const int g = g0 + 4 * u;
+      const bool in = g < ng;
+      wq[u] = buffer_load16<kCachePolicyNT>(qr, in ? qoff + 64u * g : kBufferOob);
+      sb[u] = buffer_load2<kCachePolicyNT>(sr, in ? soff + 2u * g : kBufferOob);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const short8v xa = as_short8(xv[jj]);
-      tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, int4x8_offset_bf16(word_of(wq, jj)), tmp, 0, 0, 0);
-      tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, c8, tmp, 0, 0, 0);
+      for (int jj = 0; jj < 4; ++jj) xv[u][jj] = buffer_load16(xr, in ? xoff + 256u * g + 16u * jj : kBufferOob);
     }
-    acc += sc * tmp;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kI4Batch; ++u) {
+      float4v tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const short8v xa = as_short8(xv[u][jj]);
+        tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, int4x8_offset_bf16(word_of(wq[u], jj)), tmp, 0, 0, 0);
+        tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, c8, tmp, 0, 0, 0);
+      }
+      acc += f16_bits_to_f32(sb[u]) * tmp;
+    }
   }
 
   __shared__ float4v red[4][64];
