@@ -121,6 +121,11 @@ __device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kAux);
 }
 
+template <int kAux = 0>
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kAux);
+}
+
 // Largest bf16 magnitude pattern among the two bf16 in a dword.
 __device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
   uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;

@@ -7,24 +7,20 @@
 // (about one VALU op per weight value: the E2M1 conversion and the block
 // scale multiply, two values per instruction each) from becoming the limit.
 //
-// Three kernels:
+// Two kernels:
 //  - row-slot GEMV (M <= 2): W is read in storage order, one contiguous
 //    1 KB per load instruction; the MFMA reduces along each lane's own data
 //    (diagonal trick below).
-//  - packed row-block GEMM (3 <= M <= 8): 16 rows of W per workgroup, the
-//    MFMA's columns shared by P = 16 / Mp K-chunks of Mp activation rows, so
-//    the activation decode is shared and each load reads R = 16 / P rows x
-//    1024 / R contiguous bytes;
-//  - row-block GEMM (9 <= M <= 16): 16 rows of W per workgroup, the
-//    activation rows in the MFMA's columns; each load instruction reads 64
-//    bytes of 16 rows, which HBM serves less efficiently.
+//  - row-block GEMM (3 <= M <= 16): 48 rows of W per workgroup, the
+//    activation rows in the MFMA's columns, each decoded activation fragment
+//    shared by three 16-row groups; the 16 lanes of a row read whole
+//    128-byte lines.
 #include "common.h"
 #include "launch.h"
 
 namespace nvfp4k {
 
 namespace {
-constexpr int kBatch = 4;                       // row-block kernel: chunks in flight per wave
 constexpr int kMaxSlots = 16;                   // row-slot kernel: K <= 16 * 2048
 constexpr uint32_t kOob = kBufferOob;
 
@@ -156,118 +152,6 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_rowslot_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Packed row-block GEMM (3 <= M <= 8).
-//
-// A workgroup owns 16 rows of W; its 4 waves split K.  The product runs on
-// v_mfma_f32_16x16x32_f16 with W in the rows and the activation in the
-// columns, but the 16 columns carry P = 16 / Mp K-chunks of Mp activation
-// rows (Mp >= M): A row c R + w holds W row rg R + w (R = 16 / P, row group
-// rg) at chunk c, B column c Mp + m holds activation row m at the same
-// chunk, so the useful outputs are the P diagonal blocks D[c R + w][c Mp + m],
-// summed at the end.  Every W value enters exactly one MFMA, as with P = 1,
-// but each decoded activation fragment serves all P row groups, so the
-// activation decode (at P = 1 as much VALU work as the weight decode) drops
-// by P; and one load instruction covers R rows x 1024 / R contiguous bytes
-// (4 rows x 256 B at P = 4) instead of 16 rows x 64 B.  (P = 16 would be the
-// diagonal trick of the row-slot GEMV.)
-//
-// Lane (i, g) = i + 16 g handles 16-byte piece p = g + 4 (c + P t) of its
-// rows in iteration t (any assignment of K positions to lanes gives the same
-// dot products as long as both operands use it).  Every wave issues the same
-// unconditional buffer loads (pieces past K and rows past N or M read as
-// zero), kU iterations at a time, before decoding them.  (With P = 1, i.e.
-// 9 <= M <= 16, this layout measured slower than the row-block kernel
-// below, which is used there.)
-template <int P, bool kLora, int kU>
-__global__ __launch_bounds__(256) void nvfp4_gemm_rowpack_kernel(
-    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
-    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
-    uint16_t* __restrict__ out, int M, int N, int K, const float* __restrict__ lora_t,
-    const uint16_t* __restrict__ lora_up, int rank) {
-  constexpr int R = 16 / P;     // W rows per row group = A rows per chunk = activation rows per chunk
-  // kU: iterations in flight per wave (P W loads each)
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t row_bytes = (uint32_t)K / 2, row_scales = (uint32_t)K / 16;
-  const int n0 = blockIdx.x * 16;
-  const uint32_t nrows = (uint32_t)min(16, N - n0);
-  const auto wr = buffer_of(w_codes + (int64_t)n0 * row_bytes, nrows * row_bytes);
-  const auto wsr = buffer_of(w_scales + (int64_t)n0 * row_scales, nrows * row_scales);
-  const auto ar = buffer_of(a_codes, (uint32_t)M * row_bytes);      // rows >= M read as zero
-  const auto asr = buffer_of(a_scales, (uint32_t)M * row_scales);
-  const int i = lane & 15, g = lane >> 4, w = i % R, c = i / R;
-  const uint32_t pbase = (uint32_t)(g + 4 * c);                    // piece in iteration 0
-  const uint32_t niter = (row_bytes + 64u * P - 1) / (64u * P);
-
-  float4v acc[P];
-#pragma unroll
-  for (int rg = 0; rg < P; ++rg) acc[rg] = float4v{0.f, 0.f, 0.f, 0.f};
-  for (uint32_t t0 = wave; t0 < niter; t0 += 4 * kU) {
-    uint4 wc[kU][P], xc[kU];
-    uint32_t ws[kU][P], xs[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const uint32_t p = pbase + 4u * P * (t0 + 4u * u);
-      const bool in = 16u * p < row_bytes && t0 + 4u * u < niter;
-#pragma unroll
-      for (int rg = 0; rg < P; ++rg) {
-        const uint32_t row = (uint32_t)(rg * R + w);
-        wc[u][rg] = buffer_load16<kCachePolicyNT>(wr, in ? row * row_bytes + 16u * p : kOob);
-        ws[u][rg] = buffer_load2<kCachePolicyNT>(wsr, in ? row * row_scales + 2u * p : kOob);
-      }
-      xc[u] = buffer_load16(ar, in ? (uint32_t)w * row_bytes + 16u * p : kOob);
-      xs[u] = buffer_load2(asr, in ? (uint32_t)w * row_scales + 2u * p : kOob);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const half2v xs2 = e4m3x2_to_f16x2_div256(xs[u]);
-      const half2v x0 = {xs2.x, xs2.x}, x1 = {xs2.y, xs2.y};
-      half8v xv[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) xv[jj] = dequant8_f16_div256(word_of(xc[u], jj), jj < 2 ? x0 : x1);
-#pragma unroll
-      for (int rg = 0; rg < P; ++rg) {
-        const half2v ws2 = e4m3x2_to_f16x2_div256(ws[u][rg]);
-        const half2v w0 = {ws2.x, ws2.x}, w1 = {ws2.y, ws2.y};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16_div256(word_of(wc[u][rg], jj), jj < 2 ? w0 : w1),
-                                                           xv[jj], acc[rg], 0, 0, 0);
-      }
-    }
-  }
-
-  // D[ii][jj] (16 x 16) sits at lane jj + 16 (ii / 4), register ii % 4.
-  // Output (W row rg R + w, activation row m) sums, over the waves in order
-  // and then the chunks c, D[c R + w][c R + m].
-  __shared__ float4v red[4][P][64];
-#pragma unroll
-  for (int rg = 0; rg < P; ++rg) red[wave][rg][lane] = acc[rg];
-  __syncthreads();
-  const float gg = (*a_g) * (*w_g);
-  for (int t = threadIdx.x; t < 16 * R; t += blockDim.x) {
-    const int nrow = t / R, mm = t % R;
-    const int n = n0 + nrow;
-    if (mm >= M || n >= N) continue;
-    const int rg = nrow / R, wr_ = nrow % R;
-    float v = 0.f;
-#pragma unroll
-    for (int wv = 0; wv < 4; ++wv)
-#pragma unroll
-      for (int cc = 0; cc < P; ++cc) {
-        const int ii = cc * R + wr_, jj = cc * R + mm;
-        v += red[wv][rg][jj + 16 * (ii >> 2)][ii & 3];
-      }
-    v *= gg;
-    if (kLora)      // low-rank branch: + sum_j T[mm][j] L_up[n][j]
-      for (int q = 0; q < rank; ++q)
-        v += lora_t[(int64_t)mm * rank + q] * bf16_bits_to_f32(lora_up[(int64_t)n * rank + q]);
-    out[(int64_t)mm * N + n] = (uint16_t)f32_to_bf16_rne(v);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Weight-only row-slot GEMV (M <= 2): bf16 activation x NVFP4 weight.
 //
 // The weight side is the row-slot GEMV above.  The activation is bf16 and is
@@ -383,102 +267,121 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_w4a16_rowslot_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Row-block GEMM (M <= 16).
+// Row-block GEMM (3 <= M <= 16).
 //
-//  - One workgroup per 16 weight rows; its 4 waves split K in 128-value
-//    chunks (chunk c goes to wave c % 4) and are summed in LDS in a fixed
-//    order, so results are deterministic.
-//  - Per chunk a lane loads 16 bytes of codes (32 values) of one W row and
-//    the 2 scale bytes of those values, and the same for one activation row;
-//    each wave issues kBatch chunks' loads before decoding any of them.
-//  - v_mfma_f32_16x16x32_f16 with W as the first operand: M <= 16 is padded
-//    to the MFMA's 16 columns (lanes of rows >= M feed zeros); the decoded
-//    fp16 operands are exact, as in the tiled kernel.
-__global__ __launch_bounds__(256) void nvfp4_gemm_rowblock_kernel(
+//  - A workgroup owns kRbGroups x 16 rows of W; its kRbWaves waves split K
+//    in steps of 256 values (128 bytes of a row), step t going to wave
+//    t % kRbWaves, and are summed in LDS in a fixed order, so results are
+//    deterministic.
+//  - Per step a lane (i, g) = i + 16 g loads bytes [32 g, 32 g + 32) of the
+//    step from row i of each row group and from activation row i, with their
+//    4 scale bytes, so the 16 lanes of a row read one whole 128-byte line
+//    per load pair.  Half lines (64 bytes of 16 rows per step) measured ~35%
+//    slower; so did the non-temporal cache policy on this pattern.
+//  - v_mfma_f32_16x16x32_f16 with W as the first operand and the activation
+//    rows as the second (columns; rows >= M read as zero); each decoded
+//    activation fragment feeds kRbGroups row groups.  The decoded operands
+//    are exact, as in the tiled kernel.
+//  - All loads are unconditional buffer loads: rows past N or M and steps
+//    past K read as zero (K % 128 == 0, so a lane's 32 bytes are all in the
+//    row or all past it).
+namespace {
+constexpr int kRbGroups = 3;   // 48 W rows per workgroup
+constexpr int kRbWaves = 8;    // waves splitting K
+}  // namespace
+
+template <bool kLora>
+__global__ __launch_bounds__(64 * kRbWaves) void nvfp4_gemm_rowblock_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
     uint16_t* __restrict__ out, int M, int N, int K, const float* __restrict__ lora_t,
     const uint16_t* __restrict__ lora_up, int rank) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 16;
-  const int r = lane & 15, grp = lane >> 4;
-  const int64_t row_bytes = K / 2, row_scales = K / 16;
-  const uint8_t* wrow = w_codes + (int64_t)min(n0 + r, N - 1) * row_bytes + 16 * grp;
-  const uint8_t* wsrow = w_scales + (int64_t)min(n0 + r, N - 1) * row_scales + 2 * grp;
-  const bool a_on = r < M;
-  const uint8_t* arow = a_codes + (int64_t)(a_on ? r : 0) * row_bytes + 16 * grp;
-  const uint8_t* asrow = a_scales + (int64_t)(a_on ? r : 0) * row_scales + 2 * grp;
-  const int nchunks = K / 128;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t row_bytes = (uint32_t)K / 2, row_scales = (uint32_t)K / 16;
+  const int n0 = blockIdx.x * 16 * kRbGroups;
+  const uint32_t nrows = (uint32_t)min(16 * kRbGroups, N - n0);
+  const auto wr = buffer_of(w_codes + (int64_t)n0 * row_bytes, nrows * row_bytes);
+  const auto wsr = buffer_of(w_scales + (int64_t)n0 * row_scales, nrows * row_scales);
+  const auto ar = buffer_of(a_codes, (uint32_t)M * row_bytes);
+  const auto asr = buffer_of(a_scales, (uint32_t)M * row_scales);
+  const int i = lane & 15, g = lane >> 4;
+  const uint32_t nsteps = (row_bytes + 127u) / 128u;
 
-  float4v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = wave; c0 < nchunks; c0 += 4 * kBatch) {
-    uint4 wc[kBatch], ac[kBatch];
-    uint32_t ws[kBatch], as[kBatch];
+  float4v acc[kRbGroups];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int c = c0 + 4 * u;
-      wc[u] = make_uint4(0, 0, 0, 0);
-      ws[u] = 0;
-      ac[u] = make_uint4(0, 0, 0, 0);
-      as[u] = 0;
-      if (c < nchunks) {
-        wc[u] = *(const uint4*)(wrow + (int64_t)c * 64);
-        ws[u] = *(const uint16_t*)(wsrow + (int64_t)c * 8);
-        if (a_on) {
-          ac[u] = *(const uint4*)(arow + (int64_t)c * 64);
-          as[u] = *(const uint16_t*)(asrow + (int64_t)c * 8);
-        }
-      }
+  for (int rg = 0; rg < kRbGroups; ++rg) acc[rg] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (uint32_t t = wave; t < nsteps; t += kRbWaves) {
+    const uint32_t off = 128u * t + 32u * g;   // byte offset in a row
+    const bool in = off < row_bytes;
+    uint4 wc[kRbGroups][2], xc[2];
+    uint32_t ws[kRbGroups], xs;
+#pragma unroll
+    for (int rg = 0; rg < kRbGroups; ++rg) {
+      const uint32_t row = 16u * rg + i;
+      wc[rg][0] = buffer_load16(wr, in ? row * row_bytes + off : kOob);
+      wc[rg][1] = buffer_load16(wr, in ? row * row_bytes + off + 16u : kOob);
+      ws[rg] = buffer_load4(wsr, in ? row * row_scales + off / 8u : kOob);
     }
+    xc[0] = buffer_load16(ar, in ? (uint32_t)i * row_bytes + off : kOob);
+    xc[1] = buffer_load16(ar, in ? (uint32_t)i * row_bytes + off + 16u : kOob);
+    xs = buffer_load4(asr, in ? (uint32_t)i * row_scales + off / 8u : kOob);
+    // all of the step's loads issue before any decoding (left to itself the
+    // compiler interleaves them with the math and waits earlier: ~18% slower)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int c = c0 + 4 * u;
-      if (c >= nchunks) break;
+    for (int p = 0; p < 2; ++p) {   // 16-byte piece p: 32 values, scale bytes 2p and 2p + 1
+      const half2v xs2 = e4m3x2_to_f16x2_div256(xs >> (16 * p));
+      const half2v x0 = {xs2.x, xs2.x}, x1 = {xs2.y, xs2.y};
+      half8v xv[4];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const half2v sw2 = e4m3_to_f16x2((ws[u] >> (8 * blk)) & 0xFFu);
-        const half2v sa2 = e4m3_to_f16x2((as[u] >> (8 * blk)) & 0xFFu);
+      for (int jj = 0; jj < 4; ++jj) xv[jj] = dequant8_f16_div256(word_of(xc[p], jj), jj < 2 ? x0 : x1);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int jj = 2 * blk + t;
-          const half8v wv = dequant8_f16(word_of(wc[u], jj), sw2);
-          const half8v av = dequant8_f16(word_of(ac[u], jj), sa2);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, av, acc, 0, 0, 0);
-        }
+      for (int rg = 0; rg < kRbGroups; ++rg) {
+        const half2v ws2 = e4m3x2_to_f16x2_div256(ws[rg] >> (16 * p));
+        const half2v w0 = {ws2.x, ws2.x}, w1 = {ws2.y, ws2.y};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16_div256(word_of(wc[rg][p], jj), jj < 2 ? w0 : w1),
+                                                           xv[jj], acc[rg], 0, 0, 0);
       }
     }
   }
 
-  __shared__ float4v red[4][64];
-  red[wave][lane] = acc;
+  __shared__ float4v red[kRbWaves][kRbGroups][64];
+#pragma unroll
+  for (int rg = 0; rg < kRbGroups; ++rg) red[wave][rg][lane] = acc[rg];
   __syncthreads();
-  if (wave != 0) return;
-  const float4v s = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
   const float gg = (*a_g) * (*w_g);
-  // D[n][m] (16 x 16): lane m + 16 (n / 4), register n % 4.
-  const int m = lane & 15;
-  const int n = n0 + 4 * (lane >> 4);
-  if (m >= M) return;
-  uint16_t* orow = out + (int64_t)m * N;
-  float v[4] = {s[0] * gg, s[1] * gg, s[2] * gg, s[3] * gg};
-  if (lora_t != nullptr) {      // low-rank branch: + sum_j T[m][j] L_up[n][j]
+  // D[n][m] (16 x 16) of row group rg: lane m + 16 (n / 4), register n % 4.
+  for (int e = threadIdx.x; e < kRbGroups * 64; e += 64 * kRbWaves) {
+    const int rg = e >> 6, ln = e & 63;
+    float4v s = red[0][rg][ln];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (n + q >= N) continue;
-      float l = 0.f;
-      for (int j = 0; j < rank; ++j) l += lora_t[(int64_t)m * rank + j] * bf16_bits_to_f32(lora_up[(int64_t)(n + q) * rank + j]);
-      v[q] += l;
+    for (int wv = 1; wv < kRbWaves; ++wv) s += red[wv][rg][ln];
+    const int m = ln & 15, n = n0 + 16 * rg + 4 * (ln >> 4);
+    if (m >= M) continue;
+    float v[4] = {s[0] * gg, s[1] * gg, s[2] * gg, s[3] * gg};
+    if (kLora) {    // low-rank branch: + sum_j T[m][j] L_up[n][j]
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (n + q >= N) continue;
+        float l = 0.f;
+        for (int j = 0; j < rank; ++j)
+          l += lora_t[(int64_t)m * rank + j] * bf16_bits_to_f32(lora_up[(int64_t)(n + q) * rank + j]);
+        v[q] += l;
+      }
     }
-  }
-  const uint32_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
-  const uint32_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
-  if ((N & 3) == 0 && n + 3 < N) {
-    *(uint2*)(orow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-  } else {
-    if (n + 0 < N) orow[n + 0] = (uint16_t)b0;
-    if (n + 1 < N) orow[n + 1] = (uint16_t)b1;
-    if (n + 2 < N) orow[n + 2] = (uint16_t)b2;
-    if (n + 3 < N) orow[n + 3] = (uint16_t)b3;
+    uint16_t* orow = out + (int64_t)m * N;
+    const uint32_t b01 = f32x2_to_bf16x2_rne(v[0], v[1]), b23 = f32x2_to_bf16x2_rne(v[2], v[3]);
+    if ((N & 3) == 0 && n + 3 < N) {
+      *(uint2*)(orow + n) = make_uint2(b01, b23);
+    } else {
+      if (n + 0 < N) orow[n + 0] = (uint16_t)b01;
+      if (n + 1 < N) orow[n + 1] = (uint16_t)(b01 >> 16);
+      if (n + 2 < N) orow[n + 2] = (uint16_t)b23;
+      if (n + 3 < N) orow[n + 3] = (uint16_t)(b23 >> 16);
+    }
   }
 }
 
@@ -533,24 +436,13 @@ hipError_t launch_nvfp4_gemm_decode_lora(const uint8_t* ac, const uint8_t* as, c
       launch_rowslot<2, 4, true>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream, lora_t, lora_up, (int)r);
     else
       launch_rowslot<2, 4>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
-  } else if (M <= 8) {
-    // packed row-block kernel: P = 4 chunks for M <= 4 (2 iterations in
-    // flight per wave), P = 2 for M <= 8 (8 in flight); the fastest settings
-    // measured on the 21504 x 5376 decode weight
-    const dim3 grid((unsigned)((N + 15) / 16)), block(256);
-    const uint16_t* up = (const uint16_t*)lora_up;
-    const int ri = (int)r;
-    if (M <= 4) {
-      if (lora) hipLaunchKernelGGL((nvfp4_gemm_rowpack_kernel<4, true, 2>), grid, block, 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, up, ri);
-      else hipLaunchKernelGGL((nvfp4_gemm_rowpack_kernel<4, false, 2>), grid, block, 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, up, ri);
-    } else {
-      if (lora) hipLaunchKernelGGL((nvfp4_gemm_rowpack_kernel<2, true, 8>), grid, block, 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, up, ri);
-      else hipLaunchKernelGGL((nvfp4_gemm_rowpack_kernel<2, false, 8>), grid, block, 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, up, ri);
-    }
   } else {
-    hipLaunchKernelGGL(nvfp4_gemm_rowblock_kernel, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream, ac, as,
-                       ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, (const uint16_t*)lora_up,
-                       (int)r);
+    const dim3 grid((unsigned)((N + 16 * kRbGroups - 1) / (16 * kRbGroups))), block(64 * kRbWaves);
+    const uint16_t* up = (const uint16_t*)lora_up;
+    if (lora)
+      hipLaunchKernelGGL(nvfp4_gemm_rowblock_kernel<true>, grid, block, 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, up, (int)r);
+    else
+      hipLaunchKernelGGL(nvfp4_gemm_rowblock_kernel<false>, grid, block, 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, up, (int)r);
   }
   return hipGetLastError();
 }

@@ -105,7 +105,7 @@ def gpu_gemm_lora(a, w, t, up_bits, algo):
 
 
 @pytest.mark.parametrize("M,N,K,r", [(1, 40, 128, 8), (2, 33, 256, 16), (4, 40, 2176, 16), (5, 70, 512, 32),
-                                     (16, 64, 384, 128),
+                                     (16, 64, 384, 128), (9, 97, 1152, 24),
                                      (130, 257, 1024, 32), (300, 200, 256, 64), (64, 96, 144, 8)])
 def test_gemm_lora(M, N, K, r):
     # T is a seeded fp32 input with full mantissas, so the epilogue's

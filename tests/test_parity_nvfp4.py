@@ -216,12 +216,13 @@ def test_gemm_decode_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (3, 17, 128), (4, 40, 2176), (5, 33, 4224), (8, 16, 5376), (9, 50, 2048), (16, 37, 16384),
-    (16, 20, 16384 + 128), (12, 64, 6144)])
-def test_gemm_packed_decode_shapes(M, N, K):
-    # 3 <= M <= 16 runs the packed row-slot kernel (P = 4, 2, 1 activation
-    # chunks per MFMA for M <= 4, <= 8, <= 16): partial last slot, ragged N,
-    # 8 slots (K = 16384); K past 8 slots falls back to the row-block kernel.
+    (3, 17, 128), (4, 40, 2176), (5, 49, 4224), (8, 16, 5376), (9, 50, 2048), (16, 37, 16384),
+    (16, 20, 16384 + 128), (12, 64, 6144), (6, 97, 5376), (16, 144, 2304), (11, 95, 33024)])
+def test_gemm_rowblock_decode_shapes(M, N, K):
+    # 3 <= M <= 16 runs the row-block kernel: 48 W rows per workgroup (N
+    # ragged against 48 and against 4), 8 waves taking 256-value steps in
+    # turn (K % 256 == 128 leaves a half step; K = 5376 gives the waves
+    # unequal step counts; K = 33024 is past the row-slot limit).
     a_bits = workloads.random_bf16(M * 19 + K, (M, K), outlier_frac=0.01, outlier_mul=30)
     w_bits = workloads.random_bf16(N * 23 + K, (N, K), sigma=0.02, zero_frac=0.05)
     check_gemm(a_bits, w_bits, algos=(0, 2), label=f"packed decode {M}x{N}x{K}")
