@@ -53,75 +53,103 @@ __device__ __forceinline__ short8v as_short8(const uint4& v) { return __builtin_
 }  // namespace
 
 // ---- M <= 16: stream the weight once -------------------------------------
-// One workgroup per 16 weight rows; 4 waves split the 128-value groups
-// (group g goes to wave g % 4), kI4Batch groups' loads in flight per wave.
-// v_mfma_f32_16x16x32_bf16 with x as the first operand (rows m, padded to
-// 16) and the weight as the second (columns n), so each lane's accumulators
-// share one column n and one group scale.  All loads are unconditional
-// buffer loads: rows past N or M and groups past K read as zero.
+// A workgroup owns kI4Groups x 16 weight rows; its kI4Waves waves take steps
+// of two 128-value groups (128 bytes of a row) in turn, step t going to wave
+// t % kI4Waves, and are summed in LDS in a fixed order.
+//  - Per step a lane (i, g) = i + 16 g loads 16 bytes at 16 g of both groups
+//    of the step from row i of each row group (the wave reads both halves of
+//    each 128-byte line back to back; half lines split across waves measured
+//    ~40% slower), the rows' two group scales, and x row i at the same
+//    positions.  All loads are unconditional buffer loads (rows past N or M
+//    and groups past K read as zero) and issue before any decoding.
+//  - v_mfma_f32_16x16x32_bf16 with x as the first operand (rows m) and the
+//    weight as the second (columns n), so each lane's accumulators share one
+//    column n and one group scale.  The -8 offset term of a group, sum x (-8),
+//    does not depend on the weight row: it is computed once per group on the
+//    matrix cores and starts each row group's accumulation, so every row
+//    group costs four MFMAs per group.
+//  - Bound by the loads: on 28672 x 8192 removing the decode or the MFMAs
+//    changed nothing, removing the x loads saved 6 us at M = 3 and 15 us at
+//    M = 16.
 namespace {
-constexpr int kI4Batch = 4;
+constexpr int kI4Groups = 4;   // 64 weight rows per workgroup
+constexpr int kI4Waves = 8;
 }  // namespace
 
-__global__ __launch_bounds__(256) void int4g_gemm_decode_kernel(const uint16_t* __restrict__ x,
-                                                                const uint8_t* __restrict__ q,
-                                                                const uint16_t* __restrict__ s,
-                                                                uint16_t* __restrict__ out, int M, int N, int K) {
+__global__ __launch_bounds__(64 * kI4Waves) void int4g_gemm_decode_kernel(const uint16_t* __restrict__ x,
+                                                                         const uint8_t* __restrict__ q,
+                                                                         const uint16_t* __restrict__ s,
+                                                                         uint16_t* __restrict__ out, int M, int N,
+                                                                         int K) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * 16;
-  const int r = lane & 15, grp = lane >> 4;
-  const int ng = K / 128;
+  const int n0 = blockIdx.x * 16 * kI4Groups;
+  const int i = lane & 15, g = lane >> 4;
+  const uint32_t ng = (uint32_t)K / 128;
   const uint32_t row_bytes = (uint32_t)K / 2;
-  const uint32_t nrows = (uint32_t)min(16, N - n0);
+  const uint32_t nrows = (uint32_t)min(16 * kI4Groups, N - n0);
   const auto qr = buffer_of(q + (int64_t)n0 * row_bytes, nrows * row_bytes);
-  const auto sr = buffer_of(s + (int64_t)n0 * ng, nrows * (uint32_t)ng * 2u);
+  const auto sr = buffer_of(s + (int64_t)n0 * ng, nrows * ng * 2u);
   const auto xr = buffer_of(x, (uint32_t)M * (uint32_t)K * 2u);
-  const uint32_t qoff = (uint32_t)r * row_bytes + 16u * grp;
-  const uint32_t soff = (uint32_t)r * (uint32_t)ng * 2u;
-  const uint32_t xoff = ((uint32_t)r * (uint32_t)K + 32u * grp) * 2u;
   const short8v c8 = {kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16,
                       kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16};
+  const uint32_t nsteps = (ng + 1) / 2;
 
-  float4v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int g0 = wave; g0 < ng; g0 += 4 * kI4Batch) {
-    uint4 wq[kI4Batch], xv[kI4Batch][4];
-    uint32_t sb[kI4Batch];
+  float4v acc[kI4Groups];
 #pragma unroll
-    for (int u = 0; u < kI4Batch; ++u) {
-      const int g = g0 + 4 * u;
-      const bool in = g < ng;
-      wq[u] = buffer_load16<kCachePolicyNT>(qr, in ? qoff + 64u * g : kBufferOob);
-      sb[u] = buffer_load2<kCachePolicyNT>(sr, in ? soff + 2u * g : kBufferOob);
+  for (int rg = 0; rg < kI4Groups; ++rg) acc[rg] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (uint32_t t = wave; t < nsteps; t += kI4Waves) {
+    uint4 wq[kI4Groups][2], xv[2][4];
+    uint32_t sb[kI4Groups][2];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) xv[u][jj] = buffer_load16(xr, in ? xoff + 256u * g + 16u * jj : kBufferOob);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t grp = 2 * t + h;
+      const bool in = grp < ng;
+#pragma unroll
+      for (int rg = 0; rg < kI4Groups; ++rg) {
+        const uint32_t row = 16u * rg + i;
+        wq[rg][h] = buffer_load16(qr, in ? row * row_bytes + 64u * grp + 16u * g : kBufferOob);
+        sb[rg][h] = buffer_load2(sr, in ? (row * ng + grp) * 2u : kBufferOob);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        xv[h][jj] = buffer_load16(xr, in ? ((uint32_t)i * (uint32_t)K + 128u * grp + 32u * g + 8u * jj) * 2u : kBufferOob);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < kI4Batch; ++u) {
-      float4v tmp = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) {
+      float4v off = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const short8v xa = as_short8(xv[u][jj]);
-        tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, int4x8_offset_bf16(word_of(wq[u], jj)), tmp, 0, 0, 0);
-        tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, c8, tmp, 0, 0, 0);
+      for (int jj = 0; jj < 4; ++jj) off = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_short8(xv[h][jj]), c8, off, 0, 0, 0);
+#pragma unroll
+      for (int rg = 0; rg < kI4Groups; ++rg) {
+        float4v tmp = off;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_short8(xv[h][jj]), int4x8_offset_bf16(word_of(wq[rg][h], jj)),
+                                                        tmp, 0, 0, 0);
+        acc[rg] += f16_bits_to_f32(sb[rg][h]) * tmp;
       }
-      acc += f16_bits_to_f32(sb[u]) * tmp;
     }
   }
 
-  __shared__ float4v red[4][64];
-  red[wave][lane] = acc;
-  __syncthreads();
-  if (wave != 0) return;
-  const float4v sum = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
-  // D[m][n] (16 x 16): lane n + 16 (m / 4), register m % 4.
-  const int n = n0 + (lane & 15);
-  if (n >= N) return;
+  __shared__ float4v red[kI4Waves][kI4Groups][64];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 4 * (lane >> 4) + i;
-    if (m < M) out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(sum[i]);
+  for (int rg = 0; rg < kI4Groups; ++rg) red[wave][rg][lane] = acc[rg];
+  __syncthreads();
+  for (int e = threadIdx.x; e < kI4Groups * 64; e += 64 * kI4Waves) {
+    const int rg = e >> 6, ln = e & 63;
+    float4v sum = red[0][rg][ln];
+#pragma unroll
+    for (int wv = 1; wv < kI4Waves; ++wv) sum += red[wv][rg][ln];
+    // D[m][n] (16 x 16): lane n + 16 (m / 4), register m % 4.
+    const int n = n0 + 16 * rg + (ln & 15);
+    if (n >= N) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * (ln >> 4) + r;
+      if (m < M) out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(sum[r]);
+    }
   }
 }
 
@@ -396,7 +424,8 @@ hipError_t launch_int4g_gemm_decode(const void* x, const uint8_t* q, const void*
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL(int4g_gemm_decode_kernel, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(int4g_gemm_decode_kernel, dim3((unsigned)((N + 16 * kI4Groups - 1) / (16 * kI4Groups))),
+                     dim3(64 * kI4Waves), 0, stream,
                      (const uint16_t*)x, q, (const uint16_t*)s, (uint16_t*)out, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }

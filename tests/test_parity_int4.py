@@ -94,10 +94,13 @@ def test_int4_gemv_ragged(M, N, K):
     check_gemv(x, w, algos=algos, label=f"int4 {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 9, 128), (2, 13, 256), (1, 17, 2176), (2, 20, 4096), (1, 3, 32768 + 128)])
+@pytest.mark.parametrize("M,N,K", [(1, 9, 128), (2, 13, 256), (1, 17, 2176), (2, 20, 4096), (1, 3, 32768 + 128),
+                                   (3, 65, 384), (7, 130, 2304), (12, 64, 1024), (16, 100, 4224), (9, 47, 128)])
 def test_int4_decode_shapes(M, N, K):
     # M <= 2 runs the row-slot GEMV (1 KB slots of 16 groups, partial last
-    # slot, ragged N); K > 32768 falls back to the row-block kernel.
+    # slot, ragged N); K > 32768 and 3 <= M <= 16 run the row-block kernel
+    # (64 rows per workgroup, N ragged against it; an odd group count leaves
+    # a half step; K = 2304 gives its 8 waves unequal step counts).
     x = workloads.random_bf16(M + K, (M, K), outlier_frac=0.01, outlier_mul=20)
     w = workloads.random_bf16(N + K + 1, (N, K), sigma=0.02, zero_frac=0.05)
     check_gemv(x, w, algos=(0, 2), label=f"int4 decode {M}x{N}x{K}")
