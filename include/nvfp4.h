@@ -140,7 +140,8 @@ nvfp4_status nvfp4_quantize_ex(const void* x_bf16, int64_t rows, int64_t cols,
  * bfloat16 output).  Each decoded product is exact; sums are fp32.
  * a_codes [M, K/2], a_scales [M, K/16], w_codes [N, K/2], w_scales
  * [N, K/16]; a_gscale and w_gscale are device fp32 pointers (no host sync).
- * K % 16 == 0.  M <= 16 runs the decode kernel that streams W once.
+ * K % 16 == 0.  M <= 16 runs the decode kernel that streams W once
+ * (K % 128 == 0 and K <= 2^24; other K take the simple kernel).
  * K == 0 writes zeros (the packed operands may then be NULL).
  * out must not overlap any input.
  */
@@ -152,7 +153,8 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
 typedef enum nvfp4_algo {
   NVFP4_ALGO_AUTO = 0,    /* what nvfp4_gemm / int4g_gemv pick */
   NVFP4_ALGO_TILED = 1,   /* the LDS-staged MFMA tile kernel (any M) */
-  NVFP4_ALGO_DECODE = 2,  /* the weight-streaming kernel (M <= 16 only) */
+  NVFP4_ALGO_DECODE = 2,  /* the weight-streaming kernel (M <= 16, K % 128 == 0
+                             and K <= 2^24 only; else NVFP4_ERR_UNSUPPORTED) */
   NVFP4_ALGO_SIMPLE = 3   /* one output per thread, fp32 FMA (any shape) */
 } nvfp4_algo;
 
@@ -225,7 +227,8 @@ nvfp4_status int4g_quantize(const void* w_bf16, int64_t N, int64_t K, int64_t gr
  * them.  Passage: same formula block (x ~ s*q with a scale per group); the
  * weight-only GPU kernels of the same page's method chart.  Each group's
  * integer-weighted sum is taken in fp32, then scaled once by its s16.
- * Any M >= 1: M <= 16 streams the weight once; larger M runs MFMA tiles.
+ * Any M >= 1: M <= 16 streams the weight once (K <= 2^24; larger K take
+ * the simple kernel); larger M runs MFMA tiles.
  */
 nvfp4_status int4g_gemv(const void* x_bf16, const uint8_t* q, const void* scales_fp16,
                         void* out_bf16, int64_t M, int64_t N, int64_t K, int64_t group,

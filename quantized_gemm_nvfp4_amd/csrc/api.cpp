@@ -60,6 +60,10 @@ nvfp4_status check_disjoint(const Range* outs, int nout, const Range* ins, int n
 }
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
+// The weight-streaming kernels address a workgroup's weight rows and the
+// whole activation through buffer resources with 32-bit byte ranges (at
+// most 64 rows x K values); 2^24 keeps every range far below 2^31.
+constexpr int64_t kDecodeMaxK = int64_t(1) << 24;
 
 #define REQUIRE_PTR(p)                                                               \
   do {                                                                               \
@@ -118,7 +122,9 @@ nvfp4_status gemm_impl(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   if (M == 0 || N == 0) return ok();
   if (nvfp4_status s = check_disjoint(outs, 2, ins, 8)) return s;
   const bool k128 = (K % 128) == 0 && K > 0;
-  if (algo == NVFP4_ALGO_AUTO) algo = !k128 ? NVFP4_ALGO_SIMPLE : (M <= 16 ? NVFP4_ALGO_DECODE : NVFP4_ALGO_TILED);
+  if (algo == NVFP4_ALGO_AUTO)
+    algo = !k128 ? NVFP4_ALGO_SIMPLE
+                 : (M <= 16 ? (K <= kDecodeMaxK ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE) : NVFP4_ALGO_TILED);
   hipStream_t st = (hipStream_t)stream;
   switch (algo) {
     case NVFP4_ALGO_TILED:
@@ -132,8 +138,8 @@ nvfp4_status gemm_impl(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                                                            (int64_t)workspace_bytes, st),
                         "nvfp4_gemm tiled launch");
     case NVFP4_ALGO_DECODE:
-      if (!k128 || M > 16)
-        return fail(NVFP4_ERR_UNSUPPORTED, "decode kernel needs M <= 16 and K %% 128 == 0 (M=%lld, K=%lld)",
+      if (!k128 || M > 16 || K > kDecodeMaxK)
+        return fail(NVFP4_ERR_UNSUPPORTED, "decode kernel needs M <= 16, K %% 128 == 0 and K <= 2^24 (M=%lld, K=%lld)",
                     (long long)M, (long long)K);
       return hip_status(nvfp4k::launch_nvfp4_gemm_decode_lora(a_codes, a_scales, a_gscale, w_codes, w_scales,
                                                               w_gscale, out_bf16, M, N, K, lora_t, lora_up, r, st),
@@ -324,7 +330,9 @@ nvfp4_status int4g_gemv_ex(const void* x_bf16, const uint8_t* q, const void* sca
   const Range ins[3] = {{x_bf16, M * K * 2, "x"}, {q, N * K / 2, "q"}, {scales_fp16, N * (K / 128) * 2, "scales"}};
   if (M == 0 || N == 0) return ok();
   if (nvfp4_status s = check_disjoint(outs, 1, ins, 3)) return s;
-  if (algo == NVFP4_ALGO_AUTO) algo = (K == 0) ? NVFP4_ALGO_SIMPLE : (M <= 16 ? NVFP4_ALGO_DECODE : NVFP4_ALGO_TILED);
+  if (algo == NVFP4_ALGO_AUTO)
+    algo = (K == 0) ? NVFP4_ALGO_SIMPLE
+                    : (M <= 16 ? (K <= kDecodeMaxK ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE) : NVFP4_ALGO_TILED);
   hipStream_t st = (hipStream_t)stream;
   switch (algo) {
     case NVFP4_ALGO_TILED:
@@ -332,7 +340,9 @@ nvfp4_status int4g_gemv_ex(const void* x_bf16, const uint8_t* q, const void* sca
       return hip_status(nvfp4k::launch_int4g_gemm_tiled(x_bf16, q, scales_fp16, out_bf16, M, N, K, st),
                         "int4g_gemv tiled launch");
     case NVFP4_ALGO_DECODE:
-      if (M > 16 || K == 0) return fail(NVFP4_ERR_UNSUPPORTED, "decode kernel needs M <= 16 and K > 0 (M=%lld)", (long long)M);
+      if (M > 16 || K == 0 || K > kDecodeMaxK)
+        return fail(NVFP4_ERR_UNSUPPORTED, "decode kernel needs M <= 16 and 0 < K <= 2^24 (M=%lld, K=%lld)",
+                    (long long)M, (long long)K);
       return hip_status(nvfp4k::launch_int4g_gemm_decode(x_bf16, q, scales_fp16, out_bf16, M, N, K, st),
                         "int4g_gemv decode launch");
     default:

@@ -106,6 +106,15 @@ def test_gemm_validation():
     assert q.lib().nvfp4_gemm_workspace_bytes(4096, 4096, 120) == 0              # K % 128
 
 
+def test_decode_k_limit():
+    # the weight-streaming kernels take K <= 2^24; beyond it an explicit
+    # decode request is refused (before any device work)
+    far = [P(k << 36) for k in range(1, 8)]      # fake, far apart: no overlap at this K
+    K = (1 << 24) + 128
+    assert q.lib().nvfp4_gemm_ex(*far, 4, 8, K, q.ALGO_DECODE, None) == UNSUP
+    assert q.lib().int4g_gemv_ex(far[0], far[1], far[2], far[3], 4, 8, K, 128, q.ALGO_DECODE, None) == UNSUP
+
+
 def test_int4_validation():
     lib = q.lib()
     assert lib.int4g_quantize(A, 8, 256, 64, B, C, None) == UNSUP      # group must be 128
