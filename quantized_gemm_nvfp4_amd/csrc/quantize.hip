@@ -72,26 +72,68 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
   return (c & 8u) ? -v : v;
 }
 
-// Element code of the bf16 pattern h under d (the quantizer's rule).
-__device__ __forceinline__ uint32_t element_code(uint32_t h, float d) {
-  const float y = (d != 0.0f) ? bf16_bits_to_f32(h & 0x7FFFu) / d : 0.0f;
+// The element step divides |x| by the block's d with one rounding.  Per
+// element that division is replaced by the block's reciprocal r = 1/d
+// (correctly rounded, once per block) and Markstein's correction: q = |x| r
+// lies within one ulp of the quotient, the remainder |x| - q d is exact in
+// one fma, and q + (|x| - q d) r rounded once is the correctly rounded
+// quotient.  It equals the division for every bf16 significand against
+// every fp32 significand (tests/quotient_check.c runs all 2^30 pairs) as
+// long as no step under- or overflows, which holds for 2^-64 <= d < 2^100;
+// blocks outside that range divide.
+constexpr float kQuotLo = 0x1p-64f, kQuotHi = 0x1p100f;
+
+__device__ __forceinline__ bool quot_fast(float d) { return d >= kQuotLo && d < kQuotHi; }
+
+// Element code of the bf16 pattern h under d (the quantizer's rule); with
+// kFast, r = 1/d and quot_fast(d).
+template <bool kFast>
+__device__ __forceinline__ uint32_t element_code(uint32_t h, float d, float r) {
+#pragma clang fp contract(off)
+  const float ax = bf16_bits_to_f32(h & 0x7FFFu);
+  float y;
+  if (kFast) {
+    const float q = ax * r;
+    y = __builtin_fmaf(__builtin_fmaf(-q, d, ax), r, q);
+  } else {
+    y = (d != 0.0f) ? ax / d : 0.0f;
+  }
   return e2m1_code_from_f32(y) | ((h >> 12) & 8u);
 }
 
-__device__ __forceinline__ float block_error(const uint32_t (&w)[8], uint32_t sc, float g) {
+template <bool kFast>
+__device__ __forceinline__ float block_error_d(const uint32_t (&w)[8], float d, float r) {
 #pragma clang fp contract(off)
-  const float d = e4m3_to_f32(sc) * g;
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
     const float x = bf16_bits_to_f32(h);
-    const float xhat = e2m1_value(element_code(h, d)) * d;
+    const float xhat = e2m1_value(element_code<kFast>(h, d, r)) * d;
     const float e = x - xhat;
     const float sq = e * e;
     acc = acc + sq;
   }
   return acc;
+}
+
+__device__ __forceinline__ float block_error(const uint32_t (&w)[8], uint32_t sc, float g) {
+#pragma clang fp contract(off)
+  const float d = e4m3_to_f32(sc) * g;
+  return quot_fast(d) ? block_error_d<true>(w, d, 1.0f / d) : block_error_d<false>(w, d, 0.0f);
+}
+
+// Codes of a block under d, two per byte (element 2j in the low nibble).
+template <bool kFast>
+__device__ __forceinline__ uint2 encode_block(const uint32_t (&w)[8], float d, float r) {
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t clo = element_code<kFast>(w[i] & 0xFFFFu, d, r);
+    const uint32_t chi = element_code<kFast>(w[i] >> 16, d, r);
+    packed[i >> 2] |= (clo | (chi << 4)) << (8 * (i & 3));
+  }
+  return make_uint2(packed[0], packed[1]);
 }
 
 __device__ __forceinline__ uint32_t scale_code(float amax_b, float top, float g) {
@@ -163,14 +205,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
       }
     }
     const float d = e4m3_to_f32(sc) * g;
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t clo = element_code(w[i] & 0xFFFFu, d);
-      const uint32_t chi = element_code(w[i] >> 16, d);
-      packed[i >> 2] |= (clo | (chi << 4)) << (8 * (i & 3));
-    }
-    codes[b] = make_uint2(packed[0], packed[1]);
+    codes[b] = quot_fast(d) ? encode_block<true>(w, d, 1.0f / d) : encode_block<false>(w, d, 0.0f);
     scales[b] = (uint8_t)sc;
   }
 }
