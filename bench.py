@@ -46,24 +46,57 @@ def dev_bf16(torch, bits):
 
 
 class Timer:
-    """Events on the current (launch) stream."""
+    """Elapsed-time events recorded on the launch stream.
 
-    def __init__(self, torch):
-        self.torch = torch
+    They are created with hipEventDisableSystemFence: a default event record
+    ends with a system-scope release (L2 writeback and invalidation), which on
+    this GPU left the next kernel idle for ~10 us, so events between the
+    calls of a step would lengthen the step they measure.  These events are
+    read only after a host synchronize, for timestamps."""
+    FLAGS = 0x20000000     # hipEventDisableSystemFence
+    _hip = None
+
+    def __init__(self, torch, stream):
+        import ctypes
+        if Timer._hip is None:
+            torch.cuda.init()
+            hip = ctypes.CDLL("libamdhip64.so.7")      # the runtime torch has loaded
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            Timer._hip = hip
+        self.ctypes = ctypes
+        self.stream = stream
         self.pairs = []
 
-    def start(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
+    def _check(self, err, what):
+        if err != 0:
+            raise RuntimeError(f"{what} failed with HIP error {err}")
+
+    def _event(self):
+        e = self.ctypes.c_void_p()
+        self._check(Timer._hip.hipEventCreateWithFlags(self.ctypes.byref(e), Timer.FLAGS), "hipEventCreateWithFlags")
+        self._check(Timer._hip.hipEventRecord(e, self.stream), "hipEventRecord")
         return e
 
+    def start(self):
+        return self._event()
+
     def stop(self, s):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.pairs.append((s, e))
+        self.pairs.append((s, self._event()))
 
     def ms(self):
-        return [s.elapsed_time(e) for s, e in self.pairs]
+        """Durations in ms (call after a synchronize); releases the events."""
+        out = []
+        for s, e in self.pairs:
+            v = self.ctypes.c_float()
+            self._check(Timer._hip.hipEventElapsedTime(self.ctypes.byref(v), s, e), "hipEventElapsedTime")
+            out.append(v.value)
+            Timer._hip.hipEventDestroy(s)
+            Timer._hip.hipEventDestroy(e)
+        self.pairs = []
+        return out
 
 
 def kernel_source_hash():
@@ -128,53 +161,57 @@ def run_prefill(torch, q, steps, warmup):
                                    out.shape[0], out.shape[1], a[0].shape[1] * 2, q.ALGO_TILED, P(gw), gw.numel(),
                                    stream))
 
-    gemm_timer = Timer(torch)
-    quant_timer = Timer(torch)
-
-    def step(timed):
-        t = quant_timer.start() if timed else None
+    def step():
         quant(x, a1)
-        if timed:
-            quant_timer.stop(t)
-            t = gemm_timer.start()
         gemm(a1, wu, h, gws[0])
-        if timed:
-            gemm_timer.stop(t)
-            t = quant_timer.start()
         quant(h, a2)
-        if timed:
-            quant_timer.stop(t)
-            t = gemm_timer.start()
         gemm(a2, wd, y, gws[1])
-        if timed:
-            gemm_timer.stop(t)
 
     for _ in range(warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
+    # The timed steps carry no events between their calls: on this GPU every
+    # event record between two kernels left the next one idle for ~9 us.
+    whole = Timer(torch, stream)
+    t = whole.start()
     for i in range(steps):
-        step(True)
+        step()
         if (i + 1) % max(1, steps // 4) == 0:
             log(f"prefill step {i + 1}/{steps} enqueued")
-    t1.record()
+    whole.stop(t)
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / steps
+    ms_step = whole.ms()[0] / steps
+
+    # Per-call durations: each call of the step repeated back to back on the
+    # step's own operands (same results, same cache footprint), events
+    # around each batch only.
+    reps = max(4, steps // 2)
+
+    def per_call(fn):
+        fn()
+        torch.cuda.synchronize()
+        tm = Timer(torch, stream)
+        t = tm.start()
+        for _ in range(reps):
+            fn()
+        tm.stop(t)
+        torch.cuda.synchronize()
+        return tm.ms()[0] / reps
+
+    gemm_ms = [per_call(lambda: gemm(a1, wu, h, gws[0])), per_call(lambda: gemm(a2, wd, y, gws[1]))]
+    quant_ms = [per_call(lambda: quant(x, a1)), per_call(lambda: quant(h, a2))]
     flops = 2.0 * M * N1 * K1 + 2.0 * M * N2 * K2
-    gemm_ms = gemm_timer.ms()
-    quant_ms = quant_timer.ms()
     gemm_avg = float(np.mean(gemm_ms))
     return {
         "ms_per_step": ms_step,
         "tflops": flops / (ms_step * 1e-3) / 1e12,
         "gemm_avg_ms": gemm_avg,
+        "gemm_launches_timed": 2 * reps,
         "gemm_flops_per_launch": 2.0 * M * N1 * K1,
         "gemm_tflops": (2.0 * M * N1 * K1) / (gemm_avg * 1e-3) / 1e12,
         "quant_avg_ms": float(np.mean(quant_ms)),
-        "gemm_ms_up_down": [float(np.mean(gemm_ms[0::2])), float(np.mean(gemm_ms[1::2]))],
-        "quant_ms_x_h": [float(np.mean(quant_ms[0::2])), float(np.mean(quant_ms[1::2]))],
+        "gemm_ms_up_down": gemm_ms,
+        "quant_ms_x_h": quant_ms,
     }
 
 
@@ -544,7 +581,8 @@ def main():
                    "format": "E2M1 codes, E4M3 scale per 16, fp32 per-tensor scale"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": load_traffic(), "kernel": "nvfp4_gemm_tiled_kernel",
+                     "traffic": load_traffic(),
+                     "kernel": "nvfp4_gemm_tiled_kernel (+ nvfp4_gemm_tiled_reduce_kernel: one GEMM call)",
                      "avg_launch_ms": round(pre["gemm_avg_ms"], 4)},
         "cpu_baseline": cpu,
         "prefill": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in pre.items()},
