@@ -151,18 +151,30 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
                                                           int use_given, const float* __restrict__ t_part,
                                                           int t_splits, float* __restrict__ t_out, int64_t t_n) {
   __shared__ float s_g;
-  if (threadIdx.x < 64) {
-    float g;
-    if (use_given) {
-      g = *gscale;
-    } else {
-      uint32_t m = 0;
-      for (int i = threadIdx.x; i < npartial; i += 64) m = max(m, partial[i]);
-      m = wave_max_u32(m);
-      g = bf16_bits_to_f32(m) / 2688.0f;               // amax / (6 * 448)
-      if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = g;
+  __shared__ uint32_t s_max[4];
+  if (use_given) {
+    if (threadIdx.x == 0) s_g = *gscale;
+  } else {
+    // All 256 threads load their partials four at a time before using any,
+    // so a workgroup waits for about one memory latency, not one per load.
+    // (buffer loads: indices past npartial read as zero, no branches)
+    const auto pr = buffer_of(partial, 4u * (uint32_t)npartial);
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < npartial; i += 1024) {
+      uint32_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = buffer_load4(pr, 4u * (uint32_t)(i + 256 * u));
+      m = max(m, max(max(v[0], v[1]), max(v[2], v[3])));
     }
-    if (threadIdx.x == 0) s_g = g;
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      m = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+      const float g = bf16_bits_to_f32(m) / 2688.0f;   // amax / (6 * 448)
+      if (blockIdx.x == 0) *gscale = g;
+      s_g = g;
+    }
   }
   __syncthreads();
   const float g = s_g;
