@@ -185,6 +185,36 @@ nvfp4_status nvfp4_gemm_ws(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_gemm_ws (AUTO kernel choice) that also leaves the global amax of
+ * its output ready for nvfp4_quantize_amax, so that quantizing the output
+ * (the next layer's activation, quantized on every forward: "NVFP4 en
+ * difusión", section 2) skips its own read of the output for max|out|.
+ * amax_slots: >= nvfp4_gemm_amax_slots(M, N, K) uint32 of device memory,
+ * 4-byte aligned, no initialization, not overlapping any argument.  Every
+ * slot is written with a bf16 magnitude pattern (sign cleared) and the
+ * largest of them is that of max|out[m, n]|: the tiled kernel (M > 16,
+ * K % 128 == 0) writes one slot per 256 x 256 output tile from its
+ * epilogue; other shapes run a separate pass over out.  N % 16 == 0 (the
+ * output is quantized along N); workspace as for nvfp4_gemm_ws.
+ */
+size_t nvfp4_gemm_amax_slots(int64_t M, int64_t N, int64_t K);
+nvfp4_status nvfp4_gemm_amax(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                             const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                             void* out_bf16, int64_t M, int64_t N, int64_t K, void* workspace,
+                             size_t workspace_bytes, uint32_t* amax_slots, void* stream);
+
+/*
+ * nvfp4_quantize (absmax rule) with max|x| taken from nslots bf16 magnitude
+ * patterns (1 <= nslots <= 2^28) instead of a pass over x: g = (largest
+ * pattern as bf16) / 2688, written to *global_scale, then the codes and
+ * scales of nvfp4_quantize.  With the slots nvfp4_gemm_amax wrote for x,
+ * the result is bit-identical to nvfp4_quantize(x).  No workspace.
+ */
+nvfp4_status nvfp4_quantize_amax(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes,
+                                 uint8_t* scales, float* global_scale, const uint32_t* amax_slots,
+                                 int64_t nslots, void* stream);
+
+/*
  * Weight-only NVFP4 GEMM: out[M, N] (bf16) = bf16_RNE( g_w * sum_k x[m, k] *
  * W[n, k] ) with x a bf16 activation that is not quantized and W the NVFP4
  * weight of nvfp4_gemm.  Passages: the weight format of "NVFP4 en

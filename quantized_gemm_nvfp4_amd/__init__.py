@@ -10,6 +10,8 @@ Function names follow the C ABI:
 * ``nvfp4_quantize(x, rule=...)``     -> (codes, scales, global_scale); rule absmax /
   four_over_six / mse
 * ``nvfp4_gemm(a, w, algo=AUTO)``     -> bf16 [M, N]; a, w are the 3-tuples above
+* ``nvfp4_gemm_amax(a, w)``           -> (bf16 [M, N], amax slots of the output)
+* ``nvfp4_quantize_amax(x, slots)``   -> nvfp4_quantize(x) with max|x| from the slots
 * ``nvfp4_gemm_w4a16(x, w)``          -> bf16 [M, N]; x bf16 (weight-only NVFP4)
 * ``int4g_quantize(w, group=128)``    -> (q, scales_fp16)
 * ``int4g_gemv(x, q, scales, ...)``   -> bf16 [M, N]
@@ -38,6 +40,9 @@ SIGNATURES = {
     "nvfp4_gemm_ex": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P], ctypes.c_int),
     "nvfp4_gemm_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),
     "nvfp4_gemm_ws": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "nvfp4_gemm_amax_slots": ([_I64, _I64, _I64], ctypes.c_size_t),
+    "nvfp4_gemm_amax": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
+    "nvfp4_quantize_amax": ([_P, _I64, _I64, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "nvfp4_gemm_w4a16": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "nvfp4_gemm_w4a16_ex": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P], ctypes.c_int),
     "int4g_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
@@ -183,6 +188,64 @@ def nvfp4_gemm(a, w, algo=ALGO_AUTO, out=None, workspace=None):
                                M, N, K, int(algo), _ptr(workspace) if workspace is not None else None,
                                workspace.numel() if workspace is not None else 0, _stream(ac)))
     return out
+
+
+def nvfp4_gemm_amax(a, w, out=None, workspace=None, slots=None):
+    """nvfp4_gemm that also returns the amax slots of its output (uint32
+    device tensor) for nvfp4_quantize_amax.  N % 16 == 0."""
+    torch = _torch()
+    ac, as_, ag = a
+    wc, ws, wg = w
+    M, N = ac.shape[0], wc.shape[0]
+    K = ac.shape[1] * 2
+    _need(ac, torch.uint8, (M, K // 2), "a_codes")
+    _need(as_, torch.uint8, (M, K // 16), "a_scales")
+    _need(ag, torch.float32, (1,), "a_gscale")
+    _need(wc, torch.uint8, (N, K // 2), "w_codes")
+    _need(ws, torch.uint8, (N, K // 16), "w_scales")
+    _need(wg, torch.float32, (1,), "w_gscale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=ac.device)
+    _need(out, torch.bfloat16, (M, N), "out")
+    nslots = lib().nvfp4_gemm_amax_slots(M, N, K)
+    if slots is None:
+        slots = torch.empty(max(1, nslots), dtype=torch.int32, device=ac.device)
+    _need(slots, torch.int32, None, "slots")
+    if slots.numel() < nslots:
+        raise ValueError(f"slots holds {slots.numel()} values, the call writes {nslots}")
+    if workspace is None:
+        nbytes = lib().nvfp4_gemm_workspace_bytes(M, N, K)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=ac.device)
+    if workspace is not None:
+        _need(workspace, torch.uint8, None, "workspace")
+    _check(lib().nvfp4_gemm_amax(_ptr(ac), _ptr(as_), _ptr(ag), _ptr(wc), _ptr(ws), _ptr(wg), _ptr(out), M, N, K,
+                                 _ptr(workspace) if workspace is not None else None,
+                                 workspace.numel() if workspace is not None else 0, _ptr(slots), _stream(ac)))
+    return out, slots[:nslots]
+
+
+def nvfp4_quantize_amax(x, slots, out=None):
+    """nvfp4_quantize(x) (absmax rule) with max|x| read from `slots` (as
+    nvfp4_gemm_amax returns them for x) instead of a pass over x."""
+    torch = _torch()
+    _need(x, torch.bfloat16, None, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    _need(slots, torch.int32, None, "slots")
+    rows, cols = x.shape
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+        g = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        codes, scales, g = out
+    _need(codes, torch.uint8, (rows, cols // 2), "codes")
+    _need(scales, torch.uint8, (rows, cols // 16), "scales")
+    _need(g, torch.float32, (1,), "global_scale")
+    _check(lib().nvfp4_quantize_amax(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(g), _ptr(slots),
+                                     slots.numel(), _stream(x)))
+    return codes, scales, g
 
 
 def nvfp4_gemm_w4a16(x, w, algo=ALGO_AUTO, out=None):

@@ -84,13 +84,41 @@ nvfp4_status check_dims(int64_t a, const char* an, int64_t b, const char* bn, in
   return NVFP4_OK;
 }
 
-// Shared by nvfp4_gemm_ex and nvfp4_gemm_lora_ex; lora_t == nullptr means
-// no low-rank branch (its arguments were validated by the caller).
+// Matrix sizes whose element counts stay below 2^40 (far past any device
+// memory), so byte counts and ranges never overflow int64.
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+nvfp4_status check_products(int64_t M, int64_t N, int64_t K) {
+  if ((N > 0 && M > kMaxElems / N) || (K > 0 && M > kMaxElems / K) || (K > 0 && N > kMaxElems / K))
+    return fail(NVFP4_ERR_UNSUPPORTED, "a matrix exceeds 2^40 elements (M=%lld, N=%lld, K=%lld)", (long long)M,
+                (long long)N, (long long)K);
+  return NVFP4_OK;
+}
+
+// Which kernel AUTO picks for the NVFP4 GEMM.
+int auto_algo(int64_t M, int64_t K) {
+  const bool k128 = (K % 128) == 0 && K > 0;
+  return !k128 ? NVFP4_ALGO_SIMPLE
+               : (M <= 16 ? (K <= kDecodeMaxK ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE) : NVFP4_ALGO_TILED);
+}
+
+// Slots nvfp4_gemm_amax writes for AUTO's kernel choice: one per output tile
+// of the tiled kernel, else the partial maxima of a separate pass over out.
+int64_t amax_slots(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0) return 0;
+  if (auto_algo(M, K) == NVFP4_ALGO_TILED) return nvfp4k::nvfp4_gemm_tiled_amax_slots(M, N);
+  return nvfp4k::amax_partial_count(M * N);
+}
+
+// Shared by nvfp4_gemm_ex, nvfp4_gemm_lora_ex and nvfp4_gemm_amax; lora_t ==
+// nullptr means no low-rank branch (its arguments were validated by the
+// caller); amax != nullptr (AUTO, no branch, N % 16 == 0) also writes the
+// output's amax slots.
 nvfp4_status gemm_impl(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale, void* out_bf16,
                        int64_t M, int64_t N, int64_t K, int algo, const float* lora_t, const void* lora_up,
-                       int64_t r, void* workspace, size_t workspace_bytes, void* stream) {
+                       int64_t r, void* workspace, size_t workspace_bytes, void* stream, uint32_t* amax = nullptr) {
   if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
+  if (nvfp4_status s = check_products(M, N, K)) return s;
   if (K > 0) {  // with K == 0 the packed operands are empty and never read
     REQUIRE_PTR(a_codes);
     REQUIRE_PTR(a_scales);
@@ -113,19 +141,24 @@ nvfp4_status gemm_impl(const uint8_t* a_codes, const uint8_t* a_scales, const fl
     REQUIRE_ALIGN(workspace, 256);
     if (workspace_bytes > (size_t)INT64_MAX) return fail(NVFP4_ERR_INVALID_ARG, "workspace_bytes is too large");
   }
-  const Range outs[2] = {{out_bf16, M * N * 2, "out"},
-                         {workspace, workspace ? (int64_t)workspace_bytes : 0, "workspace"}};
+  const Range outs[3] = {{out_bf16, M * N * 2, "out"},
+                         {workspace, workspace ? (int64_t)workspace_bytes : 0, "workspace"},
+                         {amax, amax ? 4 * amax_slots(M, N, K) : 0, "amax_slots"}};
   const Range ins[8] = {{a_codes, M * K / 2, "a_codes"}, {a_scales, M * K / 16, "a_scales"},
                         {a_gscale, 4, "a_gscale"},       {w_codes, N * K / 2, "w_codes"},
                         {w_scales, N * K / 16, "w_scales"}, {w_gscale, 4, "w_gscale"},
                         {lora_t, lora_t ? M * r * 4 : 0, "lora_t"}, {lora_up, lora_t ? N * r * 2 : 0, "lora_up"}};
   if (M == 0 || N == 0) return ok();
-  if (nvfp4_status s = check_disjoint(outs, 2, ins, 8)) return s;
+  if (nvfp4_status s = check_disjoint(outs, 3, ins, 8)) return s;
   const bool k128 = (K % 128) == 0 && K > 0;
-  if (algo == NVFP4_ALGO_AUTO)
-    algo = !k128 ? NVFP4_ALGO_SIMPLE
-                 : (M <= 16 ? (K <= kDecodeMaxK ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE) : NVFP4_ALGO_TILED);
+  if (algo == NVFP4_ALGO_AUTO) algo = auto_algo(M, K);
   hipStream_t st = (hipStream_t)stream;
+  if (amax && algo != NVFP4_ALGO_TILED) {    // the output's maxima from a separate pass
+    nvfp4_status s = gemm_impl(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_bf16, M, N, K, algo,
+                               nullptr, nullptr, 0, workspace, workspace_bytes, stream);
+    if (s != NVFP4_OK) return s;
+    return hip_status(nvfp4k::launch_amax_partials(out_bf16, M * N, amax, st), "nvfp4_gemm_amax amax pass");
+  }
   switch (algo) {
     case NVFP4_ALGO_TILED:
       if (!k128) return fail(NVFP4_ERR_UNSUPPORTED, "tiled kernel needs K %% 128 == 0 and K > 0 (K=%lld)", (long long)K);
@@ -135,7 +168,7 @@ nvfp4_status gemm_impl(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                           "nvfp4_gemm_lora tiled launch");
       return hip_status(nvfp4k::launch_nvfp4_gemm_tiled_ws(a_codes, a_scales, a_gscale, w_codes, w_scales,
                                                            w_gscale, out_bf16, M, N, K, workspace,
-                                                           (int64_t)workspace_bytes, st),
+                                                           (int64_t)workspace_bytes, st, amax),
                         "nvfp4_gemm tiled launch");
     case NVFP4_ALGO_DECODE:
       if (!k128 || M > 16 || K > kDecodeMaxK)
@@ -241,6 +274,52 @@ nvfp4_status nvfp4_gemm_ws(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            void* stream) {
   return gemm_impl(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_bf16, M, N, K, algo, nullptr,
                    nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+size_t nvfp4_gemm_amax_slots(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  if (check_products(M, N, K) != NVFP4_OK) return 0;
+  return (size_t)amax_slots(M, N, K);
+}
+
+nvfp4_status nvfp4_gemm_amax(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                             const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale, void* out_bf16,
+                             int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                             uint32_t* amax_slots, void* stream) {
+  REQUIRE_PTR(amax_slots);
+  REQUIRE_ALIGN(amax_slots, 4);
+  if (N % 16 != 0)
+    return fail(NVFP4_ERR_SHAPE, "N=%lld is not a multiple of 16 (the output is quantized along N)", (long long)N);
+  return gemm_impl(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_bf16, M, N, K, NVFP4_ALGO_AUTO,
+                   nullptr, nullptr, 0, workspace, workspace_bytes, stream, amax_slots);
+}
+
+nvfp4_status nvfp4_quantize_amax(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                 float* global_scale, const uint32_t* amax_slots, int64_t nslots, void* stream) {
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  REQUIRE_PTR(global_scale);
+  REQUIRE_PTR(amax_slots);
+  if (nvfp4_status s = check_dims(rows, "rows", cols, "cols", nslots, "nslots")) return s;
+  if (nslots < 1 || nslots > (int64_t(1) << 28))
+    return fail(NVFP4_ERR_INVALID_ARG, "nslots=%lld is outside [1, 2^28]", (long long)nslots);
+  if (cols % 16 != 0) return fail(NVFP4_ERR_SHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  if (rows > 0 && cols > kMaxElems / rows) return fail(NVFP4_ERR_UNSUPPORTED, "rows*cols exceeds 2^40");
+  REQUIRE_ALIGN(x_bf16, 16);
+  REQUIRE_ALIGN(codes, 16);
+  REQUIRE_ALIGN(scales, 16);
+  REQUIRE_ALIGN(global_scale, 4);
+  REQUIRE_ALIGN(amax_slots, 4);
+  const int64_t n = rows * cols;
+  const Range outs[3] = {{codes, n / 2, "codes"}, {scales, n / 16, "scales"}, {global_scale, 4, "global_scale"}};
+  const Range ins[2] = {{x_bf16, n * 2, "x"}, {amax_slots, 4 * nslots, "amax_slots"}};
+  if (n == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 3, ins, 2)) return s;
+  return hip_status(nvfp4k::launch_nvfp4_quantize_pass2(x_bf16, rows, cols, codes, scales, global_scale, 0,
+                                                        nvfp4k::kRuleAbsmax, (int)nslots,
+                                                        const_cast<uint32_t*>(amax_slots), (hipStream_t)stream),
+                    "nvfp4_quantize_amax launch");
 }
 
 nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,

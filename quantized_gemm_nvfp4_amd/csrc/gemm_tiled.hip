@@ -423,12 +423,14 @@ __device__ __forceinline__ void tiled_stage4(const TiledCtx<4>& c, int ls, float
 // bf16 stores of one 32 x 32 fragment times gmul: rows m, columns
 // nb + 8 rq + 4 h + (0..3) from registers 4 rq .. 4 rq + 3.  D[n][m] of a
 // fragment sits at lane m + 32((n/4)%2), register (n%4) + 4(n/8): four
-// consecutive n per register quad.
-__device__ __forceinline__ void store_frag(const float16v& a, float gmul, uint16_t* __restrict__ out, int M, int N,
-                                           int m, int nb, int h) {
-  if (m >= M) return;
+// consecutive n per register quad.  Returns the largest |bf16| bit pattern
+// (sign cleared) among the values stored (0 if none).
+__device__ __forceinline__ uint32_t store_frag(const float16v& a, float gmul, uint16_t* __restrict__ out, int M,
+                                               int N, int m, int nb, int h) {
+  if (m >= M) return 0u;
   uint16_t* orow = out + (int64_t)m * N;
   const bool vec_ok = (N & 3) == 0;
+  uint32_t mx = 0u;
 #pragma unroll
   for (int rq = 0; rq < 4; ++rq) {
     const int n = nb + 8 * rq + 4 * h;
@@ -436,25 +438,44 @@ __device__ __forceinline__ void store_frag(const float16v& a, float gmul, uint16
     const uint32_t b23 = f32x2_to_bf16x2_rne(a[4 * rq + 2] * gmul, a[4 * rq + 3] * gmul);
     if (vec_ok && n + 3 < N) {
       *(uint2*)(orow + n) = make_uint2(b01, b23);
+      mx = max(mx, max(bf16x2_absmax_bits(b01), bf16x2_absmax_bits(b23)));
     } else {
-      if (n + 0 < N) orow[n + 0] = (uint16_t)b01;
-      if (n + 1 < N) orow[n + 1] = (uint16_t)(b01 >> 16);
-      if (n + 2 < N) orow[n + 2] = (uint16_t)b23;
-      if (n + 3 < N) orow[n + 3] = (uint16_t)(b23 >> 16);
+      if (n + 0 < N) orow[n + 0] = (uint16_t)b01, mx = max(mx, b01 & 0x7FFFu);
+      if (n + 1 < N) orow[n + 1] = (uint16_t)(b01 >> 16), mx = max(mx, (b01 >> 16) & 0x7FFFu);
+      if (n + 2 < N) orow[n + 2] = (uint16_t)b23, mx = max(mx, b23 & 0x7FFFu);
+      if (n + 3 < N) orow[n + 3] = (uint16_t)(b23 >> 16), mx = max(mx, (b23 >> 16) & 0x7FFFu);
     }
   }
+  return mx;
 }
 
 // A wave's 4 kJ fragments: fragment (j, i) covers rows m0 + 128 wm + 32 i
-// and columns n0 + 32 kJ wn + 32 j.
+// and columns n0 + 32 kJ wn + 32 j.  Returns the lane's largest |bf16|
+// pattern stored.
 template <int kJ>
-__device__ __forceinline__ void store_tile(const float16v (&acc)[kJ][4], float gmul, uint16_t* __restrict__ out,
-                                           int M, int N, int m0, int n0, int wm, int wn, int h, int r32) {
+__device__ __forceinline__ uint32_t store_tile(const float16v (&acc)[kJ][4], float gmul, uint16_t* __restrict__ out,
+                                               int M, int N, int m0, int n0, int wm, int wn, int h, int r32) {
+  uint32_t mx = 0u;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < kJ; ++j)
-      store_frag(acc[j][i], gmul, out, M, N, m0 + 128 * wm + 32 * i + r32, n0 + 32 * kJ * wn + 32 * j, h);
+      mx = max(mx, store_frag(acc[j][i], gmul, out, M, N, m0 + 128 * wm + 32 * i + r32, n0 + 32 * kJ * wn + 32 * j, h));
+  return mx;
+}
+
+// Largest of v over the workgroup's kW waves, valid in thread 0 (red: kW
+// words of LDS; the caller's threads all take part).
+template <int kW>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+  v = wave_max_u32(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t m = 0u;
+  if (threadIdx.x == 0)
+#pragma unroll
+    for (int w = 0; w < kW; ++w) m = max(m, red[w]);
+  return m;
 }
 
 // Low-rank branch: D = L_up T^T on the same 32 x 32 fragments (L_up rows n
@@ -548,13 +569,17 @@ __device__ __forceinline__ void lora_epilogue(float16v (&acc)[TiledCtx<kW>::kJ][
 // stores its unscaled fp32 accumulators to part[(t S + p)] in lane order
 // (kW == 4 only).  kLora: add the low-rank branch T L_up^T (T fp32 [M, r],
 // L_up bf16 [N, r]) to each output before the bf16 rounding (launched
-// with kW == 8 and without splits).
-template <int kW, bool kLora>
+// with kW == 8 and without splits).  kAmax (kW == 4, no low-rank branch):
+// amax[tile] receives the largest |bf16| pattern of the tile's outputs;
+// for a split tile it is set to 0 here and raised by the reduce kernel.
+template <int kW, bool kLora, bool kAmax = false>
 __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
     uint16_t* __restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int full_tiles, int splits,
-    float* __restrict__ part, const float* __restrict__ lora_t, const uint16_t* __restrict__ lora_up, int r) {
+    float* __restrict__ part, const float* __restrict__ lora_t, const uint16_t* __restrict__ lora_up, int r,
+    uint32_t* __restrict__ amax) {
+  static_assert(!kAmax || (kW == 4 && !kLora), "amax slots: 4-wave kernel without the low-rank branch");
   using Ctx = TiledCtx<kW>;
   constexpr int kFr = Ctx::kFr, kJ = Ctx::kJ;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -647,6 +672,7 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
 
   const int h = c.h, r32 = c.r32, wm = c.wm, wn = c.wn;
   if (kW == 4 && unit >= 0) {
+    if (kAmax && tid == 0 && unit % splits == 0) amax[tile_id] = 0u;
     // K part of a split tile: fragment (j, i) of wave w at
     // part[unit][(w * 16 + j * 4 + i) * 64 + lane][16].
     float* dst = part + (int64_t)unit * kPartFloats + (int64_t)wave * 16 * 64 * 16 + lane * 16;
@@ -663,19 +689,25 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
   }
   const float gg = (*a_g) * (*w_g);
   if (kLora) lora_epilogue<kW>(acc, gg, lora_t, lora_up, r, M, N, m0, n0, wm, wn, h, r32);
-  store_tile<kJ>(acc, kLora ? 1.0f : gg, out, M, N, m0, n0, wm, wn, h, r32);
+  const uint32_t mx = store_tile<kJ>(acc, kLora ? 1.0f : gg, out, M, N, m0, n0, wm, wn, h, r32);
+  if (kAmax) {
+    __shared__ uint32_t red[kW];
+    const uint32_t m = block_max_u32<kW>(mx, red);
+    if (tid == 0) amax[tile_id] = m;
+  }
 }
 
 // Leftover tile t: workgroup (t, g) sums, for fragments 4g .. 4g + 3 of
 // the tile (one per wave; fragment f = 16 w + 4 j + i of the GEMM's wave w),
 // the `splits` K parts in order, scales by g_a g_w, rounds to bf16 and
-// stores.
+// stores.  With amax, it raises amax[full_tiles + t] (zeroed by the tile
+// kernel) to the largest |bf16| pattern it stored.
 __global__ __launch_bounds__(256) void nvfp4_gemm_tiled_reduce_kernel(const float* __restrict__ part,
                                                                       const float* __restrict__ a_g,
                                                                       const float* __restrict__ w_g,
                                                                       uint16_t* __restrict__ out, int M, int N,
                                                                       int tiles_m, int tiles_n, int full_tiles,
-                                                                      int splits) {
+                                                                      int splits, uint32_t* __restrict__ amax) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x >> 4;
   const int f = 4 * (blockIdx.x & 15) + (threadIdx.x >> 6);
@@ -686,8 +718,13 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_tiled_reduce_kernel(const floa
   float16v s = *(const float16v*)src;
   for (int p = 1; p < splits; ++p) s += *(const float16v*)(src + p * kPartFloats);
   const int wm = w >> 1, wn = w & 1;
-  store_frag(s, (*a_g) * (*w_g), out, M, N, tile_m * TM + 128 * wm + 32 * i + (lane & 31),
-             tile_n * TN + 128 * wn + 32 * j, lane >> 5);
+  const uint32_t mx = store_frag(s, (*a_g) * (*w_g), out, M, N, tile_m * TM + 128 * wm + 32 * i + (lane & 31),
+                                 tile_n * TN + 128 * wn + 32 * j, lane >> 5);
+  if (amax != nullptr) {
+    __shared__ uint32_t red[4];
+    const uint32_t m = block_max_u32<4>(mx, red);
+    if (threadIdx.x == 0) atomicMax(amax + full_tiles + t, m);
+  }
 }
 
 namespace {
@@ -745,22 +782,32 @@ int64_t nvfp4_gemm_tiled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return plan_tiled(M, N, K, true).part_bytes;
 }
 
+int64_t nvfp4_gemm_tiled_amax_slots(int64_t M, int64_t N) {
+  return ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+}
+
 hipError_t launch_nvfp4_gemm_tiled_ws(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
                                       const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
-                                      int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+                                      int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t stream,
+                                      uint32_t* amax) {
   TiledPlan p = plan_tiled(M, N, K, workspace != nullptr);
   if (p.part_bytes > workspace_bytes) p = plan_tiled(M, N, K, false);
   const int tiles = p.tiles_m * p.tiles_n;
   const int grid = p.full_tiles + (tiles - p.full_tiles) * p.splits;
-  hipLaunchKernelGGL((nvfp4_gemm_tiled_kernel<4, false>), dim3((unsigned)grid), dim3(256), 0, stream, ac, as, ag, wc, ws,
-                     wg, (uint16_t*)out, (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n, p.full_tiles, p.splits,
-                     (float*)workspace, nullptr, nullptr, 0);
+  if (amax != nullptr)
+    hipLaunchKernelGGL((nvfp4_gemm_tiled_kernel<4, false, true>), dim3((unsigned)grid), dim3(256), 0, stream, ac, as,
+                       ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n, p.full_tiles,
+                       p.splits, (float*)workspace, nullptr, nullptr, 0, amax);
+  else
+    hipLaunchKernelGGL((nvfp4_gemm_tiled_kernel<4, false>), dim3((unsigned)grid), dim3(256), 0, stream, ac, as, ag, wc,
+                       ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n, p.full_tiles, p.splits,
+                       (float*)workspace, nullptr, nullptr, 0, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.full_tiles == tiles) return e;
   hipLaunchKernelGGL(nvfp4_gemm_tiled_reduce_kernel, dim3((unsigned)(16 * (tiles - p.full_tiles))), dim3(256), 0,
                      stream,
                      (const float*)workspace, ag, wg, (uint16_t*)out, (int)M, (int)N, p.tiles_m, p.tiles_n,
-                     p.full_tiles, p.splits);
+                     p.full_tiles, p.splits, amax);
   return hipGetLastError();
 }
 
@@ -777,7 +824,7 @@ hipError_t launch_nvfp4_gemm_tiled_lora(const uint8_t* ac, const uint8_t* as, co
   const TiledPlan p = plan_tiled(M, N, K, false);
   hipLaunchKernelGGL((nvfp4_gemm_tiled_kernel<8, true>), dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(512), 0, stream,
                      ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n,
-                     p.tiles_m * p.tiles_n, 1, nullptr, lora_t, (const uint16_t*)lora_up, (int)r);
+                     p.tiles_m * p.tiles_n, 1, nullptr, lora_t, (const uint16_t*)lora_up, (int)r, nullptr);
   return hipGetLastError();
 }
 

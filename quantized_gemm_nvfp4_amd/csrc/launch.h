@@ -17,6 +17,10 @@ enum ScaleRule { kRuleAbsmax = 0, kRuleFourOverSix = 1, kRuleMse = 2 };
 
 hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                                  float* gscale, int use_given, int rule, uint32_t* workspace, hipStream_t stream);
+// The first pass alone: partial maxima of |x| (bf16 patterns, sign cleared)
+// over n bf16 values (n % 8 == 0), written to partial[0 .. amax_partial_count(n)).
+int amax_partial_count(int64_t n);
+hipError_t launch_amax_partials(const void* x, int64_t n, uint32_t* partial, hipStream_t stream);
 // The second pass alone (codes and scales), reducing `npartial` partial
 // maxima from workspace unless use_given.  With t_splits > 1 it also sums
 // t_splits partial products t_part[s][t_n] into t_out[t_n], in order of s.
@@ -60,10 +64,14 @@ hipError_t launch_int4g_quantize(const void* w, int64_t N, int64_t K, uint8_t* q
 // Tiled GEMM with the leftover tiles of a partial last round split along K
 // (fp32 parts in `workspace`, summed by a second kernel); without a large
 // enough workspace every tile runs whole.
+// With amax, amax[0 .. nvfp4_gemm_tiled_amax_slots(M, N)) receives each
+// tile's largest |bf16| output pattern (for the global amax of out).
 int64_t nvfp4_gemm_tiled_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int64_t nvfp4_gemm_tiled_amax_slots(int64_t M, int64_t N);
 hipError_t launch_nvfp4_gemm_tiled_ws(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
                                       const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
-                                      int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t stream);
+                                      int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t stream,
+                                      uint32_t* amax = nullptr);
 hipError_t launch_nvfp4_gemm_tiled(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,
                                    const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N, int64_t K,
                                    hipStream_t stream);

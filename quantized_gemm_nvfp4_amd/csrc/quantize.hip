@@ -286,18 +286,24 @@ hipError_t launch_nvfp4_quantize_pass2(const void* x, int64_t rows, int64_t cols
   return hipGetLastError();
 }
 
+int amax_partial_count(int64_t n) {
+  const int64_t grid = (n / 8 + 255) / 256;
+  return (int)(grid < 1 ? 1 : (grid > kAmaxPartials ? kAmaxPartials : grid));
+}
+
+hipError_t launch_amax_partials(const void* x, int64_t n, uint32_t* partial, hipStream_t stream) {
+  hipLaunchKernelGGL(amax_partial_kernel, dim3((unsigned)amax_partial_count(n)), dim3(256), 0, stream,
+                     (const uint4*)x, n / 8, partial);
+  return hipGetLastError();
+}
+
 hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                                  float* gscale, int use_given, int rule, uint32_t* workspace, hipStream_t stream) {
   const int64_t n = rows * cols;
   int npartial = 0;
   if (!use_given) {
-    const int64_t n_vec = n / 8;
-    int64_t grid = (n_vec + 255) / 256;
-    if (grid > kAmaxPartials) grid = kAmaxPartials;
-    npartial = (int)grid;
-    hipLaunchKernelGGL(amax_partial_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       (const uint4*)x, n_vec, workspace);
-    hipError_t e = hipGetLastError();
+    npartial = amax_partial_count(n);
+    hipError_t e = launch_amax_partials(x, n, workspace, stream);
     if (e != hipSuccess) return e;
   }
   return launch_nvfp4_quantize_pass2(x, rows, cols, codes, scales, gscale, use_given, rule, npartial, workspace,

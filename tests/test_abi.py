@@ -106,6 +106,30 @@ def test_gemm_validation():
     assert q.lib().nvfp4_gemm_workspace_bytes(4096, 4096, 120) == 0              # K % 128
 
 
+def test_amax_validation():
+    lib = q.lib()
+    assert lib.nvfp4_gemm_amax_slots(4096, 21504, 5376) == 16 * 84      # one per 256 x 256 tile
+    assert lib.nvfp4_gemm_amax_slots(4096, 21504, 5376 + 16) == 1024    # simple kernel: a separate pass
+    assert lib.nvfp4_gemm_amax_slots(8, 160, 256) == 1                  # decode: 1280 values, one partial
+    assert lib.nvfp4_gemm_amax_slots(0, 160, 256) == 0
+    good = [A, B, C, D, E, F, G]
+    W = P(0x100000)
+    S = P(0x200000)
+    f = lib.nvfp4_gemm_amax
+    assert f(*good, 32, 64, 128, W, 4096, None, None) == INVALID                 # no slots
+    assert f(*good, 32, 72, 128, W, 4096, S, None) == SHAPE                      # N % 16
+    assert f(*good, 32, 64, 128, W, 4096, P(0x200002), None) == ALIGN
+    assert f(*good, 32, 64, 128, W, 4096, P(0x70000), None) == INVALID           # slots overlap out
+    assert f(*good, 0, 64, 128, W, 4096, S, None) == OK
+    g = lib.nvfp4_quantize_amax
+    assert g(A, 4, 64, B, C, D, E, 0, None) == INVALID                           # nslots >= 1
+    assert g(A, 4, 60, B, C, D, E, 4, None) == SHAPE
+    assert g(A, 4, 64, B, C, D, None, 4, None) == INVALID
+    assert g(A, 4, 64, B, C, D, P(0x50002), 4, None) == ALIGN
+    assert g(A, 4, 64, A, C, D, E, 4, None) == INVALID                           # codes alias x
+    assert g(A, 0, 64, B, C, D, E, 4, None) == OK
+
+
 def test_decode_k_limit():
     # the weight-streaming kernels take K <= 2^24; beyond it an explicit
     # decode request is refused (before any device work)
