@@ -127,6 +127,74 @@ def load_traffic():
     return t.get("bytes_per_launch")
 
 
+def summarize_traffic(fetch_csv, write_csv):
+    """Write TRAFFIC_FILE from the counter CSVs of two rocprofv3 --pmc runs
+    of `bench.py --steps 5 --warmup 2 --no-extras --no-cpu-baseline
+    --copy-calibration` (FETCH_SIZE, then WRITE_SIZE).  Counter units are
+    converted to bytes with what the same counter reads for the 1 GiB device
+    copies of the run; medians over the launches of each GEMM (up: the
+    instance with the amax epilogue, down: the plain one; a reduce kernel
+    belongs to the GEMM dispatched before it)."""
+    import csv
+
+    def load(path, counter):
+        rows = sorted((r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter),
+                      key=lambda r: int(r["Dispatch_Id"]))
+        vals = {"up": [], "down": [], "reduce_up": [], "reduce_down": [], "copy": []}
+        last = None
+        for r in rows:
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if "nvfp4_gemm_tiled_kernel<4, false, true>" in name:
+                last = "up"
+                vals["up"].append(v)
+            elif "nvfp4_gemm_tiled_kernel<4, false, false>" in name:
+                last = "down"
+                vals["down"].append(v)
+            elif "nvfp4_gemm_tiled_reduce_kernel" in name and last:
+                vals["reduce_" + last].append(v)
+            elif "copyBuffer" in name:
+                vals["copy"].append(v)
+        return {k: float(np.median(v)) if v else 0.0 for k, v in vals.items()}
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy_bytes = 1 << 30
+    fu, wu = copy_bytes / fetch["copy"], copy_bytes / write["copy"]
+    M = 4096
+    shapes = {"up": (21504, 5376), "down": (5376, 21504)}
+    per = {}
+    for k, (N, K) in shapes.items():
+        alg = M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + M * N * 2 + 8
+        per[k] = {"gemm_fetch_bytes": round(fetch[k] * fu), "gemm_write_bytes": round(write[k] * wu),
+                  "reduce_fetch_bytes": round(fetch["reduce_" + k] * fu),
+                  "reduce_write_bytes": round(write["reduce_" + k] * wu), "algorithmic_bytes": alg,
+                  "gemm_traffic_over_algorithmic": round((fetch[k] * fu + write[k] * wu) / alg, 2)}
+    cmd = "rocprofv3 --pmc {c} --output-format csv -d <dir> -o {o} -- python3 -u bench.py --steps 5 --warmup 2 " \
+          "--no-extras --no-cpu-baseline --copy-calibration"
+    out = {
+        "kernel": "nvfp4_gemm_tiled_kernel<4, false, true> (up, with the amax epilogue) and <4, false, false> (down)",
+        "workload": "prefill up (M=4096, N=21504, K=5376) and down (M=4096, N=5376, K=21504) GEMMs, with the "
+                    "last-round K split, as bench.py times them",
+        "kernel_source_hash": kernel_source_hash(),
+        "bytes_per_launch": round(np.mean([per[k]["gemm_fetch_bytes"] + per[k]["gemm_write_bytes"] for k in per])),
+        "per_shape": per,
+        "calibration": {"copy_bytes": copy_bytes, "FETCH_SIZE_per_copy": fetch["copy"],
+                        "WRITE_SIZE_per_copy": write["copy"], "bytes_per_FETCH_unit": fu, "bytes_per_WRITE_unit": wu},
+        "commands": [cmd.format(c="FETCH_SIZE", o="fetch"), cmd.format(c="WRITE_SIZE", o="write"),
+                     "python3 bench.py --traffic-from <dir>/fetch_counter_collection.csv "
+                     "<dir>/write_counter_collection.csv"],
+        "note": "Counter values scaled by what the same counters read for a 1 GiB device copy (torch copy_, the "
+                "__amd_rocclr_copyBuffer dispatches in the same run); medians over the launches of each shape. "
+                "bytes_per_launch is the mean of the up and down GEMM kernels (fetch + write), matching "
+                "roofline.achieved, which averages the two launches.",
+        "hash_note": "sha256 (first 16 hex digits) of gemm_tiled.hip + common.h with comments and whitespace "
+                     "removed, as bench.py computes it",
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=2)
+        f.write("\n")
+    return out
+
+
 def run_prefill(torch, q, steps, warmup):
     import workloads
     x_bits, wu_bits, wd_bits = workloads.prefill()
@@ -325,7 +393,8 @@ def run_weight_quant(torch, q, reps=5):
 
 
 def run_dit(torch, q, reps=3):
-    """4 denoising steps x (qkv, up, down) with fresh activations; TFLOP/s incl. act quant."""
+    """4 denoising steps x (qkv, up, down) with fresh activations; TFLOP/s incl. act quant
+    (the up projection's output is quantized from the amax its GEMM leaves)."""
     import workloads
     wq, wu, wd = [q.nvfp4_quantize(dev_bf16(torch, b)) for b in workloads.dit_weights()]
     xs = [dev_bf16(torch, workloads.dit_x(t)) for t in range(4)]
@@ -335,8 +404,8 @@ def run_dit(torch, q, reps=3):
         for t in range(4):
             a = q.nvfp4_quantize(xs[t])
             q.nvfp4_gemm(a, wq)
-            hh = q.nvfp4_gemm(a, wu)
-            q.nvfp4_gemm(q.nvfp4_quantize(hh), wd)
+            hh, slots = q.nvfp4_gemm_amax(a, wu)
+            q.nvfp4_gemm(q.nvfp4_quantize_amax(hh, slots), wd)
 
     run()
     torch.cuda.synchronize()
@@ -536,7 +605,13 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--only", choices=["decode", "dit", "int4", "weight_quant", "lora"],
                     help="time only this extra workload")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the GEMM traffic summary from two rocprofv3 --pmc runs and exit (no GPU)")
     args = ap.parse_args()
+    if args.traffic_from:
+        out = summarize_traffic(*args.traffic_from)
+        print(json.dumps({"traffic_bytes_per_launch": out["bytes_per_launch"], "file": TRAFFIC_FILE}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a "
               f"single GPU; see the sharding notes in the design document)", file=sys.stderr)
