@@ -258,17 +258,124 @@ __global__ __launch_bounds__(1024) void int4g_gemv_rowslot_kernel(const uint16_t
 // ---- any M: LDS-staged MFMA tiles -----------------------------------------
 // Workgroup tile 128 (m) x 256 (n), K stage = one 128-value group; 4 waves of
 // 64 x 128 (2 x 4 tiles of 32 x 32).  x fragments are stored in LDS in lane
-// order (one 1 KB region per MFMA step), the packed weight as in the NVFP4
-// kernel; both are copied with global_load_lds (16-byte transfers, which
-// land at lane * 16 in LDS).  Per group: tmp tiles start
-// from zero, collect 8 steps, and are added to the accumulators times the
-// lane's column scale.
+// order (one 1 KB region per MFMA step), the packed weight likewise; both
+// are copied with global_load_lds (16-byte transfers, which land at
+// lane * 16 in LDS) into a ring of three stage slots, two stages ahead of
+// the MFMAs.  Each stage waits only for its own copies (vmcnt counts the
+// next stage's as still in flight) and one barrier, which also frees the
+// slot the stage after next is copied into.  The slots are distinct LDS
+// objects and the stage loop is unrolled by three, so the compiler sees that
+// copies in flight never alias the slot being read.  Per group: tmp tiles
+// start from zero, collect 8 steps, and are added to the accumulators times
+// the lane's column scale (read from global memory with the stage's copies).
 namespace {
 constexpr int IT_M = 128, IT_N = 256, IT_K = 128;
 constexpr int kXBytes = IT_M * IT_K * 2;        // 32 KB
 constexpr int kQBytes = IT_N * IT_K / 2;        // 16 KB
 constexpr int kIStage = kXBytes + kQBytes;
-constexpr int kISmem = 2 * kIStage;
+constexpr int kIRing = 3;
+constexpr int kILoads = 16;                     // vector memory instructions per wave per stage
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+#define INT4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
+
+// A workgroup barrier without the memory fence of __syncthreads() (which
+// would drain the copies in flight).
+__device__ __forceinline__ void i4_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+}  // namespace
+
+__shared__ __attribute__((aligned(1024))) uint8_t g_i4s0[kIStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_i4s1[kIStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_i4s2[kIStage];
+
+namespace {
+template <int B> __device__ __forceinline__ uint8_t* i4_slot() { return B == 0 ? g_i4s0 : (B == 1 ? g_i4s1 : g_i4s2); }
+
+struct I4Ctx {
+  const uint16_t* gx[8];   // x copy sources of this lane
+  int lds_x[8];
+  const uint8_t* gq[4];    // weight copy sources
+  int lds_q[4];
+  const uint16_t* gsc[4];  // group-scale rows of this lane's 4 output columns
+  uint32_t scr[kIRing][4]; // group scales per ring slot (raw fp16)
+  int wm, wn, lane;
+};
+
+// Copies of stage (group) g into slot B, and its group scales: kILoads
+// vector memory instructions per wave.
+template <int B>
+__device__ __forceinline__ void i4_issue(I4Ctx& c, int g) {
+  uint8_t* base = i4_slot<B>();
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_global_load_lds((gbl_void_t)(c.gx[i] + (int64_t)g * 128), (lds_void_t)(base + c.lds_x[i]), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds((gbl_void_t)(c.gq[i] + (int64_t)g * 64), (lds_void_t)(base + c.lds_q[i]), 16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c.scr[B][j] = c.gsc[j][g];
+}
+
+template <int B>
+__device__ __forceinline__ void i4_compute(I4Ctx& c, float16v (&acc)[2][4]) {
+  const uint8_t* base = i4_slot<B>();
+  const int lane = c.lane, wm = c.wm, wn = c.wn;
+  const short8v c8 = {kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16,
+                      kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16};
+  float sc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sc[j] = f16_bits_to_f32(c.scr[B][j]);
+  uint4 cq[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+      cq[j][hs] = *(const uint4*)(base + kXBytes + ((4 * wn + j) * 2 + hs) * 1024 + lane * 16);
+  float16v tmp[2][4], corr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    corr[i] = float16v{};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tmp[i][j] = float16v{};
+  }
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    short8v xa[2], wb[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) xa[i] = as_short8(*(const uint4*)(base + ((2 * wm + i) * 8 + jj) * 1024 + lane * 16));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wb[j] = int4x8_offset_bf16(word_of(cq[j][jj >> 2], jj & 3));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], c8, corr[i], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        tmp[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], wb[j], tmp[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] += sc[j] * (tmp[i][j] + corr[i]);
+}
+
+// Stage g in slot B.  kChecked: near the end, where stage g + 1 or g + 2
+// may not exist (all conditions are uniform).
+template <int B, bool kChecked>
+__device__ __forceinline__ void i4_stage(I4Ctx& c, int g, int ng, float16v (&acc)[2][4]) {
+  if (!kChecked || g + 1 < ng) {
+    INT4_WAIT_VMCNT(kILoads);     // stage g + 1's loads may stay in flight
+  } else {
+    INT4_WAIT_VMCNT(0);
+  }
+  i4_barrier();                   // stage g landed for every wave; slot (B + 2) % 3 is free
+  if (!kChecked || g + 2 < ng) i4_issue<(B + 2) % kIRing>(c, g + 2);
+  i4_compute<B>(c, acc);
+}
 }  // namespace
 
 __global__ __launch_bounds__(256, 1) void int4g_gemm_tiled_kernel(const uint16_t* __restrict__ x,
@@ -276,8 +383,7 @@ __global__ __launch_bounds__(256, 1) void int4g_gemm_tiled_kernel(const uint16_t
                                                                   const uint16_t* __restrict__ s,
                                                                   uint16_t* __restrict__ out, int M, int N, int K,
                                                                   int tiles_m, int tiles_n) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // XCD-aware order: each XCD gets a contiguous run of tiles, n fastest.
   const int total = tiles_m * tiles_n;
   int id = blockIdx.x;
@@ -286,106 +392,59 @@ __global__ __launch_bounds__(256, 1) void int4g_gemm_tiled_kernel(const uint16_t
   const int m0 = tile_m * IT_M, n0 = tile_n * IT_N;
   const int ng = K / 128;
 
+  I4Ctx c;
+  c.lane = lane;
+  c.wm = wave >> 1;
+  c.wn = wave & 1;
   // x: 4 fragments x 8 steps; wave w copies steps 2w, 2w+1 of every fragment.
   // Lane l of region (f, jj): row 32f + l%32, values 64(l/32) + 8jj .. +8.
-  const uint16_t* gx[8];
-  int lds_x[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int f = i >> 1, jj = 2 * wave + (i & 1);
     const int row = min(m0 + 32 * f + (lane & 31), M - 1);
-    gx[i] = x + (int64_t)row * K + 64 * (lane >> 5) + 8 * jj;
-    lds_x[i] = (f * 8 + jj) * 1024;
+    c.gx[i] = x + (int64_t)row * K + 64 * (lane >> 5) + 8 * jj;
+    c.lds_x[i] = (f * 8 + jj) * 1024;
   }
-  const uint8_t* gq[4];
-  int lds_q[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int qd = 4 * wave + i, f = qd >> 1, hs = qd & 1;
     const int row = min(n0 + 32 * f + (lane & 31), N - 1);
-    gq[i] = q + (int64_t)row * (K / 2) + 32 * (lane >> 5) + 16 * hs;
-    lds_q[i] = kXBytes + qd * 1024;
+    c.gq[i] = q + (int64_t)row * (K / 2) + 32 * (lane >> 5) + 16 * hs;
+    c.lds_q[i] = kXBytes + qd * 1024;
   }
-  // Group scales of this lane's 4 output columns, read straight from global
-  // memory one group ahead (they are 1/64 of the weight bytes).
-  const uint16_t* gsc[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) gsc[j] = s + (int64_t)min(n0 + 128 * (wave & 1) + 32 * j + (lane & 31), N - 1) * ng;
+  for (int j = 0; j < 4; ++j) c.gsc[j] = s + (int64_t)min(n0 + 128 * (wave & 1) + 32 * j + (lane & 31), N - 1) * ng;
 
-  auto issue = [&](int g, int buf) {
-    uint8_t* base = smem + buf * kIStage;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds((gbl_void_t)(gx[i] + (int64_t)g * 128), (lds_void_t)(base + lds_x[i]), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((gbl_void_t)(gq[i] + (int64_t)g * 64), (lds_void_t)(base + lds_q[i]), 16, 0, 0);
-  };
-
-  const int wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5, r32 = lane & 31;
-  const short8v c8 = {kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16,
-                      kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16};
   float16v acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float16v{};
 
-  uint32_t sc_next[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) sc_next[j] = gsc[j][0];
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int g = 0; g < ng; ++g) {
-    const int buf = g & 1;
-    float sc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sc[j] = f16_bits_to_f32(sc_next[j]);
-    if (g + 1 < ng) {
-      issue(g + 1, buf ^ 1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sc_next[j] = gsc[j][g + 1];
-    }
-    const uint8_t* base = smem + buf * kIStage;
-    uint4 cq[4][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
-        cq[j][hs] = *(const uint4*)(base + kXBytes + ((4 * wn + j) * 2 + hs) * 1024 + lane * 16);
-    float16v tmp[2][4], corr[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      corr[i] = float16v{};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) tmp[i][j] = float16v{};
-    }
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      short8v xa[2], wb[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) xa[i] = as_short8(*(const uint4*)(base + ((2 * wm + i) * 8 + jj) * 1024 + lane * 16));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wb[j] = int4x8_offset_bf16(word_of(cq[j][jj >> 2], jj & 3));
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], c8, corr[i], 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          tmp[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], wb[j], tmp[i][j], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] += sc[j] * (tmp[i][j] + corr[i]);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  // Prologue: stages 0 and 1 in flight.  With a single group slot 1 gets
+  // group 0 again (never read): no branch here, so the compiler's count of
+  // copies in flight is the same on every path into the stage loop (a
+  // branch made it wait for all copies before each group's first stage).
+  i4_issue<0>(c, 0);
+  i4_issue<1>(c, ng > 1 ? 1 : 0);
+  int g = 0;
+  // Whole groups of three stages while every wait and copy of the group is
+  // in range (the last stage issued is g + 4).
+  for (; g + 5 <= ng; g += 3) {
+    i4_stage<0, false>(c, g, ng, acc);
+    i4_stage<1, false>(c, g + 1, ng, acc);
+    i4_stage<2, false>(c, g + 2, ng, acc);
   }
+  // The last (up to 5) stages; g % 3 == 0 here.
+  for (; g < ng; g += 3) {
+    i4_stage<0, true>(c, g, ng, acc);
+    if (g + 1 < ng) i4_stage<1, true>(c, g + 1, ng, acc);
+    if (g + 2 < ng) i4_stage<2, true>(c, g + 2, ng, acc);
+  }
+  INT4_WAIT_VMCNT(0);      // no copy may land in LDS after the workgroup ends
 
   // D[m][n] of each 32 x 32 tile: lane n + 32((m/4)%2), register (m%4) + 4(m/8).
+  const int wm = c.wm, wn = c.wn, h = lane >> 5, r32 = lane & 31;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + 128 * wn + 32 * j + r32;
@@ -432,15 +491,8 @@ hipError_t launch_int4g_gemm_decode(const void* x, const uint8_t* q, const void*
 
 hipError_t launch_int4g_gemm_tiled(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,
                                    int64_t N, int64_t K, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)int4g_gemm_tiled_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kISmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const int tiles_m = (int)((M + IT_M - 1) / IT_M), tiles_n = (int)((N + IT_N - 1) / IT_N);
-  hipLaunchKernelGGL(int4g_gemm_tiled_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), kISmem, stream,
+  hipLaunchKernelGGL(int4g_gemm_tiled_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream,
                      (const uint16_t*)x, q, (const uint16_t*)s, (uint16_t*)out, (int)M, (int)N, (int)K, tiles_m,
                      tiles_n);
   return hipGetLastError();
