@@ -21,6 +21,10 @@
 
 namespace nvfp4k {
 
+namespace {
+constexpr int64_t kSmallQuantBlocks = 2048;   // one workgroup quantizes up to 32K values
+}  // namespace
+
 // ---- pass 1: partial maxima of |x| over a bf16 tensor ---------------------
 // x is read as 16-byte vectors (8 bf16); n_vec = elements / 8.
 __global__ __launch_bounds__(256) void amax_partial_kernel(const uint4* __restrict__ x, int64_t n_vec,
@@ -171,6 +175,44 @@ __device__ __forceinline__ uint32_t scale_code(float amax_b, float top, float g)
 }
 }  // namespace
 
+// One 16-value block b of x: its scale under rule kRule (given g) and its
+// codes, stored at codes[b] and scales[b].
+template <int kRule>
+__device__ __forceinline__ void quantize_block(const uint4* __restrict__ x, int64_t b, float g,
+                                               uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, bf16x2_absmax_bits(w[i]));
+  const float amax_b = bf16_bits_to_f32(amax_bits);
+  uint32_t sc = scale_code(amax_b, 6.0f, g);
+  if (kRule != kRuleAbsmax) {
+    float best = block_error(w, sc, g);
+    if (kRule == kRuleFourOverSix) {
+      const uint32_t c4 = scale_code(amax_b, 4.0f, g);
+      if (block_error(w, c4, g) < best) sc = c4;
+    } else {
+      const int c6 = (int)sc;
+      for (int step = 1; step <= 8; ++step) {
+#pragma unroll
+        for (int sgn = 0; sgn < 2; ++sgn) {
+          const int c = sgn ? c6 + step : c6 - step;
+          if (c < 1 || c > 0x7E) continue;
+          const float e = block_error(w, (uint32_t)c, g);
+          if (e < best) {
+            best = e;
+            sc = (uint32_t)c;
+          }
+        }
+      }
+    }
+  }
+  const float d = e4m3_to_f32(sc) * g;
+  codes[b] = quot_fast(d) ? encode_block<true>(w, d, 1.0f / d) : encode_block<false>(w, d, 0.0f);
+  scales[b] = (uint8_t)sc;
+}
+
 // x: bf16 [nblocks * 16]; codes: 8 bytes per block; scales: 1 byte per block.
 template <int kRule>
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restrict__ x, int64_t nblocks,
@@ -216,39 +258,45 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
     for (int sp = 1; sp < t_splits; ++sp) v += t_part[(int64_t)sp * t_n + e];
     t_out[e] = v;
   }
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
-    const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t amax_bits = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, bf16x2_absmax_bits(w[i]));
-    const float amax_b = bf16_bits_to_f32(amax_bits);
-    uint32_t sc = scale_code(amax_b, 6.0f, g);
-    if (kRule != kRuleAbsmax) {
-      float best = block_error(w, sc, g);
-      if (kRule == kRuleFourOverSix) {
-        const uint32_t c4 = scale_code(amax_b, 4.0f, g);
-        if (block_error(w, c4, g) < best) sc = c4;
-      } else {
-        const int c6 = (int)sc;
-        for (int step = 1; step <= 8; ++step) {
-#pragma unroll
-          for (int sgn = 0; sgn < 2; ++sgn) {
-            const int c = sgn ? c6 + step : c6 - step;
-            if (c < 1 || c > 0x7E) continue;
-            const float e = block_error(w, (uint32_t)c, g);
-            if (e < best) {
-              best = e;
-              sc = (uint32_t)c;
-            }
-          }
-        }
-      }
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride)
+    quantize_block<kRule>(x, b, g, codes, scales);
+}
+
+// Small tensors (decode activations, at most kSmallQuantBlocks blocks): one
+// workgroup takes both passes, so a call is a single launch.  The maximum is
+// the same integer max of |bf16| patterns and the blocks go through the same
+// quantize_block, so g, scales and codes equal the two-pass kernels'.
+template <int kRule>
+__global__ __launch_bounds__(1024) void nvfp4_quant_small_kernel(const uint4* __restrict__ x, int64_t nblocks,
+                                                                uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                                float* __restrict__ gscale, int use_given) {
+  __shared__ float s_g;
+  __shared__ uint32_t s_max[16];
+  if (use_given) {
+    if (threadIdx.x == 0) s_g = *gscale;
+  } else {
+    uint32_t m = 0;
+    const int n_vec = (int)(2 * nblocks);
+#pragma unroll 4
+    for (int i = threadIdx.x; i < n_vec; i += 1024) {
+      const uint4 v = x[i];
+      m = max(m, max(max(bf16x2_absmax_bits(v.x), bf16x2_absmax_bits(v.y)),
+                     max(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w))));
     }
-    const float d = e4m3_to_f32(sc) * g;
-    codes[b] = quot_fast(d) ? encode_block<true>(w, d, 1.0f / d) : encode_block<false>(w, d, 0.0f);
-    scales[b] = (uint8_t)sc;
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int w = 1; w < 16; ++w) m = max(m, s_max[w]);
+      const float g = bf16_bits_to_f32(m) / 2688.0f;   // amax / (6 * 448)
+      *gscale = g;
+      s_g = g;
+    }
   }
+  __syncthreads();
+  const float g = s_g;
+  for (int64_t b = threadIdx.x; b < nblocks; b += 1024) quantize_block<kRule>(x, b, g, codes, scales);
 }
 
 // ---- INT4 per-group (128) quantization ------------------------------------
@@ -329,6 +377,20 @@ hipError_t launch_amax_partials(const void* x, int64_t n, uint32_t* partial, hip
 hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                                  float* gscale, int use_given, int rule, uint32_t* workspace, hipStream_t stream) {
   const int64_t n = rows * cols;
+  const int64_t nblocks = n / kBlock;
+  if (nblocks <= kSmallQuantBlocks) {
+    const dim3 grid(1), block(1024);
+    if (rule == kRuleFourOverSix)
+      hipLaunchKernelGGL(nvfp4_quant_small_kernel<kRuleFourOverSix>, grid, block, 0, stream, (const uint4*)x, nblocks,
+                         (uint2*)codes, scales, gscale, use_given);
+    else if (rule == kRuleMse)
+      hipLaunchKernelGGL(nvfp4_quant_small_kernel<kRuleMse>, grid, block, 0, stream, (const uint4*)x, nblocks,
+                         (uint2*)codes, scales, gscale, use_given);
+    else
+      hipLaunchKernelGGL(nvfp4_quant_small_kernel<kRuleAbsmax>, grid, block, 0, stream, (const uint4*)x, nblocks,
+                         (uint2*)codes, scales, gscale, use_given);
+    return hipGetLastError();
+  }
   int npartial = 0;
   if (!use_given) {
     npartial = amax_partial_count(n);

@@ -75,6 +75,14 @@ def test_quantize_random(seed, shape, kw):
     assert_quant_equal(workloads.random_bf16(seed, shape, **kw), label=f"seed {seed}")
 
 
+@pytest.mark.parametrize("shape", [(8, 4096), (1, 2049 * 16), (4, 5376), (16, 5376)])
+def test_quantize_single_launch_boundary(shape):
+    # up to 2048 blocks one workgroup takes both passes; 2049 blocks take the
+    # two-pass kernels; both must give the oracle's bytes
+    log(f"quantize {shape}")
+    assert_quant_equal(workloads.random_bf16(shape[1] + 5, shape, outlier_frac=0.01, outlier_mul=40), label=str(shape))
+
+
 def test_quantize_degenerate():
     z = np.zeros((4, 64), np.uint16)
     z[1, 3] = 0x8000                                   # -0.0
