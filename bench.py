@@ -144,10 +144,10 @@ def summarize_traffic(fetch_csv, write_csv):
         last = None
         for r in rows:
             name, v = r["Kernel_Name"], float(r["Counter_Value"])
-            if "nvfp4_gemm_tiled_kernel<4, false, true>" in name:
+            if "nvfp4_gemm_tiled_kernel<4, false, true" in name:
                 last = "up"
                 vals["up"].append(v)
-            elif "nvfp4_gemm_tiled_kernel<4, false, false>" in name:
+            elif "nvfp4_gemm_tiled_kernel<4, false, false" in name:
                 last = "down"
                 vals["down"].append(v)
             elif "nvfp4_gemm_tiled_reduce_kernel" in name and last:
@@ -171,7 +171,8 @@ def summarize_traffic(fetch_csv, write_csv):
     cmd = "rocprofv3 --pmc {c} --output-format csv -d <dir> -o {o} -- python3 -u bench.py --steps 5 --warmup 2 " \
           "--no-extras --no-cpu-baseline --copy-calibration"
     out = {
-        "kernel": "nvfp4_gemm_tiled_kernel<4, false, true> (up, with the amax epilogue) and <4, false, false> (down)",
+        "kernel": "nvfp4_gemm_tiled_kernel<4, false, true, true> (up, with the amax epilogue) and "
+                  "<4, false, false, true> (down); the last argument: scales copied four K stages at a time",
         "workload": "prefill up (M=4096, N=21504, K=5376) and down (M=4096, N=5376, K=21504) GEMMs, with the "
                     "last-round K split, as bench.py times them",
         "kernel_source_hash": kernel_source_hash(),

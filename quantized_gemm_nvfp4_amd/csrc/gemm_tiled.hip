@@ -23,10 +23,15 @@
 //    global_load_lds into a ring of four stage slots, three stages ahead of
 //    the MFMAs.  Each code copy instruction reads 32 rows x 32 contiguous
 //    bytes.  The slots are distinct LDS objects and the stage loop is
-//    unrolled by four, so the compiler sees that copies in flight never alias
-//    what is being read; every stage issues the same copies (24 instructions
-//    per workgroup) and one wait per stage leaves the newest stage's copies
-//    in flight.
+//    unrolled, so the compiler sees that copies in flight never alias what
+//    is being read; one wait per stage leaves the newest stage's copies in
+//    flight.
+//  - A copy instruction costs one cache-line lookup per row it touches, and
+//    a stage holds only 4 scale bytes per row, so per-stage scale copies
+//    cost as much as the code copies.  When K is a multiple of 256 the
+//    4-wave kernel copies the scales of four stages at once (16 bytes per
+//    row, one lane per row) into two alternating group buffers: a quarter
+//    of the scale copy instructions.
 //  - With copies in flight the compiler waits for all outstanding LDS reads
 //    before consuming any, so within a step single MFMAs are interleaved with
 //    the next step's LDS reads and the decoding (explicit scheduling groups):
@@ -70,6 +75,10 @@ constexpr int kRing = 4;                             // packed stage slots
 constexpr int kGroupM = 4;
 constexpr int kMaxSplit = 8;
 constexpr int kMinPartStages = 4;
+constexpr int kGroupStages = 4;                      // stages per scale group
+constexpr int kGroupRow = kGroupStages * kScaleRow;  // 16 scale bytes per row per group
+constexpr int kGroupBytes = TM * kGroupRow;          // 4 KB per operand per group
+static_assert(kMinPartStages >= kGroupStages, "every split part must hold a whole scale group");
 constexpr int64_t kPartFloats = (int64_t)TM * TN;    // one tile's fp32 accumulators
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
@@ -133,6 +142,8 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_sc0[2 * kScaleBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sc1[2 * kScaleBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sc2[2 * kScaleBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sc3[2 * kScaleBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_sg0[2 * kGroupBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_sg1[2 * kGroupBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_af0[kAf16Bytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_af1[kAf16Bytes];
 
@@ -145,6 +156,7 @@ template <int B> __device__ __forceinline__ uint8_t* w_slot() {
 template <int B> __device__ __forceinline__ uint8_t* s_slot() {
   return B == 0 ? g_sc0 : (B == 1 ? g_sc1 : (B == 2 ? g_sc2 : g_sc3));
 }
+template <int P> __device__ __forceinline__ uint8_t* sg_buf() { return P == 0 ? g_sg0 : g_sg1; }
 template <int F> __device__ __forceinline__ uint8_t* af_buf() { return F == 0 ? g_af0 : g_af1; }
 
 // Per-thread state of the tiled kernel with kW waves.  The stage copies are
@@ -420,6 +432,156 @@ __device__ __forceinline__ void tiled_stage4(const TiledCtx<4>& c, int ls, float
   }
 }
 
+// Prologue of the per-stage paths: stages 0-2 in flight, stage 0's A
+// decoded.
+template <int kW>
+__device__ __forceinline__ void tiled_prologue(const TiledCtx<kW>& c) {
+  constexpr int kFr = TiledCtx<kW>::kFr;
+  tiled_issue<0>(c, 0);
+  tiled_issue<1>(c, 1);
+  tiled_issue<2>(c, 2);
+  NVFP4_WAIT_VMCNT(2 * TiledCtx<kW>::kCopies);
+  stage_barrier();
+#pragma unroll
+  for (int q = 0; q < kFr; ++q) {
+    const ADecode d = decode_a_load<0>(kFr * c.wave + q, c.lane);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) decode_a_step<0>(d, jj);
+  }
+}
+
+// Scale groups (K a multiple of 256, 4-wave kernel).  Group lg holds the
+// scale bytes of local stages 4 lg .. 4 lg + 3 in group buffer lg % 2, laid
+// out [operand][row][stage][4 bytes]; copy slot vw (the same rows as the
+// per-stage scale copies) moves rows 64 (vw % 4) + lane of operand vw / 4
+// with one 16-byte copy per lane.  Past the last group the copies repeat
+// it.  The part's first stage is a multiple of 4 and a scale row holds K/16
+// bytes, so every copy source is 16-byte aligned.
+template <int P>
+__device__ __forceinline__ void group_copy(const TiledCtx<4>& c, int lg) {
+  const int st = c.st0 + kGroupStages * min(lg, c.nst / kGroupStages - 1);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int vw = 2 * c.wave + q;
+    g2lds16(c.gs[q] + st * kScaleRow, sg_buf<P>() + (vw >> 2) * kGroupBytes + (vw & 3) * 1024);
+  }
+}
+
+// The code copies of copy slot 2w + q (A, then W) for local stage ls into
+// ring slot B.
+template <int B>
+__device__ __forceinline__ void code_copy_part(const TiledCtx<4>& c, int ls, int q) {
+  const int st = c.st0 + min(ls, c.nst - 1);
+  const int vw = 2 * c.wave + q;
+  g2lds16(c.ga[q] + st * kRowBytes, a_slot<B>() + vw * 1024);
+  g2lds16(c.gw[q] + st * kRowBytes, w_slot<B>() + vw * 1024);
+}
+
+// decode_a_load and w_prefetch with the scale bytes taken from group buffer
+// P, stage T of the group.
+template <int B, int P, int T>
+__device__ __forceinline__ ADecode decode_a_load_g(int f, int lane) {
+  const int r = 32 * f + (lane & 31), hh = lane >> 5;
+  ADecode d;
+  d.codes = *(const uint4*)(a_slot<B>() + piece_slot(r, hh) * 16);
+  const uint32_t sb = *(const uint16_t*)(sg_buf<P>() + r * kGroupRow + T * kScaleRow + 2 * hh);
+  d.s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+  d.dst = f * 4096 + lane * 16;
+  return d;
+}
+
+template <int B, int P, int T>
+__device__ __forceinline__ void w_prefetch_g(const TiledCtx<4>& c, WPre& p) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 32 * (4 * c.wn + j) + c.r32;
+    p.cw[j] = *(const uint4*)(w_slot<B>() + piece_slot(row, c.h) * 16);
+    p.sb[j] = *(const uint16_t*)(sg_buf<P>() + kGroupBytes + row * kGroupRow + T * kScaleRow + 2 * c.h);
+  }
+}
+
+// tiled_stage4 with scale groups; B8 = ls % 8.  Each stage copies the codes
+// of stage ls + 3 (four instructions per wave, steps 0-1); the first stage
+// of group lg (B8 % 4 == 0) also copies the scales of group lg + 1 (two
+// instructions, step 2) into the buffer that group lg - 1 used, whose last
+// reader ran two stages before.  Group lg + 1 is first read at stage
+// 4 lg + 3, by which time the per-stage waits have retired everything
+// issued up to stage 4 lg + 1.  Each stage waits until only the previous
+// stage's copies (six after a group's first stage, else four) are in
+// flight.
+template <int B8>
+__device__ __forceinline__ void tiled_stage4g(const TiledCtx<4>& c, int ls, float16v (&acc)[4][4], WPre (&pw)[2]) {
+  constexpr int B = B8 & 3;                 // ring slot and W registers of stage ls
+  constexpr int R1 = (B + 1) & 3;           // ring slot of stage ls + 1
+  constexpr int P1 = ((B8 + 1) >> 2) & 1;   // its group buffer
+  constexpr int T1 = (B8 + 1) & 3;          // its place in the group
+  constexpr int PN = ((B8 >> 2) + 1) & 1;   // buffer of the group copied here
+  NVFP4_WAIT_VMCNT(B == 1 ? 6 : 4);
+  stage_barrier();
+  const int lane = c.lane, wm = c.wm;
+  const uint8_t* af = af_buf<B & 1>();
+  half8v av[2][4], wv[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) av[0][i] = *(const half8v*)(af + ((4 * wm + i) * 4 + 0) * 1024 + lane * 16);
+  __builtin_amdgcn_sched_barrier(0);
+  const ADecode dec0 = decode_a_load_g<R1, P1, T1>(2 * c.wave, lane);
+  const ADecode dec1 = decode_a_load_g<R1, P1, T1>(2 * c.wave + 1, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  const WPre& cur = pw[B & 1];
+  half2v sw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sw[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.sb[j], 1.0f, false);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wv[0][j] = dequant8_f16(word_of(cur.cw[j], 0), sw[j].xx);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int cu = jj & 1, nx = cu ^ 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[cu][j], av[cu][i], acc[j][i], 0, 0, 0);
+    if (jj < 2) code_copy_part<(B + 3) & 3>(c, ls + 3, jj);
+    if (B == 0 && jj == 2) group_copy<PN>(c, ls / kGroupStages + 1);
+    if (jj + 1 < 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        av[nx][i] = *(const half8v*)(af + ((4 * wm + i) * 4 + jj + 1) * 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wv[nx][j] = dequant8_f16(word_of(cur.cw[j], jj + 1), jj + 1 < 2 ? sw[j].xx : sw[j].yy);
+    } else {
+      w_prefetch_g<R1, P1, T1>(c, pw[(B + 1) & 1]);
+    }
+    decode_a_step<(B + 1) & 1>(dec0, jj);
+    decode_a_step<(B + 1) & 1>(dec1, jj);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // bf16 stores of one 32 x 32 fragment times gmul: rows m, columns
 // nb + 8 rq + 4 h + (0..3) from registers 4 rq .. 4 rq + 3.  D[n][m] of a
 // fragment sits at lane m + 32((n/4)%2), register (n%4) + 4(n/8): four
@@ -572,7 +734,11 @@ __device__ __forceinline__ void lora_epilogue(float16v (&acc)[TiledCtx<kW>::kJ][
 // with kW == 8 and without splits).  kAmax (kW == 4, no low-rank branch):
 // amax[tile] receives the largest |bf16| pattern of the tile's outputs;
 // for a split tile it is set to 0 here and raised by the reduce kernel.
-template <int kW, bool kLora, bool kAmax = false>
+// kGroups (kW == 4, K a multiple of 256, scale arrays 16-byte aligned):
+// scales move in groups of four stages, and part boundaries are multiples
+// of four stages (part p of S: groups [p G / S, (p + 1) G / S) of the
+// G = K / 256).
+template <int kW, bool kLora, bool kAmax = false, bool kGroups = false>
 __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
@@ -580,6 +746,7 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
     float* __restrict__ part, const float* __restrict__ lora_t, const uint16_t* __restrict__ lora_up, int r,
     uint32_t* __restrict__ amax) {
   static_assert(!kAmax || (kW == 4 && !kLora), "amax slots: 4-wave kernel without the low-rank branch");
+  static_assert(!kGroups || kW == 4, "scale groups: 4-wave kernel");
   using Ctx = TiledCtx<kW>;
   constexpr int kFr = Ctx::kFr, kJ = Ctx::kJ;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -592,8 +759,14 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
     unit = bid - full_tiles;
     const int p = unit % splits;
     tile_id = full_tiles + unit / splits;
-    st0 = p * nst_all / splits;
-    st1 = (p + 1) * nst_all / splits;
+    if (kGroups) {
+      const int ng = nst_all / kGroupStages;
+      st0 = kGroupStages * (p * ng / splits);
+      st1 = kGroupStages * ((p + 1) * ng / splits);
+    } else {
+      st0 = p * nst_all / splits;
+      st1 = (p + 1) * nst_all / splits;
+    }
   }
   int tile_m, tile_n;
   tile_of(tile_id, tiles_m, tiles_n, tile_m, tile_n);
@@ -632,19 +805,45 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = float16v{};
 
-  // Prologue: stages 0-2 in flight, stage 0's A decoded.
-  tiled_issue<0>(c, 0);
-  tiled_issue<1>(c, 1);
-  tiled_issue<2>(c, 2);
-  NVFP4_WAIT_VMCNT(2 * Ctx::kCopies);
-  stage_barrier();
+  if constexpr (kGroups) {
+    // Prologue: scale group 0 and the codes of stages 0-2 in flight, then
+    // stage 0's A decoded and its W read.
+    group_copy<0>(c, 0);
+    code_copy_part<0>(c, 0, 0);
+    code_copy_part<0>(c, 0, 1);
+    code_copy_part<1>(c, 1, 0);
+    code_copy_part<1>(c, 1, 1);
+    code_copy_part<2>(c, 2, 0);
+    code_copy_part<2>(c, 2, 1);
+    NVFP4_WAIT_VMCNT(8);
+    stage_barrier();
 #pragma unroll
-  for (int q = 0; q < kFr; ++q) {
-    const ADecode d = decode_a_load<0>(kFr * wave + q, lane);
+    for (int q = 0; q < 2; ++q) {
+      const ADecode d = decode_a_load_g<0, 0, 0>(2 * wave + q, lane);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) decode_a_step<0>(d, jj);
-  }
-  if constexpr (kW == 4) {
+      for (int jj = 0; jj < 4; ++jj) decode_a_step<0>(d, jj);
+    }
+    WPre pw[2];
+    w_prefetch_g<0, 0, 0>(c, pw[0]);
+    int ls = 0;
+    for (; ls + 8 <= c.nst; ls += 8) {
+      tiled_stage4g<0>(c, ls, acc, pw);
+      tiled_stage4g<1>(c, ls + 1, acc, pw);
+      tiled_stage4g<2>(c, ls + 2, acc, pw);
+      tiled_stage4g<3>(c, ls + 3, acc, pw);
+      tiled_stage4g<4>(c, ls + 4, acc, pw);
+      tiled_stage4g<5>(c, ls + 5, acc, pw);
+      tiled_stage4g<6>(c, ls + 6, acc, pw);
+      tiled_stage4g<7>(c, ls + 7, acc, pw);
+    }
+    if (ls < c.nst) {      // nst is a multiple of 4: one group left
+      tiled_stage4g<0>(c, ls, acc, pw);
+      tiled_stage4g<1>(c, ls + 1, acc, pw);
+      tiled_stage4g<2>(c, ls + 2, acc, pw);
+      tiled_stage4g<3>(c, ls + 3, acc, pw);
+    }
+  } else if constexpr (kW == 4) {
+    tiled_prologue<kW>(c);
     WPre pw[2];
     w_prefetch<0>(c, pw[0]);
     int ls = 0;
@@ -661,6 +860,7 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
       tiled_stage4<3, true>(c, ls + 3, acc, pw);
     }
   } else {
+    tiled_prologue<kW>(c);
     for (int ls = 0; ls < c.nst; ls += 4) {
       tiled_stage<0>(c, ls, acc);
       tiled_stage<1>(c, ls + 1, acc);
@@ -742,6 +942,7 @@ int device_cus() {
 
 struct TiledPlan {
   int tiles_m, tiles_n, full_tiles, splits;
+  bool groups;          // scales in groups of four stages (K a multiple of 256)
   int64_t part_bytes;
 };
 
@@ -760,6 +961,7 @@ TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K, bool allow_split) {
   const int tiles = p.tiles_m * p.tiles_n;
   p.full_tiles = tiles;
   p.splits = 1;
+  p.groups = K % (kGroupStages * TK) == 0;
   p.part_bytes = 0;
   if (!allow_split) return p;
   const int cus = device_cus();
@@ -773,6 +975,17 @@ TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K, bool allow_split) {
   p.full_tiles = tiles - left;
   p.splits = s;
   p.part_bytes = (int64_t)left * s * kPartFloats * 4;
+  if (p.groups) {
+    // With scale groups a stage runs about 4% faster, but a split part is
+    // whole groups, so the longest part can have up to 3 more stages (84
+    // stages in 4 parts: 24 instead of 21).  Keep groups when the estimated
+    // time of the full rounds plus the split round is lower.
+    const int64_t rounds = p.full_tiles / cus;
+    const int64_t ng = nst / kGroupStages;
+    const int64_t t_groups = 24 * (rounds * nst + kGroupStages * ((ng + s - 1) / s));
+    const int64_t t_stages = 25 * (rounds * nst + (nst + s - 1) / s);
+    p.groups = t_groups < t_stages;
+  }
   return p;
 }
 }  // namespace
@@ -794,14 +1007,17 @@ hipError_t launch_nvfp4_gemm_tiled_ws(const uint8_t* ac, const uint8_t* as, cons
   if (p.part_bytes > workspace_bytes) p = plan_tiled(M, N, K, false);
   const int tiles = p.tiles_m * p.tiles_n;
   const int grid = p.full_tiles + (tiles - p.full_tiles) * p.splits;
-  if (amax != nullptr)
-    hipLaunchKernelGGL((nvfp4_gemm_tiled_kernel<4, false, true>), dim3((unsigned)grid), dim3(256), 0, stream, ac, as,
-                       ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n, p.full_tiles,
-                       p.splits, (float*)workspace, nullptr, nullptr, 0, amax);
-  else
-    hipLaunchKernelGGL((nvfp4_gemm_tiled_kernel<4, false>), dim3((unsigned)grid), dim3(256), 0, stream, ac, as, ag, wc,
-                       ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n, p.full_tiles, p.splits,
-                       (float*)workspace, nullptr, nullptr, 0, nullptr);
+  // Scale groups copy 16 bytes per row: the scale arrays must be 16-byte
+  // aligned (rows are, as K is a multiple of 256).  The C entry points
+  // require that alignment; other callers get the per-stage copies.
+  const bool groups = p.groups && ((reinterpret_cast<uintptr_t>(as) | reinterpret_cast<uintptr_t>(ws)) & 15) == 0;
+  auto kernel = amax != nullptr ? (groups ? nvfp4_gemm_tiled_kernel<4, false, true, true>
+                                          : nvfp4_gemm_tiled_kernel<4, false, true, false>)
+                                : (groups ? nvfp4_gemm_tiled_kernel<4, false, false, true>
+                                          : nvfp4_gemm_tiled_kernel<4, false, false, false>);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out,
+                     (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n, p.full_tiles, p.splits, (float*)workspace,
+                     nullptr, nullptr, 0, amax);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.full_tiles == tiles) return e;
   hipLaunchKernelGGL(nvfp4_gemm_tiled_reduce_kernel, dim3((unsigned)(16 * (tiles - p.full_tiles))), dim3(256), 0,

@@ -212,6 +212,31 @@ def test_gemm_tiled_split_and_whole(M, N, K, split):
         assert np.array_equal(outs["split"], outs["whole"])
 
 
+def test_gemm_tiled_scale_groups_uneven_split():
+    # K = 1792 (a multiple of 256): the tiled kernel copies the scale bytes
+    # of four stages at once and splits the leftover round (64 of 320 tiles,
+    # 4 parts) at whole 4-stage groups, 1 or 2 groups per part; 28 stages is
+    # not a multiple of the 8-stage loop.  Checked on sampled rows.
+    M, N, K = 4096, 5120, 1792
+    q = _q()
+    import torch
+    a_bits = workloads.random_bf16(71, (M, K))
+    w_bits = workloads.random_bf16(72, (N, K), sigma=0.02, outlier_frac=0.005, outlier_mul=20)
+    a = assert_quant_equal(a_bits, label="groups A")
+    w = assert_quant_equal(w_bits, label="groups W")
+    assert q.lib().nvfp4_gemm_workspace_bytes(M, N, K) > 0
+    rows = np.sort(np.random.default_rng(3).choice(M, 48, replace=False))
+    ref = O.gemm_rows(*O.quantize(a_bits), *O.quantize(w_bits), rows)
+    out = Guarded((M, N), torch.bfloat16)
+    q.nvfp4_gemm(a, w, algo=q.ALGO_TILED, out=out.t)
+    torch.cuda.synchronize()
+    assert out.intact(), "wrote outside its output"
+    y = F.bf16_from_bits(host_bits(out.t)).astype(np.float64)[rows]
+    ok, rl, rr = Mx.check_output(y, ref)
+    log(f"tiled scale groups {M}x{N}x{K}: rel_l2={rl:.3e} row_ratio={rr:.3e}")
+    assert ok, f"rel_l2={rl:.3e} row_ratio={rr:.3e}"
+
+
 @pytest.mark.parametrize("M,N,K", [
     (1, 1, 128), (2, 3, 128), (1, 9, 2048), (2, 37, 2176), (1, 33, 4224), (2, 8, 6144), (1, 5, 32768 + 128)])
 def test_gemm_decode_shapes(M, N, K):
