@@ -12,10 +12,15 @@
 // it is given 1.0) and one packed fp16 multiply by the block scale.
 //
 // Design for CDNA4:
-//  - Workgroup tile 256 x 256, K stage of 64 values, 4 waves of 128 (m) x
-//    128 (n), one wave per SIMD; a wave's 16 accumulator fragments (256
-//    registers) live in the accumulation register file.  Each A fragment
-//    read from LDS feeds 4 MFMAs.  The variant with the low-rank epilogue
+//  - Workgroup tile 256 x 256, K stage of 64 values, 4 waves, one per SIMD;
+//    a wave's 16 accumulator fragments (256 registers) live in the
+//    accumulation register file.  With scale groups (below) each wave
+//    covers 256 (m) x 64 (n): it reads all eight A fragments from LDS (each
+//    feeding 2 MFMAs) and decodes only its own two W fragments, so every
+//    value of both operands is decoded once per workgroup (2 decode
+//    instructions per MFMA).  Otherwise a wave covers 128 x 128 (each A
+//    fragment feeds 4 MFMAs, and two waves decode each W fragment: 3 per
+//    MFMA).  The variant with the low-rank epilogue
 //    uses 8 waves of 128 x 64 (two per SIMD, accumulators in ordinary
 //    registers), because its epilogue scales and extends the accumulators
 //    with vector instructions, which cannot read the accumulation file.
@@ -582,6 +587,105 @@ __device__ __forceinline__ void tiled_stage4g(const TiledCtx<4>& c, int ls, floa
   }
 }
 
+// Wave tile 256 (m) x 64 (n) for the scale-group path: every wave
+// multiplies all eight 32-row A fragments of the workgroup's fp16 A tile
+// with its own two W fragments (rows 64 w .. 64 w + 63 of the W tile), so
+// each W fragment is decoded by one wave only (with 128 x 128 wave tiles
+// two waves decode each).  Per lane and stage that is 64 W and 64 A values
+// decoded for 64 MFMAs, against 128 + 64; each A fragment read from LDS
+// feeds two MFMAs instead of four.
+struct WPre2 {
+  uint4 cw[2];
+  uint32_t sb[2];
+};
+
+template <int B, int P, int T>
+__device__ __forceinline__ void w_prefetch_n64(const TiledCtx<4>& c, WPre2& p) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 64 * c.wave + 32 * j + c.r32;
+    p.cw[j] = *(const uint4*)(w_slot<B>() + piece_slot(row, c.h) * 16);
+    p.sb[j] = *(const uint16_t*)(sg_buf<P>() + kGroupBytes + row * kGroupRow + T * kScaleRow + 2 * c.h);
+  }
+}
+
+// tiled_stage4g with the 256 x 64 wave tile; acc[j][i]: W fragment j, A
+// fragment i.
+template <int B8>
+__device__ __forceinline__ void tiled_stage_n64(const TiledCtx<4>& c, int ls, float16v (&acc)[2][8],
+                                                WPre2 (&pw)[2]) {
+  constexpr int B = B8 & 3;
+  constexpr int R1 = (B + 1) & 3;
+  constexpr int P1 = ((B8 + 1) >> 2) & 1;
+  constexpr int T1 = (B8 + 1) & 3;
+  constexpr int PN = ((B8 >> 2) + 1) & 1;
+  NVFP4_WAIT_VMCNT(B == 1 ? 6 : 4);
+  stage_barrier();
+  const int lane = c.lane;
+  const uint8_t* af = af_buf<B & 1>();
+  half8v av[2][8], wv[2][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) av[0][i] = *(const half8v*)(af + (i * 4 + 0) * 1024 + lane * 16);
+  __builtin_amdgcn_sched_barrier(0);
+  const ADecode dec0 = decode_a_load_g<R1, P1, T1>(2 * c.wave, lane);
+  const ADecode dec1 = decode_a_load_g<R1, P1, T1>(2 * c.wave + 1, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  const WPre2& cur = pw[B & 1];
+  half2v sw[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sw[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.sb[j], 1.0f, false);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) wv[0][j] = dequant8_f16(word_of(cur.cw[j], 0), sw[j].xx);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int cu = jj & 1, nx = cu ^ 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[cu][j], av[cu][i], acc[j][i], 0, 0, 0);
+    if (jj < 2) code_copy_part<(B + 3) & 3>(c, ls + 3, jj);
+    if (B == 0 && jj == 2) group_copy<PN>(c, ls / kGroupStages + 1);
+    if (jj + 1 < 4) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) av[nx][i] = *(const half8v*)(af + (i * 4 + jj + 1) * 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        wv[nx][j] = dequant8_f16(word_of(cur.cw[j], jj + 1), jj + 1 < 2 ? sw[j].xx : sw[j].yy);
+    } else {
+      w_prefetch_n64<R1, P1, T1>(c, pw[(B + 1) & 1]);
+    }
+    decode_a_step<(B + 1) & 1>(dec0, jj);
+    decode_a_step<(B + 1) & 1>(dec1, jj);
+    // MFMA, copy, 2 VALU (x2); MFMA, read, 2 VALU (x8); MFMA, 3 VALU (x4);
+    // MFMA, write (x2)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // bf16 stores of one 32 x 32 fragment times gmul: rows m, columns
 // nb + 8 rq + 4 h + (0..3) from registers 4 rq .. 4 rq + 3.  D[n][m] of a
 // fragment sits at lane m + 32((n/4)%2), register (n%4) + 4(n/8): four
@@ -823,25 +927,60 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) decode_a_step<0>(d, jj);
     }
-    WPre pw[2];
-    w_prefetch_g<0, 0, 0>(c, pw[0]);
+    float16v acc2[2][8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc2[j][i] = float16v{};
+    WPre2 pw[2];
+    w_prefetch_n64<0, 0, 0>(c, pw[0]);
     int ls = 0;
     for (; ls + 8 <= c.nst; ls += 8) {
-      tiled_stage4g<0>(c, ls, acc, pw);
-      tiled_stage4g<1>(c, ls + 1, acc, pw);
-      tiled_stage4g<2>(c, ls + 2, acc, pw);
-      tiled_stage4g<3>(c, ls + 3, acc, pw);
-      tiled_stage4g<4>(c, ls + 4, acc, pw);
-      tiled_stage4g<5>(c, ls + 5, acc, pw);
-      tiled_stage4g<6>(c, ls + 6, acc, pw);
-      tiled_stage4g<7>(c, ls + 7, acc, pw);
+      tiled_stage_n64<0>(c, ls, acc2, pw);
+      tiled_stage_n64<1>(c, ls + 1, acc2, pw);
+      tiled_stage_n64<2>(c, ls + 2, acc2, pw);
+      tiled_stage_n64<3>(c, ls + 3, acc2, pw);
+      tiled_stage_n64<4>(c, ls + 4, acc2, pw);
+      tiled_stage_n64<5>(c, ls + 5, acc2, pw);
+      tiled_stage_n64<6>(c, ls + 6, acc2, pw);
+      tiled_stage_n64<7>(c, ls + 7, acc2, pw);
     }
     if (ls < c.nst) {      // nst is a multiple of 4: one group left
-      tiled_stage4g<0>(c, ls, acc, pw);
-      tiled_stage4g<1>(c, ls + 1, acc, pw);
-      tiled_stage4g<2>(c, ls + 2, acc, pw);
-      tiled_stage4g<3>(c, ls + 3, acc, pw);
+      tiled_stage_n64<0>(c, ls, acc2, pw);
+      tiled_stage_n64<1>(c, ls + 1, acc2, pw);
+      tiled_stage_n64<2>(c, ls + 2, acc2, pw);
+      tiled_stage_n64<3>(c, ls + 3, acc2, pw);
     }
+    NVFP4_WAIT_VMCNT(0);
+    const int h = c.h, r32 = c.r32;
+    if (unit >= 0) {
+      if (kAmax && tid == 0 && unit % splits == 0) amax[tile_id] = 0u;
+      // fragment (j, i) of wave w at part[unit][(w * 16 + j * 8 + i) * 64 + lane][16]
+      float* dst = part + (int64_t)unit * kPartFloats + (int64_t)wave * 16 * 64 * 16 + lane * 16;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float4* d4 = (float4*)(dst + (j * 8 + i) * 64 * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            d4[e] = make_float4(acc2[j][i][4 * e], acc2[j][i][4 * e + 1], acc2[j][i][4 * e + 2], acc2[j][i][4 * e + 3]);
+        }
+      return;
+    }
+    const float gg = (*a_g) * (*w_g);
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        mx = max(mx, store_frag(acc2[j][i], gg, out, M, N, m0 + 32 * i + r32, n0 + 64 * wave + 32 * j, h));
+    if (kAmax) {
+      __shared__ uint32_t red2[4];
+      const uint32_t m = block_max_u32<4>(mx, red2);
+      if (tid == 0) amax[tile_id] = m;
+    }
+    return;
   } else if constexpr (kW == 4) {
     tiled_prologue<kW>(c);
     WPre pw[2];
@@ -898,10 +1037,14 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
 }
 
 // Leftover tile t: workgroup (t, g) sums, for fragments 4g .. 4g + 3 of
-// the tile (one per wave; fragment f = 16 w + 4 j + i of the GEMM's wave w),
-// the `splits` K parts in order, scales by g_a g_w, rounds to bf16 and
-// stores.  With amax, it raises amax[full_tiles + t] (zeroed by the tile
-// kernel) to the largest |bf16| pattern it stored.
+// the tile (one per wave), the `splits` K parts in order, scales by
+// g_a g_w, rounds to bf16 and stores.  Fragment f of the GEMM's wave w is
+// f = 16 w + 4 j + i with 128 x 128 wave tiles (rows 128 (w / 2) + 32 i,
+// columns 128 (w % 2) + 32 j) and f = 16 w + 8 j + i with 256 x 64 wave
+// tiles (kN64: rows 32 i, columns 64 w + 32 j).  With amax, it raises
+// amax[full_tiles + t] (zeroed by the tile kernel) to the largest |bf16|
+// pattern it stored.
+template <bool kN64>
 __global__ __launch_bounds__(256) void nvfp4_gemm_tiled_reduce_kernel(const float* __restrict__ part,
                                                                       const float* __restrict__ a_g,
                                                                       const float* __restrict__ w_g,
@@ -911,15 +1054,16 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_tiled_reduce_kernel(const floa
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x >> 4;
   const int f = 4 * (blockIdx.x & 15) + (threadIdx.x >> 6);
-  const int w = f >> 4, j = (f >> 2) & 3, i = f & 3;
+  const int w = f >> 4;
+  const int fm = kN64 ? 32 * (f & 7) : 128 * (w >> 1) + 32 * (f & 3);
+  const int fn = kN64 ? 64 * w + 32 * ((f >> 3) & 1) : 128 * (w & 1) + 32 * ((f >> 2) & 3);
   int tile_m, tile_n;
   tile_of(full_tiles + t, tiles_m, tiles_n, tile_m, tile_n);
   const float* src = part + (int64_t)t * splits * kPartFloats + ((int64_t)f * 64 + lane) * 16;
   float16v s = *(const float16v*)src;
   for (int p = 1; p < splits; ++p) s += *(const float16v*)(src + p * kPartFloats);
-  const int wm = w >> 1, wn = w & 1;
-  const uint32_t mx = store_frag(s, (*a_g) * (*w_g), out, M, N, tile_m * TM + 128 * wm + 32 * i + (lane & 31),
-                                 tile_n * TN + 128 * wn + 32 * j, lane >> 5);
+  const uint32_t mx = store_frag(s, (*a_g) * (*w_g), out, M, N, tile_m * TM + fm + (lane & 31), tile_n * TN + fn,
+                                 lane >> 5);
   if (amax != nullptr) {
     __shared__ uint32_t red[4];
     const uint32_t m = block_max_u32<4>(mx, red);
@@ -1020,8 +1164,8 @@ hipError_t launch_nvfp4_gemm_tiled_ws(const uint8_t* ac, const uint8_t* as, cons
                      nullptr, nullptr, 0, amax);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.full_tiles == tiles) return e;
-  hipLaunchKernelGGL(nvfp4_gemm_tiled_reduce_kernel, dim3((unsigned)(16 * (tiles - p.full_tiles))), dim3(256), 0,
-                     stream,
+  hipLaunchKernelGGL(groups ? nvfp4_gemm_tiled_reduce_kernel<true> : nvfp4_gemm_tiled_reduce_kernel<false>,
+                     dim3((unsigned)(16 * (tiles - p.full_tiles))), dim3(256), 0, stream,
                      (const float*)workspace, ag, wg, (uint16_t*)out, (int)M, (int)N, p.tiles_m, p.tiles_n,
                      p.full_tiles, p.splits, amax);
   return hipGetLastError();
