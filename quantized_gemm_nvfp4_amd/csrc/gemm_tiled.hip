@@ -31,12 +31,13 @@
 //    unrolled, so the compiler sees that copies in flight never alias what
 //    is being read; one wait per stage leaves the newest stage's copies in
 //    flight.
-//  - A copy instruction costs one cache-line lookup per row it touches, and
-//    a stage holds only 4 scale bytes per row, so per-stage scale copies
-//    cost as much as the code copies.  When K is a multiple of 256 the
-//    4-wave kernel copies the scales of four stages at once (16 bytes per
-//    row, one lane per row) into two alternating group buffers: a quarter
-//    of the scale copy instructions.
+//  - A copy instruction costs about one cache-line lookup per row it
+//    touches, and a stage holds only 32 code and 4 scale bytes per row.
+//    When K is a multiple of 256 the 4-wave kernel copies the codes of two
+//    stages at once (64 bytes per row, 16 rows per instruction) into two
+//    pair slots, and the scales of four stages at once (16 bytes per row,
+//    one lane per row) into two group buffers: half the lines of the code
+//    copies, a quarter of the scale copy instructions.
 //  - With copies in flight the compiler waits for all outstanding LDS reads
 //    before consuming any, so within a step single MFMAs are interleaved with
 //    the next step's LDS reads and the decoding (explicit scheduling groups):
@@ -115,6 +116,8 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding), as
 // a builtin so the compiler's own wait insertion accounts for it.
 #define NVFP4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
+// s_waitcnt lgkmcnt(0): this wave's LDS accesses are complete.
+#define NVFP4_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 // A workgroup barrier without the memory fence of __syncthreads() (which
 // would drain the copies in flight); the empty asm statements keep the
@@ -131,6 +134,12 @@ __device__ __forceinline__ void stage_barrier() {
 // in 16 distinct groups of a 256-byte window.
 __device__ __forceinline__ int piece_swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 __device__ __forceinline__ int piece_slot(int r, int p) { return 2 * r + (p ^ piece_swz(r)); }
+// The same for rows of two stages (four 16-byte pieces, 64 bytes): piece p
+// of row r at slot 4 r + (p ^ pair_swz(r)); one piece of any 8 consecutive
+// rows lands in 8 distinct 16-byte groups of a 128-byte window, and of any
+// 16 in 16 distinct groups of a 256-byte window.
+__device__ __forceinline__ int pair_swz(int r) { return 2 * ((r >> 2) & 1) + (((r >> 1) ^ (r >> 3)) & 1); }
+__device__ __forceinline__ int pair_piece_slot(int r, int p) { return 4 * r + (p ^ pair_swz(r)); }
 }  // namespace
 
 // Packed stage slots (A codes, W codes, A+W scales) and the decoded A tiles,
@@ -147,6 +156,10 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_sc0[2 * kScaleBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sc1[2 * kScaleBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sc2[2 * kScaleBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sc3[2 * kScaleBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_ap0[2 * kCodeBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_ap1[2 * kCodeBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_wp0[2 * kCodeBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_wp1[2 * kCodeBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sg0[2 * kGroupBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sg1[2 * kGroupBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_af0[kAf16Bytes];
@@ -162,6 +175,8 @@ template <int B> __device__ __forceinline__ uint8_t* s_slot() {
   return B == 0 ? g_sc0 : (B == 1 ? g_sc1 : (B == 2 ? g_sc2 : g_sc3));
 }
 template <int P> __device__ __forceinline__ uint8_t* sg_buf() { return P == 0 ? g_sg0 : g_sg1; }
+template <int S> __device__ __forceinline__ uint8_t* ap_slot() { return S == 0 ? g_ap0 : g_ap1; }
+template <int S> __device__ __forceinline__ uint8_t* wp_slot() { return S == 0 ? g_wp0 : g_wp1; }
 template <int F> __device__ __forceinline__ uint8_t* af_buf() { return F == 0 ? g_af0 : g_af1; }
 
 // Per-thread state of the tiled kernel with kW waves.  The stage copies are
@@ -175,6 +190,8 @@ struct TiledCtx {
   const uint8_t* ga[kFr];  // A code copy sources (row, piece) of this lane
   const uint8_t* gw[kFr];  // W code copy sources
   const uint8_t* gs[kFr];  // scale copy sources (A for copy slots 0-3, W for 4-7)
+  const uint8_t* gpa[4];   // pair copy sources of A and W (scale-group path)
+  const uint8_t* gpw[4];
   int wave, lane, wm, wn, h, r32;
   int st0, nst;            // first K stage and number of stages of this workgroup
 };
@@ -455,13 +472,15 @@ __device__ __forceinline__ void tiled_prologue(const TiledCtx<kW>& c) {
   }
 }
 
-// Scale groups (K a multiple of 256, 4-wave kernel).  Group lg holds the
-// scale bytes of local stages 4 lg .. 4 lg + 3 in group buffer lg % 2, laid
-// out [operand][row][stage][4 bytes]; copy slot vw (the same rows as the
-// per-stage scale copies) moves rows 64 (vw % 4) + lane of operand vw / 4
-// with one 16-byte copy per lane.  Past the last group the copies repeat
-// it.  The part's first stage is a multiple of 4 and a scale row holds K/16
-// bytes, so every copy source is 16-byte aligned.
+// Scale-group path (K a multiple of 256, 4-wave kernel).
+//
+// Scale groups: group lg holds the scale bytes of local stages 4 lg ..
+// 4 lg + 3 in group buffer lg % 2, laid out [operand][row][stage][4 bytes];
+// copy slot vw (the same rows as the per-stage scale copies) moves rows
+// 64 (vw % 4) + lane of operand vw / 4 with one 16-byte copy per lane.
+// Past the last group the copies repeat it.  The part's first stage is a
+// multiple of 4 and a scale row holds K/16 bytes, so every copy source is
+// 16-byte aligned.
 template <int P>
 __device__ __forceinline__ void group_copy(const TiledCtx<4>& c, int lg) {
   const int st = c.st0 + kGroupStages * min(lg, c.nst / kGroupStages - 1);
@@ -472,165 +491,91 @@ __device__ __forceinline__ void group_copy(const TiledCtx<4>& c, int lg) {
   }
 }
 
-// The code copies of copy slot 2w + q (A, then W) for local stage ls into
-// ring slot B.
-template <int B>
-__device__ __forceinline__ void code_copy_part(const TiledCtx<4>& c, int ls, int q) {
-  const int st = c.st0 + min(ls, c.nst - 1);
-  const int vw = 2 * c.wave + q;
-  g2lds16(c.ga[q] + st * kRowBytes, a_slot<B>() + vw * 1024);
-  g2lds16(c.gw[q] + st * kRowBytes, w_slot<B>() + vw * 1024);
+// Code pairs: the codes of stages 2 lq and 2 lq + 1 (64 bytes per row) go
+// to pair slot lq % 2 ([row][4 pieces], pair_piece_slot), one instruction
+// per 16 rows (4 lanes per row): a copy touches 16 cache lines instead of
+// 32.  Wave w copies rows 64 w .. 64 w + 63 of both operands; part 0-1: A,
+// 2-3: W, two instructions each.  Past the last pair the copies repeat it.
+template <int S>
+__device__ __forceinline__ void pair_copy_part(const TiledCtx<4>& c, int lq, int part) {
+  const int st = c.st0 + 2 * min(lq, c.nst / 2 - 1);
+#pragma unroll
+  for (int k = 2 * (part & 1); k < 2 * (part & 1) + 2; ++k) {
+    if (part < 2) g2lds16(c.gpa[k] + st * kRowBytes, ap_slot<S>() + (4 * c.wave + k) * 1024);
+    else g2lds16(c.gpw[k] + st * kRowBytes, wp_slot<S>() + (4 * c.wave + k) * 1024);
+  }
 }
 
-// decode_a_load and w_prefetch with the scale bytes taken from group buffer
-// P, stage T of the group.
-template <int B, int P, int T>
-__device__ __forceinline__ ADecode decode_a_load_g(int f, int lane) {
+// decode_a_load from pair slot S (stage TH of the pair) and group buffer P
+// (stage T of the group).
+template <int S, int TH, int P, int T>
+__device__ __forceinline__ ADecode decode_a_load_p(int f, int lane) {
   const int r = 32 * f + (lane & 31), hh = lane >> 5;
   ADecode d;
-  d.codes = *(const uint4*)(a_slot<B>() + piece_slot(r, hh) * 16);
+  d.codes = *(const uint4*)(ap_slot<S>() + pair_piece_slot(r, 2 * TH + hh) * 16);
   const uint32_t sb = *(const uint16_t*)(sg_buf<P>() + r * kGroupRow + T * kScaleRow + 2 * hh);
   d.s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
   d.dst = f * 4096 + lane * 16;
   return d;
 }
 
-template <int B, int P, int T>
-__device__ __forceinline__ void w_prefetch_g(const TiledCtx<4>& c, WPre& p) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 32 * (4 * c.wn + j) + c.r32;
-    p.cw[j] = *(const uint4*)(w_slot<B>() + piece_slot(row, c.h) * 16);
-    p.sb[j] = *(const uint16_t*)(sg_buf<P>() + kGroupBytes + row * kGroupRow + T * kScaleRow + 2 * c.h);
-  }
-}
-
-// tiled_stage4 with scale groups; B8 = ls % 8.  Each stage copies the codes
-// of stage ls + 3 (four instructions per wave, steps 0-1); the first stage
-// of group lg (B8 % 4 == 0) also copies the scales of group lg + 1 (two
-// instructions, step 2) into the buffer that group lg - 1 used, whose last
-// reader ran two stages before.  Group lg + 1 is first read at stage
-// 4 lg + 3, by which time the per-stage waits have retired everything
-// issued up to stage 4 lg + 1.  Each stage waits until only the previous
-// stage's copies (six after a group's first stage, else four) are in
-// flight.
-template <int B8>
-__device__ __forceinline__ void tiled_stage4g(const TiledCtx<4>& c, int ls, float16v (&acc)[4][4], WPre (&pw)[2]) {
-  constexpr int B = B8 & 3;                 // ring slot and W registers of stage ls
-  constexpr int R1 = (B + 1) & 3;           // ring slot of stage ls + 1
-  constexpr int P1 = ((B8 + 1) >> 2) & 1;   // its group buffer
-  constexpr int T1 = (B8 + 1) & 3;          // its place in the group
-  constexpr int PN = ((B8 >> 2) + 1) & 1;   // buffer of the group copied here
-  NVFP4_WAIT_VMCNT(B == 1 ? 6 : 4);
-  stage_barrier();
-  const int lane = c.lane, wm = c.wm;
-  const uint8_t* af = af_buf<B & 1>();
-  half8v av[2][4], wv[2][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) av[0][i] = *(const half8v*)(af + ((4 * wm + i) * 4 + 0) * 1024 + lane * 16);
-  __builtin_amdgcn_sched_barrier(0);
-  const ADecode dec0 = decode_a_load_g<R1, P1, T1>(2 * c.wave, lane);
-  const ADecode dec1 = decode_a_load_g<R1, P1, T1>(2 * c.wave + 1, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  const WPre& cur = pw[B & 1];
-  half2v sw[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) sw[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.sb[j], 1.0f, false);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) wv[0][j] = dequant8_f16(word_of(cur.cw[j], 0), sw[j].xx);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int cu = jj & 1, nx = cu ^ 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[cu][j], av[cu][i], acc[j][i], 0, 0, 0);
-    if (jj < 2) code_copy_part<(B + 3) & 3>(c, ls + 3, jj);
-    if (B == 0 && jj == 2) group_copy<PN>(c, ls / kGroupStages + 1);
-    if (jj + 1 < 4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        av[nx][i] = *(const half8v*)(af + ((4 * wm + i) * 4 + jj + 1) * 1024 + lane * 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        wv[nx][j] = dequant8_f16(word_of(cur.cw[j], jj + 1), jj + 1 < 2 ? sw[j].xx : sw[j].yy);
-    } else {
-      w_prefetch_g<R1, P1, T1>(c, pw[(B + 1) & 1]);
-    }
-    decode_a_step<(B + 1) & 1>(dec0, jj);
-    decode_a_step<(B + 1) & 1>(dec1, jj);
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// Wave tile 256 (m) x 64 (n) for the scale-group path: every wave
-// multiplies all eight 32-row A fragments of the workgroup's fp16 A tile
-// with its own two W fragments (rows 64 w .. 64 w + 63 of the W tile), so
-// each W fragment is decoded by one wave only (with 128 x 128 wave tiles
-// two waves decode each).  Per lane and stage that is 64 W and 64 A values
-// decoded for 64 MFMAs, against 128 + 64; each A fragment read from LDS
-// feeds two MFMAs instead of four.
+// Wave tile 256 (m) x 64 (n): every wave multiplies all eight 32-row A
+// fragments of the workgroup's fp16 A tile with its own two W fragments
+// (rows 64 w .. 64 w + 63 of the W tile), so each W fragment is decoded by
+// one wave only (with 128 x 128 wave tiles two waves decode each).  Per
+// lane and stage that is 64 W and 64 A values decoded for 64 MFMAs,
+// against 128 + 64; each A fragment read from LDS feeds two MFMAs instead
+// of four.
 struct WPre2 {
   uint4 cw[2];
   uint32_t sb[2];
 };
 
-template <int B, int P, int T>
-__device__ __forceinline__ void w_prefetch_n64(const TiledCtx<4>& c, WPre2& p) {
+template <int S, int TH, int P, int T>
+__device__ __forceinline__ void w_prefetch_p(const TiledCtx<4>& c, WPre2& p) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = 64 * c.wave + 32 * j + c.r32;
-    p.cw[j] = *(const uint4*)(w_slot<B>() + piece_slot(row, c.h) * 16);
+    p.cw[j] = *(const uint4*)(wp_slot<S>() + pair_piece_slot(row, 2 * TH + c.h) * 16);
     p.sb[j] = *(const uint16_t*)(sg_buf<P>() + kGroupBytes + row * kGroupRow + T * kScaleRow + 2 * c.h);
   }
 }
 
-// tiled_stage4g with the 256 x 64 wave tile; acc[j][i]: W fragment j, A
-// fragment i.
+// One K stage of the scale-group path; B8 = ls % 8, acc[j][i]: W fragment
+// j, A fragment i.  As in tiled_stage4, the stage multiplies stage ls while
+// decoding A of stage ls + 1 and reading its W into registers.  Copies:
+// an odd stage copies code pair (ls + 3) / 2 (stages ls + 3, ls + 4; eight
+// instructions per wave, two per step) into the slot of the pair holding
+// stages ls - 1 and ls, whose last readers ran in stage ls - 1: each wave
+// first waits for its own LDS reads, so after the barrier none is still in
+// flight.  The first stage of group lg (B8 % 4 == 0) copies the scales of
+// group lg + 1 (two instructions, step 2) into the buffer group lg - 1
+// used.  Each stage waits until only the previous stage's copies are in
+// flight: 8 after an odd stage, 2 after a group's first stage, else none.
+// A pair is first read two stages after it is issued, a group three.
 template <int B8>
 __device__ __forceinline__ void tiled_stage_n64(const TiledCtx<4>& c, int ls, float16v (&acc)[2][8],
                                                 WPre2 (&pw)[2]) {
-  constexpr int B = B8 & 3;
-  constexpr int R1 = (B + 1) & 3;
-  constexpr int P1 = ((B8 + 1) >> 2) & 1;
-  constexpr int T1 = (B8 + 1) & 3;
-  constexpr int PN = ((B8 >> 2) + 1) & 1;
-  NVFP4_WAIT_VMCNT(B == 1 ? 6 : 4);
+  constexpr int S1 = ((B8 + 1) >> 1) & 1;   // pair slot of stage ls + 1
+  constexpr int TH1 = (B8 + 1) & 1;         // its place in the pair
+  constexpr int P1 = ((B8 + 1) >> 2) & 1;   // its group buffer
+  constexpr int T1 = (B8 + 1) & 3;          // its place in the group
+  constexpr int SN = ((B8 + 3) >> 1) & 1;   // slot of the pair copied here (odd B8)
+  constexpr int PN = ((B8 >> 2) + 1) & 1;   // buffer of the group copied here (B8 % 4 == 0)
+  constexpr int kPrev = (B8 & 1) ? ((B8 & 2) ? 0 : 2) : 8;
+  if (B8 & 1) NVFP4_WAIT_LGKM0();
+  NVFP4_WAIT_VMCNT(kPrev);
   stage_barrier();
   const int lane = c.lane;
-  const uint8_t* af = af_buf<B & 1>();
+  const uint8_t* af = af_buf<B8 & 1>();
   half8v av[2][8], wv[2][2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) av[0][i] = *(const half8v*)(af + (i * 4 + 0) * 1024 + lane * 16);
   __builtin_amdgcn_sched_barrier(0);
-  const ADecode dec0 = decode_a_load_g<R1, P1, T1>(2 * c.wave, lane);
-  const ADecode dec1 = decode_a_load_g<R1, P1, T1>(2 * c.wave + 1, lane);
+  const ADecode dec0 = decode_a_load_p<S1, TH1, P1, T1>(2 * c.wave, lane);
+  const ADecode dec1 = decode_a_load_p<S1, TH1, P1, T1>(2 * c.wave + 1, lane);
   __builtin_amdgcn_sched_barrier(0);
-  const WPre2& cur = pw[B & 1];
+  const WPre2& cur = pw[B8 & 1];
   half2v sw[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) sw[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.sb[j], 1.0f, false);
@@ -645,8 +590,8 @@ __device__ __forceinline__ void tiled_stage_n64(const TiledCtx<4>& c, int ls, fl
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[cu][j], av[cu][i], acc[j][i], 0, 0, 0);
-    if (jj < 2) code_copy_part<(B + 3) & 3>(c, ls + 3, jj);
-    if (B == 0 && jj == 2) group_copy<PN>(c, ls / kGroupStages + 1);
+    if (B8 & 1) pair_copy_part<SN>(c, (ls + 3) >> 1, jj);
+    if ((B8 & 3) == 0 && jj == 2) group_copy<PN>(c, ls / kGroupStages + 1);
     if (jj + 1 < 4) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) av[nx][i] = *(const half8v*)(af + (i * 4 + jj + 1) * 1024 + lane * 16);
@@ -654,10 +599,10 @@ __device__ __forceinline__ void tiled_stage_n64(const TiledCtx<4>& c, int ls, fl
       for (int j = 0; j < 2; ++j)
         wv[nx][j] = dequant8_f16(word_of(cur.cw[j], jj + 1), jj + 1 < 2 ? sw[j].xx : sw[j].yy);
     } else {
-      w_prefetch_n64<R1, P1, T1>(c, pw[(B + 1) & 1]);
+      w_prefetch_p<S1, TH1, P1, T1>(c, pw[(B8 + 1) & 1]);
     }
-    decode_a_step<(B + 1) & 1>(dec0, jj);
-    decode_a_step<(B + 1) & 1>(dec1, jj);
+    decode_a_step<(B8 + 1) & 1>(dec0, jj);
+    decode_a_step<(B8 + 1) & 1>(dec1, jj);
     // MFMA, copy, 2 VALU (x2); MFMA, read, 2 VALU (x8); MFMA, 3 VALU (x4);
     // MFMA, write (x2)
 #pragma unroll
@@ -903,6 +848,19 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
                      : w_scales + (int64_t)min(n0 + sr, N - 1) * row_scales;
   }
 
+  if constexpr (kGroups) {
+    // Pair copy k (0-3) of this wave: rows 16 (4 wave + k) + lane / 4, slot
+    // lane % 4 of the row's 64 bytes, which holds piece (lane % 4) ^
+    // pair_swz(row).
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int rr = 16 * (4 * wave + k) + (lane >> 2);
+      const int piece = (lane & 3) ^ pair_swz(rr);
+      c.gpa[k] = a_codes + (int64_t)min(m0 + rr, M - 1) * row_bytes + 16 * piece;
+      c.gpw[k] = w_codes + (int64_t)min(n0 + rr, N - 1) * row_bytes + 16 * piece;
+    }
+  }
+
   float16v acc[kJ][4];
 #pragma unroll
   for (int j = 0; j < kJ; ++j)
@@ -910,20 +868,18 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
     for (int i = 0; i < 4; ++i) acc[j][i] = float16v{};
 
   if constexpr (kGroups) {
-    // Prologue: scale group 0 and the codes of stages 0-2 in flight, then
-    // stage 0's A decoded and its W read.
+    // Prologue: scale group 0 and code pairs 0 and 1 in flight, then stage
+    // 0's A decoded and its W read.
     group_copy<0>(c, 0);
-    code_copy_part<0>(c, 0, 0);
-    code_copy_part<0>(c, 0, 1);
-    code_copy_part<1>(c, 1, 0);
-    code_copy_part<1>(c, 1, 1);
-    code_copy_part<2>(c, 2, 0);
-    code_copy_part<2>(c, 2, 1);
+#pragma unroll
+    for (int part = 0; part < 4; ++part) pair_copy_part<0>(c, 0, part);
+#pragma unroll
+    for (int part = 0; part < 4; ++part) pair_copy_part<1>(c, 1, part);
     NVFP4_WAIT_VMCNT(8);
     stage_barrier();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const ADecode d = decode_a_load_g<0, 0, 0>(2 * wave + q, lane);
+      const ADecode d = decode_a_load_p<0, 0, 0, 0>(2 * wave + q, lane);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) decode_a_step<0>(d, jj);
     }
@@ -933,7 +889,7 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc2[j][i] = float16v{};
     WPre2 pw[2];
-    w_prefetch_n64<0, 0, 0>(c, pw[0]);
+    w_prefetch_p<0, 0, 0, 0>(c, pw[0]);
     int ls = 0;
     for (; ls + 8 <= c.nst; ls += 8) {
       tiled_stage_n64<0>(c, ls, acc2, pw);
