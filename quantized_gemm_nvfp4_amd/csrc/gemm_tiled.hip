@@ -96,6 +96,14 @@ __device__ __forceinline__ void g2lds16(const void* g, void* l) {
 __device__ __forceinline__ void g2lds4(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((gbl_void_t)g, (lds_void_t)l, 4, 0, 0);
 }
+// The same 16-byte copy through a buffer resource.  While a global_load_lds
+// is in flight the compiler waits for every outstanding LDS access before
+// using any LDS read (it counts the copy as a possible LDS access); with
+// the buffer form it keeps exact counts, so an MFMA waits only for its own
+// operand.
+__device__ __forceinline__ void b2lds16(__amdgpu_buffer_rsrc_t r, uint32_t off, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)l, 16, off, 0, 0, 0);
+}
 
 // Tile (tm, tn) of tile index id: groups of kGroupM tile-rows, column-major
 // within a group.
@@ -190,8 +198,10 @@ struct TiledCtx {
   const uint8_t* ga[kFr];  // A code copy sources (row, piece) of this lane
   const uint8_t* gw[kFr];  // W code copy sources
   const uint8_t* gs[kFr];  // scale copy sources (A for copy slots 0-3, W for 4-7)
-  const uint8_t* gpa[4];   // pair copy sources of A and W (scale-group path)
-  const uint8_t* gpw[4];
+  // Scale-group path: buffer resources over the tile's rows of the A and W
+  // codes and scales, and this lane's offsets in them.
+  __amdgpu_buffer_rsrc_t rca, rcw, rsg[2];
+  uint32_t opa[4], opw[4], osg[2];
   int wave, lane, wm, wn, h, r32;
   int st0, nst;            // first K stage and number of stages of this workgroup
 };
@@ -487,7 +497,7 @@ __device__ __forceinline__ void group_copy(const TiledCtx<4>& c, int lg) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int vw = 2 * c.wave + q;
-    g2lds16(c.gs[q] + st * kScaleRow, sg_buf<P>() + (vw >> 2) * kGroupBytes + (vw & 3) * 1024);
+    b2lds16(c.rsg[q], c.osg[q] + st * kScaleRow, sg_buf<P>() + (vw >> 2) * kGroupBytes + (vw & 3) * 1024);
   }
 }
 
@@ -501,22 +511,35 @@ __device__ __forceinline__ void pair_copy_part(const TiledCtx<4>& c, int lq, int
   const int st = c.st0 + 2 * min(lq, c.nst / 2 - 1);
 #pragma unroll
   for (int k = 2 * (part & 1); k < 2 * (part & 1) + 2; ++k) {
-    if (part < 2) g2lds16(c.gpa[k] + st * kRowBytes, ap_slot<S>() + (4 * c.wave + k) * 1024);
-    else g2lds16(c.gpw[k] + st * kRowBytes, wp_slot<S>() + (4 * c.wave + k) * 1024);
+    if (part < 2) b2lds16(c.rca, c.opa[k] + st * kRowBytes, ap_slot<S>() + (4 * c.wave + k) * 1024);
+    else b2lds16(c.rcw, c.opw[k] + st * kRowBytes, wp_slot<S>() + (4 * c.wave + k) * 1024);
   }
 }
 
 // decode_a_load from pair slot S (stage TH of the pair) and group buffer P
-// (stage T of the group).
+// (stage T of the group).  The scale bytes stay raw until the first decode
+// step, so that nothing before the stage's first MFMA waits for these
+// reads (they are issued after that MFMA's operands).
+struct ADecodeRaw {
+  uint4 codes;
+  uint32_t sb;
+  int dst;
+};
+
 template <int S, int TH, int P, int T>
-__device__ __forceinline__ ADecode decode_a_load_p(int f, int lane) {
+__device__ __forceinline__ ADecodeRaw decode_a_load_p(int f, int lane) {
   const int r = 32 * f + (lane & 31), hh = lane >> 5;
-  ADecode d;
+  ADecodeRaw d;
   d.codes = *(const uint4*)(ap_slot<S>() + pair_piece_slot(r, 2 * TH + hh) * 16);
-  const uint32_t sb = *(const uint16_t*)(sg_buf<P>() + r * kGroupRow + T * kScaleRow + 2 * hh);
-  d.s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+  d.sb = *(const uint16_t*)(sg_buf<P>() + r * kGroupRow + T * kScaleRow + 2 * hh);
   d.dst = f * 4096 + lane * 16;
   return d;
+}
+
+template <int F>
+__device__ __forceinline__ void decode_a_step_raw(const ADecodeRaw& d, int jj) {
+  const half2v s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.sb, 1.0f, false);
+  *(half8v*)(af_buf<F>() + d.dst + jj * 1024) = dequant8_f16(word_of(d.codes, jj), jj < 2 ? s2.xx : s2.yy);
 }
 
 // Wave tile 256 (m) x 64 (n): every wave multiplies all eight 32-row A
@@ -572,8 +595,8 @@ __device__ __forceinline__ void tiled_stage_n64(const TiledCtx<4>& c, int ls, fl
 #pragma unroll
   for (int i = 0; i < 8; ++i) av[0][i] = *(const half8v*)(af + (i * 4 + 0) * 1024 + lane * 16);
   __builtin_amdgcn_sched_barrier(0);
-  const ADecode dec0 = decode_a_load_p<S1, TH1, P1, T1>(2 * c.wave, lane);
-  const ADecode dec1 = decode_a_load_p<S1, TH1, P1, T1>(2 * c.wave + 1, lane);
+  const ADecodeRaw dec0 = decode_a_load_p<S1, TH1, P1, T1>(2 * c.wave, lane);
+  const ADecodeRaw dec1 = decode_a_load_p<S1, TH1, P1, T1>(2 * c.wave + 1, lane);
   __builtin_amdgcn_sched_barrier(0);
   const WPre2& cur = pw[B8 & 1];
   half2v sw[2];
@@ -601,8 +624,8 @@ __device__ __forceinline__ void tiled_stage_n64(const TiledCtx<4>& c, int ls, fl
     } else {
       w_prefetch_p<S1, TH1, P1, T1>(c, pw[(B8 + 1) & 1]);
     }
-    decode_a_step<(B8 + 1) & 1>(dec0, jj);
-    decode_a_step<(B8 + 1) & 1>(dec1, jj);
+    decode_a_step_raw<(B8 + 1) & 1>(dec0, jj);
+    decode_a_step_raw<(B8 + 1) & 1>(dec1, jj);
     // MFMA, copy, 2 VALU (x2); MFMA, read, 2 VALU (x8); MFMA, 3 VALU (x4);
     // MFMA, write (x2)
 #pragma unroll
@@ -849,15 +872,28 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
   }
 
   if constexpr (kGroups) {
-    // Pair copy k (0-3) of this wave: rows 16 (4 wave + k) + lane / 4, slot
-    // lane % 4 of the row's 64 bytes, which holds piece (lane % 4) ^
-    // pair_swz(row).
+    // Buffer resources over the tile's rows (at most 256 x K/2 < 2^31 bytes:
+    // the host takes this path only for K < 2^24).  Pair copy k (0-3) of
+    // this wave: rows 16 (4 wave + k) + lane / 4, slot lane % 4 of the row's
+    // 64 bytes, which holds piece (lane % 4) ^ pair_swz(row).  Rows past M
+    // or N re-read the last row.
+    const int rows_a = min(TM, M - m0), rows_w = min(TN, N - n0);
+    c.rca = buffer_of(a_codes + (int64_t)m0 * row_bytes, (uint32_t)(rows_a * row_bytes));
+    c.rcw = buffer_of(w_codes + (int64_t)n0 * row_bytes, (uint32_t)(rows_w * row_bytes));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int rr = 16 * (4 * wave + k) + (lane >> 2);
       const int piece = (lane & 3) ^ pair_swz(rr);
-      c.gpa[k] = a_codes + (int64_t)min(m0 + rr, M - 1) * row_bytes + 16 * piece;
-      c.gpw[k] = w_codes + (int64_t)min(n0 + rr, N - 1) * row_bytes + 16 * piece;
+      c.opa[k] = (uint32_t)(min(rr, rows_a - 1) * row_bytes + 16 * piece);
+      c.opw[k] = (uint32_t)(min(rr, rows_w - 1) * row_bytes + 16 * piece);
+    }
+    const auto rsa = buffer_of(a_scales + (int64_t)m0 * row_scales, (uint32_t)(rows_a * row_scales));
+    const auto rsw = buffer_of(w_scales + (int64_t)n0 * row_scales, (uint32_t)(rows_w * row_scales));
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int vw = 2 * wave + q, sr = 64 * (vw & 3) + lane;
+      c.rsg[q] = vw < 4 ? rsa : rsw;
+      c.osg[q] = (uint32_t)(min(sr, (vw < 4 ? rows_a : rows_w) - 1) * row_scales);
     }
   }
 
@@ -879,9 +915,9 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
     stage_barrier();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const ADecode d = decode_a_load_p<0, 0, 0, 0>(2 * wave + q, lane);
+      const ADecodeRaw d = decode_a_load_p<0, 0, 0, 0>(2 * wave + q, lane);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) decode_a_step<0>(d, jj);
+      for (int jj = 0; jj < 4; ++jj) decode_a_step_raw<0>(d, jj);
     }
     float16v acc2[2][8];
 #pragma unroll
@@ -1061,7 +1097,9 @@ TiledPlan plan_tiled(int64_t M, int64_t N, int64_t K, bool allow_split) {
   const int tiles = p.tiles_m * p.tiles_n;
   p.full_tiles = tiles;
   p.splits = 1;
-  p.groups = K % (kGroupStages * TK) == 0;
+  // Scale groups need K % 256 == 0; their buffer offsets cover a tile's
+  // rows, 256 x K/2 bytes, which must stay below 2^31.
+  p.groups = K % (kGroupStages * TK) == 0 && K < ((int64_t)1 << 24);
   p.part_bytes = 0;
   if (!allow_split) return p;
   const int cus = device_cus();
