@@ -258,7 +258,8 @@ nvfp4_status int4g_quantize(const void* w_bf16, int64_t N, int64_t K, int64_t gr
  * weight-only GPU kernels of the same page's method chart.  Each group's
  * integer-weighted sum is taken in fp32, then scaled once by its s16.
  * Any M >= 1: M <= 16 streams the weight once (K <= 2^24; larger K take
- * the simple kernel); larger M runs MFMA tiles.
+ * the simple kernel); larger M runs MFMA tiles (K < 2^22; larger K take the
+ * simple kernel, and NVFP4_ALGO_TILED returns NVFP4_ERR_UNSUPPORTED).
  */
 nvfp4_status int4g_gemv(const void* x_bf16, const uint8_t* q, const void* scales_fp16,
                         void* out_bf16, int64_t M, int64_t N, int64_t K, int64_t group,

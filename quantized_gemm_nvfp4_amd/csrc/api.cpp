@@ -60,6 +60,9 @@ nvfp4_status check_disjoint(const Range* outs, int nout, const Range* ins, int n
 }
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
+// The INT4 tiled kernel addresses a tile's rows of x (128 x 2K bytes) with
+// 32-bit buffer offsets.
+constexpr int64_t kInt4TiledKLimit = (int64_t)1 << 22;
 // The weight-streaming kernels address a workgroup's weight rows and the
 // whole activation through buffer resources with 32-bit byte ranges (at
 // most 64 rows x K values); 2^24 keeps every range far below 2^31.
@@ -411,11 +414,13 @@ nvfp4_status int4g_gemv_ex(const void* x_bf16, const uint8_t* q, const void* sca
   if (nvfp4_status s = check_disjoint(outs, 1, ins, 3)) return s;
   if (algo == NVFP4_ALGO_AUTO)
     algo = (K == 0) ? NVFP4_ALGO_SIMPLE
-                    : (M <= 16 ? (K <= kDecodeMaxK ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE) : NVFP4_ALGO_TILED);
+                    : (M <= 16 ? (K <= kDecodeMaxK ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE)
+                               : (K < kInt4TiledKLimit ? NVFP4_ALGO_TILED : NVFP4_ALGO_SIMPLE));
   hipStream_t st = (hipStream_t)stream;
   switch (algo) {
     case NVFP4_ALGO_TILED:
-      if (K == 0) return fail(NVFP4_ERR_UNSUPPORTED, "tiled kernel needs K > 0");
+      if (K == 0 || K >= kInt4TiledKLimit)
+        return fail(NVFP4_ERR_UNSUPPORTED, "tiled kernel needs 0 < K < 2^22 (K=%lld)", (long long)K);
       return hip_status(nvfp4k::launch_int4g_gemm_tiled(x_bf16, q, scales_fp16, out_bf16, M, N, K, st),
                         "int4g_gemv tiled launch");
     case NVFP4_ALGO_DECODE:

@@ -296,9 +296,14 @@ namespace {
 template <int B> __device__ __forceinline__ uint8_t* i4_slot() { return B == 0 ? g_i4s0 : (B == 1 ? g_i4s1 : g_i4s2); }
 
 struct I4Ctx {
-  const uint16_t* gx[8];   // x copy sources of this lane
+  // Copies go through buffer resources over the tile's rows of x and of the
+  // codes (with a global_load_lds in flight the compiler waits for every
+  // outstanding LDS access before using any LDS read; with the buffer form
+  // it keeps exact counts).
+  __amdgpu_buffer_rsrc_t rx, rq;
+  uint32_t ox[8];          // x copy offsets of this lane
   int lds_x[8];
-  const uint8_t* gq[4];    // weight copy sources
+  uint32_t oq[4];          // weight copy offsets
   int lds_q[4];
   const uint16_t* gsc[4];  // group-scale rows of this lane's 4 output columns
   uint32_t scr[kIRing][4]; // group scales per ring slot (raw fp16)
@@ -312,10 +317,10 @@ __device__ __forceinline__ void i4_issue(I4Ctx& c, int g) {
   uint8_t* base = i4_slot<B>();
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_global_load_lds((gbl_void_t)(c.gx[i] + (int64_t)g * 128), (lds_void_t)(base + c.lds_x[i]), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rx, (lds_void_t)(base + c.lds_x[i]), 16, c.ox[i] + 256u * g, 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_global_load_lds((gbl_void_t)(c.gq[i] + (int64_t)g * 64), (lds_void_t)(base + c.lds_q[i]), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rq, (lds_void_t)(base + c.lds_q[i]), 16, c.oq[i] + 64u * g, 0, 0, 0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) c.scr[B][j] = c.gsc[j][g];
 }
@@ -398,18 +403,24 @@ __global__ __launch_bounds__(256, 1) void int4g_gemm_tiled_kernel(const uint16_t
   c.wn = wave & 1;
   // x: 4 fragments x 8 steps; wave w copies steps 2w, 2w+1 of every fragment.
   // Lane l of region (f, jj): row 32f + l%32, values 64(l/32) + 8jj .. +8.
+  // Offsets are relative to the tile's first row (at most 128 x 2K bytes of
+  // x and 256 x K/2 of codes: the host takes this kernel only for K < 2^22).
+  // Rows past M or N re-read the last row.
+  const int rows_x = min(IT_M, M - m0), rows_q = min(IT_N, N - n0);
+  c.rx = buffer_of(x + (int64_t)m0 * K, (uint32_t)rows_x * (uint32_t)K * 2u);
+  c.rq = buffer_of(q + (int64_t)n0 * (K / 2), (uint32_t)rows_q * (uint32_t)(K / 2));
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int f = i >> 1, jj = 2 * wave + (i & 1);
-    const int row = min(m0 + 32 * f + (lane & 31), M - 1);
-    c.gx[i] = x + (int64_t)row * K + 64 * (lane >> 5) + 8 * jj;
+    const int row = min(32 * f + (lane & 31), rows_x - 1);
+    c.ox[i] = 2u * ((uint32_t)row * (uint32_t)K + 64u * (lane >> 5) + 8u * jj);
     c.lds_x[i] = (f * 8 + jj) * 1024;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int qd = 4 * wave + i, f = qd >> 1, hs = qd & 1;
-    const int row = min(n0 + 32 * f + (lane & 31), N - 1);
-    c.gq[i] = q + (int64_t)row * (K / 2) + 32 * (lane >> 5) + 16 * hs;
+    const int row = min(32 * f + (lane & 31), rows_q - 1);
+    c.oq[i] = (uint32_t)row * (uint32_t)(K / 2) + 32u * (lane >> 5) + 16u * hs;
     c.lds_q[i] = kXBytes + qd * 1024;
   }
 #pragma unroll

@@ -139,6 +139,15 @@ def test_decode_k_limit():
     assert q.lib().int4g_gemv_ex(far[0], far[1], far[2], far[3], 4, 8, K, 128, q.ALGO_DECODE, None) == UNSUP
 
 
+def test_int4_tiled_k_limit():
+    # the INT4 tiled kernel addresses a tile's rows with 32-bit offsets: an
+    # explicit tiled request with K >= 2^22 is refused before any device work
+    far = [P(k << 38) for k in range(1, 5)]
+    K = 1 << 22
+    assert q.lib().int4g_gemv_ex(*far, 32, 8, K, 128, q.ALGO_TILED, None) == UNSUP
+    assert "2^22" in _err()
+
+
 def test_int4_validation():
     lib = q.lib()
     assert lib.int4g_quantize(A, 8, 256, 64, B, C, None) == UNSUP      # group must be 128
