@@ -152,7 +152,9 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
 /* Kernel choice for nvfp4_gemm_ex / int4g_gemv_ex. */
 typedef enum nvfp4_algo {
   NVFP4_ALGO_AUTO = 0,    /* what nvfp4_gemm / int4g_gemv pick */
-  NVFP4_ALGO_TILED = 1,   /* the LDS-staged MFMA tile kernel (any M) */
+  NVFP4_ALGO_TILED = 1,   /* the LDS-staged MFMA tile kernel (any M; nvfp4_gemm:
+                             K % 128 == 0 and K < 2^24, int4g_gemv: K < 2^22;
+                             else NVFP4_ERR_UNSUPPORTED) */
   NVFP4_ALGO_DECODE = 2,  /* the weight-streaming kernel (M <= 16, K % 128 == 0
                              and K <= 2^24 only; else NVFP4_ERR_UNSUPPORTED) */
   NVFP4_ALGO_SIMPLE = 3   /* one output per thread, fp32 FMA (any shape) */
@@ -175,7 +177,7 @@ nvfp4_status nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, cons
  * workspace: >= nvfp4_gemm_workspace_bytes(M, N, K) bytes of device memory
  * for the current device, 256-byte aligned, no initialization, not shared
  * with a concurrent call, not overlapping any argument.  The size is 0 when
- * no split applies (M <= 16, K % 128 != 0, whole rounds); with workspace
+ * no split applies (M <= 16, K % 128 != 0, K >= 2^24, whole rounds); with workspace
  * NULL or workspace_bytes below the size, the call runs as nvfp4_gemm_ex.
  */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -193,7 +195,7 @@ nvfp4_status nvfp4_gemm_ws(const uint8_t* a_codes, const uint8_t* a_scales, cons
  * 4-byte aligned, no initialization, not overlapping any argument.  Every
  * slot is written with a bf16 magnitude pattern (sign cleared) and the
  * largest of them is that of max|out[m, n]|: the tiled kernel (M > 16,
- * K % 128 == 0) writes one slot per 256 x 256 output tile from its
+ * K % 128 == 0, K < 2^24) writes one slot per 256 x 256 output tile from its
  * epilogue; other shapes run a separate pass over out.  N % 16 == 0 (the
  * output is quantized along N); workspace as for nvfp4_gemm_ws.
  */

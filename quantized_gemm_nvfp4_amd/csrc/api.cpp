@@ -67,6 +67,9 @@ constexpr int64_t kInt4TiledKLimit = (int64_t)1 << 22;
 // whole activation through buffer resources with 32-bit byte ranges (at
 // most 64 rows x K values); 2^24 keeps every range far below 2^31.
 constexpr int64_t kDecodeMaxK = int64_t(1) << 24;
+// The NVFP4 tiled kernel addresses a tile's rows (256 x K/2 bytes) with
+// 32-bit buffer offsets.
+constexpr int64_t kTiledKLimit = int64_t(1) << 24;
 
 #define REQUIRE_PTR(p)                                                               \
   do {                                                                               \
@@ -101,7 +104,8 @@ nvfp4_status check_products(int64_t M, int64_t N, int64_t K) {
 int auto_algo(int64_t M, int64_t K) {
   const bool k128 = (K % 128) == 0 && K > 0;
   return !k128 ? NVFP4_ALGO_SIMPLE
-               : (M <= 16 ? (K <= kDecodeMaxK ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE) : NVFP4_ALGO_TILED);
+               : (M <= 16 ? (K <= kDecodeMaxK ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE)
+                          : (K < kTiledKLimit ? NVFP4_ALGO_TILED : NVFP4_ALGO_SIMPLE));
 }
 
 // Slots nvfp4_gemm_amax writes for AUTO's kernel choice: one per output tile
@@ -164,7 +168,8 @@ nvfp4_status gemm_impl(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   }
   switch (algo) {
     case NVFP4_ALGO_TILED:
-      if (!k128) return fail(NVFP4_ERR_UNSUPPORTED, "tiled kernel needs K %% 128 == 0 and K > 0 (K=%lld)", (long long)K);
+      if (!k128 || K >= kTiledKLimit)
+        return fail(NVFP4_ERR_UNSUPPORTED, "tiled kernel needs K %% 128 == 0 and 0 < K < 2^24 (K=%lld)", (long long)K);
       if (lora_t)
         return hip_status(nvfp4k::launch_nvfp4_gemm_tiled_lora(a_codes, a_scales, a_gscale, w_codes, w_scales,
                                                                w_gscale, out_bf16, M, N, K, lora_t, lora_up, r, st),
@@ -267,7 +272,7 @@ nvfp4_status nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, cons
 }
 
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 16 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  if (M <= 16 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K >= kTiledKLimit) return 0;
   return (size_t)nvfp4k::nvfp4_gemm_tiled_workspace_bytes(M, N, K);
 }
 

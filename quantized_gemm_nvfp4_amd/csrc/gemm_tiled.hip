@@ -88,21 +88,18 @@ static_assert(kMinPartStages >= kGroupStages, "every split part must hold a whol
 constexpr int64_t kPartFloats = (int64_t)TM * TN;    // one tile's fp32 accumulators
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
-typedef __attribute__((address_space(1))) void* gbl_void_t;
 
-__device__ __forceinline__ void g2lds16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t)g, (lds_void_t)l, 16, 0, 0);
-}
-__device__ __forceinline__ void g2lds4(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t)g, (lds_void_t)l, 4, 0, 0);
-}
-// The same 16-byte copy through a buffer resource.  While a global_load_lds
-// is in flight the compiler waits for every outstanding LDS access before
-// using any LDS read (it counts the copy as a possible LDS access); with
-// the buffer form it keeps exact counts, so an MFMA waits only for its own
-// operand.
+// Global -> LDS copies (LDS DMA) through buffer resources: lane i's 16 (4)
+// bytes at offset off land at l + 16 i (4 i).  The buffer form, not
+// global_load_lds: while a global_load_lds is in flight the compiler waits
+// for every outstanding LDS access before using any LDS read (it counts the
+// copy as a possible LDS access); with the buffer form it keeps exact
+// counts, so an MFMA waits only for its own operand.
 __device__ __forceinline__ void b2lds16(__amdgpu_buffer_rsrc_t r, uint32_t off, void* l) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)l, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void b2lds4(__amdgpu_buffer_rsrc_t r, uint32_t off, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)l, 4, off, 0, 0, 0);
 }
 
 // Tile (tm, tn) of tile index id: groups of kGroupM tile-rows, column-major
@@ -195,13 +192,11 @@ struct TiledCtx {
   static constexpr int kFr = 8 / kW;       // copy slots and A fragments per wave
   static constexpr int kJ = kW == 4 ? 4 : 2;  // W fragments per wave
   static constexpr int kCopies = 3 * kFr;  // copy instructions per wave per stage
-  const uint8_t* ga[kFr];  // A code copy sources (row, piece) of this lane
-  const uint8_t* gw[kFr];  // W code copy sources
-  const uint8_t* gs[kFr];  // scale copy sources (A for copy slots 0-3, W for 4-7)
-  // Scale-group path: buffer resources over the tile's rows of the A and W
-  // codes and scales, and this lane's offsets in them.
-  __amdgpu_buffer_rsrc_t rca, rcw, rsg[2];
-  uint32_t opa[4], opw[4], osg[2];
+  // Buffer resources over the tile's rows of the A and W codes, and of the
+  // scales each copy slot moves (A for copy slots 0-3, W for 4-7).
+  __amdgpu_buffer_rsrc_t rca, rcw, rsq[kFr];
+  uint32_t oa[kFr], ow[kFr], os[kFr];   // per-stage path: this lane's copy offsets
+  uint32_t opa[4], opw[4];               // scale-group path: pair copy offsets
   int wave, lane, wm, wn, h, r32;
   int st0, nst;            // first K stage and number of stages of this workgroup
 };
@@ -216,9 +211,9 @@ __device__ __forceinline__ void tiled_issue(const TiledCtx<kW>& c, int ls) {
 #pragma unroll
   for (int q = 0; q < kFr; ++q) {
     const int vw = kFr * c.wave + q;
-    g2lds16(c.ga[q] + st * kRowBytes, a_slot<B>() + vw * 1024);
-    g2lds16(c.gw[q] + st * kRowBytes, w_slot<B>() + vw * 1024);
-    g2lds4(c.gs[q] + st * kScaleRow, s_slot<B>() + (vw >> 2) * kScaleBytes + (vw & 3) * 256);
+    b2lds16(c.rca, c.oa[q] + st * kRowBytes, a_slot<B>() + vw * 1024);
+    b2lds16(c.rcw, c.ow[q] + st * kRowBytes, w_slot<B>() + vw * 1024);
+    b2lds4(c.rsq[q], c.os[q] + st * kScaleRow, s_slot<B>() + (vw >> 2) * kScaleBytes + (vw & 3) * 256);
   }
 }
 
@@ -377,9 +372,9 @@ __device__ __forceinline__ void tiled_copy_part(const TiledCtx<4>& c, int ls, in
 #pragma unroll
   for (int e = 2 * part; e < 2 * part + 2; ++e) {
     const int q = e / 3, kind = e % 3, vw = 2 * c.wave + q;
-    if (kind == 0) g2lds16(c.ga[q] + st * kRowBytes, a_slot<B>() + vw * 1024);
-    else if (kind == 1) g2lds16(c.gw[q] + st * kRowBytes, w_slot<B>() + vw * 1024);
-    else g2lds4(c.gs[q] + st * kScaleRow, s_slot<B>() + (vw >> 2) * kScaleBytes + (vw & 3) * 256);
+    if (kind == 0) b2lds16(c.rca, c.oa[q] + st * kRowBytes, a_slot<B>() + vw * 1024);
+    else if (kind == 1) b2lds16(c.rcw, c.ow[q] + st * kRowBytes, w_slot<B>() + vw * 1024);
+    else b2lds4(c.rsq[q], c.os[q] + st * kScaleRow, s_slot<B>() + (vw >> 2) * kScaleBytes + (vw & 3) * 256);
   }
 }
 
@@ -497,7 +492,7 @@ __device__ __forceinline__ void group_copy(const TiledCtx<4>& c, int lg) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int vw = 2 * c.wave + q;
-    b2lds16(c.rsg[q], c.osg[q] + st * kScaleRow, sg_buf<P>() + (vw >> 2) * kGroupBytes + (vw & 3) * 1024);
+    b2lds16(c.rsq[q], c.os[q] + st * kScaleRow, sg_buf<P>() + (vw >> 2) * kGroupBytes + (vw & 3) * 1024);
   }
 }
 
@@ -854,32 +849,19 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
   c.r32 = lane & 31;
   c.st0 = st0;
   c.nst = st1 - st0;
-#pragma unroll
-  for (int q = 0; q < kFr; ++q) {
-    // Code copies of copy slot vw: lane l holds row 32 vw + l/2 and piece
-    // (l%2) ^ piece_swz(row), so it lands at piece_slot(row, piece).  Rows
-    // past M or N re-read the last row: those results are never stored.
-    // Scale copies: slots 0-3 copy A's rows 64 (vw%4) + lane, 4-7 W's; laid
-    // out [operand][row][4 bytes].
-    const int vw = kFr * wave + q;
-    const int rr = 32 * vw + (lane >> 1);
-    const int piece = (lane & 1) ^ piece_swz(rr);
-    c.ga[q] = a_codes + (int64_t)min(m0 + rr, M - 1) * row_bytes + 16 * piece;
-    c.gw[q] = w_codes + (int64_t)min(n0 + rr, N - 1) * row_bytes + 16 * piece;
-    const int sr = 64 * (vw & 3) + lane;
-    c.gs[q] = vw < 4 ? a_scales + (int64_t)min(m0 + sr, M - 1) * row_scales
-                     : w_scales + (int64_t)min(n0 + sr, N - 1) * row_scales;
-  }
-
+  // Buffer resources over the tile's rows (at most 256 x K/2 < 2^31 bytes:
+  // the tiled kernel takes K < 2^24).  Rows past M or N re-read the last
+  // row: those results are never stored.
+  const int rows_a = min(TM, M - m0), rows_w = min(TN, N - n0);
+  c.rca = buffer_of(a_codes + (int64_t)m0 * row_bytes, (uint32_t)(rows_a * row_bytes));
+  c.rcw = buffer_of(w_codes + (int64_t)n0 * row_bytes, (uint32_t)(rows_w * row_bytes));
+  const auto rsa = buffer_of(a_scales + (int64_t)m0 * row_scales, (uint32_t)(rows_a * row_scales));
+  const auto rsw = buffer_of(w_scales + (int64_t)n0 * row_scales, (uint32_t)(rows_w * row_scales));
   if constexpr (kGroups) {
-    // Buffer resources over the tile's rows (at most 256 x K/2 < 2^31 bytes:
-    // the host takes this path only for K < 2^24).  Pair copy k (0-3) of
-    // this wave: rows 16 (4 wave + k) + lane / 4, slot lane % 4 of the row's
-    // 64 bytes, which holds piece (lane % 4) ^ pair_swz(row).  Rows past M
-    // or N re-read the last row.
-    const int rows_a = min(TM, M - m0), rows_w = min(TN, N - n0);
-    c.rca = buffer_of(a_codes + (int64_t)m0 * row_bytes, (uint32_t)(rows_a * row_bytes));
-    c.rcw = buffer_of(w_codes + (int64_t)n0 * row_bytes, (uint32_t)(rows_w * row_bytes));
+    // Pair copy k (0-3) of this wave: rows 16 (4 wave + k) + lane / 4, slot
+    // lane % 4 of the row's 64 bytes, which holds piece (lane % 4) ^
+    // pair_swz(row).  Scale groups: copy slot vw = 2 wave + q moves rows
+    // 64 (vw % 4) + lane of operand vw / 4.
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int rr = 16 * (4 * wave + k) + (lane >> 2);
@@ -887,13 +869,27 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
       c.opa[k] = (uint32_t)(min(rr, rows_a - 1) * row_bytes + 16 * piece);
       c.opw[k] = (uint32_t)(min(rr, rows_w - 1) * row_bytes + 16 * piece);
     }
-    const auto rsa = buffer_of(a_scales + (int64_t)m0 * row_scales, (uint32_t)(rows_a * row_scales));
-    const auto rsw = buffer_of(w_scales + (int64_t)n0 * row_scales, (uint32_t)(rows_w * row_scales));
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int vw = 2 * wave + q, sr = 64 * (vw & 3) + lane;
-      c.rsg[q] = vw < 4 ? rsa : rsw;
-      c.osg[q] = (uint32_t)(min(sr, (vw < 4 ? rows_a : rows_w) - 1) * row_scales);
+      c.rsq[q] = vw < 4 ? rsa : rsw;
+      c.os[q] = (uint32_t)(min(sr, (vw < 4 ? rows_a : rows_w) - 1) * row_scales);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kFr; ++q) {
+      // Code copies of copy slot vw: lane l holds row 32 vw + l/2 and piece
+      // (l%2) ^ piece_swz(row), so it lands at piece_slot(row, piece).
+      // Scale copies: slots 0-3 copy A's rows 64 (vw%4) + lane, 4-7 W's;
+      // laid out [operand][row][4 bytes].
+      const int vw = kFr * wave + q;
+      const int rr = 32 * vw + (lane >> 1);
+      const int piece = (lane & 1) ^ piece_swz(rr);
+      c.oa[q] = (uint32_t)(min(rr, rows_a - 1) * row_bytes + 16 * piece);
+      c.ow[q] = (uint32_t)(min(rr, rows_w - 1) * row_bytes + 16 * piece);
+      const int sr = 64 * (vw & 3) + lane;
+      c.rsq[q] = vw < 4 ? rsa : rsw;
+      c.os[q] = (uint32_t)(min(sr, (vw < 4 ? rows_a : rows_w) - 1) * row_scales);
     }
   }
 

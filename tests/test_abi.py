@@ -139,6 +139,17 @@ def test_decode_k_limit():
     assert q.lib().int4g_gemv_ex(far[0], far[1], far[2], far[3], 4, 8, K, 128, q.ALGO_DECODE, None) == UNSUP
 
 
+def test_nvfp4_tiled_k_limit():
+    # the NVFP4 tiled kernel addresses a tile's rows with 32-bit offsets: an
+    # explicit tiled request with K >= 2^24 is refused, no workspace is sized
+    far = [P(k << 40) for k in range(1, 8)]
+    K = 1 << 24
+    assert q.lib().nvfp4_gemm_ex(*far, 32, 16, K, q.ALGO_TILED, None) == UNSUP
+    assert "2^24" in _err()
+    assert q.lib().nvfp4_gemm_workspace_bytes(4096, 4096, K) == 0
+    assert q.lib().nvfp4_gemm_workspace_bytes(4096, 4096 + 256, K - 128) > 0
+
+
 def test_int4_tiled_k_limit():
     # the INT4 tiled kernel addresses a tile's rows with 32-bit offsets: an
     # explicit tiled request with K >= 2^22 is refused before any device work
