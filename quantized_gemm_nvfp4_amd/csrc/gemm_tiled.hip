@@ -792,6 +792,87 @@ __device__ __forceinline__ void lora_epilogue(float16v (&acc)[TiledCtx<kW>::kJ][
   }
 }
 
+// Low-rank branch for the 256 x 64 wave tiles of the scale-group path.  The
+// accumulators live in the accumulation registers, which vector
+// instructions cannot scale in place, so instead of g_a g_w acc + L_up T^T
+// the tile computes g_a g_w (L_up (T / (g_a g_w))^T + acc): this function
+// runs first, on the zeroed accumulators, before the product's main loop
+// (the decoded-A buffers are still free), and the store multiplies by
+// g_a g_w (tscale = 1 / (g_a g_w)).  With g_a g_w = 0 the caller skips the
+// product and passes tscale = 1 (store multiplier 1).  T is staged as bf16
+// hi + lo parts as in lora_epilogue, one thread per row of the tile (256 T
+// rows and 256 L_up rows per 32-rank chunk).
+__device__ __forceinline__ void lora_branch_n64(float16v (&acc)[2][8], float tscale,
+                                                const float* __restrict__ lora_t,
+                                                const uint16_t* __restrict__ lora_up, int r, int M, int N, int m0,
+                                                int n0, int wave, int h, int r32) {
+  const auto tr = buffer_of(lora_t, (uint32_t)M * (uint32_t)r * 4u);
+  const auto ur = buffer_of(lora_up, (uint32_t)N * (uint32_t)r * 2u);
+  uint4* st = (uint4*)g_af0;      // [256 rows][8 pieces]
+  uint4* su = (uint4*)g_af1;      // [256 rows][4 pieces]
+  const int srow = threadIdx.x;
+  for (int c0 = 0; c0 < r; c0 += 32) {
+    __syncthreads();              // previous users of the buffers are done
+    {
+      const uint32_t m = (uint32_t)(m0 + srow), n = (uint32_t)(n0 + srow);
+      uint4 tv[8], uv[4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t k = (uint32_t)(c0 + 4 * e);
+        tv[e] = buffer_load16(tr, m < (uint32_t)M && k < (uint32_t)r ? 4u * (m * r + k) : kBufferOob);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = (uint32_t)(c0 + 8 * e);
+        uv[e] = buffer_load16(ur, n < (uint32_t)N && k < (uint32_t)r ? 2u * (n * r + k) : kBufferOob);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 t0 = tv[2 * q], t1 = tv[2 * q + 1];
+        const float f[8] = {__uint_as_float(t0.x) * tscale, __uint_as_float(t0.y) * tscale,
+                            __uint_as_float(t0.z) * tscale, __uint_as_float(t0.w) * tscale,
+                            __uint_as_float(t1.x) * tscale, __uint_as_float(t1.y) * tscale,
+                            __uint_as_float(t1.z) * tscale, __uint_as_float(t1.w) * tscale};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const uint32_t h0 = f32_to_bf16_rne(f[2 * x]), h1 = f32_to_bf16_rne(f[2 * x + 1]);
+          const uint32_t l0 = f32_to_bf16_rne(f[2 * x] - bf16_bits_to_f32(h0));
+          const uint32_t l1 = f32_to_bf16_rne(f[2 * x + 1] - bf16_bits_to_f32(h1));
+          hi[x] = h0 | (h1 << 16);
+          lo[x] = l0 | (l1 << 16);
+        }
+        st[srow * 8 + ((2 * q) ^ (srow & 7))] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        st[srow * 8 + ((2 * q + 1) ^ (srow & 7))] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        su[srow * 4 + (q ^ (srow & 3))] = uv[q];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (c0 + 16 * kk >= r) break;
+      const int q = 2 * kk + h;
+      short8v up[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = 64 * wave + 32 * j + r32;
+        up[j] = __builtin_bit_cast(short8v, su[col * 4 + (q ^ (col & 3))]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 32 * i + r32;
+        const short8v hi = __builtin_bit_cast(short8v, st[row * 8 + ((2 * q) ^ (row & 7))]);
+        const short8v lo = __builtin_bit_cast(short8v, st[row * 8 + ((2 * q + 1) ^ (row & 7))]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(up[j], hi, acc[j][i], 0, 0, 0);
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(up[j], lo, acc[j][i], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
 // Grid: full_tiles whole tiles, then (tiles - full_tiles) x splits K parts.
 // Whole tiles are visited in an XCD-aware order when full_tiles % 8 == 0.
 // Part p of leftover tile t takes stages [p nst / S, (p + 1) nst / S) and
@@ -814,6 +895,7 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
     uint32_t* __restrict__ amax) {
   static_assert(!kAmax || (kW == 4 && !kLora), "amax slots: 4-wave kernel without the low-rank branch");
   static_assert(!kGroups || kW == 4, "scale groups: 4-wave kernel");
+  static_assert(!kLora || kW == 8 || kGroups, "low-rank branch: 8-wave kernel or the scale-group path");
   using Ctx = TiledCtx<kW>;
   constexpr int kFr = Ctx::kFr, kJ = Ctx::kJ;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -900,6 +982,19 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
     for (int i = 0; i < 4; ++i) acc[j][i] = float16v{};
 
   if constexpr (kGroups) {
+    float16v acc2[2][8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc2[j][i] = float16v{};
+    // With the low-rank branch and g_a g_w = 0 the product adds nothing: it
+    // is skipped, and the branch alone is stored (store multiplier 1).
+    const float gg = (*a_g) * (*w_g);
+    const float gmul = kLora && gg == 0.f ? 1.f : gg;
+    if constexpr (kLora) {
+      lora_branch_n64(acc2, 1.f / gmul, lora_t, lora_up, r, M, N, m0, n0, wave, c.h, c.r32);
+      __syncthreads();            // the decoded-A buffers are free again
+    }
     // Prologue: scale group 0 and code pairs 0 and 1 in flight, then stage
     // 0's A decoded and its W read.
     group_copy<0>(c, 0);
@@ -915,14 +1010,9 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) decode_a_step_raw<0>(d, jj);
     }
-    float16v acc2[2][8];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc2[j][i] = float16v{};
     WPre2 pw[2];
     w_prefetch_p<0, 0, 0, 0>(c, pw[0]);
-    int ls = 0;
+    int ls = kLora && gg == 0.f ? c.nst : 0;
     for (; ls + 8 <= c.nst; ls += 8) {
       tiled_stage_n64<0>(c, ls, acc2, pw);
       tiled_stage_n64<1>(c, ls + 1, acc2, pw);
@@ -956,13 +1046,12 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
         }
       return;
     }
-    const float gg = (*a_g) * (*w_g);
     uint32_t mx = 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        mx = max(mx, store_frag(acc2[j][i], gg, out, M, N, m0 + 32 * i + r32, n0 + 64 * wave + 32 * j, h));
+        mx = max(mx, store_frag(acc2[j][i], gmul, out, M, N, m0 + 32 * i + r32, n0 + 64 * wave + 32 * j, h));
     if (kAmax) {
       __shared__ uint32_t red2[4];
       const uint32_t m = block_max_u32<4>(mx, red2);
@@ -1171,10 +1260,20 @@ hipError_t launch_nvfp4_gemm_tiled_lora(const uint8_t* ac, const uint8_t* as, co
                                         const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
                                         int64_t K, const float* lora_t, const void* lora_up, int64_t r,
                                         hipStream_t stream) {
+  // The 4-wave scale-group kernel for grids of at least half a round of
+  // tiles; a lone tile runs faster on the 8-wave kernel (two waves per SIMD
+  // hide more latency: 28 vs 34 us for 6 tiles, 300 x 700 x 1024).
   const TiledPlan p = plan_tiled(M, N, K, false);
-  hipLaunchKernelGGL((nvfp4_gemm_tiled_kernel<8, true>), dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(512), 0, stream,
-                     ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n,
-                     p.tiles_m * p.tiles_n, 1, nullptr, lora_t, (const uint16_t*)lora_up, (int)r, nullptr);
+  const int tiles = p.tiles_m * p.tiles_n;
+  if (p.groups && 2 * tiles >= device_cus() &&
+      ((reinterpret_cast<uintptr_t>(as) | reinterpret_cast<uintptr_t>(ws)) & 15) == 0)
+    hipLaunchKernelGGL((nvfp4_gemm_tiled_kernel<4, true, false, true>), dim3((unsigned)tiles), dim3(256), 0, stream,
+                       ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n, tiles, 1,
+                       nullptr, lora_t, (const uint16_t*)lora_up, (int)r, nullptr);
+  else
+    hipLaunchKernelGGL((nvfp4_gemm_tiled_kernel<8, true>), dim3((unsigned)tiles), dim3(512), 0, stream, ac, as, ag,
+                       wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, p.tiles_m, p.tiles_n, tiles, 1, nullptr,
+                       lora_t, (const uint16_t*)lora_up, (int)r, nullptr);
   return hipGetLastError();
 }
 

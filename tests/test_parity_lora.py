@@ -106,7 +106,8 @@ def gpu_gemm_lora(a, w, t, up_bits, algo):
 
 @pytest.mark.parametrize("M,N,K,r", [(1, 40, 128, 8), (2, 33, 256, 16), (4, 40, 2176, 16), (5, 70, 512, 32),
                                      (16, 64, 384, 128), (9, 97, 1152, 24),
-                                     (130, 257, 1024, 32), (300, 200, 256, 64), (64, 96, 144, 8)])
+                                     (130, 257, 1024, 32), (300, 200, 256, 64), (64, 96, 144, 8),
+                                     (2048, 4096, 512, 32), (2100, 4100, 768, 24)])
 def test_gemm_lora(M, N, K, r):
     # T is a seeded fp32 input with full mantissas, so the epilogue's
     # two-part bf16 split of T is exercised.
@@ -147,6 +148,33 @@ def test_gemm_lora_branch_only():
     ref = F.bf16_round(t.astype(np.float64) @ F.bf16_from_bits(up).astype(np.float64).T)
     ok, rl, rr = Mx.check_output(y, ref)
     assert ok, f"rel_l2={rl:.3e} row_ratio={rr:.3e}"
+
+
+@pytest.mark.parametrize("zero", ["x", "w"])
+def test_gemm_lora_zero_global_scale(zero):
+    # An all-zero activation or weight has global scale 0, so the product
+    # term vanishes and the output is the branch alone.  At 128 tiles the
+    # tiled kernel adds the branch to its unscaled accumulators as
+    # L_up (T / (g_a g_w))^T, which takes a separate path when g_a g_w = 0.
+    q = _q()
+    M, N, K, r = 2048, 4096, 512, 16
+    x = workloads.random_bf16(41, (M, K))
+    w = workloads.random_bf16(42, (N, K), sigma=0.02)
+    if zero == "x":
+        x = np.zeros_like(x)
+    else:
+        w = np.zeros_like(w)
+    up = workloads.random_bf16(43, (N, r), sigma=0.02)
+    t = workloads.random_f32(44, (M, r))
+    a_d, w_d = q.nvfp4_quantize(dev_bf16(x)), q.nvfp4_quantize(dev_bf16(w))
+    oa, ow = O.quantize(x), O.quantize(w)
+    assert np.float32((oa if zero == "x" else ow)[2]) == 0.0
+    ref = L.gemm_lora(*oa, *ow, t, up)
+    for algo in (0, 1):
+        y = gpu_gemm_lora(a_d, w_d, _dev_f32(t), up, algo)
+        ok, rl, rr = Mx.check_output(y, ref)
+        log(f"lora zero {zero} algo={algo}: rel_l2={rl:.3e} row_ratio={rr:.3e}")
+        assert ok, f"algo={algo}: rel_l2={rl:.3e} row_ratio={rr:.3e}"
 
 
 def test_linear_lora_dit_qkv():
