@@ -212,6 +212,50 @@ def test_gemm_tiled_split_and_whole(M, N, K, split):
         assert np.array_equal(outs["split"], outs["whole"])
 
 
+def _random_tiled_shapes(n, seed):
+    # Ragged M and N (edge tiles, rows re-read past M or N), K both a
+    # multiple of 256 (scale groups and code pairs, loop tails of 4 stages)
+    # and an odd multiple of 128 (per-stage copies), grids small enough to
+    # be split along K and large enough to run whole rounds.
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        M = int(rng.integers(17, 700))
+        N = int(rng.integers(1, 60)) * 16 + (int(rng.integers(0, 16)) if i % 3 else 0)
+        K = 128 * (2 * int(rng.integers(1, 13)) + (i % 2))
+        shapes.append((M, N, K))
+    return shapes
+
+
+@pytest.mark.parametrize("M,N,K", _random_tiled_shapes(12, 2024))
+def test_gemm_tiled_random_shapes(M, N, K):
+    # The tiled kernel, with and without a workspace (K split of the last
+    # round), against the oracle; with the workspace also its amax variant,
+    # whose output bits must equal the plain call's.
+    q = _q()
+    import torch
+    a_bits = workloads.random_bf16(M * 3 + K, (M, K), outlier_frac=0.01, outlier_mul=20)
+    w_bits = workloads.random_bf16(N * 5 + K, (N, K), sigma=0.02, zero_frac=0.02)
+    a = assert_quant_equal(a_bits, label="random A")
+    w = assert_quant_equal(w_bits, label="random W")
+    ref = O.gemm(*O.quantize(a_bits), *O.quantize(w_bits))
+    outs = []
+    for name, ws in (("auto workspace", None), ("no workspace", torch.empty(0, dtype=torch.uint8, device="cuda:0"))):
+        out = Guarded((M, N), torch.bfloat16)
+        q.nvfp4_gemm(a, w, algo=q.ALGO_TILED, out=out.t, workspace=ws)
+        torch.cuda.synchronize()
+        assert out.intact(), "wrote outside its output"
+        y = F.bf16_from_bits(host_bits(out.t)).astype(np.float64)
+        ok, rl, rr = Mx.check_output(y, ref)
+        log(f"tiled random {M}x{N}x{K} {name}: rel_l2={rl:.3e} row_ratio={rr:.3e}")
+        assert ok, f"{name}: rel_l2={rl:.3e} row_ratio={rr:.3e}"
+        outs.append(host_bits(out.t))
+    if N % 16 == 0:
+        y2, _ = q.nvfp4_gemm_amax(a, w)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(y2), outs[0]), "amax variant changed the output"
+
+
 def test_gemm_tiled_scale_groups_uneven_split():
     # K = 1792 (a multiple of 256): the tiled kernel copies the scale bytes
     # of four stages at once and splits the leftover round (64 of 320 tiles,
