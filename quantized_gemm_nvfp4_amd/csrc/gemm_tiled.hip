@@ -20,17 +20,17 @@
 //    value of both operands is decoded once per workgroup (2 decode
 //    instructions per MFMA).  Otherwise a wave covers 128 x 128 (each A
 //    fragment feeds 4 MFMAs, and two waves decode each W fragment: 3 per
-//    MFMA).  The variant with the low-rank epilogue
-//    uses 8 waves of 128 x 64 (two per SIMD, accumulators in ordinary
-//    registers), because its epilogue scales and extends the accumulators
-//    with vector instructions, which cannot read the accumulation file.
-//  - The packed operands (codes and scale bytes) are copied global -> LDS with
-//    global_load_lds into a ring of four stage slots, three stages ahead of
-//    the MFMAs.  Each code copy instruction reads 32 rows x 32 contiguous
-//    bytes.  The slots are distinct LDS objects and the stage loop is
-//    unrolled, so the compiler sees that copies in flight never alias what
-//    is being read; one wait per stage leaves the newest stage's copies in
-//    flight.
+//    MFMA).  A low-rank branch runs on the scale-group kernel before the
+//    product (lora_branch_n64); otherwise, and for small grids, on 8 waves
+//    of 128 x 64 (two per SIMD, accumulators in ordinary registers), whose
+//    epilogue scales and extends the accumulators with vector instructions.
+//  - The packed operands (codes and scale bytes) are copied global -> LDS
+//    (LDS DMA through buffer resources) three stages ahead of the MFMAs,
+//    into a ring of single stages (each code copy instruction 32 rows x 32
+//    contiguous bytes) or, on the scale-group path, of stage pairs.  The
+//    slots are distinct LDS objects and the stage loop is unrolled, so the
+//    compiler sees that copies in flight never alias what is being read;
+//    one wait per stage leaves the newest stage's copies in flight.
 //  - A copy instruction costs about one cache-line lookup per row it
 //    touches, and a stage holds only 32 code and 4 scale bytes per row.
 //    When K is a multiple of 256 the 4-wave kernel copies the codes of two
@@ -38,10 +38,10 @@
 //    pair slots, and the scales of four stages at once (16 bytes per row,
 //    one lane per row) into two group buffers: half the lines of the code
 //    copies, a quarter of the scale copy instructions.
-//  - With copies in flight the compiler waits for all outstanding LDS reads
-//    before consuming any, so within a step single MFMAs are interleaved with
-//    the next step's LDS reads and the decoding (explicit scheduling groups):
-//    the reads are issued early and have completed by the next step.
+//  - Within a step single MFMAs are interleaved with the next step's LDS
+//    reads and the decoding (explicit scheduling groups): the reads are
+//    issued early and have completed by the next step, and each MFMA waits
+//    only for its own operand.
 //  - A is decoded once per workgroup, one stage ahead, into a double-buffered
 //    fp16 tile in LDS (16384 values per stage); the MFMA reads it with one
 //    ds_read_b128 per fragment and step.  W stays packed in LDS and each
@@ -50,10 +50,11 @@
 //    feeds does not change the sum as long as both operands use the same
 //    assignment.  Lane-half h takes K [32h, 32h + 32) of the stage, 8 per
 //    step, so a lane's W codes for the whole stage are one 16-byte piece.
-//    In LDS the two 16-byte pieces of a row's stage segment sit at slot
-//    2*row + (piece ^ swz(row)): the copy writes them in order, and 16
-//    readers of 16 consecutive rows hit 16 distinct bank groups.  The fp16 A
-//    tile is stored in MFMA lane order (conflict-free reads).
+//    In LDS the 16-byte pieces of a row's segment (two per stage, four per
+//    stage pair) sit XOR-swizzled by the row (piece_slot, pair_piece_slot):
+//    the copy writes them in order, and 16 readers of 16 consecutive rows
+//    hit 16 distinct bank groups.  The fp16 A tile is stored in MFMA lane
+//    order (conflict-free reads).
 //  - The W fragment is the MFMA's first operand, so each lane's accumulators
 //    hold 4 consecutive output columns n: 8-byte bf16 stores.
 //  - One workgroup fills a CU (LDS), so a grid of T tiles runs in
