@@ -679,6 +679,26 @@ __device__ __forceinline__ uint32_t store_frag(const float16v& a, float gmul, ui
   return mx;
 }
 
+// Adds the low-rank branch sum_k T[m][k] L_up[n][k] (fp32, plain loops) to
+// the bf16 values of one stored 32 x 32 fragment: out = bf16(out + branch),
+// for the elements this lane stored (store_frag's layout).
+__device__ __noinline__ void add_branch_frag(const float* __restrict__ lora_t, const uint16_t* __restrict__ lora_up,
+                                             int r, uint16_t* __restrict__ out, int M, int N, int m, int nb, int h) {
+  if (m >= M) return;
+  uint16_t* orow = out + (int64_t)m * N;
+  const float* trow = lora_t + (int64_t)m * r;
+#pragma unroll 1
+  for (int q = 0; q < 16; ++q) {
+    const int n = nb + 8 * (q >> 2) + 4 * h + (q & 3);
+    if (n >= N) continue;
+    const uint16_t* urow = lora_up + (int64_t)n * r;
+    float v = 0.f;
+#pragma unroll 1
+    for (int k = 0; k < r; ++k) v += trow[k] * bf16_bits_to_f32(urow[k]);
+    orow[n] = (uint16_t)f32_to_bf16_rne(bf16_bits_to_f32(orow[n]) + v);
+  }
+}
+
 // A wave's 4 kJ fragments: fragment (j, i) covers rows m0 + 128 wm + 32 i
 // and columns n0 + 32 kJ wn + 32 j.  Returns the lane's largest |bf16|
 // pattern stored.
@@ -800,7 +820,10 @@ __device__ __forceinline__ void lora_epilogue(float16v (&acc)[TiledCtx<kW>::kJ][
 // runs first, on the zeroed accumulators, before the product's main loop
 // (the decoded-A buffers are still free), and the store multiplies by
 // g_a g_w (tscale = 1 / (g_a g_w)).  With g_a g_w = 0 the caller skips the
-// product and passes tscale = 1 (store multiplier 1).  T is staged as bf16
+// product and passes tscale = 1 (store multiplier 1).  With g_a g_w outside
+// [2^-64, 2^64] the branch divided by it could leave the fp32 range: the
+// caller then skips this, stores the product alone and adds the branch to
+// the stored tile (add_branch_frag).  T is staged as bf16
 // hi + lo parts as in lora_epilogue, one thread per row of the tile (256 T
 // rows and 256 L_up rows per 32-rank chunk).
 __device__ __forceinline__ void lora_branch_n64(float16v (&acc)[2][8], float tscale,
@@ -989,11 +1012,13 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc2[j][i] = float16v{};
     // With the low-rank branch and g_a g_w = 0 the product adds nothing: it
-    // is skipped, and the branch alone is stored (store multiplier 1).
+    // is skipped, and the branch alone is stored (store multiplier 1).  With
+    // g_a g_w far from 1 the branch is added after the store instead.
     const float gg = (*a_g) * (*w_g);
     const float gmul = kLora && gg == 0.f ? 1.f : gg;
+    const bool late = kLora && gg != 0.f && !(gg >= 0x1p-64f && gg <= 0x1p64f);
     if constexpr (kLora) {
-      lora_branch_n64(acc2, 1.f / gmul, lora_t, lora_up, r, M, N, m0, n0, wave, c.h, c.r32);
+      if (!late) lora_branch_n64(acc2, 1.f / gmul, lora_t, lora_up, r, M, N, m0, n0, wave, c.h, c.r32);
       __syncthreads();            // the decoded-A buffers are free again
     }
     // Prologue: scale group 0 and code pairs 0 and 1 in flight, then stage
@@ -1053,7 +1078,15 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         mx = max(mx, store_frag(acc2[j][i], gmul, out, M, N, m0 + 32 * i + r32, n0 + 64 * wave + 32 * j, h));
+    if constexpr (kLora) {
+      if (late) {
+#pragma unroll 1
+        for (int f = 0; f < 16; ++f)
+          add_branch_frag(lora_t, lora_up, r, out, M, N, m0 + 32 * (f & 7) + r32, n0 + 64 * wave + 32 * (f >> 3), h);
+      }
+    }
     if (kAmax) {
+      static_assert(!(kAmax && kLora), "the low-rank variant reports no amax");
       __shared__ uint32_t red2[4];
       const uint32_t m = block_max_u32<4>(mx, red2);
       if (tid == 0) amax[tile_id] = m;

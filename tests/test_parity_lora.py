@@ -177,6 +177,35 @@ def test_gemm_lora_zero_global_scale(zero):
         assert ok, f"algo={algo}: rel_l2={rl:.3e} row_ratio={rr:.3e}"
 
 
+@pytest.mark.parametrize("case", ["tiny", "huge"])
+def test_gemm_lora_extreme_global_scale(case):
+    # g_a g_w far from 1: a main weight with amax ~1e-36 has a subnormal
+    # global scale (T / (g_a g_w) would overflow fp32, and the output is
+    # almost entirely the branch); operands ~1e15 give g_a g_w ~1e24 (the
+    # branch is negligible).  The tiled kernel then adds the branch after
+    # storing the product.
+    q = _q()
+    M, N, K, r = 2048, 4096, 512, 16
+    sx, sw = (1.0, 1e-36) if case == "tiny" else (1e15, 1e15)
+    x = workloads.random_bf16(51, (M, K), sigma=sx)
+    w = workloads.random_bf16(52, (N, K), sigma=sw)
+    up = workloads.random_bf16(53, (N, r), sigma=0.02)
+    t = workloads.random_f32(54, (M, r))
+    a_d, w_d = q.nvfp4_quantize(dev_bf16(x)), q.nvfp4_quantize(dev_bf16(w))
+    oa, ow = O.quantize(x), O.quantize(w)
+    assert np.array_equal(host_u8(w_d[0]), ow[0]) and np.array_equal(host_u8(w_d[1]), ow[1])
+    gg = np.float32(oa[2]) * np.float32(ow[2])
+    assert 0 < gg < 2.0 ** -100 if case == "tiny" else 2.0 ** 70 < gg < 2.0 ** 100
+    ref = L.gemm_lora(*oa, *ow, t, up)
+    assert np.all(np.isfinite(ref))
+    for algo in (0, 1, 3):
+        y = gpu_gemm_lora(a_d, w_d, _dev_f32(t), up, algo)
+        assert np.all(np.isfinite(y))
+        ok, rl, rr = Mx.check_output(y, ref)
+        log(f"lora {case} global scale algo={algo}: rel_l2={rl:.3e} row_ratio={rr:.3e}")
+        assert ok, f"algo={algo}: rel_l2={rl:.3e} row_ratio={rr:.3e}"
+
+
 def test_linear_lora_dit_qkv():
     # The diffusion qkv projection [4096 x 3072] x [9216 x 3072] with a
     # rank-32 adapter, end to end (quantize with the fused down projection,
