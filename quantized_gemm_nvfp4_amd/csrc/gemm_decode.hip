@@ -412,10 +412,13 @@ bool nvfp4_w4a16_decode_supported(int64_t M, int64_t K) {
 
 hipError_t launch_nvfp4_w4a16_decode(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
                                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  // 8 rows per workgroup at M = 1 and 2: at M = 2 (21504 x 5376) 8 rows took
+  // 19.4 us per call against 21.5 us for 4 and 20.5 us for 6; 12 and more
+  // spill registers.
   if (M == 1) {
     launch_w4a16_rowslot<1, 8>(x, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
   } else {
-    launch_w4a16_rowslot<2, 4>(x, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
+    launch_w4a16_rowslot<2, 8>(x, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
   }
   return hipGetLastError();
 }
