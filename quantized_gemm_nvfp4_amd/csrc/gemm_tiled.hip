@@ -1182,7 +1182,6 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_tiled_reduce_kernel(const floa
   }
 }
 
-namespace {
 int device_cus() {
   static int cached[64] = {0};
   int dev = 0;
@@ -1194,6 +1193,8 @@ int device_cus() {
   }
   return cached[dev];
 }
+
+namespace {
 
 struct TiledPlan {
   int tiles_m, tiles_n, full_tiles, splits;

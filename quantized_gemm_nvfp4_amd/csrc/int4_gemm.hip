@@ -71,11 +71,18 @@ __device__ __forceinline__ short8v as_short8(const uint4& v) { return __builtin_
 //  - Bound by the loads: on 28672 x 8192 removing the decode or the MFMAs
 //    changed nothing, removing the x loads saved 6 us at M = 3 and 15 us at
 //    M = 16.
+//  - Workgroups of 4 row groups (64 rows), or 7 (112 rows) from M = 8 when
+//    N covers a workgroup per compute unit: the time follows the busiest
+//    compute unit, and on 28672 x 8192 the 448 workgroups of 64 rows put
+//    two on 192 CUs and one on the other 64, while 112 rows make exactly
+//    one per CU.  Interleaved runs (us, 64 / 112 rows): M = 3 43.6 / 45.3,
+//    M = 6 45.3 / 46.0, M = 8 47.0 / 46.2, M = 12 49.7 / 47.1, M = 16
+//    53.0 / 48.3 (identical outputs).
 namespace {
-constexpr int kI4Groups = 4;   // 64 weight rows per workgroup
 constexpr int kI4Waves = 8;
 }  // namespace
 
+template <int kI4Groups, int kI4Waves>
 __global__ __launch_bounds__(64 * kI4Waves) void int4g_gemm_decode_kernel(const uint16_t* __restrict__ x,
                                                                          const uint8_t* __restrict__ q,
                                                                          const uint16_t* __restrict__ s,
@@ -484,19 +491,24 @@ void launch_int4_rowslot(const void* x, const uint8_t* q, const void* s, void* o
 
 hipError_t launch_int4g_gemm_decode(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,
                                     int64_t N, int64_t K, hipStream_t stream) {
+  // Row-slot: 8 rows per workgroup at M = 1 and 2 (28672 x 8192, M = 2:
+  // 30.1 us against 39.5 us with 4 rows; M = 1: 23.0 against 27.8 us).
   if (K <= 16 * 2048 && (int64_t)M * K * 2 < (1ll << 31)) {
     if (M == 1) {
       launch_int4_rowslot<1, 8>(x, q, s, out, (int)M, (int)N, (int)K, stream);
       return hipGetLastError();
     }
     if (M == 2) {
-      launch_int4_rowslot<2, 4>(x, q, s, out, (int)M, (int)N, (int)K, stream);
+      launch_int4_rowslot<2, 8>(x, q, s, out, (int)M, (int)N, (int)K, stream);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL(int4g_gemm_decode_kernel, dim3((unsigned)((N + 16 * kI4Groups - 1) / (16 * kI4Groups))),
-                     dim3(64 * kI4Waves), 0, stream,
-                     (const uint16_t*)x, q, (const uint16_t*)s, (uint16_t*)out, (int)M, (int)N, (int)K);
+  if (M >= 8 && N >= 112ll * device_cus())
+    hipLaunchKernelGGL((int4g_gemm_decode_kernel<7, kI4Waves>), dim3((unsigned)((N + 111) / 112)), dim3(64 * kI4Waves), 0,
+                       stream, (const uint16_t*)x, q, (const uint16_t*)s, (uint16_t*)out, (int)M, (int)N, (int)K);
+  else
+    hipLaunchKernelGGL((int4g_gemm_decode_kernel<4, kI4Waves>), dim3((unsigned)((N + 63) / 64)), dim3(64 * kI4Waves), 0,
+                       stream, (const uint16_t*)x, q, (const uint16_t*)s, (uint16_t*)out, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 

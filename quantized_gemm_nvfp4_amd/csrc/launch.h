@@ -107,6 +107,8 @@ hipError_t launch_nvfp4_gemm_simple_lora(const uint8_t* ac, const uint8_t* as, c
 
 // INT4 per-group (128) W4A16 kernels; out[M, N] bf16 = x . dequant(q, s)^T.
 // decode: M <= 16.  tiled: any M.  simple: any M.  All need K % 128 == 0.
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus();
 hipError_t launch_int4g_gemm_decode(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,
                                     int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_int4g_gemm_tiled(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,

@@ -95,12 +95,14 @@ def test_int4_gemv_ragged(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 9, 128), (2, 13, 256), (1, 17, 2176), (2, 20, 4096), (1, 3, 32768 + 128),
-                                   (3, 65, 384), (7, 130, 2304), (12, 64, 1024), (16, 100, 4224), (9, 47, 128)])
+                                   (3, 65, 384), (7, 130, 2304), (12, 64, 1024), (16, 100, 4224), (9, 47, 128),
+                                   (8, 28679, 384), (13, 28800, 256)])
 def test_int4_decode_shapes(M, N, K):
     # M <= 2 runs the row-slot GEMV (1 KB slots of 16 groups, partial last
     # slot, ragged N); K > 32768 and 3 <= M <= 16 run the row-block kernel
     # (64 rows per workgroup, N ragged against it; an odd group count leaves
-    # a half step; K = 2304 gives its 8 waves unequal step counts).
+    # a half step; K = 2304 gives its 8 waves unequal step counts; from M = 8
+    # with N >= 112 per compute unit, 112 rows per workgroup, N ragged).
     x = workloads.random_bf16(M + K, (M, K), outlier_frac=0.01, outlier_mul=20)
     w = workloads.random_bf16(N + K + 1, (N, K), sigma=0.02, zero_frac=0.05)
     check_gemv(x, w, algos=(0, 2), label=f"int4 decode {M}x{N}x{K}")
@@ -112,7 +114,7 @@ def test_int4_config():
     log("int4 config: quantize W [28672, 8192]")
     qt, st = check_gemv(x[:1], w, label="int4 M=1")
     op, osb, _ = I.int4g_quantize(w)
-    for M in (16,):
+    for M in (2, 16):
         y = gpu_gemv(x[:M], qt, st)
         ok, rl, rr = Mx.check_output(y, I.int4g_gemm(x[:M], op, osb))
         log(f"int4 M={M}: rel_l2={rl:.3e} row_ratio={rr:.3e}")
