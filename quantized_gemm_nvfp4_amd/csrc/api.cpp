@@ -366,7 +366,7 @@ nvfp4_status nvfp4_gemm_w4a16_ex(const void* x_bf16, const uint8_t* w_codes, con
   hipStream_t st = (hipStream_t)stream;
   if (algo == NVFP4_ALGO_DECODE) {
     if (!decode_ok)
-      return fail(NVFP4_ERR_UNSUPPORTED, "weight-only decode kernel needs M <= 2, K %% 128 == 0 and K <= 32768 "
+      return fail(NVFP4_ERR_UNSUPPORTED, "weight-only decode kernel needs M <= 16, K %% 128 == 0 and K <= 32768 "
                   "(M=%lld, K=%lld)", (long long)M, (long long)K);
     return hip_status(nvfp4k::launch_nvfp4_w4a16_decode(x_bf16, w_codes, w_scales, w_gscale, out_bf16, M, N, K, st),
                       "nvfp4_gemm_w4a16 decode launch");
