@@ -7,10 +7,13 @@
 // (about one VALU op per weight value: the E2M1 conversion and the block
 // scale multiply, two values per instruction each) from becoming the limit.
 //
-// Two kernels:
-//  - row-slot GEMV (M <= 2): W is read in storage order, one contiguous
-//    1 KB per load instruction; the MFMA reduces along each lane's own data
-//    (diagonal trick below).
+// Three kernels:
+//  - streaming row GEMV (M <= 2, K <= 8192): a persistent grid in which each
+//    wave reads whole rows of W, one contiguous 1 KB per load instruction,
+//    with the next rows' loads in flight while it decodes; the MFMA reduces
+//    along each lane's own data (diagonal trick below).
+//  - row-slot GEMV (M <= 2, larger K, and the low-rank branch): the same
+//    product, one workgroup per 4 rows.
 //  - row-block GEMM (3 <= M <= 16): 48 rows of W per workgroup, the
 //    activation rows in the MFMA's columns, each decoded activation fragment
 //    shared by three 16-row groups; the 16 lanes of a row read whole
@@ -149,6 +152,160 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_rowslot_kernel(
     const int rho = pair / kM, m = pair % kM;
     if (ii == 0 && m < M && n0 + rho < N) out[(int64_t)m * N + n0 + rho] = (uint16_t)f32_to_bf16_rne(kLora ? v : v * gg);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming row GEMV (M <= 2, K <= kS * 2048).
+//
+// A persistent grid: wave gw of TW computes rows gw, gw + TW, gw + 2 TW, ...
+// Each row is read whole by its wave, kS load instructions of up to 1 KB of
+// contiguous codes each (slot s = bytes [1024 s, 1024 s + 1024) of the row),
+// and kD rows are in flight per wave: the codes of slot s of row k + kD are
+// requested as soon as slot s of row k has been decoded, so the memory
+// system always holds about kD rows of every wave while the wave computes.
+// Interleaving the rows over the grid keeps the chip's outstanding reads in
+// one window of about kD TW consecutive rows that sweeps the weight once
+// (on the 21504 x 5376 weight this pattern read as fast as flat streaming
+// of the same bytes; deeper prefetch or more waves widened the window and
+// read slower).
+//
+// The product is the row-slot kernel's diagonal MFMA: lane i + 16 g feeds A
+// with 8 of its W values and B with the activation values at the same K
+// positions, so D[i][i] holds 16 pieces of the row's dot product; even and
+// odd K steps go to two accumulators (two independent MFMA chains), added at
+// the end of the row.  The activation is decoded once per wave into
+// registers (it is the same for every row).  Each finished row leaves its 16
+// diagonal values in the wave's own LDS area; every kStreamBatch rows the
+// wave sums them (lane = row, fixed order), scales by g_a g_w and stores.
+namespace {
+constexpr int kStreamBatch = 64;                // rows per wave between LDS flushes
+constexpr int kStreamDepth = 2;                 // rows in flight per wave
+constexpr int kStreamWaves = 4;                 // waves per workgroup
+constexpr int kStreamWgsPerCu = 2;              // workgroups per compute unit
+constexpr int kStreamMaxSlots = 4;              // K <= 8192
+}  // namespace
+
+template <int kM, int kS>
+__global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_gemv_stream_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
+    uint16_t* __restrict__ out, int M, int N, int K) {
+  constexpr int kD = kStreamDepth;
+  __shared__ __attribute__((aligned(16))) float s_part[kStreamWaves][kStreamBatch * kM * 16];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * kStreamWaves + wave, TW = gridDim.x * kStreamWaves;
+  const uint32_t row_bytes = (uint32_t)K / 2, row_scales = (uint32_t)K / 16;
+  float* part = s_part[wave];
+
+  // Row `row`'s codes and scales; a row past N gets an empty buffer range,
+  // so its loads read zeros.  Lanes past the row's end read zeros too (their
+  // offsets lie outside the row's range).
+  auto row_codes = [&](int row) {
+    const bool valid = row < N;
+    return buffer_of(w_codes + (int64_t)(valid ? row : 0) * row_bytes, valid ? row_bytes : 0u);
+  };
+  auto row_scl = [&](int row) {
+    const bool valid = row < N;
+    return buffer_of(w_scales + (int64_t)(valid ? row : 0) * row_scales, valid ? row_scales : 0u);
+  };
+  uint4 wc[kD][kS];
+  uint32_t ws[kD][kS];
+  // the first kD rows are requested before the activation is decoded
+#pragma unroll
+  for (int d = 0; d < kD; ++d) {
+    const auto wr = row_codes(gw + d * TW), wsr = row_scl(gw + d * TW);
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      wc[d][s] = buffer_load16<kCachePolicyNT>(wr, 1024u * s + 16u * lane);
+      ws[d][s] = buffer_load2<kCachePolicyNT>(wsr, 128u * s + 2u * lane);
+    }
+  }
+
+  // The activation's 32 values per lane and slot, decoded once.
+  const auto ar = buffer_of(a_codes, (uint32_t)M * row_bytes);      // rows >= M read as zero
+  const auto asr = buffer_of(a_scales, (uint32_t)M * row_scales);
+  half8v xv[kM][kS][4];
+#pragma unroll
+  for (int s = 0; s < kS; ++s)
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      const bool in = 1024u * s + 16u * lane < row_bytes;
+      const uint4 xc = buffer_load16(ar, in ? 1024u * s + 16u * lane + m * row_bytes : kOob);
+      const uint32_t xs = buffer_load2(asr, in ? 128u * s + 2u * lane + m * row_scales : kOob);
+      const half2v sc = e4m3x2_to_f16x2_div256(xs);
+      const half2v s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) xv[m][s][jj] = dequant8_f16_div256(word_of(xc, jj), jj < 2 ? s0 : s1);
+    }
+
+  const int i = lane & 15;
+  const bool diag_lane = (i >> 2) == (lane >> 4);
+  const float gg = (*a_g) * (*w_g);
+  int nbat = 0;                 // rows of the current batch
+  int row0 = gw;                // first row of the current batch
+  auto flush = [&]() {
+    // lane l < nbat: row row0 + l TW, the sum of its 16 diagonal values
+    if (lane < nbat) {
+      const int n = row0 + lane * TW;
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        const float4v* p = (const float4v*)(part + (lane * kM + m) * 16);
+        float v = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4v t = p[q];
+          v += t[0];
+          v += t[1];
+          v += t[2];
+          v += t[3];
+        }
+        if (m < M) out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v * gg);
+      }
+    }
+  };
+  for (int row = gw; row < N; row += kD * TW) {
+#pragma unroll
+    for (int d = 0; d < kD; ++d) {
+      const int r = row + d * TW;
+      const auto wr = row_codes(r + kD * TW), wsr = row_scl(r + kD * TW);
+      float4v acc[kM][2];
+#pragma unroll
+      for (int m = 0; m < kM; ++m) acc[m][0] = acc[m][1] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kS; ++s) {
+        half8v wv[4];
+        const half2v sc = e4m3x2_to_f16x2_div256(ws[d][s]);
+        const half2v s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) wv[jj] = dequant8_f16_div256(word_of(wc[d][s], jj), jj < 2 ? s0 : s1);
+        // slot s of row r + kD TW into the registers just decoded
+        wc[d][s] = buffer_load16<kCachePolicyNT>(wr, 1024u * s + 16u * lane);
+        ws[d][s] = buffer_load2<kCachePolicyNT>(wsr, 128u * s + 2u * lane);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int m = 0; m < kM; ++m)
+            acc[m][jj & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[jj], xv[m][s][jj], acc[m][jj & 1], 0, 0, 0);
+      }
+      if (r < N) {
+        if (diag_lane) {
+#pragma unroll
+          for (int m = 0; m < kM; ++m) {
+            const float4v a = acc[m][0] + acc[m][1];
+            const int c = i & 3;
+            part[(nbat * kM + m) * 16 + i] = c == 0 ? a[0] : (c == 1 ? a[1] : (c == 2 ? a[2] : a[3]));
+          }
+        }
+        if (++nbat == kStreamBatch) {
+          flush();
+          nbat = 0;
+          row0 = r + TW;
+        }
+      }
+    }
+  }
+  flush();
 }
 
 // ---------------------------------------------------------------------------
@@ -406,6 +563,31 @@ void launch_w4a16_rowslot(const void* x, const uint8_t* wc, const uint8_t* ws, c
 }
 }  // namespace
 
+namespace {
+template <int kM, int kS>
+void launch_stream(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc, const uint8_t* ws,
+                   const float* wg, void* out, int M, int N, int K, hipStream_t stream) {
+  const int64_t cap = (int64_t)device_cus() * kStreamWgsPerCu;
+  const int64_t need = ((int64_t)N + kStreamWaves - 1) / kStreamWaves;
+  const unsigned grid = (unsigned)(need < cap ? need : cap);
+  hipLaunchKernelGGL((nvfp4_gemv_stream_kernel<kM, kS>), dim3(grid), dim3(64 * kStreamWaves), 0, stream, ac, as, ag,
+                     wc, ws, wg, (uint16_t*)out, M, N, K);
+}
+// Launches the streaming GEMV for M <= 2 and K <= kStreamMaxSlots * 2048;
+// false if the shape is outside that range.
+template <int kM>
+bool launch_stream_k(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc, const uint8_t* ws,
+                     const float* wg, void* out, int M, int N, int K, hipStream_t stream) {
+  switch ((K + 2047) / 2048) {
+    case 1: launch_stream<kM, 1>(ac, as, ag, wc, ws, wg, out, M, N, K, stream); return true;
+    case 2: launch_stream<kM, 2>(ac, as, ag, wc, ws, wg, out, M, N, K, stream); return true;
+    case 3: launch_stream<kM, 3>(ac, as, ag, wc, ws, wg, out, M, N, K, stream); return true;
+    case 4: launch_stream<kM, 4>(ac, as, ag, wc, ws, wg, out, M, N, K, stream); return true;
+    default: return false;
+  }
+}
+}  // namespace
+
 bool nvfp4_w4a16_decode_supported(int64_t M, int64_t K) {
   return M >= 1 && M <= 16 && K > 0 && K % 128 == 0 && K <= (int64_t)kMaxSlots * 2048;
 }
@@ -436,6 +618,11 @@ hipError_t launch_nvfp4_gemm_decode_lora(const uint8_t* ac, const uint8_t* as, c
                                          hipStream_t stream) {
   const bool rowslot_k = K <= (int64_t)kMaxSlots * 2048;
   const bool lora = lora_t != nullptr;
+  if (M <= 2 && !lora) {
+    const bool done = M == 1 ? launch_stream_k<1>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream)
+                             : launch_stream_k<2>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
+    if (done) return hipGetLastError();
+  }
   if (M == 1 && rowslot_k) {
     if (lora)
       launch_rowslot<1, 4, true>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream, lora_t, lora_up, (int)r);

@@ -282,11 +282,15 @@ def test_gemm_tiled_scale_groups_uneven_split():
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (1, 1, 128), (2, 3, 128), (1, 9, 2048), (2, 37, 2176), (1, 33, 4224), (2, 8, 6144), (1, 5, 32768 + 128)])
+    (1, 1, 128), (2, 3, 128), (1, 9, 2048), (2, 37, 2176), (1, 33, 4224), (2, 8, 6144), (1, 300, 8192),
+    (2, 70, 8192 + 128), (1, 5, 32768 + 128), (1, 140001, 128), (2, 140001, 256)])
 def test_gemm_decode_shapes(M, N, K):
-    # M <= 2 runs the row-slot GEMV: one 1 KB slot per 2048 values of K (the
-    # last one partial), 4 rows per workgroup (N ragged); K > 32768 falls back
-    # to the row-block kernel.
+    # M <= 2 and K <= 8192 run the streaming GEMV: one 1 KB slot per 2048
+    # values of K (the last one partial), rows spread over the grid's waves;
+    # with N = 140001 each wave takes more than 64 rows, so its partial sums
+    # are flushed from LDS more than once.  8192 < K <= 32768 runs the
+    # row-slot GEMV (4 rows per workgroup, N ragged); K > 32768 falls back to
+    # the row-block kernel.
     a_bits = workloads.random_bf16(M * 13 + K, (M, K), outlier_frac=0.01, outlier_mul=30)
     w_bits = workloads.random_bf16(N * 17 + K, (N, K), sigma=0.02, zero_frac=0.05)
     check_gemm(a_bits, w_bits, algos=(0, 2), label=f"decode {M}x{N}x{K}")
@@ -303,6 +307,18 @@ def test_gemm_rowblock_decode_shapes(M, N, K):
     a_bits = workloads.random_bf16(M * 19 + K, (M, K), outlier_frac=0.01, outlier_mul=30)
     w_bits = workloads.random_bf16(N * 23 + K, (N, K), sigma=0.02, zero_frac=0.05)
     check_gemm(a_bits, w_bits, algos=(0, 2), label=f"packed decode {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (3, 1, 128), (4, 7, 384), (5, 33, 2176), (8, 1001, 5376), (7, 30001, 256), (4, 61, 8192), (6, 45, 8192 + 128),
+    (8, 10, 16384), (3, 257, 16384 + 256)])
+def test_gemm_rowblock_ragged_shapes(M, N, K):
+    # More row-block shapes: N below one 48-row workgroup and not a multiple
+    # of 4, K % 256 == 128 (a half step), K = 8192 and 16384, and N = 30001
+    # (626 workgroups, a partial last one).
+    a_bits = workloads.random_bf16(M * 29 + K, (M, K), outlier_frac=0.01, outlier_mul=30)
+    w_bits = workloads.random_bf16(N * 31 + K, (N, K), sigma=0.02, zero_frac=0.05)
+    check_gemm(a_bits, w_bits, algos=(0, 2), label=f"row-block {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("K", [16, 48, 80, 272])
