@@ -63,10 +63,16 @@ constexpr int64_t kMaxDim = 0x7FFFFFFF;
 // The INT4 tiled kernel addresses a tile's rows of x (128 x 2K bytes) with
 // 32-bit buffer offsets.
 constexpr int64_t kInt4TiledKLimit = (int64_t)1 << 22;
-// The weight-streaming kernels address a workgroup's weight rows and the
-// whole activation through buffer resources with 32-bit byte ranges (at
-// most 64 rows x K values); 2^24 keeps every range far below 2^31.
+// The weight-streaming kernels address at most kDecodeMaxRows packed weight
+// rows (the 112-row workgroup of the INT4 decode kernel is the largest) and
+// the whole bf16 activation of M <= 16 rows through buffer resources with
+// 32-bit byte ranges.  Offsets at or past 2^31 mark loads that must read
+// zero, so every range must stay below 2^31; K <= 2^24 guarantees it.
 constexpr int64_t kDecodeMaxK = int64_t(1) << 24;
+constexpr int64_t kDecodeMaxRows = 112;
+constexpr int64_t kBufferOobOffset = int64_t(1) << 31;
+static_assert(kDecodeMaxRows * (kDecodeMaxK / 2) < kBufferOobOffset, "weight rows of a decode workgroup");
+static_assert(16 * kDecodeMaxK * 2 < kBufferOobOffset, "bf16 activation of a decode call");
 // The NVFP4 tiled kernel addresses a tile's rows (256 x K/2 bytes) with
 // 32-bit buffer offsets.
 constexpr int64_t kTiledKLimit = int64_t(1) << 24;
@@ -341,6 +347,7 @@ nvfp4_status nvfp4_gemm_w4a16_ex(const void* x_bf16, const uint8_t* w_codes, con
                                  const float* w_gscale, void* out_bf16, int64_t M, int64_t N, int64_t K, int algo,
                                  void* stream) {
   if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
+  if (nvfp4_status s = check_products(M, N, K)) return s;
   if (K > 0) {
     REQUIRE_PTR(x_bf16);
     REQUIRE_PTR(w_codes);
@@ -406,6 +413,7 @@ nvfp4_status int4g_gemv_ex(const void* x_bf16, const uint8_t* q, const void* sca
   REQUIRE_PTR(scales_fp16);
   REQUIRE_PTR(out_bf16);
   if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
+  if (nvfp4_status s = check_products(M, N, K)) return s;
   if (group != 128) return fail(NVFP4_ERR_UNSUPPORTED, "group=%lld; only 128 is supported", (long long)group);
   if (K % 128 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of the group (128)", (long long)K);
   if (algo < NVFP4_ALGO_AUTO || algo > NVFP4_ALGO_SIMPLE) return fail(NVFP4_ERR_INVALID_ARG, "unknown algo %d", algo);
@@ -475,6 +483,7 @@ nvfp4_status int4g_asym_gemv_ex(const void* x_bf16, const uint8_t* q, const void
   REQUIRE_PTR(zeros);
   REQUIRE_PTR(out_bf16);
   if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
+  if (nvfp4_status s = check_products(M, N, K)) return s;
   if (group != 128) return fail(NVFP4_ERR_UNSUPPORTED, "group=%lld; only 128 is supported", (long long)group);
   if (K % 128 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of the group (128)", (long long)K);
   if (algo != NVFP4_ALGO_AUTO && algo != NVFP4_ALGO_DECODE && algo != NVFP4_ALGO_SIMPLE)

@@ -172,6 +172,11 @@ def test_int4_validation():
     assert g(A, B, C, ODD, 4, 8, 256, 128, 0, None) == ALIGN
     assert g(A, B, C, D, 0, 8, 256, 128, 0, None) == OK
     assert lib.int4g_gemv(A, B, C, D, 4, 8, 256, 64, None) == UNSUP
+    # out [M, N] past 2^40 elements: rejected before any range arithmetic
+    big = (1 << 31) - 1
+    assert g(A, B, C, D, big, big, 256, 128, 0, None) == UNSUP and "2^40" in _err()
+    assert lib.int4g_asym_gemv_ex(A, B, C, D, E, big, big, 256, 128, 0, None) == UNSUP and "2^40" in _err()
+    assert lib.nvfp4_gemm_w4a16_ex(A, B, C, D, E, big, big, 256, 0, None) == UNSUP and "2^40" in _err()
 
 
 def test_lora_workspace_size():
