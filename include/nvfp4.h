@@ -98,6 +98,23 @@ nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols,
                             uint8_t* codes, uint8_t* scales, float* global_scale,
                             int use_given_global_scale, void* workspace, void* stream);
 
+/*
+ * nvfp4_quantize without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same steps, arguments, outputs and
+ * errors as nvfp4_quantize (absmax rule); codes, scales and g are
+ * byte-identical to its results.  The first pass's partial maxima go to a
+ * static 4 KB device array that the library holds on each GPU it runs on
+ * until the process ends (1024 slots, the most the pass ever writes, so
+ * every size nvfp4_quantize accepts fits).  The entry point itself allocates
+ * nothing; its first call on a device looks up that array's address once.
+ * Every call on one GPU shares the array: calls that overlap on one GPU
+ * (different streams without ordering) race and may produce wrong results.
+ */
+nvfp4_status nvfp4_quantize_noalloc(const void* x_bf16, int64_t rows, int64_t cols,
+                                    uint8_t* codes, uint8_t* scales, float* global_scale,
+                                    int use_given_global_scale, void* stream);
+
 /* Block-scale selection rules for nvfp4_quantize_ex. */
 typedef enum nvfp4_scale_rule {
   NVFP4_SCALE_ABSMAX = 0,        /* the block max maps to 6 (nvfp4_quantize) */

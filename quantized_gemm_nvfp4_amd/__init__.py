@@ -36,6 +36,7 @@ SIGNATURES = {
     "nvfp4_quantize_workspace_bytes": ([], ctypes.c_size_t),
     "nvfp4_quantize": ([_P, _I64, _I64, _P, _P, _P, _I, _P, _P], ctypes.c_int),
     "nvfp4_quantize_ex": ([_P, _I64, _I64, _P, _P, _P, _I, _I, _P, _P], ctypes.c_int),
+    "nvfp4_quantize_noalloc": ([_P, _I64, _I64, _P, _P, _P, _I, _P], ctypes.c_int),
     "nvfp4_gemm": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "nvfp4_gemm_ex": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P], ctypes.c_int),
     "nvfp4_gemm_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),

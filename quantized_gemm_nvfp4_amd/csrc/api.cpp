@@ -270,6 +270,37 @@ nvfp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, uint
                            NVFP4_SCALE_ABSMAX, workspace, stream);
 }
 
+nvfp4_status nvfp4_quantize_noalloc(const void* x_bf16, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                    float* global_scale, int use_given_global_scale, void* stream) {
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  REQUIRE_PTR(global_scale);
+  if (nvfp4_status s = check_dims(rows, "rows", cols, "cols", 0, "-")) return s;
+  if (cols % 16 != 0) return fail(NVFP4_ERR_SHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  if (rows > 0 && cols > kMaxElems / rows) return fail(NVFP4_ERR_UNSUPPORTED, "rows*cols exceeds 2^40");
+  REQUIRE_ALIGN(x_bf16, 16);
+  REQUIRE_ALIGN(codes, 16);
+  REQUIRE_ALIGN(scales, 16);
+  REQUIRE_ALIGN(global_scale, 4);
+  const int64_t n = rows * cols;
+  const Range outs[3] = {{codes, n / 2, "codes"}, {scales, n / 16, "scales"}, {global_scale, 4, "global_scale"}};
+  const Range ins[1] = {{x_bf16, n * 2, "x"}};
+  if (n == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 3, ins, 1)) return s;
+  // the first pass writes at most kAmaxPartials partial maxima, which is
+  // exactly the scratch's size, for every input size accepted above
+  uint32_t* partials = nullptr;
+  if (!use_given_global_scale) {
+    const hipError_t e = nvfp4k::quantize_scratch((hipStream_t)stream, &partials);
+    if (e != hipSuccess) return hip_status(e, "nvfp4_quantize_noalloc scratch lookup");
+  }
+  return hip_status(nvfp4k::launch_nvfp4_quantize(x_bf16, rows, cols, codes, scales, global_scale,
+                                                  use_given_global_scale, NVFP4_SCALE_ABSMAX, partials,
+                                                  (hipStream_t)stream),
+                    "nvfp4_quantize_noalloc launch");
+}
+
 nvfp4_status nvfp4_gemm_ex(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
                            const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale, void* out_bf16,
                            int64_t M, int64_t N, int64_t K, int algo, void* stream) {

@@ -58,6 +58,9 @@ hipError_t launch_nvfp4_quantize_lora(const void* x, int64_t rows, int64_t cols,
 
 hipError_t launch_int4g_quantize(const void* w, int64_t N, int64_t K, uint8_t* q, void* scales,
                                  hipStream_t stream);
+// Device address of the quantizer's static scratch (kAmaxPartials uint32) on
+// the device of `stream` (the current device for the null stream).
+hipError_t quantize_scratch(hipStream_t stream, uint32_t** out);
 
 // NVFP4 GEMM kernels; out[M, N] bf16 = g_a g_w * A . W^T.
 // tiled: K % 128 == 0.  decode: M <= 16, K % 128 == 0.  simple: K % 16 == 0.

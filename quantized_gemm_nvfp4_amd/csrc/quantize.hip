@@ -16,6 +16,8 @@
 // INT4 ("Cuantización e inferencia local", formula block, b = 4): per row
 // and group of 128 values, s = max|w| / 7 stored as fp16, q = clamp(rint(w /
 // s), -7, 7) stored as two's-complement nibbles.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -399,6 +401,47 @@ hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint
   }
   return launch_nvfp4_quantize_pass2(x, rows, cols, codes, scales, gscale, use_given, rule, npartial, workspace,
                                      stream);
+}
+
+// ---- scratch for callers that cannot allocate ------------------------------
+// nvfp4_quantize_noalloc keeps the first pass's partial maxima here instead
+// of in a caller workspace.  Each GPU holds its own copy of the array until
+// the process ends; host code never passes the array's name to a kernel (on
+// the host it only stands for the symbol), but the device address that
+// hipGetSymbolAddress returns for the device, looked up once per device with
+// that device current.
+static __device__ __align__(256) uint32_t scratch[kAmaxPartials];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t quantize_scratch(hipStream_t stream, uint32_t** out) {
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = (uint32_t*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_int4g_quantize(const void* w, int64_t N, int64_t K, uint8_t* q, void* scales,

@@ -179,6 +179,19 @@ def test_int4_validation():
     assert lib.nvfp4_gemm_w4a16_ex(A, B, C, D, E, big, big, 256, 0, None) == UNSUP and "2^40" in _err()
 
 
+def test_quantize_noalloc_validation():
+    lib = q.lib()
+    f = lib.nvfp4_quantize_noalloc
+    # x, rows, cols, codes, scales, g, use_given, stream
+    assert f(None, 4, 32, B, C, D, 0, None) == INVALID and "x_bf16" in _err()
+    assert f(A, 4, 24, B, C, D, 0, None) == SHAPE
+    assert f(A, 4, 32, ODD, C, D, 0, None) == ALIGN
+    assert f(A, 4, 32, A, C, D, 0, None) == INVALID and "overlap" in _err()
+    assert f(A, -1, 32, B, C, D, 0, None) == INVALID
+    assert f(A, 1 << 30, 1 << 30, B, C, D, 0, None) == UNSUP
+    assert f(A, 0, 32, B, C, D, 0, None) == OK
+
+
 def test_lora_workspace_size():
     f = q.lib().nvfp4_quantize_lora_workspace_bytes
     # one K slice: only the 1024 partial maxima
