@@ -53,6 +53,8 @@ __device__ __forceinline__ short8v as_short8(const uint4& v) { return __builtin_
 }  // namespace
 
 // ---- M <= 16: stream the weight once -------------------------------------
+// (Serves 3 <= M <= 16 when K % 512 != 0 or K > 32768; other decode shapes
+// take the activation-stationary kernel below or the row-slot GEMV.)
 // A workgroup owns kI4Groups x 16 weight rows; its kI4Waves waves take steps
 // of two 128-value groups (128 bytes of a row) in turn, step t going to wave
 // t % kI4Waves, and are summed in LDS in a fixed order.
@@ -157,6 +159,259 @@ __global__ __launch_bounds__(64 * kI4Waves) void int4g_gemm_decode_kernel(const 
       const int m = 4 * (ln >> 4) + r;
       if (m < M) out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(sum[r]);
     }
+  }
+}
+
+// ---- 3 <= M <= 16: activation-stationary GEMM, weight through LDS ---------
+// The decode kernel above loads the weight straight into the MFMA's operand
+// layout, 16 rows x 64 bytes per instruction, and reloads its x slice for
+// every 112 rows; both cost: a pure read of this layout ran at ~60% of the
+// speed of contiguous rows, and the x reloads (x is four times the weight's
+// bytes per K range at M = 16) were a third of its loads.  Here:
+//  - Wave w of the workgroup owns the 512-value K piece p * kXsWaves + w of
+//    every weight row in pass p; its slice of x (16 rows x 512 values) is
+//    loaded once per pass into registers, in MFMA order, with the -8 offset
+//    terms of its four groups.
+//  - The weight arrives through LDS: per 16-row group the wave copies its
+//    piece (16 rows x 256 bytes) with four LDS-DMA instructions, each 4 rows
+//    x 256 contiguous bytes (global memory serves 4-row bands nearly as fast
+//    as whole rows), and the 16 x 4 group scales with a fifth, into a
+//    private ring of kXsDepth stages, so no barrier is needed until the
+//    epilogue.  Lane 4 c + r of a code copy takes bytes [16 c, 16 c + 16) of
+//    band row r, and each 1 KB copy region is padded by 64 bytes, so the
+//    MFMA-order reads below hit 16 different banks.
+//  - Lane (n, g) then reads row n's bytes [64 G + 16 g, +16) for group G:
+//    the 32 values of MFMA steps (G, 0..3), whose K positions the x slice
+//    was loaded to match.  Per group: its offset term, four MFMAs
+//    (v_mfma_f32_16x16x32_bf16, x as A, the weight q + 8 as B), and one
+//    multiply-add by the lane's column scale.
+//  - The row groups are taken in batches of kRG; after each batch the ring
+//    is drained and the waves' accumulators are added through it, in wave
+//    order.
+// Needs K % 512 == 0 (whole pieces; every 4-byte scale pair aligned).
+namespace {
+constexpr int kXsWaves = 8;
+constexpr int kXsPiece = 512;                     // K values per wave per pass
+constexpr int kXsPass = kXsWaves * kXsPiece;      // K values per pass
+constexpr int kXsDepth = 4;                       // stages in flight per wave (one LDS object each)
+constexpr int kXsRegion = 1024 + 64;              // one code copy (4 rows x 256 B) + bank padding
+constexpr int kXsScaleOff = 4 * kXsRegion;        // 16 rows x 4 fp16 scales (256 B copied)
+constexpr int kXsStage = kXsScaleOff + 256;
+constexpr int kXsStageLoads = 5;                  // LDS-DMA instructions per stage
+
+#define INT4_XS_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
+#define INT4_XS_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+// A workgroup barrier without the memory fence of __syncthreads() (which
+// would drain the copies in flight).
+__device__ __forceinline__ void xs_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+}  // namespace
+
+// The four ring slots are distinct LDS objects and every slot index below is
+// a compile-time constant (row group rg uses slot rg % 4; kRG is a multiple
+// of 4), so the compiler can see that the copies in flight never alias the
+// slot being read and waits only where the explicit counts say.
+__shared__ __attribute__((aligned(1024))) uint8_t g_xs0[kXsWaves][kXsStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_xs1[kXsWaves][kXsStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_xs2[kXsWaves][kXsStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_xs3[kXsWaves][kXsStage];
+
+namespace {
+template <int S>
+__device__ __forceinline__ uint8_t* xs_slot(int wave) {
+  return S == 0 ? g_xs0[wave] : (S == 1 ? g_xs1[wave] : (S == 2 ? g_xs2[wave] : g_xs3[wave]));
+}
+
+// Byte address in LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+typedef unsigned uint4v __attribute__((ext_vector_type(4)));
+typedef unsigned uint2v __attribute__((ext_vector_type(2)));
+
+struct XsCtx {
+  const uint8_t* q;
+  const uint16_t* s;
+  int r0, rows, bt, npass, nstages, wave;
+  uint32_t row_bytes, ng, lane_q, lane_s;
+};
+
+// Copies of stage t (pass t / kRG, row group t % kRG of batch bt) into slot
+// S.  The lane parts of the offsets are fixed; the stage's rows and piece go
+// into the buffer resources (uniform), whose ranges end at the workgroup's
+// last row, so rows past it and stages past the batch read zeros.
+template <int kRG, int S>
+__device__ __forceinline__ void xs_issue(const XsCtx& c, int t_in) {
+  // (opaque to the compiler: folding t's known pattern let it hoist every
+  // row group's lane offsets out of the pass loop)
+  const int t = __builtin_amdgcn_readfirstlane(t_in);
+  const int p = t / kRG, rg = t % kRG;
+  const int row0 = (c.bt * kRG + rg) * 16;
+  const int pc = p * kXsWaves + c.wave;                        // piece index
+  const bool valid = t < c.nstages && pc * (kXsPiece / 2) < (int)c.row_bytes;
+  uint8_t* dst = xs_slot<S>(c.wave);
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int left = valid ? min(max(c.rows - row0 - 4 * qq, 0), 4) : 0;
+    const auto rq = buffer_of(c.q + (int64_t)(c.r0 + row0 + 4 * qq) * c.row_bytes + pc * (kXsPiece / 2),
+                              (uint32_t)left * c.row_bytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t)(dst + qq * kXsRegion), 16, c.lane_q, 0, 0, 0);
+  }
+  const int sleft = valid ? min(max(c.rows - row0, 0), 16) : 0;
+  const auto rs = buffer_of(c.s + (int64_t)(c.r0 + row0) * c.ng + pc * 4,
+                            sleft > 0 ? (uint32_t)(sleft - 1) * c.ng * 2u + 8u : 0u);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t)(dst + kXsScaleOff), 4, c.lane_s, 0, 0, 0);
+}
+
+// Stage t from slot S into acc: wait for its copies, read the 16 rows' bytes
+// in MFMA order and their scales, refill the slot with stage t + kXsDepth,
+// then four groups of (offset term + 4 MFMAs) * scale.
+template <int kRG, int S>
+__device__ __forceinline__ void xs_stage(const XsCtx& c, int t, int lane, const uint4 (&xv)[4][4],
+                                         const float4v (&off)[4], float4v& acc) {
+  const int n16 = lane & 15, g4 = lane >> 4;
+  INT4_XS_WAIT_VMCNT((kXsDepth - 1) * kXsStageLoads);   // later stages' copies may stay in flight
+  const uint8_t* src = xs_slot<S>(c.wave);
+  // The four code reads (groups G at +256 G) and the scale read, written as
+  // one asm block that also waits for them: the compiler's own tracking of
+  // LDS copies lost track of the slot after the first read and waited for
+  // every copy in flight before the others.  (The wait inside the block
+  // keeps no load in flight past it.)
+  const uint32_t a_w = lds_addr(src + (n16 >> 2) * kXsRegion + 16 * (4 * g4 + (n16 & 3)));
+  const uint32_t a_s = lds_addr(src + kXsScaleOff + 8 * n16);
+  uint4v w0, w1, w2, w3;
+  uint2v sbv;
+  asm volatile(
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %5 offset:256\n\t"
+      "ds_read_b128 %2, %5 offset:512\n\t"
+      "ds_read_b128 %3, %5 offset:768\n\t"
+      "ds_read_b64 %4, %6\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(sbv)
+      : "v"(a_w), "v"(a_s)
+      : "memory");
+  const uint4 w[4] = {make_uint4(w0[0], w0[1], w0[2], w0[3]), make_uint4(w1[0], w1[1], w1[2], w1[3]),
+                      make_uint4(w2[0], w2[1], w2[2], w2[3]), make_uint4(w3[0], w3[1], w3[2], w3[3])};
+  const uint2 sb = make_uint2(sbv[0], sbv[1]);
+  xs_issue<kRG, S>(c, t + kXsDepth);                     // the slot may be overwritten now
+  const float sc[4] = {f16_bits_to_f32(sb.x & 0xFFFFu), f16_bits_to_f32(sb.x >> 16), f16_bits_to_f32(sb.y & 0xFFFFu),
+                       f16_bits_to_f32(sb.y >> 16)};
+#pragma unroll
+  for (int G = 0; G < 4; ++G) {
+    float4v tmp = off[G];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      tmp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_short8(xv[G][jj]), int4x8_offset_bf16(word_of(w[G], jj)), tmp,
+                                                    0, 0, 0);
+    acc += sc[G] * tmp;
+  }
+  // keep the unrolled row groups apart (hoisting the next group's reads and
+  // decoding above this one's MFMAs only raised register pressure)
+  __builtin_amdgcn_sched_barrier(0);
+}
+}  // namespace
+
+template <int kRG>
+__global__ __launch_bounds__(64 * kXsWaves) void int4g_gemm_xs_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint8_t* __restrict__ q,
+                                                                     const uint16_t* __restrict__ s,
+                                                                     uint16_t* __restrict__ out, int M, int N,
+                                                                     int K) {
+  static_assert(kRG % kXsDepth == 0, "row group rg uses slot rg % kXsDepth");
+  static_assert(sizeof(float4v) * kXsWaves * kRG * 64 <= sizeof(g_xs0) * kXsDepth, "the reduction reuses the ring");
+  float4v(*s_red)[kRG][64] = (float4v(*)[kRG][64])&g_xs0[0][0];     // [wave][rg][lane], after the drain
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15, g4 = lane >> 4;          // MFMA column (weight row) / K quarter
+  const int r0 = (int)((int64_t)blockIdx.x * N / gridDim.x), r1 = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x);
+  const uint32_t row_bytes = (uint32_t)K / 2, ng = (uint32_t)K / 128;
+  const auto xr = buffer_of(x, (uint32_t)M * (uint32_t)K * 2u);    // rows >= M read as zero
+  const int npass = (K + kXsPass - 1) / kXsPass;
+  const int nbatch = (r1 - r0 + 16 * kRG - 1) / (16 * kRG);
+  const short8v c8 = {kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16,
+                      kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16};
+  XsCtx c;
+  c.q = q;
+  c.s = s;
+  c.r0 = r0;
+  c.rows = r1 - r0;
+  c.npass = npass;
+  c.nstages = npass * kRG;
+  c.wave = wave;
+  c.row_bytes = row_bytes;
+  c.ng = ng;
+  // copy lane 4 c + r: band row r, bytes [16 c, +16); scale lane 2 n + h
+  // (< 32): row n, groups 2 h and 2 h + 1 of the piece
+  c.lane_q = ((uint32_t)lane & 3u) * row_bytes + 16u * ((uint32_t)lane >> 2);
+  c.lane_s = lane < 32 ? ((uint32_t)lane >> 1) * ng * 2u + 4u * ((uint32_t)lane & 1u) : kBufferOob;
+
+  for (int bt = 0; bt < nbatch; ++bt) {
+    c.bt = bt;
+    xs_issue<kRG, 0>(c, 0);
+    xs_issue<kRG, 1>(c, 1);
+    xs_issue<kRG, 2>(c, 2);
+    xs_issue<kRG, 3>(c, 3);
+    float4v acc[kRG];
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) acc[rg] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < npass; ++p) {
+      // x rows m = n16 (A rows), 8 values per MFMA step (G, jj) at K offset
+      // 128 G + 32 g + 8 jj of this wave's piece
+      const uint32_t k0 = (uint32_t)(p * kXsWaves + wave) * kXsPiece;
+      uint4 xv[4][4];
+#pragma unroll
+      for (int G = 0; G < 4; ++G)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint32_t k = k0 + 128u * G + 32u * g4 + 8u * jj;
+          xv[G][jj] = buffer_load16(xr, k < (uint32_t)K ? ((uint32_t)n16 * (uint32_t)K + k) * 2u : kBufferOob);
+        }
+      float4v off[4];
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        off[G] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          off[G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_short8(xv[G][jj]), c8, off[G], 0, 0, 0);
+      }
+      const int t0 = p * kRG;
+#pragma unroll
+      for (int rg = 0; rg < kRG; rg += 4) {
+        xs_stage<kRG, 0>(c, t0 + rg, lane, xv, off, acc[rg]);
+        xs_stage<kRG, 1>(c, t0 + rg + 1, lane, xv, off, acc[rg + 1]);
+        xs_stage<kRG, 2>(c, t0 + rg + 2, lane, xv, off, acc[rg + 2]);
+        xs_stage<kRG, 3>(c, t0 + rg + 3, lane, xv, off, acc[rg + 3]);
+      }
+    }
+    // drain the copies past the batch, then add the waves' partial sums in
+    // wave order; D[m][n]: lane n + 16 (m / 4), register m % 4
+    INT4_XS_WAIT_VMCNT(0);
+    xs_barrier();
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) s_red[wave][rg][lane] = acc[rg];
+    INT4_XS_WAIT_LGKM0();
+    xs_barrier();
+    for (int e = threadIdx.x; e < kRG * 64; e += 64 * kXsWaves) {
+      const int rg = e >> 6, ln = e & 63;
+      float4v sum = s_red[0][rg][ln];
+#pragma unroll
+      for (int wv = 1; wv < kXsWaves; ++wv) sum += s_red[wv][rg][ln];
+      const int row = (bt * kRG + rg) * 16 + (ln & 15);
+      if (row >= r1 - r0) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * (ln >> 4) + r;
+        if (m < M) out[(int64_t)m * N + r0 + row] = (uint16_t)f32_to_bf16_rne(sum[r]);
+      }
+    }
+    INT4_XS_WAIT_LGKM0();
+    xs_barrier();                // the ring is refilled by the next batch
   }
 }
 
@@ -502,6 +757,23 @@ hipError_t launch_int4g_gemm_decode(const void* x, const uint8_t* q, const void*
       launch_int4_rowslot<2, 8>(x, q, s, out, (int)M, (int)N, (int)K, stream);
       return hipGetLastError();
     }
+  }
+  if (M >= 3 && K % kXsPiece == 0 && (int64_t)M * K * 2 < (1ll << 31)) {
+    const int64_t cus = device_cus();
+    // 8 row groups (128 rows) per batch and, where N allows, one batch per
+    // workgroup; 4 row groups when N has fewer than 128 rows per CU
+    const bool big = N >= 128 * cus / 2;
+    const int64_t per = big ? 128 : 64;
+    const int64_t grid = (N + per - 1) / per < cus ? (N + per - 1) / per : cus;
+    const dim3 g3((unsigned)grid), b3(64 * kXsWaves);
+    const uint16_t* xx = (const uint16_t*)x;
+    const uint16_t* ss = (const uint16_t*)s;
+    uint16_t* oo = (uint16_t*)out;
+    if (big)
+      hipLaunchKernelGGL(int4g_gemm_xs_kernel<8>, g3, b3, 0, stream, xx, q, ss, oo, (int)M, (int)N, (int)K);
+    else
+      hipLaunchKernelGGL(int4g_gemm_xs_kernel<4>, g3, b3, 0, stream, xx, q, ss, oo, (int)M, (int)N, (int)K);
+    return hipGetLastError();
   }
   if (M >= 8 && N >= 112ll * device_cus())
     hipLaunchKernelGGL((int4g_gemm_decode_kernel<7, kI4Waves>), dim3((unsigned)((N + 111) / 112)), dim3(64 * kI4Waves), 0,

@@ -99,13 +99,27 @@ def test_int4_gemv_ragged(M, N, K):
                                    (8, 28679, 384), (13, 28800, 256)])
 def test_int4_decode_shapes(M, N, K):
     # M <= 2 runs the row-slot GEMV (1 KB slots of 16 groups, partial last
-    # slot, ragged N); K > 32768 and 3 <= M <= 16 run the row-block kernel
+    # slot, ragged N); K > 32768 and 3 <= M <= 16 with K % 512 != 0 run the
+    # row-block kernel
     # (64 rows per workgroup, N ragged against it; an odd group count leaves
     # a half step; K = 2304 gives its 8 waves unequal step counts; from M = 8
     # with N >= 112 per compute unit, 112 rows per workgroup, N ragged).
     x = workloads.random_bf16(M + K, (M, K), outlier_frac=0.01, outlier_mul=20)
     w = workloads.random_bf16(N + K + 1, (N, K), sigma=0.02, zero_frac=0.05)
     check_gemv(x, w, algos=(0, 2), label=f"int4 decode {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 33, 512), (5, 100, 4608), (16, 16500, 8192), (11, 33769, 1024),
+                                   (4, 70, 12288), (16, 1, 512), (8, 129, 4096)])
+def test_int4_stationary_shapes(M, N, K):
+    # 3 <= M <= 16 with K % 512 == 0 runs the activation-stationary kernel:
+    # 512-value pieces per wave and 4096 values per pass (K = 4608 leaves a
+    # pass of one piece; K = 12288 takes three passes), 4 or 8 row groups per
+    # batch (N >= 64 rows per compute unit takes 8), two batches when a
+    # workgroup holds more than 128 rows (N = 33769), N not a multiple of 16.
+    x = workloads.random_bf16(M * 7 + K, (M, K), outlier_frac=0.01, outlier_mul=20)
+    w = workloads.random_bf16(N * 3 + K, (N, K), sigma=0.02, zero_frac=0.05)
+    check_gemv(x, w, algos=(0, 2), label=f"int4 stationary {M}x{N}x{K}")
 
 
 def test_int4_config():
