@@ -197,4 +197,30 @@ __device__ __forceinline__ uint32_t int4x2_to_bf16x2(uint32_t w, int sel) {
   return bhi | blo;
 }
 
+// ---- waits, barriers and LDS addresses for kernels that copy into LDS ----
+typedef unsigned uint2v __attribute__((ext_vector_type(2)));
+typedef unsigned uint4v __attribute__((ext_vector_type(4)));
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+// s_waitcnt lgkmcnt(0): this wave's LDS accesses are complete.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// A workgroup barrier without the memory fence of __syncthreads() (which
+// would also wait for every copy in flight).
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Byte address in LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
 }  // namespace nvfp4k

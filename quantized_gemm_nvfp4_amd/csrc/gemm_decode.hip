@@ -24,6 +24,7 @@
 namespace nvfp4k {
 
 namespace {
+typedef __attribute__((address_space(3))) void* lds_void_t;
 constexpr int kMaxSlots = 16;                   // row-slot kernel: K <= 16 * 2048
 constexpr uint32_t kOob = kBufferOob;
 
@@ -307,6 +308,288 @@ __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_gemv_stream_kernel(
   }
   flush();
 }
+
+// ---------------------------------------------------------------------------
+// Weight-only GEMM for 3 <= M <= 16 (bf16 activation x NVFP4 weight),
+// activation-stationary with the weight through LDS: the structure of the
+// INT4 kernel of the same name, so the weight is read once for all M rows.
+//  - Each of the workgroup's nw waves owns the 512-value K piece p nw + w of
+//    every weight row in pass p (nw and the pass count chosen so the pieces
+//    fill the passes; the last piece of a row may be partial).  Its slice of
+//    the activation (16 rows x 512 values) sits in registers for the pass in
+//    MFMA order, bf16 converted to fp16 after a per-row power of two that
+//    puts the row's largest magnitude in the slice in [2^15, 2^16) (exact
+//    for values within 2^32 of it); the partial sums are multiplied back
+//    before they are added.
+//  - Per 16-row group the wave copies its piece of the codes (4 rows x 256
+//    contiguous bytes per LDS-DMA) and of the scales (2 x 8 rows x 32 bytes)
+//    into a private ring of four stages, each a distinct LDS object, so
+//    only the explicit counts wait; the slot is read by one asm block that
+//    also waits for its reads.
+//  - Lane (n, g) decodes row n's bytes [64 G + 16 g, +16) (group G of the
+//    piece: 32 values, two blocks) with their two scales, and v_mfma_f32_
+//    16x16x32_f16 takes the activation as A (rows m) and the weight as B
+//    (columns n).  The decoded weight is exact in fp16, as elsewhere.
+//  - Row groups go in batches of kRG; after a batch the ring is drained and
+//    the waves' sums are added through it in wave order, then scaled by g_w
+//    and rounded.
+namespace {
+constexpr int kNxWaves = 8;
+constexpr int kNxPiece = 512;                     // K values per wave per pass
+constexpr int kNxDepth = 4;                       // stages in flight per wave
+constexpr int kNxRegion = 1024 + 64;              // one code copy (4 rows x 256 B) + bank padding
+constexpr int kNxScaleOff = 4 * kNxRegion;        // 16 rows x 32 scale bytes
+constexpr int kNxStage = kNxScaleOff + 512;
+constexpr int kNxStageLoads = 6;                  // LDS-DMA instructions per stage
+}  // namespace
+
+__shared__ __attribute__((aligned(1024))) uint8_t g_nx0[kNxWaves][kNxStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_nx1[kNxWaves][kNxStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_nx2[kNxWaves][kNxStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_nx3[kNxWaves][kNxStage];
+
+namespace {
+template <int S>
+__device__ __forceinline__ uint8_t* nx_slot(int wave) {
+  return S == 0 ? g_nx0[wave] : (S == 1 ? g_nx1[wave] : (S == 2 ? g_nx2[wave] : g_nx3[wave]));
+}
+
+struct NxCtx {
+  const uint8_t* wc;
+  const uint8_t* ws;
+  int r0, rows, bt, nstages, wave, nw;
+  uint32_t row_bytes, row_scales, lane_q, lane_s, lane_col, lane_scol;
+};
+
+// Copies of stage t (pass t / kRG, row group t % kRG of batch bt) into slot
+// S; the stage's rows and piece go into the (uniform) buffer resources,
+// whose ranges end at the workgroup's last row.
+template <int kRG, int S>
+__device__ __forceinline__ void nx_issue(const NxCtx& c, int t_in) {
+  const int t = __builtin_amdgcn_readfirstlane(t_in);     // (keeps lane offsets from being hoisted per stage)
+  const int p = t / kRG, rg = t % kRG;
+  const int row0 = (c.bt * kRG + rg) * 16;
+  const int pc = p * c.nw + c.wave;
+  const bool valid = t < c.nstages && pc * (kNxPiece / 2) < (int)c.row_bytes;
+  // the last piece of a row may be partial (K % 512 == 128, 256 or 384):
+  // its lanes past the row's end read zeros instead of the next row
+  const int vbytes = valid ? min((int)c.row_bytes - pc * (kNxPiece / 2), kNxPiece / 2) : 0;
+  const uint32_t lq = c.lane_col < (uint32_t)vbytes ? c.lane_q : kOob;
+  const uint32_t ls = c.lane_scol < (uint32_t)(vbytes / 8) ? c.lane_s : kOob;
+  uint8_t* dst = nx_slot<S>(c.wave);
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int left = valid ? min(max(c.rows - row0 - 4 * qq, 0), 4) : 0;
+    const auto rq = buffer_of(c.wc + (int64_t)(c.r0 + row0 + 4 * qq) * c.row_bytes + pc * (kNxPiece / 2),
+                              (uint32_t)left * c.row_bytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t)(dst + qq * kNxRegion), 16, lq, 0, 0, 0);
+  }
+  // scales: two copies of 8 rows x 32 bytes (4 bytes per lane)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int sleft = valid ? min(max(c.rows - row0 - 8 * h, 0), 8) : 0;
+    const auto rs = buffer_of(c.ws + (int64_t)(c.r0 + row0 + 8 * h) * c.row_scales + pc * (kNxPiece / 16),
+                              sleft > 0 ? (uint32_t)(sleft - 1) * c.row_scales + 32u : 0u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t)(dst + kNxScaleOff + 256 * h), 4, ls, 0, 0, 0);
+  }
+}
+
+// Stage t from slot S: wait for its copies, read and decode the 16 rows'
+// piece in MFMA order, refill the slot with stage t + kNxDepth, 16 MFMAs.
+template <int kRG, int S>
+__device__ __forceinline__ void nx_stage(const NxCtx& c, int t, int lane, const half8v (&xv)[4][4],
+                                         const float4v& unscale, float4v& acc) {
+  const int n16 = lane & 15, g4 = lane >> 4;
+  wait_vmcnt<(kNxDepth - 1) * kNxStageLoads>();   // later stages' copies may stay in flight
+  const uint8_t* src = nx_slot<S>(c.wave);
+  const uint32_t a_w = lds_addr(src + (n16 >> 2) * kNxRegion + 16 * (4 * g4 + (n16 & 3)));
+  const uint32_t a_s = lds_addr(src + kNxScaleOff + 32 * n16 + 2 * g4);
+  uint4v w0, w1, w2, w3;
+  uint32_t s0, s1, s2, s3;
+  // one asm block with its own wait (the compiler's tracking of the copies
+  // would wait for every copy in flight before the second read)
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:256\n\t"
+      "ds_read_b128 %2, %8 offset:512\n\t"
+      "ds_read_b128 %3, %8 offset:768\n\t"
+      "ds_read_u16 %4, %9\n\t"
+      "ds_read_u16 %5, %9 offset:8\n\t"
+      "ds_read_u16 %6, %9 offset:16\n\t"
+      "ds_read_u16 %7, %9 offset:24\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
+      : "v"(a_w), "v"(a_s)
+      : "memory");
+  nx_issue<kRG, S>(c, t + kNxDepth);              // the slot may be overwritten now
+  const uint4 w[4] = {make_uint4(w0[0], w0[1], w0[2], w0[3]), make_uint4(w1[0], w1[1], w1[2], w1[3]),
+                      make_uint4(w2[0], w2[1], w2[2], w2[3]), make_uint4(w3[0], w3[1], w3[2], w3[3])};
+  const uint32_t sb[4] = {s0, s1, s2, s3};
+  float4v tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int G = 0; G < 4; ++G) {
+    const half2v sc = e4m3x2_to_f16x2_div256(sb[G]);
+    const half2v lo = {sc.x, sc.x}, hi = {sc.y, sc.y};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[G][jj], dequant8_f16_div256(word_of(w[G], jj), jj < 2 ? lo : hi),
+                                                   tmp, 0, 0, 0);
+  }
+  acc += tmp * unscale;
+  __builtin_amdgcn_sched_barrier(0);
+}
+}  // namespace
+
+template <int kRG>
+__global__ __launch_bounds__(64 * kNxWaves) void nvfp4_w4a16_xs_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
+    const float* __restrict__ w_g, uint16_t* __restrict__ out, int M, int N, int K) {
+  static_assert(kRG % kNxDepth == 0, "row group rg uses slot rg % kNxDepth");
+  static_assert(sizeof(float4v) * kNxWaves * kRG * 64 <= sizeof(g_nx0) * kNxDepth, "the reduction reuses the ring");
+  float4v(*s_red)[kRG][64] = (float4v(*)[kRG][64])&g_nx0[0][0];     // [wave][rg][lane], after the drain
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int r0 = (int)((int64_t)blockIdx.x * N / gridDim.x), r1 = (int)((int64_t)(blockIdx.x + 1) * N / gridDim.x);
+  const uint32_t row_bytes = (uint32_t)K / 2, row_scales = (uint32_t)K / 16;
+  const int nw = blockDim.x >> 6;                     // waves (<= kNxWaves), one K piece each per pass
+  const int npass = (K + nw * kNxPiece - 1) / (nw * kNxPiece);
+  const int nbatch = (r1 - r0 + 16 * kRG - 1) / (16 * kRG);
+  NxCtx c;
+  c.wc = w_codes;
+  c.ws = w_scales;
+  c.r0 = r0;
+  c.rows = r1 - r0;
+  c.nstages = npass * kRG;
+  c.wave = wave;
+  c.nw = nw;
+  c.row_bytes = row_bytes;
+  c.row_scales = row_scales;
+  // code copy lane 4 c + r: band row r, bytes [16 c, +16); scale copy lane
+  // 8 n + b: row n (of 8), scale bytes [4 b, +4) of the piece
+  c.lane_q = ((uint32_t)lane & 3u) * row_bytes + 16u * ((uint32_t)lane >> 2);
+  c.lane_s = ((uint32_t)lane >> 3) * row_scales + 4u * ((uint32_t)lane & 7u);
+  c.lane_col = 16u * ((uint32_t)lane >> 2);       // the lane's byte column in a piece (codes)
+  c.lane_scol = 4u * ((uint32_t)lane & 7u);       // and in the piece's scales
+
+  for (int bt = 0; bt < nbatch; ++bt) {
+    c.bt = bt;
+    nx_issue<kRG, 0>(c, 0);
+    nx_issue<kRG, 1>(c, 1);
+    nx_issue<kRG, 2>(c, 2);
+    nx_issue<kRG, 3>(c, 3);
+    float4v acc[kRG];
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) acc[rg] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < npass; ++p) {
+      // activation row m = n16, MFMA step (G, jj): K offset 128 G + 32 g + 8 jj of the piece
+      const uint32_t k0 = (uint32_t)(p * nw + wave) * kNxPiece;
+      half8v xv[4][4];
+      float4v unscale = {1.f, 1.f, 1.f, 1.f};
+      {
+        const auto xr = buffer_of(x, (uint32_t)M * (uint32_t)K * 2u);   // rows >= M read as zero
+        uint4 xb[4][4];
+        uint32_t mx = 0;
+#pragma unroll
+        for (int G = 0; G < 4; ++G)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const uint32_t k = k0 + 128u * G + 32u * g4 + 8u * jj;
+            xb[G][jj] = buffer_load16(xr, k < (uint32_t)K ? ((uint32_t)n16 * (uint32_t)K + k) * 2u : kOob);
+            mx = max(max(max(mx, bf16x2_absmax_bits(xb[G][jj].x)), bf16x2_absmax_bits(xb[G][jj].y)),
+                     max(bf16x2_absmax_bits(xb[G][jj].z), bf16x2_absmax_bits(xb[G][jj].w)));
+          }
+        // the row's maximum over its four lanes (lanes n16 + 16 g)
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+        // k = (biased exponent of the max) - 127 - 15, kept where 2^-k and
+        // 2^k are normal fp32 numbers
+        const int kexp = min(max((int)(mx >> 7) - 142, -126), 126);
+        const float pre = __uint_as_float((uint32_t)(127 - kexp) << 23);
+        const float post = __uint_as_float((uint32_t)(127 + kexp) << 23);
+#pragma unroll
+        for (int G = 0; G < 4; ++G)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const uint32_t wv[4] = {xb[G][jj].x, xb[G][jj].y, xb[G][jj].z, xb[G][jj].w};
+            half8v h;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const half2v pr = __builtin_bit_cast(
+                  half2v, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(wv[u] << 16) * pre,
+                                                     __uint_as_float(wv[u] & 0xFFFF0000u) * pre));
+              h[2 * u] = pr.x;
+              h[2 * u + 1] = pr.y;
+            }
+            xv[G][jj] = h;
+          }
+        // D row m = 4 (lane / 16) + r takes row m's factor
+        const int src = 4 * (lane >> 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) unscale[r] = __shfl(post, src + r);
+      }
+      const int t0 = p * kRG;
+#pragma unroll
+      for (int rg = 0; rg < kRG; rg += 4) {
+        nx_stage<kRG, 0>(c, t0 + rg, lane, xv, unscale, acc[rg]);
+        nx_stage<kRG, 1>(c, t0 + rg + 1, lane, xv, unscale, acc[rg + 1]);
+        nx_stage<kRG, 2>(c, t0 + rg + 2, lane, xv, unscale, acc[rg + 2]);
+        nx_stage<kRG, 3>(c, t0 + rg + 3, lane, xv, unscale, acc[rg + 3]);
+      }
+    }
+    // drain the copies past the batch, then add the waves' sums in wave
+    // order; D[m][n]: lane n + 16 (m / 4), register m % 4
+    wait_vmcnt<0>();
+    barrier_nofence();
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) s_red[wave][rg][lane] = acc[rg];
+    wait_lgkm0();
+    barrier_nofence();
+    const float gg = *w_g;
+    for (int e = threadIdx.x; e < kRG * 64; e += 64 * nw) {
+      const int rg = e >> 6, ln = e & 63;
+      float4v sum = s_red[0][rg][ln];
+      for (int wv = 1; wv < nw; ++wv) sum += s_red[wv][rg][ln];
+      const int row = (bt * kRG + rg) * 16 + (ln & 15);
+      if (row >= r1 - r0) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * (ln >> 4) + r;
+        if (m < M) out[(int64_t)m * N + r0 + row] = (uint16_t)f32_to_bf16_rne(sum[r] * gg);
+      }
+    }
+    wait_lgkm0();
+    barrier_nofence();                // the ring is refilled by the next batch
+  }
+}
+
+namespace {
+// The weight-only GEMM for 3 <= M <= 16; false if the shape is outside its
+// range.  Waves per workgroup and passes: P = ceil(pieces / 8) passes of
+// ceil(pieces / P) waves, so few pieces of the last pass are empty (the
+// 5376-value rows of the decode weight: 11 pieces, 2 passes of 6).
+bool launch_w4a16_xs(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out, int64_t M,
+                     int64_t N, int64_t K, hipStream_t stream) {
+  if (M < 3 || M > 16 || K % 128 != 0 || K <= 0 || K > (1 << 24) || M * K * 2 >= (1ll << 31)) return false;
+  const int64_t pieces = (K + kNxPiece - 1) / kNxPiece;
+  const int64_t passes = (pieces + kNxWaves - 1) / kNxWaves;
+  const int nw = (int)((pieces + passes - 1) / passes);
+  const int64_t cus = device_cus();
+  // 8 row groups (128 rows) per batch and, where N allows, one batch per
+  // workgroup; 4 row groups when N has fewer than 64 rows per CU
+  const bool big = N >= 64 * cus;
+  const int64_t per = big ? 128 : 64;
+  const int64_t grid = (N + per - 1) / per < cus ? (N + per - 1) / per : cus;
+  const dim3 g3((unsigned)grid), b3(64 * nw);
+  const uint16_t* xx = (const uint16_t*)x;
+  uint16_t* o = (uint16_t*)out;
+  if (big)
+    hipLaunchKernelGGL(nvfp4_w4a16_xs_kernel<8>, g3, b3, 0, stream, xx, wc, ws, wg, o, (int)M, (int)N, (int)K);
+  else
+    hipLaunchKernelGGL(nvfp4_w4a16_xs_kernel<4>, g3, b3, 0, stream, xx, wc, ws, wg, o, (int)M, (int)N, (int)K);
+  return true;
+}
+}  // namespace
 
 // ---------------------------------------------------------------------------
 // Weight-only row-slot GEMV (M <= 2): bf16 activation x NVFP4 weight.
@@ -594,21 +877,18 @@ bool nvfp4_w4a16_decode_supported(int64_t M, int64_t K) {
 
 hipError_t launch_nvfp4_w4a16_decode(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
                                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  // 8 rows per workgroup at M = 1 and 2: at M = 2 (21504 x 5376) 8 rows took
-  // 19.4 us per call against 21.5 us for 4 and 20.5 us for 6; 12 and more
-  // spill registers.
-  // From M = 3 the kernel runs once per pair of activation rows (and once
-  // more for an odd last row): each row's arithmetic is the M <= 2 kernel's,
-  // and the weight is read ceil(M / 2) times (21504 x 5376, M = 16: about
-  // 8 x 19 us, against ~1 ms for the one-output-per-thread kernel).
-  for (int64_t m0 = 0; m0 < M; m0 += 2) {
-    const uint16_t* xm = (const uint16_t*)x + m0 * K;
-    uint16_t* om = (uint16_t*)out + m0 * N;
-    if (M - m0 >= 2)
-      launch_w4a16_rowslot<2, 8>(xm, wc, ws, wg, om, 2, (int)N, (int)K, stream);
-    else
-      launch_w4a16_rowslot<1, 8>(xm, wc, ws, wg, om, 1, (int)N, (int)K, stream);
+  // M <= 2: the row-slot GEMV, 8 rows per workgroup (at M = 2 on 21504 x
+  // 5376, 8 rows took 19.4 us per call against 21.5 us for 4 and 20.5 us for
+  // 6; 12 and more spill registers).  3 <= M <= 16: the activation-
+  // stationary kernel, which reads the weight once for all rows.
+  if (M >= 3) {
+    if (!launch_w4a16_xs(x, wc, ws, wg, out, M, N, K, stream)) return hipErrorInvalidValue;
+    return hipGetLastError();
   }
+  if (M == 2)
+    launch_w4a16_rowslot<2, 8>(x, wc, ws, wg, out, 2, (int)N, (int)K, stream);
+  else
+    launch_w4a16_rowslot<1, 8>(x, wc, ws, wg, out, 1, (int)N, (int)K, stream);
   return hipGetLastError();
 }
 

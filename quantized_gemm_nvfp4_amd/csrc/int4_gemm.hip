@@ -199,16 +199,6 @@ constexpr int kXsScaleOff = 4 * kXsRegion;        // 16 rows x 4 fp16 scales (25
 constexpr int kXsStage = kXsScaleOff + 256;
 constexpr int kXsStageLoads = 5;                  // LDS-DMA instructions per stage
 
-#define INT4_XS_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
-#define INT4_XS_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
-
-// A workgroup barrier without the memory fence of __syncthreads() (which
-// would drain the copies in flight).
-__device__ __forceinline__ void xs_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 }  // namespace
 
 // The four ring slots are distinct LDS objects and every slot index below is
@@ -225,14 +215,6 @@ template <int S>
 __device__ __forceinline__ uint8_t* xs_slot(int wave) {
   return S == 0 ? g_xs0[wave] : (S == 1 ? g_xs1[wave] : (S == 2 ? g_xs2[wave] : g_xs3[wave]));
 }
-
-// Byte address in LDS of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
-
-typedef unsigned uint4v __attribute__((ext_vector_type(4)));
-typedef unsigned uint2v __attribute__((ext_vector_type(2)));
 
 struct XsCtx {
   const uint8_t* q;
@@ -275,7 +257,7 @@ template <int kRG, int S>
 __device__ __forceinline__ void xs_stage(const XsCtx& c, int t, int lane, const uint4 (&xv)[4][4],
                                          const float4v (&off)[4], float4v& acc) {
   const int n16 = lane & 15, g4 = lane >> 4;
-  INT4_XS_WAIT_VMCNT((kXsDepth - 1) * kXsStageLoads);   // later stages' copies may stay in flight
+  wait_vmcnt<(kXsDepth - 1) * kXsStageLoads>();   // later stages' copies may stay in flight
   const uint8_t* src = xs_slot<S>(c.wave);
   // The four code reads (groups G at +256 G) and the scale read, written as
   // one asm block that also waits for them: the compiler's own tracking of
@@ -391,12 +373,12 @@ __global__ __launch_bounds__(64 * kXsWaves) void int4g_gemm_xs_kernel(const uint
     }
     // drain the copies past the batch, then add the waves' partial sums in
     // wave order; D[m][n]: lane n + 16 (m / 4), register m % 4
-    INT4_XS_WAIT_VMCNT(0);
-    xs_barrier();
+    wait_vmcnt<0>();
+    barrier_nofence();
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) s_red[wave][rg][lane] = acc[rg];
-    INT4_XS_WAIT_LGKM0();
-    xs_barrier();
+    wait_lgkm0();
+    barrier_nofence();
     for (int e = threadIdx.x; e < kRG * 64; e += 64 * kXsWaves) {
       const int rg = e >> 6, ln = e & 63;
       float4v sum = s_red[0][rg][ln];
@@ -410,8 +392,8 @@ __global__ __launch_bounds__(64 * kXsWaves) void int4g_gemm_xs_kernel(const uint
         if (m < M) out[(int64_t)m * N + r0 + row] = (uint16_t)f32_to_bf16_rne(sum[r]);
       }
     }
-    INT4_XS_WAIT_LGKM0();
-    xs_barrier();                // the ring is refilled by the next batch
+    wait_lgkm0();
+    barrier_nofence();                // the ring is refilled by the next batch
   }
 }
 

@@ -45,6 +45,20 @@ def test_decode_shapes(M, N, K):
     check(x, w, algos=(0, 2, 3), label=f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(4, 300, 5376), (7, 20000, 4096), (16, 70, 12288), (9, 33000, 512),
+                                   (3, 1, 128), (12, 17, 4608)])
+def test_stationary_shapes(M, N, K):
+    # 3 <= M <= 16 runs the activation-stationary kernel: 512-value pieces
+    # per wave, 6 waves x 2 passes for K = 5376 (a half piece at the end of
+    # each row), 8 x 1 for 4096, 8 x 3 for 12288, 8 row groups per batch when
+    # N >= 64 rows per compute unit (N = 20000) and two batches when a
+    # workgroup holds more than 128 rows (N = 33000), a lone partial piece
+    # (K = 128), N not a multiple of 16.
+    x = workloads.random_bf16(M * 13 + K, (M, K), outlier_frac=0.01, outlier_mul=20)
+    w = workloads.random_bf16(N * 17 + K, (N, K), sigma=0.02, zero_frac=0.05)
+    check(x, w, algos=(0, 2), label=f"stationary {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(17, 40, 272), (1, 5, 32768 + 128), (5, 3, 16)])
 def test_simple_shapes(M, N, K):
     x = workloads.random_bf16(M * 7 + K, (M, K))
@@ -53,27 +67,30 @@ def test_simple_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("scale", [1e-30, 1e-6, 1e20])
-def test_activation_range_rescaling(scale):
-    # the decode kernel rescales each slot of x by a power of two before the
-    # fp16 conversion: tiny and huge activations stay within tolerance
-    x = (workloads.random_bf16(91, (2, 2048 * 3)).view(np.uint16))
+@pytest.mark.parametrize("M", [2, 5])
+def test_activation_range_rescaling(scale, M):
+    # the decode kernels rescale x by a power of two per 2048-value slot (M
+    # <= 2) or per row and 512-value piece (M >= 3) before the fp16
+    # conversion: tiny and huge activations stay within tolerance
+    x = (workloads.random_bf16(91, (M, 2048 * 3)).view(np.uint16))
     xv = (F.bf16_from_bits(x).astype(np.float64) * scale).astype(np.float32)
     xb = F.bf16_bits(F.bf16_round(xv).astype(np.float32))
     w = workloads.random_bf16(92, (24, 2048 * 3), sigma=0.02)
     check(xb, w, algos=(2,), label=f"x*{scale:g}")
 
 
-def test_wide_dynamic_range_within_a_slot():
+@pytest.mark.parametrize("M", [1, 4])
+def test_wide_dynamic_range_within_a_slot(M):
     rng = np.random.default_rng(93)
     K = 4096
-    mag = np.ldexp(1.0, rng.integers(-24, 12, size=(1, K))) * rng.choice([-1, 1], size=(1, K))
+    mag = np.ldexp(1.0, rng.integers(-24, 12, size=(M, K))) * rng.choice([-1, 1], size=(M, K))
     xb = F.bf16_bits(F.bf16_round(mag.astype(np.float32)).astype(np.float32))
     w = workloads.random_bf16(94, (40, K), sigma=0.02)
-    check(xb, w, algos=(2,), label="2^-24..2^12")
+    check(xb, w, algos=(2,), label=f"2^-24..2^12 M={M}")
 
 
 def test_decode_config():
     x_bits, _ = workloads.decode_x()
     w_bits = workloads.decode_w()
-    for M in (1, 2, 3, 16):
+    for M in (1, 2, 3, 4, 16):
         check(x_bits[:M], w_bits, algos=(0,), label=f"decode M={M}")
