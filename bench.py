@@ -328,7 +328,7 @@ def graph_time_us(torch, fn, iters, reps=9):
 
 
 def run_decode(torch, q, iters=64, copies=16):
-    """Decode on the 21504 x 5376 weight at M = 1, 4, 16; GB/s of algorithmic
+    """Decode on the 21504 x 5376 weight at M = 1, 2, 4, 16; GB/s of algorithmic
     bytes.  16 weight copies (~1.04 GB) are rotated so every call misses the
     256 MB last-level cache; calls are replayed from a HIP graph."""
     import workloads
@@ -337,7 +337,7 @@ def run_decode(torch, q, iters=64, copies=16):
     ws = [(w[0].clone(), w[1].clone(), w[2].clone()) for _ in range(copies)]
     N, K = 21504, 5376
     out = {}
-    for M in (1, 4, 16):
+    for M in (1, 2, 4, 16):
         x = dev_bf16(torch, x_bits[:M])
         a = q.nvfp4_quantize(x)
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
@@ -346,10 +346,13 @@ def run_decode(torch, q, iters=64, copies=16):
         us = graph_time_us(torch, lambda i: q.nvfp4_gemm(a, ws[i % copies], out=y), iters)
         assert torch.equal(y, ref), "graph replay differs from the eager call"
 
-        def with_quant(i):
-            q.nvfp4_quantize(x, out=a)
-            q.nvfp4_gemm(a, ws[i % copies], out=y)
-        us_q = graph_time_us(torch, with_quant, iters)
+        # nvfp4_linear: one kernel at M <= 2 (the GEMV quantizes x itself),
+        # quantize + GEMM above
+        nbytes = q.lib().nvfp4_linear_workspace_bytes(M, N, K)
+        lws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0") if nbytes else None
+        us_q = graph_time_us(torch, lambda i: q.nvfp4_linear(x, ws[i % copies], out=y, x_out=a, workspace=lws),
+                             iters)
+        assert torch.equal(y, ref), "nvfp4_linear differs from quantize + gemm"
         out[f"M{M}"] = {"us": us, "GBps": alg_bytes / (us * 1e-6) / 1e9,
                         "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                         "us_incl_act_quant": us_q, "alg_bytes": alg_bytes}

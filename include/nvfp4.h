@@ -204,6 +204,31 @@ nvfp4_status nvfp4_gemm_ws(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            size_t workspace_bytes, void* stream);
 
 /*
+ * Quantize a bf16 activation and multiply it by an NVFP4 weight: the
+ * forward of a linear layer whose activation is quantized on every call
+ * ("NVFP4 en difusión", section 2).  Results are bit-identical to
+ * nvfp4_quantize(x) (absmax rule, g from max|x|) followed by nvfp4_gemm on
+ * its codes: out [M, N] bf16, and x's codes [M, K/2], scales [M, K/16] and
+ * g (one fp32) in x_codes, x_scales, x_gscale, which the caller provides.
+ * 1 <= M <= 2 with K % 128 == 0 and K <= 8192 (a decode step) runs one
+ * kernel: each wave of the weight-streaming GEMV quantizes the activation
+ * values it needs itself, with the quantizer's arithmetic; one wave also
+ * stores them to x_codes / x_scales / x_gscale.  Other shapes run the
+ * quantizer and then the GEMM.
+ * K > 0, K % 16 == 0 (else NVFP4_ERR_SHAPE); M == 0 does nothing; N == 0
+ * only quantizes x.  x, out, x_codes, x_scales: 16-byte aligned.
+ * workspace: >= nvfp4_linear_workspace_bytes(M, N, K) bytes of device
+ * memory, 256-byte aligned, no initialization, not shared with a concurrent
+ * call (NULL when the size is 0, as for the one-kernel shapes).  No output
+ * may overlap another argument.
+ */
+size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+nvfp4_status nvfp4_linear(const void* x_bf16, const uint8_t* w_codes, const uint8_t* w_scales,
+                          const float* w_gscale, void* out_bf16, int64_t M, int64_t N, int64_t K,
+                          uint8_t* x_codes, uint8_t* x_scales, float* x_gscale, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_gemm_ws (AUTO kernel choice) that also leaves the global amax of
  * its output ready for nvfp4_quantize_amax, so that quantizing the output
  * (the next layer's activation, quantized on every forward: "NVFP4 en

@@ -17,7 +17,7 @@ Function names follow the C ABI:
 * ``int4g_gemv(x, q, scales, ...)``   -> bf16 [M, N]
 * ``int4g_asym_quantize(w)``          -> (q, scales_fp16, zeros_u8), zero-point INT4
 * ``int4g_asym_gemv(x, q, s, z)``     -> bf16 [M, N]
-* ``nvfp4_linear(x, w)``              -> quantize x, then nvfp4_gemm (two calls)
+* ``nvfp4_linear(x, w)``              -> quantize x and multiply (one kernel at M <= 2)
 """
 import ctypes
 import os
@@ -40,6 +40,8 @@ SIGNATURES = {
     "nvfp4_gemm": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "nvfp4_gemm_ex": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P], ctypes.c_int),
     "nvfp4_gemm_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),
+    "nvfp4_linear_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),
+    "nvfp4_linear": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "nvfp4_gemm_ws": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "nvfp4_gemm_amax_slots": ([_I64, _I64, _I64], ctypes.c_size_t),
     "nvfp4_gemm_amax": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P, _P], ctypes.c_int),
@@ -76,6 +78,10 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m quantized_gemm_nvfp4_amd.build` (or __graft_entry__.build())")
+        # torch first: it loads the HIP runtime it ships with, and the
+        # library then binds to that same runtime (loaded the other way
+        # round, torch can find no device)
+        _torch()
         handle = ctypes.CDLL(LIB_PATH)
         for name, (args, res) in SIGNATURES.items():
             fn = getattr(handle, name)
@@ -268,9 +274,45 @@ def nvfp4_gemm_w4a16(x, w, algo=ALGO_AUTO, out=None):
     return out
 
 
-def nvfp4_linear(x, w, algo=ALGO_AUTO):
-    """Dynamic activation quantization followed by the block-scaled GEMM."""
-    return nvfp4_gemm(nvfp4_quantize(x), w, algo=algo)
+def nvfp4_linear(x, w, out=None, x_out=None, workspace=None):
+    """Quantize bf16 x [M, K] (absmax rule, g from max|x|) and multiply by
+    the NVFP4 weight w: bit-identical to nvfp4_gemm(nvfp4_quantize(x), w).
+
+    At M <= 2, K % 128 == 0, K <= 8192 one kernel does both.  x_out:
+    optional (codes, scales, global_scale) buffers for x's NVFP4 form.
+    Returns (out bf16 [M, N], (codes, scales, global_scale)).
+    """
+    torch = _torch()
+    wc, ws, wg = w
+    _need(x, torch.bfloat16, None, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    N = wc.shape[0]
+    _need(wc, torch.uint8, (N, K // 2), "w_codes")
+    _need(ws, torch.uint8, (N, K // 16), "w_scales")
+    _need(wg, torch.float32, (1,), "w_gscale")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, (M, N), "out")
+    if x_out is None:
+        x_out = (torch.empty((M, K // 2), dtype=torch.uint8, device=x.device),
+                 torch.empty((M, K // 16), dtype=torch.uint8, device=x.device),
+                 torch.empty(1, dtype=torch.float32, device=x.device))
+    xc, xs, xg = x_out
+    _need(xc, torch.uint8, (M, K // 2), "x_codes")
+    _need(xs, torch.uint8, (M, K // 16), "x_scales")
+    _need(xg, torch.float32, (1,), "x_gscale")
+    if workspace is None:
+        nbytes = lib().nvfp4_linear_workspace_bytes(M, N, K)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _need(workspace, torch.uint8, None, "workspace")
+    _check(lib().nvfp4_linear(_ptr(x), _ptr(wc), _ptr(ws), _ptr(wg), _ptr(out), M, N, K, _ptr(xc), _ptr(xs),
+                              _ptr(xg), _ptr(workspace) if workspace is not None else None,
+                              workspace.numel() if workspace is not None else 0, _stream(x)))
+    return out, x_out
 
 
 def nvfp4_quantize_lora(x, lora_down, global_scale=None, out=None):

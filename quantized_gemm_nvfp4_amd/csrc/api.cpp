@@ -321,6 +321,70 @@ nvfp4_status nvfp4_gemm_ws(const uint8_t* a_codes, const uint8_t* a_scales, cons
                    nullptr, 0, workspace, workspace_bytes, stream);
 }
 
+size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  if (nvfp4k::nvfp4_linear_fused_supported(M, K)) return 0;
+  // the quantizer's partial maxima, then (stream-ordered, after the
+  // quantizer is done with them) the GEMM's split-K partial sums
+  const size_t g = nvfp4_gemm_workspace_bytes(M, N, K), q = nvfp4_quantize_workspace_bytes();
+  return g > q ? g : q;
+}
+
+nvfp4_status nvfp4_linear(const void* x_bf16, const uint8_t* w_codes, const uint8_t* w_scales,
+                          const float* w_gscale, void* out_bf16, int64_t M, int64_t N, int64_t K, uint8_t* x_codes,
+                          uint8_t* x_scales, float* x_gscale, void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE_PTR(x_bf16);
+  REQUIRE_PTR(w_codes);
+  REQUIRE_PTR(w_scales);
+  REQUIRE_PTR(w_gscale);
+  REQUIRE_PTR(out_bf16);
+  REQUIRE_PTR(x_codes);
+  REQUIRE_PTR(x_scales);
+  REQUIRE_PTR(x_gscale);
+  if (nvfp4_status s = check_dims(M, "M", N, "N", K, "K")) return s;
+  if (nvfp4_status s = check_products(M, N, K)) return s;
+  if (K <= 0 || K % 16 != 0)
+    return fail(NVFP4_ERR_SHAPE, "K=%lld is not a positive multiple of 16", (long long)K);
+  REQUIRE_ALIGN(x_bf16, 16);
+  REQUIRE_ALIGN(w_codes, 16);
+  REQUIRE_ALIGN(w_scales, 16);
+  REQUIRE_ALIGN(w_gscale, 4);
+  REQUIRE_ALIGN(out_bf16, 16);
+  REQUIRE_ALIGN(x_codes, 16);
+  REQUIRE_ALIGN(x_scales, 16);
+  REQUIRE_ALIGN(x_gscale, 4);
+  const size_t need = nvfp4_linear_workspace_bytes(M, N, K);
+  if (need > 0) {
+    REQUIRE_PTR(workspace);
+    REQUIRE_ALIGN(workspace, 256);
+    if (workspace_bytes < need)
+      return fail(NVFP4_ERR_INVALID_ARG, "workspace_bytes=%zu is below nvfp4_linear_workspace_bytes=%zu",
+                  workspace_bytes, need);
+  }
+  const Range outs[5] = {{out_bf16, M * N * 2, "out"},
+                         {x_codes, M * K / 2, "x_codes"},
+                         {x_scales, M * K / 16, "x_scales"},
+                         {x_gscale, 4, "x_gscale"},
+                         {workspace, need > 0 ? (int64_t)need : 0, "workspace"}};
+  const Range ins[4] = {{x_bf16, M * K * 2, "x"},
+                        {w_codes, N * K / 2, "w_codes"},
+                        {w_scales, N * K / 16, "w_scales"},
+                        {w_gscale, 4, "w_gscale"}};
+  if (M == 0) return ok();
+  if (nvfp4_status s = check_disjoint(outs, 5, ins, 4)) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (N > 0 && nvfp4k::nvfp4_linear_fused_supported(M, K))
+    return hip_status(nvfp4k::launch_nvfp4_linear_fused(x_bf16, w_codes, w_scales, w_gscale, out_bf16, M, N, K,
+                                                        x_codes, x_scales, x_gscale, st),
+                      "nvfp4_linear fused launch");
+  nvfp4_status s = hip_status(nvfp4k::launch_nvfp4_quantize(x_bf16, M, K, x_codes, x_scales, x_gscale, 0,
+                                                             NVFP4_SCALE_ABSMAX, (uint32_t*)workspace, st),
+                              "nvfp4_linear quantize launch");
+  if (s != NVFP4_OK || N == 0) return s;
+  return gemm_impl(x_codes, x_scales, x_gscale, w_codes, w_scales, w_gscale, out_bf16, M, N, K, NVFP4_ALGO_AUTO,
+                   nullptr, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
 size_t nvfp4_gemm_amax_slots(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   if (check_products(M, N, K) != NVFP4_OK) return 0;

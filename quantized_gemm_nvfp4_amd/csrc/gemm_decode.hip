@@ -7,19 +7,23 @@
 // (about one VALU op per weight value: the E2M1 conversion and the block
 // scale multiply, two values per instruction each) from becoming the limit.
 //
-// Three kernels:
+// Four kernels:
 //  - streaming row GEMV (M <= 2, K <= 8192): a persistent grid in which each
 //    wave reads whole rows of W, one contiguous 1 KB per load instruction,
 //    with the next rows' loads in flight while it decodes; the MFMA reduces
-//    along each lane's own data (diagonal trick below).
+//    along each lane's own data (diagonal trick below).  A second mode takes
+//    the bf16 activation and quantizes it in the prologue (nvfp4_linear).
 //  - row-slot GEMV (M <= 2, larger K, and the low-rank branch): the same
 //    product, one workgroup per 4 rows.
 //  - row-block GEMM (3 <= M <= 16): 48 rows of W per workgroup, the
 //    activation rows in the MFMA's columns, each decoded activation fragment
 //    shared by three 16-row groups; the 16 lanes of a row read whole
 //    128-byte lines.
+//  - weight-only GEMM (bf16 x, 3 <= M <= 16): activation-stationary, W
+//    streamed through LDS by DMA, so W is read once for all M rows.
 #include "common.h"
 #include "launch.h"
+#include "quant_block.h"
 
 namespace nvfp4k {
 
@@ -186,11 +190,19 @@ constexpr int kStreamWgsPerCu = 2;              // workgroups per compute unit
 constexpr int kStreamMaxSlots = 4;              // K <= 8192
 }  // namespace
 
-template <int kM, int kS>
+// With kQ the activation arrives as bf16 x [M, K] and every workgroup
+// quantizes all of it itself, the quantizer's steps in the same fp32
+// arithmetic (the global amax of x by an integer max over all of x, then
+// per 16-value block the absmax scale and codes), so its codes, scales and
+// g equal nvfp4_quantize's and the output equals that of nvfp4_quantize
+// followed by this kernel, bit for bit; workgroup 0 also stores them
+// (q_codes, q_scales, q_g) when those are given.
+template <int kM, int kS, bool kQ>
 __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_gemv_stream_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
-    uint16_t* __restrict__ out, int M, int N, int K) {
+    uint16_t* __restrict__ out, int M, int N, int K, const uint16_t* __restrict__ x_bf16,
+    uint8_t* __restrict__ q_codes, uint8_t* __restrict__ q_scales, float* __restrict__ q_g) {
   constexpr int kD = kStreamDepth;
   __shared__ __attribute__((aligned(16))) float s_part[kStreamWaves][kStreamBatch * kM * 16];
   const int lane = threadIdx.x & 63;
@@ -210,6 +222,37 @@ __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_gemv_stream_kernel(
     const bool valid = row < N;
     return buffer_of(w_scales + (int64_t)(valid ? row : 0) * row_scales, valid ? row_scales : 0u);
   };
+  // kQ: x's 16-value blocks t, t + 256, ... of thread t are requested
+  // before the weight (the prologue below waits for them, and the weight
+  // requests then stay in flight while it quantizes)
+  constexpr int kQB = (kM * kS + 1) / 2;                   // blocks per thread
+  const uint32_t x_bytes = (uint32_t)M * (uint32_t)K * 2u;   // <= 2 * 8192 * 2
+  uint32_t xw[kQ ? kQB : 1][8];
+  // codes path: the activation's codes and scales, likewise ahead of the weight
+  uint4 xc[kQ ? 1 : kM][kQ ? 1 : kS];
+  uint32_t xsc[kQ ? 1 : kM][kQ ? 1 : kS];
+  if (!kQ) {
+    const auto ar = buffer_of(a_codes, (uint32_t)M * row_bytes);      // rows >= M read as zero
+    const auto asr = buffer_of(a_scales, (uint32_t)M * row_scales);
+#pragma unroll
+    for (int s = 0; s < kS; ++s)
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        const bool in = 1024u * s + 16u * lane < row_bytes;
+        xc[kQ ? 0 : m][kQ ? 0 : s] = buffer_load16(ar, in ? 1024u * s + 16u * lane + m * row_bytes : kOob);
+        xsc[kQ ? 0 : m][kQ ? 0 : s] = buffer_load2(asr, in ? 128u * s + 2u * lane + m * row_scales : kOob);
+      }
+  }
+  if (kQ) {
+    const auto xr = buffer_of(x_bf16, x_bytes);              // blocks past x read zero
+#pragma unroll
+    for (int u = 0; u < kQB; ++u) {
+      const uint32_t b = threadIdx.x + 256u * u;
+      const uint4 v0 = buffer_load16(xr, 32u * b), v1 = buffer_load16(xr, 32u * b + 16u);
+      xw[u][0] = v0.x, xw[u][1] = v0.y, xw[u][2] = v0.z, xw[u][3] = v0.w;
+      xw[u][4] = v1.x, xw[u][5] = v1.y, xw[u][6] = v1.z, xw[u][7] = v1.w;
+    }
+  }
   uint4 wc[kD][kS];
   uint32_t ws[kD][kS];
   // the first kD rows are requested before the activation is decoded
@@ -223,26 +266,76 @@ __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_gemv_stream_kernel(
     }
   }
 
-  // The activation's 32 values per lane and slot, decoded once.
-  const auto ar = buffer_of(a_codes, (uint32_t)M * row_bytes);      // rows >= M read as zero
-  const auto asr = buffer_of(a_scales, (uint32_t)M * row_scales);
   half8v xv[kM][kS][4];
+  float gq = 0.f;
+  if (kQ) {
+    // The workgroup quantizes x together: thread t takes the blocks it
+    // loaded above (for the amax and for the codes), the maximum meets in
+    // LDS, and each thread leaves its blocks decoded (the same conversions
+    // as the codes path below) in the workgroup's copy of x^.
+    constexpr int kKS = kS * 2048;                         // x^ row stride
+    __shared__ __attribute__((aligned(16))) _Float16 s_xhat[kQ ? kM * kKS : 8];
+    __shared__ uint32_t s_mx[kStreamWaves];
+    const uint32_t nblk = x_bytes / 32u;
+    uint32_t mx = 0;
 #pragma unroll
-  for (int s = 0; s < kS; ++s)
+    for (int u = 0; u < kQB; ++u)
 #pragma unroll
-    for (int m = 0; m < kM; ++m) {
-      const bool in = 1024u * s + 16u * lane < row_bytes;
-      const uint4 xc = buffer_load16(ar, in ? 1024u * s + 16u * lane + m * row_bytes : kOob);
-      const uint32_t xs = buffer_load2(asr, in ? 128u * s + 2u * lane + m * row_scales : kOob);
-      const half2v sc = e4m3x2_to_f16x2_div256(xs);
-      const half2v s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
+      for (int j = 0; j < 8; ++j) mx = max(mx, bf16x2_absmax_bits(xw[u][j]));
+    mx = wave_max_u32(mx);
+    if (lane == 0) s_mx[wave] = mx;
+    __syncthreads();
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) xv[m][s][jj] = dequant8_f16_div256(word_of(xc, jj), jj < 2 ? s0 : s1);
+    for (int w = 0; w < kStreamWaves; ++w) mx = max(mx, s_mx[w]);
+    gq = bf16_bits_to_f32(mx) / 2688.0f;   // amax / (6 * 448)
+    const bool store = blockIdx.x == 0;     // workgroup 0 also returns x's NVFP4 form
+    if (store && q_g != nullptr && threadIdx.x == 0) *q_g = gq;
+#pragma unroll
+    for (int u = 0; u < kQB; ++u) {
+      const uint32_t b = threadIdx.x + 256u * u;
+      if (b < nblk) {
+        uint32_t sc;
+        const uint2 c = absmax_block(xw[u], gq, sc);
+        if (store && q_codes != nullptr) {
+          *(uint2*)(q_codes + 8u * b) = c;
+          q_scales[b] = (uint8_t)sc;
+        }
+        const half2v scl = e4m3x2_to_f16x2_div256(sc | (sc << 8));
+        const uint32_t m = 16u * b / (uint32_t)K, k = 16u * b - m * (uint32_t)K;
+        half8v* dst = (half8v*)(s_xhat + m * kKS + k);
+        dst[0] = dequant8_f16_div256(c.x, scl);
+        dst[1] = dequant8_f16_div256(c.y, scl);
+      }
     }
+    __syncthreads();
+    // each wave's 32 values per lane and slot (zero past K, as the codes
+    // path reads them)
+#pragma unroll
+    for (int s = 0; s < kS; ++s)
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        const bool in = 2048 * s + 32 * lane < K;
+        const half8v* src = (const half8v*)(s_xhat + m * kKS + 2048 * s + 32 * lane);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) xv[m][s][jj] = in ? src[jj] : half8v{};
+      }
+  } else {
+    // The activation's 32 values per lane and slot, decoded once.
+#pragma unroll
+    for (int s = 0; s < kS; ++s)
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        const half2v sc = e4m3x2_to_f16x2_div256(xsc[kQ ? 0 : m][kQ ? 0 : s]);
+        const half2v s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          xv[m][s][jj] = dequant8_f16_div256(word_of(xc[kQ ? 0 : m][kQ ? 0 : s], jj), jj < 2 ? s0 : s1);
+      }
+  }
 
   const int i = lane & 15;
   const bool diag_lane = (i >> 2) == (lane >> 4);
-  const float gg = (*a_g) * (*w_g);
+  const float gg = (kQ ? gq : *a_g) * (*w_g);
   int nbat = 0;                 // rows of the current batch
   int row0 = gw;                // first row of the current batch
   auto flush = [&]() {
@@ -847,25 +940,36 @@ void launch_w4a16_rowslot(const void* x, const uint8_t* wc, const uint8_t* ws, c
 }  // namespace
 
 namespace {
-template <int kM, int kS>
-void launch_stream(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc, const uint8_t* ws,
-                   const float* wg, void* out, int M, int N, int K, hipStream_t stream) {
+// Activation operands of the streaming GEMV: NVFP4 codes, or (kQ) bf16 x
+// with optional outputs for its codes, scales and g.
+struct StreamX {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* g;
+  const uint16_t* x;
+  uint8_t* q_codes;
+  uint8_t* q_scales;
+  float* q_g;
+};
+template <int kM, int kS, bool kQ>
+void launch_stream(const StreamX& a, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out, int M, int N,
+                   int K, hipStream_t stream) {
   const int64_t cap = (int64_t)device_cus() * kStreamWgsPerCu;
   const int64_t need = ((int64_t)N + kStreamWaves - 1) / kStreamWaves;
   const unsigned grid = (unsigned)(need < cap ? need : cap);
-  hipLaunchKernelGGL((nvfp4_gemv_stream_kernel<kM, kS>), dim3(grid), dim3(64 * kStreamWaves), 0, stream, ac, as, ag,
-                     wc, ws, wg, (uint16_t*)out, M, N, K);
+  hipLaunchKernelGGL((nvfp4_gemv_stream_kernel<kM, kS, kQ>), dim3(grid), dim3(64 * kStreamWaves), 0, stream, a.codes,
+                     a.scales, a.g, wc, ws, wg, (uint16_t*)out, M, N, K, a.x, a.q_codes, a.q_scales, a.q_g);
 }
 // Launches the streaming GEMV for M <= 2 and K <= kStreamMaxSlots * 2048;
 // false if the shape is outside that range.
-template <int kM>
-bool launch_stream_k(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc, const uint8_t* ws,
-                     const float* wg, void* out, int M, int N, int K, hipStream_t stream) {
+template <int kM, bool kQ>
+bool launch_stream_k(const StreamX& a, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out, int M, int N,
+                     int K, hipStream_t stream) {
   switch ((K + 2047) / 2048) {
-    case 1: launch_stream<kM, 1>(ac, as, ag, wc, ws, wg, out, M, N, K, stream); return true;
-    case 2: launch_stream<kM, 2>(ac, as, ag, wc, ws, wg, out, M, N, K, stream); return true;
-    case 3: launch_stream<kM, 3>(ac, as, ag, wc, ws, wg, out, M, N, K, stream); return true;
-    case 4: launch_stream<kM, 4>(ac, as, ag, wc, ws, wg, out, M, N, K, stream); return true;
+    case 1: launch_stream<kM, 1, kQ>(a, wc, ws, wg, out, M, N, K, stream); return true;
+    case 2: launch_stream<kM, 2, kQ>(a, wc, ws, wg, out, M, N, K, stream); return true;
+    case 3: launch_stream<kM, 3, kQ>(a, wc, ws, wg, out, M, N, K, stream); return true;
+    case 4: launch_stream<kM, 4, kQ>(a, wc, ws, wg, out, M, N, K, stream); return true;
     default: return false;
   }
 }
@@ -899,8 +1003,9 @@ hipError_t launch_nvfp4_gemm_decode_lora(const uint8_t* ac, const uint8_t* as, c
   const bool rowslot_k = K <= (int64_t)kMaxSlots * 2048;
   const bool lora = lora_t != nullptr;
   if (M <= 2 && !lora) {
-    const bool done = M == 1 ? launch_stream_k<1>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream)
-                             : launch_stream_k<2>(ac, as, ag, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
+    const StreamX a = {ac, as, ag, nullptr, nullptr, nullptr, nullptr};
+    const bool done = M == 1 ? launch_stream_k<1, false>(a, wc, ws, wg, out, (int)M, (int)N, (int)K, stream)
+                             : launch_stream_k<2, false>(a, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
     if (done) return hipGetLastError();
   }
   if (M == 1 && rowslot_k) {
@@ -922,6 +1027,19 @@ hipError_t launch_nvfp4_gemm_decode_lora(const uint8_t* ac, const uint8_t* as, c
       hipLaunchKernelGGL(nvfp4_gemm_rowblock_kernel<false>, grid, block, 0, stream, ac, as, ag, wc, ws, wg, (uint16_t*)out, (int)M, (int)N, (int)K, lora_t, up, (int)r);
   }
   return hipGetLastError();
+}
+
+bool nvfp4_linear_fused_supported(int64_t M, int64_t K) {
+  return M >= 1 && M <= 2 && K > 0 && K % 128 == 0 && K <= (int64_t)kStreamMaxSlots * 2048;
+}
+
+hipError_t launch_nvfp4_linear_fused(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
+                                     int64_t M, int64_t N, int64_t K, uint8_t* q_codes, uint8_t* q_scales,
+                                     float* q_g, hipStream_t stream) {
+  const StreamX a = {nullptr, nullptr, nullptr, (const uint16_t*)x, q_codes, q_scales, q_g};
+  const bool done = M == 1 ? launch_stream_k<1, true>(a, wc, ws, wg, out, (int)M, (int)N, (int)K, stream)
+                           : launch_stream_k<2, true>(a, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
+  return done ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 hipError_t launch_nvfp4_gemm_decode(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,

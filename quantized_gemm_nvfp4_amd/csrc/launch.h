@@ -85,6 +85,15 @@ hipError_t launch_nvfp4_gemm_simple(const uint8_t* ac, const uint8_t* as, const 
                                     const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
                                     int64_t K, hipStream_t stream);
 
+// Quantize bf16 x and multiply in one launch (the streaming GEMV, each wave
+// quantizing the values it needs); bit-identical to launch_nvfp4_quantize
+// followed by the decode GEMM.  q_codes / q_scales / q_g (optional) receive
+// x's codes, scales and g.  Needs nvfp4_linear_fused_supported(M, K).
+bool nvfp4_linear_fused_supported(int64_t M, int64_t K);
+hipError_t launch_nvfp4_linear_fused(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
+                                     int64_t M, int64_t N, int64_t K, uint8_t* q_codes, uint8_t* q_scales,
+                                     float* q_g, hipStream_t stream);
+
 // Weight-only NVFP4: out[M, N] bf16 = g_w * x . dequant(W)^T, x bf16.
 // decode: nvfp4_w4a16_decode_supported(M, K).  simple: K % 16 == 0.
 bool nvfp4_w4a16_decode_supported(int64_t M, int64_t K);

@@ -192,6 +192,36 @@ def test_quantize_noalloc_validation():
     assert f(A, 0, 32, B, C, D, 0, None) == OK
 
 
+def test_linear_validation():
+    lib = q.lib()
+    f = lib.nvfp4_linear
+    H, W = P(0x80000), P(0x100000)
+    # x, w_codes, w_scales, w_g, out, M, N, K, x_codes, x_scales, x_g, workspace, bytes, stream
+    good = [A, B, C, D, E]
+    xo = [F, G, H]
+    assert f(None, B, C, D, E, 1, 64, 128, *xo, None, 0, None) == INVALID and "x_bf16" in _err()
+    assert f(*good, 1, 64, 128, None, G, H, None, 0, None) == INVALID and "x_codes" in _err()
+    assert f(*good, 1, 64, 0, *xo, None, 0, None) == SHAPE                      # K must be positive
+    assert f(*good, 1, 64, 120, *xo, None, 0, None) == SHAPE                    # K % 16
+    assert f(*good, -1, 64, 128, *xo, None, 0, None) == INVALID
+    assert f(A, B, C, D, ODD, 1, 64, 128, *xo, None, 0, None) == ALIGN
+    assert f(*good, 1, 64, 128, F, G, P(0x80002), None, 0, None) == ALIGN     # x_g 4-byte
+    assert f(*good, 1, 64, 128, A, G, H, None, 0, None) == INVALID and "overlap" in _err()
+    assert f(*good, 1, 64, 128, F, G, E, None, 0, None) == INVALID and "overlap" in _err()
+    # one-kernel shapes need no workspace; the others need the quantizer's
+    assert lib.nvfp4_linear_workspace_bytes(1, 21504, 5376) == 0
+    assert lib.nvfp4_linear_workspace_bytes(2, 64, 8192) == 0
+    assert lib.nvfp4_linear_workspace_bytes(1, 64, 8192 + 128) == 4096
+    assert lib.nvfp4_linear_workspace_bytes(3, 64, 128) == 4096
+    assert lib.nvfp4_linear_workspace_bytes(2, 64, 48) == 4096
+    assert lib.nvfp4_linear_workspace_bytes(4096, 4096, 4096) >= 4096
+    assert f(*good, 3, 64, 128, *xo, None, 0, None) == INVALID and "workspace" in _err()
+    assert f(*good, 3, 64, 128, *xo, P(0x100010), 4096, None) == ALIGN
+    assert f(*good, 3, 64, 128, *xo, W, 4095, None) == INVALID
+    assert f(*good, 0, 64, 128, *xo, None, 0, None) == OK
+    assert f(*good, 1 << 30, 1 << 30, 128, *xo, None, 0, None) == UNSUP
+
+
 def test_lora_workspace_size():
     f = q.lib().nvfp4_quantize_lora_workspace_bytes
     # one K slice: only the 1024 partial maxima
