@@ -25,7 +25,7 @@
 namespace nvfp4k {
 
 namespace {
-constexpr int64_t kSmallQuantBlocks = 2048;   // one workgroup quantizes up to 32K values
+constexpr int64_t kSmallQuantBlocks = 8192;   // the single-launch kernel: up to 128K values
 }  // namespace
 
 // ---- pass 1: partial maxima of |x| over a bf16 tensor ---------------------
@@ -206,10 +206,12 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
     quantize_block<kRule>(x, b, g, codes, scales);
 }
 
-// Small tensors (decode activations, at most kSmallQuantBlocks blocks): one
-// workgroup takes both passes, so a call is a single launch.  The maximum is
-// the same integer max of |bf16| patterns and the blocks go through the same
-// quantize_block, so g, scales and codes equal the two-pass kernels'.
+// Small tensors (decode activations, at most kSmallQuantBlocks blocks): a
+// single launch of one workgroup per 1024 blocks, each of which takes the
+// maximum over all of x itself (x is at most 256 KB and stays in L2) and
+// then quantizes its own 1024 blocks.  The maximum is the same integer max
+// of |bf16| patterns and the blocks go through the same quantize_block, so
+// g, scales and codes equal the two-pass kernels'; workgroup 0 stores g.
 template <int kRule>
 __global__ __launch_bounds__(1024) void nvfp4_quant_small_kernel(const uint4* __restrict__ x, int64_t nblocks,
                                                                 uint2* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -219,13 +221,18 @@ __global__ __launch_bounds__(1024) void nvfp4_quant_small_kernel(const uint4* __
   if (use_given) {
     if (threadIdx.x == 0) s_g = *gscale;
   } else {
+    // eight 16-byte loads per thread in flight (offsets past x read zero)
     uint32_t m = 0;
-    const int n_vec = (int)(2 * nblocks);
-#pragma unroll 4
-    for (int i = threadIdx.x; i < n_vec; i += 1024) {
-      const uint4 v = x[i];
-      m = max(m, max(max(bf16x2_absmax_bits(v.x), bf16x2_absmax_bits(v.y)),
-                     max(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w))));
+    const uint32_t nbytes = (uint32_t)nblocks * 32u;
+    const auto xr = buffer_of(x, nbytes);
+    for (uint32_t i = 16u * threadIdx.x; i < nbytes; i += 8u * 16384u) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = buffer_load16(xr, i + 16384u * u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        m = max(m, max(max(bf16x2_absmax_bits(v[u].x), bf16x2_absmax_bits(v[u].y)),
+                       max(bf16x2_absmax_bits(v[u].z), bf16x2_absmax_bits(v[u].w))));
     }
     m = wave_max_u32(m);
     if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
@@ -234,13 +241,14 @@ __global__ __launch_bounds__(1024) void nvfp4_quant_small_kernel(const uint4* __
 #pragma unroll
       for (int w = 1; w < 16; ++w) m = max(m, s_max[w]);
       const float g = bf16_bits_to_f32(m) / 2688.0f;   // amax / (6 * 448)
-      *gscale = g;
+      if (blockIdx.x == 0) *gscale = g;
       s_g = g;
     }
   }
   __syncthreads();
   const float g = s_g;
-  for (int64_t b = threadIdx.x; b < nblocks; b += 1024) quantize_block<kRule>(x, b, g, codes, scales);
+  const int64_t b = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  if (b < nblocks) quantize_block<kRule>(x, b, g, codes, scales);
 }
 
 // ---- INT4 per-group (128) quantization ------------------------------------
@@ -323,7 +331,7 @@ hipError_t launch_nvfp4_quantize(const void* x, int64_t rows, int64_t cols, uint
   const int64_t n = rows * cols;
   const int64_t nblocks = n / kBlock;
   if (nblocks <= kSmallQuantBlocks) {
-    const dim3 grid(1), block(1024);
+    const dim3 grid((unsigned)((nblocks + 1023) / 1024)), block(1024);
     if (rule == kRuleFourOverSix)
       hipLaunchKernelGGL(nvfp4_quant_small_kernel<kRuleFourOverSix>, grid, block, 0, stream, (const uint4*)x, nblocks,
                          (uint2*)codes, scales, gscale, use_given);

@@ -75,10 +75,12 @@ def test_quantize_random(seed, shape, kw):
     assert_quant_equal(workloads.random_bf16(seed, shape, **kw), label=f"seed {seed}")
 
 
-@pytest.mark.parametrize("shape", [(8, 4096), (1, 2049 * 16), (4, 5376), (16, 5376)])
+@pytest.mark.parametrize("shape", [(8, 4096), (1, 2049 * 16), (4, 5376), (16, 5376), (32, 4096), (1, 8193 * 16),
+                                   (3, 1040)])
 def test_quantize_single_launch_boundary(shape):
-    # up to 2048 blocks one workgroup takes both passes; 2049 blocks take the
-    # two-pass kernels; both must give the oracle's bytes
+    # up to 8192 blocks one launch takes both passes (one workgroup per 1024
+    # blocks, the last one partial, each with its own pass for the maximum);
+    # 8193 blocks take the two-pass kernels; both must give the oracle's bytes
     log(f"quantize {shape}")
     assert_quant_equal(workloads.random_bf16(shape[1] + 5, shape, outlier_frac=0.01, outlier_mul=40), label=str(shape))
 
