@@ -99,13 +99,17 @@ class Timer:
         return out
 
 
-def kernel_source_hash():
-    """Hash of the tiled GEMM's source with comments and whitespace removed,
-    so that counters taken on a build stay valid across comment-only edits."""
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode.json")
+DECODE_SOURCES = ("gemm_decode.hip", "int4_gemm.hip", "int4_asym.hip", "quant_block.h", "common.h")
+
+
+def kernel_source_hash(files=("gemm_tiled.hip", "common.h")):
+    """Hash of kernel sources with comments and whitespace removed, so that
+    counters taken on a build stay valid across comment-only edits."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in ("gemm_tiled.hip", "common.h"):
+    for f in files:
         with open(os.path.join(ROOT, "quantized_gemm_nvfp4_amd", "csrc", f)) as fh:
             src = fh.read()
         src = re.sub(r"//[^\n]*", "", src)
@@ -194,6 +198,157 @@ def summarize_traffic(fetch_csv, write_csv):
         json.dump(out, f, indent=2)
         f.write("\n")
     return out
+
+
+# The decode-sized kernels whose HBM bytes per call bench.py --decode-traffic
+# exposes to rocprofv3 --pmc: (name, weight, M), launched in this order.
+DECODE_TRAFFIC = [
+    ("nvfp4_w4a4_M1", "nvfp4", 1), ("nvfp4_w4a4_M2", "nvfp4", 2), ("nvfp4_w4a4_M4", "nvfp4", 4),
+    ("nvfp4_w4a4_M16", "nvfp4", 16), ("nvfp4_linear_M1", "nvfp4", 1), ("nvfp4_linear_M2", "nvfp4", 2),
+    ("nvfp4_w4a16_M1", "nvfp4", 1), ("nvfp4_w4a16_M2", "nvfp4", 2), ("nvfp4_w4a16_M4", "nvfp4", 4),
+    ("nvfp4_w4a16_M16", "nvfp4", 16), ("int4_M1", "int4", 1), ("int4_M4", "int4", 4), ("int4_M16", "int4", 16),
+    ("int4_asym_M1", "int4_asym", 1)]
+DECODE_TRAFFIC_LAUNCHES = 6
+
+
+def decode_alg_bytes(name, M):
+    """Algorithmic bytes of one call: weight codes + scales (+ zeros) + the
+    activation as the call takes it + the bf16 output."""
+    if name.startswith("int4"):
+        N, K = 28672, 8192
+        per_group = 3 if name.startswith("int4_asym") else 2
+        return N * K // 2 + N * (K // 128) * per_group + M * K * 2 + M * N * 2
+    N, K = 21504, 5376
+    w = N * K // 2 + N * K // 16 + 4 + M * N * 2
+    if "w4a4" in name:
+        return w + M * K // 2 + M * K // 16 + 4
+    if "linear" in name:   # reads bf16 x, writes its codes, scales and g
+        return w + M * K * 2 + M * K // 2 + M * K // 16 + 4
+    return w + M * K * 2
+
+
+def run_decode_traffic(torch, q, launches=DECODE_TRAFFIC_LAUNCHES):
+    """For rocprofv3 --pmc runs: after three 1 GiB device copies (the counter
+    calibration), each DECODE_TRAFFIC kernel is launched `launches` times in
+    order, each launch on the next of several weight copies (~1 GB in all per
+    weight), so every call reads its weight from HBM."""
+    import workloads
+    xn, _ = workloads.decode_x()
+    wn = q.nvfp4_quantize(dev_bf16(torch, workloads.decode_w()))
+    rot_n = [tuple(t.clone() for t in wn) for _ in range(16)]
+    del wn
+    wi = workloads.int4_w()
+    xi = workloads.int4_x()
+    qi = q.int4g_quantize(dev_bf16(torch, wi))
+    rot_i = [tuple(t.clone() for t in qi) for _ in range(8)]
+    qa = q.int4g_asym_quantize(dev_bf16(torch, wi))
+    rot_a = [tuple(t.clone() for t in qa) for _ in range(8)]
+    del qi, qa, wi
+    calls = []
+    for name, weight, M in DECODE_TRAFFIC:
+        if weight == "nvfp4":
+            x = dev_bf16(torch, xn[:M])
+            a = q.nvfp4_quantize(x)
+            y = torch.empty((M, 21504), dtype=torch.bfloat16, device="cuda:0")
+            if "w4a4" in name:
+                fn = (lambda a, y: lambda i: q.nvfp4_gemm(a, rot_n[i % 16], out=y))(a, y)
+            elif "linear" in name:
+                fn = (lambda x, a, y: lambda i: q.nvfp4_linear(x, rot_n[i % 16], out=y, x_out=a))(x, a, y)
+            else:
+                fn = (lambda x, y: lambda i: q.nvfp4_gemm_w4a16(x, rot_n[i % 16], out=y))(x, y)
+        else:
+            x = dev_bf16(torch, xi[:M])
+            y = torch.empty((M, 28672), dtype=torch.bfloat16, device="cuda:0")
+            if weight == "int4":
+                fn = (lambda x, y: lambda i: q.int4g_gemv(x, *rot_i[i % 8], out=y))(x, y)
+            else:
+                fn = (lambda x, y: lambda i: q.int4g_asym_gemv(x, *rot_a[i % 8], out=y))(x, y)
+        calls.append(fn)
+    torch.cuda.synchronize()
+    run_copy_calibration(torch)
+    k = 0
+    for fn in calls:
+        for _ in range(launches):
+            fn(k)
+            k += 1
+        torch.cuda.synchronize()
+    log(f"decode traffic: {len(calls)} kernels x {launches} launches")
+    return {"kernels": [n for n, _, _ in DECODE_TRAFFIC], "launches": launches}
+
+
+def _counter_rows(path, counter):
+    import csv
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    # one row per dispatch (the value is already summed over the counter's instances)
+    by = {}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        by.setdefault(d, [r["Kernel_Name"], 0.0])
+        by[d][1] += float(r["Counter_Value"])
+    return [(d, by[d][0], by[d][1]) for d in sorted(by)]
+
+
+def summarize_decode_traffic(fetch_csv, write_csv, launches=DECODE_TRAFFIC_LAUNCHES):
+    """Write DECODE_TRAFFIC_FILE from the counter CSVs of two rocprofv3 --pmc
+    runs of `bench.py --decode-traffic` (FETCH_SIZE, then WRITE_SIZE): the
+    library's dispatches after the last calibration copy are taken in
+    DECODE_TRAFFIC order, `launches` per kernel; counter units become bytes
+    with what the same counter reads for the 1 GiB copies; medians per kernel."""
+    out_k = {}
+    calib = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, counter)
+        copies = [i for i, (_, n, _) in enumerate(rows) if "copyBuffer" in n]
+        unit = (1 << 30) / float(np.median([rows[i][2] for i in copies[-3:]]))
+        calib[counter] = {"per_GiB_copy": float(np.median([rows[i][2] for i in copies[-3:]])),
+                          "bytes_per_unit": unit}
+        lib = [(n, v) for (_, n, v) in rows[copies[-1] + 1:] if "nvfp4k::" in n]
+        if len(lib) != launches * len(DECODE_TRAFFIC):
+            raise ValueError(f"{path}: {len(lib)} library dispatches after the calibration copies, expected "
+                             f"{launches * len(DECODE_TRAFFIC)}")
+        for j, (name, _, M) in enumerate(DECODE_TRAFFIC):
+            chunk = lib[j * launches:(j + 1) * launches]
+            kname = {n for n, _ in chunk}
+            if len(kname) != 1:
+                raise ValueError(f"{name}: mixed kernels {sorted(kname)}")
+            e = out_k.setdefault(name, {"kernel": next(iter(kname)).split("(")[0], "M": M,
+                                        "algorithmic_bytes": decode_alg_bytes(name, M)})
+            e["fetch_bytes" if counter == "FETCH_SIZE" else "write_bytes"] = round(
+                float(np.median([v for _, v in chunk])) * unit)
+    for e in out_k.values():
+        e["traffic_over_algorithmic"] = round((e["fetch_bytes"] + e["write_bytes"]) / e["algorithmic_bytes"], 3)
+    cmd = "rocprofv3 --pmc {c} --output-format csv -d <dir> -o {o} -- python3 -u bench.py --decode-traffic"
+    out = {
+        "workload": "decode-sized calls: NVFP4 weight 21504 x 5376 (16 rotated copies) and INT4 weight 28672 x 8192 "
+                    "(group 128, 8 rotated copies), each kernel launched " + str(launches) + " times",
+        "kernel_source_hash": kernel_source_hash(DECODE_SOURCES),
+        "per_kernel": out_k,
+        "calibration": calib,
+        "commands": [cmd.format(c="FETCH_SIZE", o="fetch"), cmd.format(c="WRITE_SIZE", o="write"),
+                     "python3 bench.py --decode-traffic-from <dir>/fetch_counter_collection.csv "
+                     "<dir>/write_counter_collection.csv"],
+        "note": "HBM bytes per call = median counter value per dispatch x bytes per counter unit (from the 1 GiB "
+                "__amd_rocclr_copyBuffer dispatches of the same run).",
+        "hash_note": "sha256 (first 16 hex digits) of " + " + ".join(DECODE_SOURCES) +
+                     " with comments and whitespace removed, as bench.py computes it",
+    }
+    with open(DECODE_TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=2)
+        f.write("\n")
+    return out
+
+
+def load_decode_traffic():
+    """Per-kernel HBM bytes of the decode-sized calls from committed
+    counters, or {} if they were taken on different kernel sources."""
+    try:
+        with open(DECODE_TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if t.get("kernel_source_hash") != kernel_source_hash(DECODE_SOURCES):
+        return {}
+    return t.get("per_kernel", {})
 
 
 def run_prefill(torch, q, steps, warmup):
@@ -358,7 +513,7 @@ def run_decode(torch, q, iters=64, copies=16):
                         "us_incl_act_quant": us_q, "alg_bytes": alg_bytes}
         log(f"decode M={M}: {us:.2f} us, {out[f'M{M}']['GBps']:.0f} GB/s; incl. act quant {us_q:.2f} us")
     # weight-only mode: bf16 activation straight into the GEMV (no quantization)
-    for M in (1, 2):
+    for M in (1, 2, 4, 16):
         x = dev_bf16(torch, x_bits[:M])
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
         alg_bytes = N * K // 2 + N * K // 16 + 4 + M * K * 2 + M * N * 2
@@ -369,6 +524,16 @@ def run_decode(torch, q, iters=64, copies=16):
                               "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "alg_bytes": alg_bytes}
         log(f"decode W4A16 M={M}: {us:.2f} us, {out[f'w4a16_M{M}']['GBps']:.0f} GB/s")
     del ws
+    # HBM bytes per call from committed rocprofv3 counters (None once the
+    # kernels have changed since they were taken)
+    tr = load_decode_traffic()
+    for key, name in [(f"M{m}", f"nvfp4_w4a4_M{m}") for m in (1, 2, 4, 16)] + \
+                     [(f"w4a16_M{m}", f"nvfp4_w4a16_M{m}") for m in (1, 2, 4, 16)]:
+        t = tr.get(name)
+        out[key]["traffic_bytes"] = t["fetch_bytes"] + t["write_bytes"] if t else None
+    for m in (1, 2):
+        t = tr.get(f"nvfp4_linear_M{m}")
+        out[f"M{m}"]["traffic_bytes_incl_act_quant"] = t["fetch_bytes"] + t["write_bytes"] if t else None
     return out
 
 
@@ -512,15 +677,18 @@ def run_int4(torch, q, iters=64, copies=8):
     del w_bits
     rot = [(qq.clone(), ss.clone()) for _ in range(copies)]      # ~0.97 GB rotated
     out = {}
-    for M in (1, 16):
+    tr = load_decode_traffic()
+    for M in (1, 4, 16):
         x = dev_bf16(torch, x_bits[:M])
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
         alg_bytes = N * K // 2 + N * (K // 128) * 2 + M * K * 2 + M * N * 2
         ref = q.int4g_gemv(x, *rot[(iters - 1) % copies]).clone()
         us = graph_time_us(torch, lambda i: q.int4g_gemv(x, *rot[i % copies], out=y), iters)
         assert torch.equal(y, ref), "graph replay differs from the eager call"
+        t = tr.get(f"int4_M{M}")
         out[f"M{M}"] = {"us": us, "GBps": alg_bytes / (us * 1e-6) / 1e9,
-                        "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+                        "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                        "traffic_bytes": t["fetch_bytes"] + t["write_bytes"] if t else None}
         log(f"int4 M={M}: {us:.2f} us, {out[f'M{M}']['GBps']:.0f} GB/s")
     x = dev_bf16(torch, x_bits)
     y = torch.empty((2048, N), dtype=torch.bfloat16, device="cuda:0")
@@ -548,8 +716,10 @@ def run_int4(torch, q, iters=64, copies=8):
     ref = q.int4g_asym_gemv(x, *rot[(iters - 1) % copies]).clone()
     us = graph_time_us(torch, lambda i: q.int4g_asym_gemv(x, *rot[i % copies], out=y), iters)
     assert torch.equal(y, ref), "graph replay differs from the eager call"
+    t = tr.get("int4_asym_M1")
     out["asym_M1"] = {"us": us, "GBps": alg_bytes / (us * 1e-6) / 1e9,
-                      "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+                      "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                      "traffic_bytes": t["fetch_bytes"] + t["write_bytes"] if t else None}
     log(f"int4 asym M=1: {us:.2f} us, {out['asym_M1']['GBps']:.0f} GB/s")
     del rot
     return out
@@ -611,10 +781,18 @@ def main():
                     help="time only this extra workload")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMM traffic summary from two rocprofv3 --pmc runs and exit (no GPU)")
+    ap.add_argument("--decode-traffic", action="store_true",
+                    help="launch each decode-sized kernel a few times for rocprofv3 --pmc and exit")
+    ap.add_argument("--decode-traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the decode traffic summary from two rocprofv3 --pmc runs and exit (no GPU)")
     args = ap.parse_args()
     if args.traffic_from:
         out = summarize_traffic(*args.traffic_from)
         print(json.dumps({"traffic_bytes_per_launch": out["bytes_per_launch"], "file": TRAFFIC_FILE}))
+        return
+    if args.decode_traffic_from:
+        out = summarize_decode_traffic(*args.decode_traffic_from)
+        print(json.dumps({k: v["traffic_over_algorithmic"] for k, v in out["per_kernel"].items()}))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a "
@@ -627,6 +805,9 @@ def main():
     q.lib()
     log(f"device {torch.cuda.get_device_name(0)}")
 
+    if args.decode_traffic:
+        print(json.dumps(run_decode_traffic(torch, q)))
+        return
     if args.only:
         res = {"decode": run_decode, "dit": run_dit, "int4": run_int4,
                "weight_quant": run_weight_quant, "lora": run_lora}[args.only](torch, q)
@@ -679,7 +860,9 @@ def main():
     if extras:
         d1 = extras["decode"]["M1"]
         line["decode_m1"] = {"value": round(d1["GBps"], 1), "unit": "GB/s", "frac_hbm": round(d1["frac_hbm"], 4),
-                             "us": round(d1["us"], 2), "us_incl_act_quant": round(d1["us_incl_act_quant"], 2)}
+                             "us": round(d1["us"], 2), "us_incl_act_quant": round(d1["us_incl_act_quant"], 2),
+                             "alg_bytes": d1["alg_bytes"], "traffic": d1.get("traffic_bytes"),
+                             "kernel": "nvfp4_gemv_stream_kernel<1, 3, false>"}
         line["extras"] = extras
     print(json.dumps(line))
 
