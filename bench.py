@@ -17,8 +17,14 @@ its average launch time, measured with events on the launch stream inside
 the timed region, against the fp16/bf16 dense MFMA peak (2.5 PFLOP/s).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
+`peaks` holds the measured denominators (peak/peak.hip: a dense fp16 MFMA
+loop, a 1 GiB read, a plain read of the decode weight's bytes per call), and
+the roofline and decode entries carry their fractions of those as well.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
                        [--no-cpu-baseline] [--copy-calibration]
+       python bench.py --decode-traffic            (for rocprofv3 --pmc runs)
+       python bench.py --traffic-from F W | --decode-traffic-from F W
 """
 import argparse
 import json
@@ -726,6 +732,68 @@ def run_int4(torch, q, iters=64, copies=8):
 
 
 
+PEAK_LIB = os.path.join(ROOT, "peak", "libpeak.so")
+
+
+def run_peaks(torch, iters=64, copies=16):
+    """Measured roofline denominators (peak/peak.hip): the dense fp16 MFMA
+    issue loop over the whole chip (TFLOP/s), a 1 GiB non-temporal read
+    (GB/s), and the per-call time of a plain read of the decode weight's
+    bytes (65,074,136) over 16 rotated buffers, replayed from a HIP graph as
+    the decode calls are (the floor a decode call could reach)."""
+    import ctypes
+    if not os.path.exists(PEAK_LIB):
+        raise RuntimeError(f"{PEAK_LIB} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(PEAK_LIB)
+    lib.peak_out_elems.restype = ctypes.c_int
+    lib.peak_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    lib.peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    out = torch.empty(lib.peak_out_elems(), dtype=torch.float32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def check(err, what):
+        if err != 0:
+            raise RuntimeError(f"{what}: HIP error {err}")
+
+    flops = ctypes.c_double()
+    for _ in range(3):
+        check(lib.peak_mfma(4096, ctypes.c_void_p(out.data_ptr()), ctypes.byref(flops), stream), "peak_mfma")
+    reps = 10
+    ms = _event_ms(torch, lambda: [check(lib.peak_mfma(4096, ctypes.c_void_p(out.data_ptr()), ctypes.byref(flops),
+                                                       stream), "peak_mfma") for _ in range(reps)], 1) / reps
+    mfma = flops.value / (ms * 1e-3) / 1e12
+    # reads: the best of three grid sizes (2, 4, 8 workgroups per CU)
+    big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    big.fill_(1)
+    read, read_wgs = 0.0, 0
+    for wgs in (2, 4, 8):
+        ms_r = _event_ms(torch, lambda: [check(lib.peak_read(ctypes.c_void_p(big.data_ptr()), big.numel(), wgs,
+                                                             ctypes.c_void_p(out.data_ptr()), stream), "peak_read")
+                                         for _ in range(reps)], 1) / reps
+        if big.numel() / (ms_r * 1e-3) / 1e9 > read:
+            read, read_wgs = big.numel() / (ms_r * 1e-3) / 1e9, wgs
+    del big
+    nb = 65074136
+    bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda:0") for _ in range(copies)]
+    floor_us, floor_wgs = float("inf"), 0
+    for wgs in (2, 4, 8):
+        def one(i, wgs=wgs):
+            s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            check(lib.peak_read(ctypes.c_void_p(bufs[i % copies].data_ptr()), nb, wgs, ctypes.c_void_p(out.data_ptr()),
+                                s), "peak_read")
+        us = graph_time_us(torch, one, iters)
+        if us < floor_us:
+            floor_us, floor_wgs = us, wgs
+    del bufs
+    res = {"mfma_f16_tflops": mfma, "mfma_frac_of_spec": mfma / PEAK_MFMA_TFLOPS,
+           "hbm_read_gbs": read, "hbm_frac_of_spec": read / PEAK_HBM_GBS, "read_wgs_per_cu": read_wgs,
+           "decode_read_floor_us": floor_us, "decode_read_floor_gbs": nb / (floor_us * 1e-6) / 1e9,
+           "floor_wgs_per_cu": floor_wgs}
+    log(f"peaks: MFMA fp16 loop {mfma:.0f} TFLOP/s ({mfma / PEAK_MFMA_TFLOPS:.3f} of spec), 1 GiB read "
+        f"{read:.0f} GB/s, 65 MB read per call (graph) {floor_us:.2f} us")
+    return res
+
+
 def run_copy_calibration(torch, nbytes=1 << 30):
     """A plain device copy of known size, for scaling rocprofv3 byte counters."""
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
@@ -737,25 +805,80 @@ def run_copy_calibration(torch, nbytes=1 << 30):
 
 
 def cpu_baseline(rows=256):
-    """The CPU oracle on a bounded sample of the prefill workload: quantize a
-    row sample of x_up (global scale over the whole tensor, as the method
-    defines it) and evaluate the up-projection GEMM for those rows in fp64."""
+    """The CPU oracle as it stands, timed on the host on bounded samples of
+    the configurations (tens of seconds in all):
+    - value: the prefill up projection, `rows` of its 4096 activation rows
+      (quantized with the whole tensor's g, as the method defines it), then
+      the fp64 GEMM of those rows against W_up, in TFLOP/s (the headline's
+      unit), BLAS on all cores;
+    - quantizer: the oracle's NVFP4 quantizer on one core (BLAS limited to
+      one thread) on activation and weight row samples, GB/s at 2.5625 B per
+      element (2 read, 0.5 + 1/16 written);
+    - per_config: the oracle's fp64 GEMM (weight decode included) in GFLOP/s
+      for each configuration, on the sample each entry names;
+    - the host: CPU model, cores this process may use, and the BLAS
+      libraries with their thread counts (threadpoolctl)."""
     import threadpoolctl
     import workloads
+    from oracle import intq as I
     from oracle import nvfp4 as O
+    info = threadpoolctl.threadpool_info()
+    blas = [{k: i.get(k) for k in ("user_api", "internal_api", "version", "num_threads", "threading_layer")}
+            for i in info]
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
     x_bits, wu_bits, _ = workloads.prefill()
     wq = O.quantize(wu_bits)                      # offline weight quantization, not timed
-    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
     sample = np.asarray(x_bits[:rows])
     g = O.global_scale(x_bits)
-    t0 = time.perf_counter()
-    a = O.quantize(sample, g=g)
-    O.gemm(*a, *wq)
-    dt = time.perf_counter() - t0
+    a, dt_q = timed(lambda: O.quantize(sample, g=g))
+    _, dt_g = timed(lambda: O.gemm(*a, *wq))
+    dt = dt_q + dt_g
     flops = 2.0 * rows * 21504 * 5376
+    per = {}
+    per["prefill_up"] = {"gflops": flops / dt_g / 1e9, "seconds": dt_g,
+                         "sample": f"{rows} x 5376 activation rows x W_up [21504, 5376]"}
+    # quantizer on one core
+    with threadpoolctl.threadpool_limits(1):
+        _, dq_x = timed(lambda: O.quantize(sample, g=g))
+        wsample = np.asarray(wu_bits[:2048])
+        _, dq_w = timed(lambda: O.quantize(wsample))
+    quant = {"activation_gbs": sample.size * 2.5625 / dq_x / 1e9, "activation_sample": f"{rows} x 5376 of x_up",
+             "weight_gbs": wsample.size * 2.5625 / dq_w / 1e9, "weight_sample": "2048 x 5376 of W_up",
+             "threads": 1}
+    # fp64 GEMM per configuration (BLAS on all cores)
+    ta, tw = workloads.tiny()
+    oa, ow = O.quantize(ta), O.quantize(tw)
+    _, d = timed(lambda: O.gemm(*oa, *ow))
+    per["tiny"] = {"gflops": 2.0 * 16 * 256 * 256 / d / 1e9, "seconds": d, "sample": "whole: 16 x 256 x 256"}
+    xd, _ = workloads.decode_x()
+    ad = O.quantize(xd[:16])
+    _, d = timed(lambda: O.gemm(*ad, *wq))
+    per["decode_M16"] = {"gflops": 2.0 * 16 * 21504 * 5376 / d / 1e9, "seconds": d,
+                         "sample": "whole: M = 16 x W [21504, 5376]"}
+    del wq, wu_bits, x_bits
+    wqkv = workloads.dit_weights()[0][:1024]
+    xq = workloads.dit_x(0)
+    aq = O.quantize(xq[:256], g=O.global_scale(xq))
+    wqq = O.quantize(wqkv)
+    _, d = timed(lambda: O.gemm(*aq, *wqq))
+    per["dit_qkv"] = {"gflops": 2.0 * 256 * 1024 * 3072 / d / 1e9, "seconds": d,
+                      "sample": "256 of 4096 activation rows x 1024 of 9216 qkv weight rows, K = 3072"}
+    w4 = workloads.int4_w()[:4096]
+    x4 = workloads.int4_x()[:16]
+    p4, s4, _ = I.int4g_quantize(w4)
+    _, d = timed(lambda: I.int4g_gemm(x4, p4, s4))
+    per["int4_M16"] = {"gflops": 2.0 * 16 * 4096 * 8192 / d / 1e9, "seconds": d,
+                       "sample": "M = 16 x 4096 of 28672 weight rows, K = 8192"}
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows} of 4096 rows of the up projection (quantize + fp64 GEMM incl. weight decode), "
+            "sample": f"{rows} of 4096 rows of the prefill up projection (quantize + fp64 GEMM incl. weight decode), "
                       f"{dt:.1f} s", "seconds": dt,
+            "quantizer_1core": quant, "per_config": per, "blas": blas,
             "cpu": _cpu_model(), "host_cores": len(os.sched_getaffinity(0))}
 
 
@@ -813,6 +936,7 @@ def main():
                "weight_quant": run_weight_quant, "lora": run_lora}[args.only](torch, q)
         print(json.dumps({"only": args.only, "result": res}))
         return
+    peaks = run_peaks(torch)
     pre = run_prefill(torch, q, args.steps, args.warmup)
     log(f"prefill: {pre['ms_per_step']:.3f} ms/step, {pre['tflops']:.1f} TFLOP/s incl. act quant; "
         f"tiled GEMM {pre['gemm_avg_ms']:.3f} ms ({pre['gemm_tflops']:.1f} TFLOP/s)")
@@ -829,7 +953,9 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline()
-        log(f"cpu baseline: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+        log(f"cpu baseline: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads; quantizer 1 core "
+            f"{cpu['quantizer_1core']['activation_gbs']:.3f} GB/s; "
+            + ", ".join(f"{k} {v['gflops']:.1f} GFLOP/s" for k, v in cpu["per_config"].items()))
 
     achieved = pre["gemm_tflops"]
     line = {
@@ -853,7 +979,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
                      "traffic": load_traffic(),
                      "kernel": "nvfp4_gemm_tiled_kernel (+ nvfp4_gemm_tiled_reduce_kernel: one GEMM call)",
-                     "avg_launch_ms": round(pre["gemm_avg_ms"], 4)},
+                     "avg_launch_ms": round(pre["gemm_avg_ms"], 4),
+                     "peak_measured": round(peaks["mfma_f16_tflops"], 1),
+                     "frac_measured": round(achieved / peaks["mfma_f16_tflops"], 4)},
+        "peaks": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in peaks.items()},
         "cpu_baseline": cpu,
         "prefill": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in pre.items()},
     }
@@ -862,7 +991,9 @@ def main():
         line["decode_m1"] = {"value": round(d1["GBps"], 1), "unit": "GB/s", "frac_hbm": round(d1["frac_hbm"], 4),
                              "us": round(d1["us"], 2), "us_incl_act_quant": round(d1["us_incl_act_quant"], 2),
                              "alg_bytes": d1["alg_bytes"], "traffic": d1.get("traffic_bytes"),
-                             "kernel": "nvfp4_gemv_stream_kernel<1, 3, false>"}
+                             "kernel": "nvfp4_gemv_stream_kernel<1, 3, false>",
+                             "frac_hbm_measured": round(d1["GBps"] / peaks["hbm_read_gbs"], 4),
+                             "read_floor_us": round(peaks["decode_read_floor_us"], 2)}
         line["extras"] = extras
     print(json.dumps(line))
 

@@ -1,0 +1,145 @@
+// Roofline denominators measured on the device itself: a dense fp16 MFMA
+// issue loop and an HBM read stream.  bench.py reports the path's fractions
+// against these next to the published peaks (2.5 PFLOP/s dense fp16,
+// 8 TB/s HBM3E).  Measurement code only: nothing in libnvfp4.so uses it.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+constexpr int kChains = 4;          // independent accumulators per wave
+constexpr int kMfmaThreads = 256;   // 4 waves per workgroup
+constexpr int kMfmaWgsPerCu = 2;    // 2 waves per SIMD
+constexpr int kReadThreads = 256;
+constexpr int kReadMaxWgsPerCu = 8;
+constexpr int kReadDepth = 8;       // 16-byte loads per lane in flight
+
+// Every wave issues kChains independent chains of v_mfma_f32_16x16x32_f16
+// (16 x 16 x 32 x 2 = 16384 flops each), `iters` (a multiple of 4) times;
+// one float per thread goes out so the loop is kept.
+__global__ __launch_bounds__(kMfmaThreads) void peak_mfma_kernel(int iters, float* __restrict__ out) {
+  const int t = blockIdx.x * kMfmaThreads + threadIdx.x;
+  half8v a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (_Float16)(float)((t + i) & 7) * (_Float16)0.125f;
+    b[i] = (_Float16)(float)((t * 3 + i) & 7) * (_Float16)0.0625f;
+  }
+  float4v acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
+  // The MFMAs are written as one asm statement per trip (16 of them, four
+  // per accumulator): written as builtins, the compiler rotated the
+  // accumulators through other registers every trip, with moves the MFMAs
+  // then waited for.  No memory access is inside.
+  for (int it = 0; it < iters; it += 4) {
+    asm volatile(
+        "v_mfma_f32_16x16x32_f16 %0, %4, %5, %0\n\t"
+        "v_mfma_f32_16x16x32_f16 %1, %4, %5, %1\n\t"
+        "v_mfma_f32_16x16x32_f16 %2, %4, %5, %2\n\t"
+        "v_mfma_f32_16x16x32_f16 %3, %4, %5, %3\n\t"
+        "v_mfma_f32_16x16x32_f16 %0, %4, %5, %0\n\t"
+        "v_mfma_f32_16x16x32_f16 %1, %4, %5, %1\n\t"
+        "v_mfma_f32_16x16x32_f16 %2, %4, %5, %2\n\t"
+        "v_mfma_f32_16x16x32_f16 %3, %4, %5, %3\n\t"
+        "v_mfma_f32_16x16x32_f16 %0, %4, %5, %0\n\t"
+        "v_mfma_f32_16x16x32_f16 %1, %4, %5, %1\n\t"
+        "v_mfma_f32_16x16x32_f16 %2, %4, %5, %2\n\t"
+        "v_mfma_f32_16x16x32_f16 %3, %4, %5, %3\n\t"
+        "v_mfma_f32_16x16x32_f16 %0, %4, %5, %0\n\t"
+        "v_mfma_f32_16x16x32_f16 %1, %4, %5, %1\n\t"
+        "v_mfma_f32_16x16x32_f16 %2, %4, %5, %2\n\t"
+        "v_mfma_f32_16x16x32_f16 %3, %4, %5, %3"
+        : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3])
+        : "v"(a), "v"(b));
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  out[t] = s;
+}
+
+__device__ __forceinline__ uint4 load_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);   // non-temporal
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Reads `bytes` (< 2^31) once: wave w takes the 1 KB chunks w, w + W,
+// w + 2W, ... (W waves in the grid), 16 bytes per lane, with kReadDepth
+// chunks in flight (each chunk's load is reissued for chunk + kReadDepth W as
+// soon as it has been consumed); XOR of everything per lane goes out.
+// Offsets past the end read zero.
+__global__ __launch_bounds__(kReadThreads) void peak_read_kernel(const void* __restrict__ src, uint32_t bytes,
+                                                                 uint32_t* __restrict__ out) {
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), 0, (int)bytes, 0x00020000);
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t w = blockIdx.x * (kReadThreads / 64) + (threadIdx.x >> 6);
+  const uint32_t W = gridDim.x * (kReadThreads / 64);
+  const uint32_t nch = (bytes + 1023u) / 1024u;
+  uint4 v[kReadDepth];
+#pragma unroll
+  for (int d = 0; d < kReadDepth; ++d) {
+    const uint32_t c = w + d * W;
+    v[d] = load_nt(r, c < nch ? 1024u * c + 16u * lane : 0x80000000u);
+  }
+  uint32_t x = 0;
+  for (uint32_t c0 = w; c0 < nch; c0 += kReadDepth * W) {
+#pragma unroll
+    for (int d = 0; d < kReadDepth; ++d) {
+      x ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+      const uint32_t c = c0 + (d + kReadDepth) * W;
+      v[d] = load_nt(r, c < nch ? 1024u * c + 16u * lane : 0x80000000u);
+    }
+  }
+  out[blockIdx.x * kReadThreads + threadIdx.x] = x;
+}
+
+int cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess)
+      n = 0;
+  }
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Threads of either kernel's largest grid: the length of `out` (floats / uint32).
+int peak_out_elems(void) {
+  const int a = cus() * kMfmaWgsPerCu * kMfmaThreads, b = cus() * kReadMaxWgsPerCu * kReadThreads;
+  return a > b ? a : b;
+}
+
+// Launches the MFMA loop on `stream`; *flops receives the flops it performs.
+// Returns a hipError_t value (0 = success).
+int peak_mfma(int iters, float* out, double* flops, void* stream) {
+  if (iters <= 0 || iters % 4 != 0 || out == nullptr || flops == nullptr || cus() <= 0)
+    return (int)hipErrorInvalidValue;
+  const int grid = cus() * kMfmaWgsPerCu;
+  *flops = (double)grid * (kMfmaThreads / 64) * iters * kChains * 16384.0;
+  hipLaunchKernelGGL(peak_mfma_kernel, dim3(grid), dim3(kMfmaThreads), 0, (hipStream_t)stream, iters, out);
+  return (int)hipGetLastError();
+}
+
+// Launches one read of `bytes` (0 < bytes < 2^31, 16-byte aligned src) on
+// `stream`, with wgs_per_cu (1 .. 8) workgroups of 4 waves per compute unit.
+// Returns a hipError_t value.
+int peak_read(const void* src, int64_t bytes, int wgs_per_cu, uint32_t* out, void* stream) {
+  if (src == nullptr || out == nullptr || bytes <= 0 || bytes >= (int64_t(1) << 31) || cus() <= 0 ||
+      wgs_per_cu < 1 || wgs_per_cu > kReadMaxWgsPerCu || (reinterpret_cast<uintptr_t>(src) & 15) != 0)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(peak_read_kernel, dim3(cus() * wgs_per_cu), dim3(kReadThreads), 0, (hipStream_t)stream, src,
+                     (uint32_t)bytes, out);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -60,5 +60,16 @@ def build(verbose=False, jobs=None):
     return LIB
 
 
+def build_peak(verbose=False):
+    """Compile peak/peak.hip (bench.py's roofline microbenchmarks, not part
+    of the library) into peak/libpeak.so; returns its path."""
+    src = os.path.join(ROOT, "peak", "peak.hip")
+    out = os.path.join(ROOT, "peak", "libpeak.so")
+    tmp = out + ".tmp"
+    _run([HIPCC, *FLAGS, "-shared", src, "-o", tmp], verbose)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
