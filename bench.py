@@ -900,7 +900,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the prefill step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["decode", "dit", "int4", "weight_quant", "lora"],
+    ap.add_argument("--only", choices=["decode", "dit", "int4", "weight_quant", "lora", "peaks"],
                     help="time only this extra workload")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMM traffic summary from two rocprofv3 --pmc runs and exit (no GPU)")
@@ -932,8 +932,8 @@ def main():
         print(json.dumps(run_decode_traffic(torch, q)))
         return
     if args.only:
-        res = {"decode": run_decode, "dit": run_dit, "int4": run_int4,
-               "weight_quant": run_weight_quant, "lora": run_lora}[args.only](torch, q)
+        res = {"decode": run_decode, "dit": run_dit, "int4": run_int4, "weight_quant": run_weight_quant,
+               "lora": run_lora, "peaks": lambda t, _: run_peaks(t)}[args.only](torch, q)
         print(json.dumps({"only": args.only, "result": res}))
         return
     peaks = run_peaks(torch)
