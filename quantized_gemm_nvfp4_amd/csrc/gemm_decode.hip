@@ -656,6 +656,198 @@ __global__ __launch_bounds__(64 * kNxWaves) void nvfp4_w4a16_xs_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-only row-band GEMM for 2 <= M <= 16, K <= 6144 (bf16 activation x
+// NVFP4 weight).
+//
+// The stationary kernel above streams the weight through LDS by DMA and, as
+// it turned out, runs at the same time per workgroup whatever the grid (a
+// per-CU limit); here the weight goes straight into registers in the
+// row-block kernel's pattern, which reads at HBM speed:
+//  - A persistent grid of one 8-wave workgroup per CU; workgroup b takes a
+//    contiguous band of the weight's 16-row groups (5 or 6 on the 21504-row
+//    decode weight).
+//  - Wave w owns K steps [w S / 8, (w + 1) S / 8) of the S steps of 256
+//    values (at most kSt).  Its slice of x (16 rows, lanes i + 16 g: values
+//    [256 t + 64 g, +64) of row i) is loaded once, scaled per row by the power
+//    of two that puts the row's largest magnitude in the wave's slice in
+//    [2^15, 2^16) (exact for values within 2^32 of it), and kept in registers
+//    as fp16, in MFMA order.
+//  - Per row group the wave loads its steps of the 16 rows (lane (i, g): 32
+//    bytes of row i at byte 128 t + 32 g, the 16 lanes of a row one whole
+//    128-byte line, and 4 scale bytes), the next group's loads in flight
+//    while it decodes; v_mfma_f32_16x16x32_f16 with the weight as A and x as
+//    B, so D[n][m] sits in lane m + 16 (n / 4) and the lane's own row factor
+//    undoes the scaling.
+//  - The waves' sums of each group meet in LDS and are added in wave order
+//    (deterministic), scaled by g_w and rounded.
+namespace {
+constexpr int kBandWaves = 8;
+constexpr int kBandMaxGroups = 8;   // row groups per pass through the band
+constexpr int kBandMaxK = 6144;     // three 256-value steps per wave
+}  // namespace
+
+template <int kSt>
+__global__ __launch_bounds__(64 * kBandWaves) void nvfp4_w4a16_band_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
+    const float* __restrict__ w_g, uint16_t* __restrict__ out, int M, int N, int K) {
+  __shared__ float4v s_red[kBandWaves][kBandMaxGroups][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, g = lane >> 4;
+  const uint32_t row_bytes = (uint32_t)K / 2, row_scales = (uint32_t)K / 16;
+  const int nsteps = (K + 255) / 256;
+  const int t0 = wave * nsteps / kBandWaves, t1 = (wave + 1) * nsteps / kBandWaves;   // t1 - t0 <= kSt
+  const int ngroups = (N + 15) / 16;
+  const int gb0 = (int)((int64_t)blockIdx.x * ngroups / gridDim.x);
+  const int gb1 = (int)((int64_t)(blockIdx.x + 1) * ngroups / gridDim.x);
+
+  // Chunk c0 of the band: up to kBandMaxGroups row groups from group c0;
+  // its buffer resources end at its last row, so rows past it read zero.
+  int c0 = gb0, nc = 0, r0 = 0;
+  __amdgpu_buffer_rsrc_t wr, wsr;
+  auto set_chunk = [&]() {
+    nc = min(kBandMaxGroups, gb1 - c0);
+    r0 = 16 * c0;
+    const uint32_t nrows = nc > 0 ? (uint32_t)min(16 * nc, N - r0) : 0u;
+    wr = buffer_of(w_codes + (int64_t)r0 * row_bytes, nrows * row_bytes);
+    wsr = buffer_of(w_scales + (int64_t)r0 * row_scales, nrows * row_scales);
+  };
+  uint4 wc[2][kSt][2];
+  uint32_t wsc[2][kSt];
+  // the wave's steps of row group c of the chunk into buffer b (nothing is
+  // read past the chunk's groups: those offsets lie outside the range)
+  auto issue = [&](int c, int b) {
+#pragma unroll
+    for (int s = 0; s < kSt; ++s) {
+      const uint32_t off = 128u * (uint32_t)(t0 + s) + 32u * (uint32_t)g;
+      const bool in = c < nc && t0 + s < t1 && off < row_bytes;
+      const uint32_t row = 16u * (uint32_t)c + (uint32_t)i;
+      wc[b][s][0] = buffer_load16(wr, in ? row * row_bytes + off : kOob);
+      wc[b][s][1] = buffer_load16(wr, in ? row * row_bytes + off + 16u : kOob);
+      wsc[b][s] = buffer_load4(wsr, in ? row * row_scales + off / 8u : kOob);
+    }
+  };
+  // the first group's weight is requested with the x slice, so both are in
+  // flight together
+  set_chunk();
+  issue(0, 0);
+
+  // x slice, scaled and converted once
+  half8v xv[kSt][2][4];
+  float post;
+  {
+    const auto xr = buffer_of(x, (uint32_t)M * (uint32_t)K * 2u);   // rows >= M read as zero
+    uint4 xb[kSt][8];
+    uint32_t mx = 0;
+#pragma unroll
+    for (int s = 0; s < kSt; ++s) {
+      const uint32_t k = 256u * (uint32_t)(t0 + s) + 64u * (uint32_t)g;
+      const bool in = t0 + s < t1 && k < (uint32_t)K;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) xb[s][u] = buffer_load16(xr, in ? ((uint32_t)i * (uint32_t)K + k) * 2u + 16u * u : kOob);
+    }
+#pragma unroll
+    for (int s = 0; s < kSt; ++s)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        mx = max(max(max(mx, bf16x2_absmax_bits(xb[s][u].x)), bf16x2_absmax_bits(xb[s][u].y)),
+                 max(bf16x2_absmax_bits(xb[s][u].z), bf16x2_absmax_bits(xb[s][u].w)));
+    // the row's maximum over its four lanes (i + 16 g)
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+    const int kexp = min(max((int)(mx >> 7) - 142, -126), 126);
+    const float pre = __uint_as_float((uint32_t)(127 - kexp) << 23);
+    post = __uint_as_float((uint32_t)(127 + kexp) << 23);
+#pragma unroll
+    for (int s = 0; s < kSt; ++s)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t wv[4] = {xb[s][u].x, xb[s][u].y, xb[s][u].z, xb[s][u].w};
+        half8v h;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const half2v pr = __builtin_bit_cast(
+              half2v, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(wv[v] << 16) * pre,
+                                                 __uint_as_float(wv[v] & 0xFFFF0000u) * pre));
+          h[2 * v] = pr.x;
+          h[2 * v + 1] = pr.y;
+        }
+        xv[s][u >> 2][u & 3] = h;
+      }
+  }
+
+  const float gw = *w_g;
+  while (nc > 0) {
+    float4v acc[kBandMaxGroups];
+#pragma unroll
+    for (int c = 0; c < kBandMaxGroups; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kBandMaxGroups; ++c) {
+      if (c >= nc) break;
+      const int b = c & 1;
+      issue(c + 1, b ^ 1);          // past nc: reads nothing
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < kSt; ++s)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const half2v ws2 = e4m3x2_to_f16x2_div256(wsc[b][s] >> (16 * p));
+          const half2v w0 = {ws2.x, ws2.x}, w1 = {ws2.y, ws2.y};
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8_f16_div256(word_of(wc[b][s][p], jj), jj < 2 ? w0 : w1),
+                                                            xv[s][p][jj], acc[c], 0, 0, 0);
+        }
+    }
+    // D[n][m]: lane m + 16 (n / 4), register n % 4; m = i, whose factor is post
+#pragma unroll
+    for (int c = 0; c < kBandMaxGroups; ++c)
+      if (c < nc) s_red[wave][c][lane] = acc[c] * post;
+    __syncthreads();
+    for (int e = threadIdx.x; e < nc * 64; e += 64 * kBandWaves) {
+      const int c = e >> 6, ln = e & 63;
+      float4v sum = s_red[0][c][ln];
+#pragma unroll
+      for (int wv = 1; wv < kBandWaves; ++wv) sum += s_red[wv][c][ln];
+      const int m = ln & 15, n = r0 + 16 * c + 4 * (ln >> 4);
+      if (m >= M) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) out[(int64_t)m * N + n + r] = (uint16_t)f32_to_bf16_rne(sum[r] * gw);
+    }
+    __syncthreads();                // s_red is reused by the next chunk
+    c0 += kBandMaxGroups;
+    set_chunk();
+    issue(0, 0);                    // nc == 0: reads nothing
+  }
+}
+
+namespace {
+template <int kSt>
+void launch_w4a16_band_st(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out, int M,
+                          int N, int K, hipStream_t stream) {
+  const int64_t cus = device_cus(), ngroups = ((int64_t)N + 15) / 16;
+  const unsigned grid = (unsigned)(ngroups < cus ? ngroups : cus);
+  hipLaunchKernelGGL(nvfp4_w4a16_band_kernel<kSt>, dim3(grid), dim3(64 * kBandWaves), 0, stream,
+                     (const uint16_t*)x, wc, ws, wg, (uint16_t*)out, M, N, K);
+}
+// The row-band kernel for M <= 16, K % 128 == 0, K <= 6144 (at most three
+// steps per wave: four spill registers); false if the shape is outside that
+// range.
+bool launch_w4a16_band(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out, int64_t M,
+                       int64_t N, int64_t K, hipStream_t stream) {
+  if (M < 1 || M > 16 || K % 128 != 0 || K <= 0 || K > kBandMaxK) return false;
+  const int nsteps = (int)((K + 255) / 256), st = (nsteps + kBandWaves - 1) / kBandWaves;
+  switch (st) {
+    case 1: launch_w4a16_band_st<1>(x, wc, ws, wg, out, (int)M, (int)N, (int)K, stream); return true;
+    case 2: launch_w4a16_band_st<2>(x, wc, ws, wg, out, (int)M, (int)N, (int)K, stream); return true;
+    case 3: launch_w4a16_band_st<3>(x, wc, ws, wg, out, (int)M, (int)N, (int)K, stream); return true;
+    default: return false;
+  }
+}
+}  // namespace
+
 namespace {
 // The weight-only GEMM for 3 <= M <= 16; false if the shape is outside its
 // range.  Waves per workgroup and passes: P = ceil(pieces / 8) passes of
@@ -981,10 +1173,13 @@ bool nvfp4_w4a16_decode_supported(int64_t M, int64_t K) {
 
 hipError_t launch_nvfp4_w4a16_decode(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
                                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  // M <= 2: the row-slot GEMV, 8 rows per workgroup (at M = 2 on 21504 x
-  // 5376, 8 rows took 19.4 us per call against 21.5 us for 4 and 20.5 us for
-  // 6; 12 and more spill registers).  3 <= M <= 16: the activation-
-  // stationary kernel, which reads the weight once for all rows.
+  // 2 <= M <= 16 and K <= 6144: the row-band kernel (on 21504 x 5376 it
+  // took 18.3 us at M = 3 against 21.5 us for the row-slot GEMV at M = 2).
+  // 3 <= M <= 16, larger K: the activation-stationary kernel.  Both read the
+  // weight once for all rows.  M = 1 and the remaining M = 2: the row-slot
+  // GEMV, 8 rows per workgroup (at M = 2, 8 rows took 19.4 us per call
+  // against 21.5 us for 4 and 20.5 us for 6; 12 and more spill registers).
+  if (M >= 2 && launch_w4a16_band(x, wc, ws, wg, out, M, N, K, stream)) return hipGetLastError();
   if (M >= 3) {
     if (!launch_w4a16_xs(x, wc, ws, wg, out, M, N, K, stream)) return hipErrorInvalidValue;
     return hipGetLastError();

@@ -45,18 +45,33 @@ def test_decode_shapes(M, N, K):
     check(x, w, algos=(0, 2, 3), label=f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(4, 300, 5376), (7, 20000, 4096), (16, 70, 12288), (9, 33000, 512),
-                                   (3, 1, 128), (12, 17, 4608)])
+@pytest.mark.parametrize("M,N,K", [(4, 300, 6272), (7, 20000, 8192), (16, 70, 12288), (9, 33000, 6656),
+                                   (3, 1, 6272), (12, 17, 8704)])
 def test_stationary_shapes(M, N, K):
-    # 3 <= M <= 16 runs the activation-stationary kernel: 512-value pieces
-    # per wave, 6 waves x 2 passes for K = 5376 (a half piece at the end of
-    # each row), 8 x 1 for 4096, 8 x 3 for 12288, 8 row groups per batch when
-    # N >= 64 rows per compute unit (N = 20000) and two batches when a
-    # workgroup holds more than 128 rows (N = 33000), a lone partial piece
-    # (K = 128), N not a multiple of 16.
+    # 3 <= M <= 16 with K > 6144 runs the activation-stationary kernel:
+    # 512-value pieces per wave, 7 waves x 2 passes for K = 6272 (a quarter
+    # piece at the end of each row), 8 x 2 for 8192, 8 x 3 for 12288, 8 row
+    # groups per batch when N >= 64 rows per compute unit (N = 20000) and two
+    # batches when a workgroup holds more than 128 rows (N = 33000), N not a
+    # multiple of 16.
     x = workloads.random_bf16(M * 13 + K, (M, K), outlier_frac=0.01, outlier_mul=20)
     w = workloads.random_bf16(N * 17 + K, (N, K), sigma=0.02, zero_frac=0.05)
     check(x, w, algos=(0, 2), label=f"stationary {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 300, 5376), (7, 20000, 4096), (9, 33000, 512), (3, 1, 128), (12, 17, 4608),
+                                   (16, 4100, 2176), (5, 140001, 256), (8, 21504, 6144), (16, 31, 6016),
+                                   (2, 20000, 5376), (2, 45, 128)])
+def test_band_shapes(M, N, K):
+    # 2 <= M <= 16 with K <= 6144 runs the row-band kernel: one workgroup per
+    # CU over contiguous bands of 16-row groups (N = 4100: one or two groups
+    # per workgroup; N = 140001: more than eight, so several passes through
+    # the band), waves owning 1-3 steps of 256 values (K = 128 and 512 leave
+    # waves without steps; K = 2176 and 6016 end with a half step; K = 6144
+    # gives every wave three), N not a multiple of 16.
+    x = workloads.random_bf16(M * 19 + K, (M, K), outlier_frac=0.01, outlier_mul=20)
+    w = workloads.random_bf16(N * 23 + K, (N, K), sigma=0.02, zero_frac=0.05)
+    check(x, w, algos=(0, 2), label=f"band {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M,N,K", [(17, 40, 272), (1, 5, 32768 + 128), (5, 3, 16)])
@@ -70,8 +85,9 @@ def test_simple_shapes(M, N, K):
 @pytest.mark.parametrize("M", [2, 5])
 def test_activation_range_rescaling(scale, M):
     # the decode kernels rescale x by a power of two per 2048-value slot (M
-    # <= 2) or per row and 512-value piece (M >= 3) before the fp16
-    # conversion: tiny and huge activations stay within tolerance
+    # <= 2) or per row and wave slice (M >= 3: 512-value pieces, or a wave's
+    # steps in the row-band kernel) before the fp16 conversion: tiny and huge
+    # activations stay within tolerance
     x = (workloads.random_bf16(91, (M, 2048 * 3)).view(np.uint16))
     xv = (F.bf16_from_bits(x).astype(np.float64) * scale).astype(np.float32)
     xb = F.bf16_bits(F.bf16_round(xv).astype(np.float32))
