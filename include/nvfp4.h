@@ -267,13 +267,15 @@ nvfp4_status nvfp4_quantize_amax(const void* x_bf16, int64_t rows, int64_t cols,
  * their outliers.
  * x [M, K] bf16 row-major; w_codes [N, K/2]; w_scales [N, K/16]; w_gscale
  * a device fp32 pointer.  K % 16 == 0; K == 0 writes zeros.
- * Exactness: W's decoded values are exact; the decode kernel (M <= 16,
- * K % 128 == 0, K <= 32768; from M = 3 it runs once per pair of rows of x,
- * reading the weight ceil(M / 2) times) feeds the matrix cores fp16, converting each
- * 2048-value slice of x after a power-of-two rescale that puts the slice's
- * largest magnitude in [2^15, 2^16): elements within 2^32 of that maximum
- * are exact, smaller ones are truncated to the fp16 subnormal grid.  Other
- * shapes run a one-output-per-thread kernel in fp32.
+ * Exactness: W's decoded values are exact; the decode kernels (M <= 16,
+ * K % 128 == 0, K <= 32768; each reads the weight once per call) feed the
+ * matrix cores fp16, converting x after a power-of-two rescale that puts
+ * the largest magnitude of each slice in [2^15, 2^16): per 2048-value slice
+ * at M = 1, per row and slice of up to 768 values at 2 <= M <= 16 with
+ * K <= 6144, per row and 512-value piece otherwise.  Elements within 2^32
+ * of their slice's maximum are exact, smaller ones are truncated to the
+ * fp16 subnormal grid.  Other shapes run a one-output-per-thread kernel in
+ * fp32.
  * algo: NVFP4_ALGO_AUTO, _DECODE or _SIMPLE; others return
  * NVFP4_ERR_INVALID_ARG.  out must not overlap any input.
  */

@@ -122,6 +122,18 @@ def test_int4_stationary_shapes(M, N, K):
     check_gemv(x, w, algos=(0, 2), label=f"int4 stationary {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(2, 28672, 8192), (16, 140001, 256), (5, 3000, 12288 + 128), (4, 9, 128),
+                                   (2, 300, 65536)])
+def test_int4_more_decode_shapes(M, N, K):
+    # the row-slot GEMV at the decode weight's shape with M = 2; the
+    # row-block kernel (K % 512 != 0) with 1250 workgroups of 112 rows (N =
+    # 140001), an odd group count (K = 12416: a half step at the end) and a
+    # lone group (K = 128); K past the row-slot GEMV's limit at M = 2
+    x = workloads.random_bf16(M * 11 + K, (M, K), outlier_frac=0.01, outlier_mul=20)
+    w = workloads.random_bf16(N * 13 + K, (N, K), sigma=0.02, zero_frac=0.05)
+    check_gemv(x, w, algos=(0, 2), label=f"int4 more {M}x{N}x{K}")
+
+
 def test_int4_config():
     w = workloads.int4_w()
     x = workloads.int4_x()
