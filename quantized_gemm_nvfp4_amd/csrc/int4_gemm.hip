@@ -14,7 +14,8 @@
 //  - The offset is removed with one more MFMA per step against a constant
 //    -8 operand: sum x (q + 8) + sum x (-8) = sum x q, both sides exact
 //    products, summed in fp32 (the offset is small, so the two sums do not
-//    cancel catastrophically).
+//    cancel catastrophically).  The tiled kernel, where that MFMA would be
+//    a third of the matrix work, decodes q itself (sign-magnitude bytes).
 //  - Each 128-value group is accumulated in its own fp32 tile, then scaled
 //    once by its fp16 scale: q * s16 is not exact in bf16, so the scale is
 //    kept out of the MFMA operands.
@@ -33,6 +34,31 @@ __device__ __forceinline__ short8v int4x8_offset_bf16(uint32_t w) {
   const uint32_t t = w ^ 0x88888888u;
   const uint32_t ev = t & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
   const uint32_t od = (t >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+  const uint32_t lo = __builtin_amdgcn_perm(od, ev, 0x05010400u);   // e0 e1 e2 e3
+  const uint32_t hi = __builtin_amdgcn_perm(od, ev, 0x07030602u);   // e4 e5 e6 e7
+  const bf16x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false);
+  const bf16x2v p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true);
+  const bf16x2v p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false);
+  const bf16x2v p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true);
+  const short2v s0 = __builtin_bit_cast(short2v, p0), s1 = __builtin_bit_cast(short2v, p1);
+  const short2v s2 = __builtin_bit_cast(short2v, p2), s3 = __builtin_bit_cast(short2v, p3);
+  return short8v{s0.x, s0.y, s1.x, s1.y, s2.x, s2.y, s3.x, s3.y};
+}
+
+// 8 int4 codes -> 8 bf16 values q (signed) in element order: each nibble
+// becomes a sign-magnitude E4M3 byte, sign in bit 7 and |q| * 2^-9 as its
+// value (subnormals for |q| <= 7, the smallest normal for 8), which the
+// conversion at scale 2^9 returns exactly.  Per nibble u (two's complement):
+// |q| = u for u < 8, else 16 - u = ((u ^ 7) & 7) + 1; on all eight nibbles
+// at once, mask = 7 where the sign is set and |q| = ((u ^ mask) & 7) + sign,
+// which never carries into the next nibble (it is at most 8).  About twice
+// the work of the offset form above, but no offset term to add.
+__device__ __forceinline__ short8v int4x8_signed_bf16(uint32_t w) {
+  const uint32_t sg = w & 0x88888888u;                      // sign bits
+  const uint32_t one = sg >> 3;                             // 1 where negative
+  const uint32_t mag = ((w ^ (sg - one)) & 0x77777777u) + one;
+  const uint32_t ev = (mag & 0x0F0F0F0Fu) | ((sg << 4) & 0x80808080u);          // elements 0, 2, 4, 6
+  const uint32_t od = ((mag >> 4) & 0x0F0F0F0Fu) | (sg & 0x80808080u);          // elements 1, 3, 5, 7
   const uint32_t lo = __builtin_amdgcn_perm(od, ev, 0x05010400u);   // e0 e1 e2 e3
   const uint32_t hi = __builtin_amdgcn_perm(od, ev, 0x07030602u);   // e4 e5 e6 e7
   const bf16x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false);
@@ -500,8 +526,11 @@ __global__ __launch_bounds__(1024) void int4g_gemv_rowslot_kernel(const uint16_t
 }
 
 // ---- any M: LDS-staged MFMA tiles -----------------------------------------
-// Workgroup tile 128 (m) x 256 (n), K stage = one 128-value group; 4 waves of
-// 64 x 128 (2 x 4 tiles of 32 x 32).  x fragments are stored in LDS in lane
+// Workgroup tile 128 (m) x 256 (n), K stage = one 128-value group; 8 waves of
+// 64 x 64 (2 x 2 tiles of 32 x 32), two per SIMD, so that while one wave
+// scales a finished group into its accumulators the other keeps the matrix
+// core busy (with one 64 x 128 wave per SIMD the scaling waited for the
+// group's last MFMAs and the next group's MFMAs waited for the scaling).  x fragments are stored in LDS in lane
 // order (one 1 KB region per MFMA step), the packed weight likewise; both
 // are copied with global_load_lds (16-byte transfers, which land at
 // lane * 16 in LDS) into a ring of three stage slots, two stages ahead of
@@ -518,7 +547,8 @@ constexpr int kXBytes = IT_M * IT_K * 2;        // 32 KB
 constexpr int kQBytes = IT_N * IT_K / 2;        // 16 KB
 constexpr int kIStage = kXBytes + kQBytes;
 constexpr int kIRing = 3;
-constexpr int kILoads = 16;                     // vector memory instructions per wave per stage
+constexpr int kIWaves = 8;
+constexpr int kILoads = 8;                      // vector memory instructions per wave per stage
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 #define INT4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
@@ -545,12 +575,12 @@ struct I4Ctx {
   // outstanding LDS access before using any LDS read; with the buffer form
   // it keeps exact counts).
   __amdgpu_buffer_rsrc_t rx, rq;
-  uint32_t ox[8];          // x copy offsets of this lane
-  int lds_x[8];
-  uint32_t oq[4];          // weight copy offsets
-  int lds_q[4];
-  const uint16_t* gsc[4];  // group-scale rows of this lane's 4 output columns
-  uint32_t scr[kIRing][4]; // group scales per ring slot (raw fp16)
+  uint32_t ox[4];          // x copy offsets of this lane
+  int lds_x[4];
+  uint32_t oq[2];          // weight copy offsets
+  int lds_q[2];
+  const uint16_t* gsc[2];  // group-scale rows of this lane's 2 output columns
+  uint32_t scr[kIRing][2]; // group scales per ring slot (raw fp16)
   int wm, wn, lane;
 };
 
@@ -560,62 +590,56 @@ template <int B>
 __device__ __forceinline__ void i4_issue(I4Ctx& c, int g) {
   uint8_t* base = i4_slot<B>();
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rx, (lds_void_t)(base + c.lds_x[i]), 16, c.ox[i] + 256u * g, 0, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rq, (lds_void_t)(base + c.lds_q[i]), 16, c.oq[i] + 64u * g, 0, 0, 0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) c.scr[B][j] = c.gsc[j][g];
+  for (int j = 0; j < 2; ++j) c.scr[B][j] = c.gsc[j][g];
 }
 
 template <int B>
-__device__ __forceinline__ void i4_compute(I4Ctx& c, float16v (&acc)[2][4]) {
+__device__ __forceinline__ void i4_compute(I4Ctx& c, float16v (&acc)[2][2]) {
   const uint8_t* base = i4_slot<B>();
   const int lane = c.lane, wm = c.wm, wn = c.wn;
-  const short8v c8 = {kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16,
-                      kMinus8Bf16, kMinus8Bf16, kMinus8Bf16, kMinus8Bf16};
-  float sc[4];
+  float sc[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sc[j] = f16_bits_to_f32(c.scr[B][j]);
-  uint4 cq[4][2];
+  for (int j = 0; j < 2; ++j) sc[j] = f16_bits_to_f32(c.scr[B][j]);
+  uint4 cq[2][2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
-      cq[j][hs] = *(const uint4*)(base + kXBytes + ((4 * wn + j) * 2 + hs) * 1024 + lane * 16);
-  float16v tmp[2][4], corr[2];
+      cq[j][hs] = *(const uint4*)(base + kXBytes + ((2 * wn + j) * 2 + hs) * 1024 + lane * 16);
+  float16v tmp[2][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    corr[i] = float16v{};
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tmp[i][j] = float16v{};
-  }
+    for (int j = 0; j < 2; ++j) tmp[i][j] = float16v{};
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    short8v xa[2], wb[4];
+    short8v xa[2], wb[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) xa[i] = as_short8(*(const uint4*)(base + ((2 * wm + i) * 8 + jj) * 1024 + lane * 16));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wb[j] = int4x8_offset_bf16(word_of(cq[j][jj >> 2], jj & 3));
+    for (int j = 0; j < 2; ++j) wb[j] = int4x8_signed_bf16(word_of(cq[j][jj >> 2], jj & 3));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], c8, corr[i], 0, 0, 0);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         tmp[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], wb[j], tmp[i][j], 0, 0, 0);
-    }
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] += sc[j] * (tmp[i][j] + corr[i]);
+    for (int j = 0; j < 2; ++j) acc[i][j] += sc[j] * tmp[i][j];
 }
 
 // Stage g in slot B.  kChecked: near the end, where stage g + 1 or g + 2
 // may not exist (all conditions are uniform).
 template <int B, bool kChecked>
-__device__ __forceinline__ void i4_stage(I4Ctx& c, int g, int ng, float16v (&acc)[2][4]) {
+__device__ __forceinline__ void i4_stage(I4Ctx& c, int g, int ng, float16v (&acc)[2][2]) {
   if (!kChecked || g + 1 < ng) {
     INT4_WAIT_VMCNT(kILoads);     // stage g + 1's loads may stay in flight
   } else {
@@ -627,7 +651,7 @@ __device__ __forceinline__ void i4_stage(I4Ctx& c, int g, int ng, float16v (&acc
 }
 }  // namespace
 
-__global__ __launch_bounds__(256, 1) void int4g_gemm_tiled_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(64 * kIWaves, 1) void int4g_gemm_tiled_kernel(const uint16_t* __restrict__ x,
                                                                   const uint8_t* __restrict__ q,
                                                                   const uint16_t* __restrict__ s,
                                                                   uint16_t* __restrict__ out, int M, int N, int K,
@@ -643,9 +667,9 @@ __global__ __launch_bounds__(256, 1) void int4g_gemm_tiled_kernel(const uint16_t
 
   I4Ctx c;
   c.lane = lane;
-  c.wm = wave >> 1;
-  c.wn = wave & 1;
-  // x: 4 fragments x 8 steps; wave w copies steps 2w, 2w+1 of every fragment.
+  c.wm = wave >> 2;
+  c.wn = wave & 3;
+  // x: 4 fragments x 8 steps; wave w copies step w of every fragment.
   // Lane l of region (f, jj): row 32f + l%32, values 64(l/32) + 8jj .. +8.
   // Offsets are relative to the tile's first row (at most 128 x 2K bytes of
   // x and 256 x K/2 of codes: the host takes this kernel only for K < 2^22).
@@ -654,27 +678,27 @@ __global__ __launch_bounds__(256, 1) void int4g_gemm_tiled_kernel(const uint16_t
   c.rx = buffer_of(x + (int64_t)m0 * K, (uint32_t)rows_x * (uint32_t)K * 2u);
   c.rq = buffer_of(q + (int64_t)n0 * (K / 2), (uint32_t)rows_q * (uint32_t)(K / 2));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int f = i >> 1, jj = 2 * wave + (i & 1);
+  for (int i = 0; i < 4; ++i) {
+    const int f = i, jj = wave;
     const int row = min(32 * f + (lane & 31), rows_x - 1);
     c.ox[i] = 2u * ((uint32_t)row * (uint32_t)K + 64u * (lane >> 5) + 8u * jj);
     c.lds_x[i] = (f * 8 + jj) * 1024;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qd = 4 * wave + i, f = qd >> 1, hs = qd & 1;
+  for (int i = 0; i < 2; ++i) {
+    const int qd = 2 * wave + i, f = qd >> 1, hs = qd & 1;
     const int row = min(32 * f + (lane & 31), rows_q - 1);
     c.oq[i] = (uint32_t)row * (uint32_t)(K / 2) + 32u * (lane >> 5) + 16u * hs;
     c.lds_q[i] = kXBytes + qd * 1024;
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) c.gsc[j] = s + (int64_t)min(n0 + 128 * (wave & 1) + 32 * j + (lane & 31), N - 1) * ng;
+  for (int j = 0; j < 2; ++j) c.gsc[j] = s + (int64_t)min(n0 + 64 * c.wn + 32 * j + (lane & 31), N - 1) * ng;
 
-  float16v acc[2][4];
+  float16v acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = float16v{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = float16v{};
 
   // Prologue: stages 0 and 1 in flight.  With a single group slot 1 gets
   // group 0 again (never read): no branch here, so the compiler's count of
@@ -701,8 +725,8 @@ __global__ __launch_bounds__(256, 1) void int4g_gemm_tiled_kernel(const uint16_t
   // D[m][n] of each 32 x 32 tile: lane n + 32((m/4)%2), register (m%4) + 4(m/8).
   const int wm = c.wm, wn = c.wn, h = lane >> 5, r32 = lane & 31;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 128 * wn + 32 * j + r32;
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + 64 * wn + 32 * j + r32;
     if (n >= N) continue;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -769,7 +793,7 @@ hipError_t launch_int4g_gemm_decode(const void* x, const uint8_t* q, const void*
 hipError_t launch_int4g_gemm_tiled(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,
                                    int64_t N, int64_t K, hipStream_t stream) {
   const int tiles_m = (int)((M + IT_M - 1) / IT_M), tiles_n = (int)((N + IT_N - 1) / IT_N);
-  hipLaunchKernelGGL(int4g_gemm_tiled_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(int4g_gemm_tiled_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kIWaves), 0, stream,
                      (const uint16_t*)x, q, (const uint16_t*)s, (uint16_t*)out, (int)M, (int)N, (int)K, tiles_m,
                      tiles_n);
   return hipGetLastError();
