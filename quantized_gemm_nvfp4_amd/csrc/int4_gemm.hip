@@ -527,10 +527,13 @@ __global__ __launch_bounds__(1024) void int4g_gemv_rowslot_kernel(const uint16_t
 
 // ---- any M: LDS-staged MFMA tiles -----------------------------------------
 // Workgroup tile 128 (m) x 256 (n), K stage = one 128-value group; 8 waves of
-// 64 x 64 (2 x 2 tiles of 32 x 32), two per SIMD, so that while one wave
+// 128 x 32 (4 x 1 tiles of 32 x 32), two per SIMD, so that while one wave
 // scales a finished group into its accumulators the other keeps the matrix
 // core busy (with one 64 x 128 wave per SIMD the scaling waited for the
-// group's last MFMAs and the next group's MFMAs waited for the scaling).  x fragments are stored in LDS in lane
+// group's last MFMAs and the next group's MFMAs waited for the scaling),
+// and each weight fragment is decoded by one wave only (the kernel is
+// bound by vector work: 64 x 64 waves, each weight fragment decoded twice,
+// took 1.29 ms at M = 2048 on 28672 x 8192 against 1.10-1.14 ms).  x fragments are stored in LDS in lane
 // order (one 1 KB region per MFMA step), the packed weight likewise; both
 // are copied with global_load_lds (16-byte transfers, which land at
 // lane * 16 in LDS) into a ring of three stage slots, two stages ahead of
@@ -548,6 +551,7 @@ constexpr int kQBytes = IT_N * IT_K / 2;        // 16 KB
 constexpr int kIStage = kXBytes + kQBytes;
 constexpr int kIRing = 3;
 constexpr int kIWaves = 8;
+constexpr int kIFi = 4, kIFj = 1;              // 32 x 32 tiles per wave along m and n
 constexpr int kILoads = 8;                      // vector memory instructions per wave per stage
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
@@ -579,8 +583,8 @@ struct I4Ctx {
   int lds_x[4];
   uint32_t oq[2];          // weight copy offsets
   int lds_q[2];
-  const uint16_t* gsc[2];  // group-scale rows of this lane's 2 output columns
-  uint32_t scr[kIRing][2]; // group scales per ring slot (raw fp16)
+  const uint16_t* gsc[kIFj];  // group-scale rows of this lane's output columns
+  uint32_t scr[kIRing][kIFj]; // group scales per ring slot (raw fp16)
   int wm, wn, lane;
 };
 
@@ -596,50 +600,51 @@ __device__ __forceinline__ void i4_issue(I4Ctx& c, int g) {
   for (int i = 0; i < 2; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rq, (lds_void_t)(base + c.lds_q[i]), 16, c.oq[i] + 64u * g, 0, 0, 0);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) c.scr[B][j] = c.gsc[j][g];
+  for (int j = 0; j < kIFj; ++j) c.scr[B][j] = c.gsc[j][g];
 }
 
 template <int B>
-__device__ __forceinline__ void i4_compute(I4Ctx& c, float16v (&acc)[2][2]) {
+__device__ __forceinline__ void i4_compute(I4Ctx& c, float16v (&acc)[kIFi][kIFj]) {
   const uint8_t* base = i4_slot<B>();
   const int lane = c.lane, wm = c.wm, wn = c.wn;
-  float sc[2];
+  float sc[kIFj];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) sc[j] = f16_bits_to_f32(c.scr[B][j]);
-  uint4 cq[2][2];
+  for (int j = 0; j < kIFj; ++j) sc[j] = f16_bits_to_f32(c.scr[B][j]);
+  uint4 cq[kIFj][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < kIFj; ++j)
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
-      cq[j][hs] = *(const uint4*)(base + kXBytes + ((2 * wn + j) * 2 + hs) * 1024 + lane * 16);
-  float16v tmp[2][2];
+      cq[j][hs] = *(const uint4*)(base + kXBytes + ((kIFj * wn + j) * 2 + hs) * 1024 + lane * 16);
+  float16v tmp[kIFi][kIFj];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kIFi; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) tmp[i][j] = float16v{};
+    for (int j = 0; j < kIFj; ++j) tmp[i][j] = float16v{};
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    short8v xa[2], wb[2];
+    short8v xa[kIFi], wb[kIFj];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) xa[i] = as_short8(*(const uint4*)(base + ((2 * wm + i) * 8 + jj) * 1024 + lane * 16));
+    for (int i = 0; i < kIFi; ++i)
+      xa[i] = as_short8(*(const uint4*)(base + ((kIFi * wm + i) * 8 + jj) * 1024 + lane * 16));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) wb[j] = int4x8_signed_bf16(word_of(cq[j][jj >> 2], jj & 3));
+    for (int j = 0; j < kIFj; ++j) wb[j] = int4x8_signed_bf16(word_of(cq[j][jj >> 2], jj & 3));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kIFi; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < kIFj; ++j)
         tmp[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], wb[j], tmp[i][j], 0, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kIFi; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] += sc[j] * tmp[i][j];
+    for (int j = 0; j < kIFj; ++j) acc[i][j] += sc[j] * tmp[i][j];
 }
 
 // Stage g in slot B.  kChecked: near the end, where stage g + 1 or g + 2
 // may not exist (all conditions are uniform).
 template <int B, bool kChecked>
-__device__ __forceinline__ void i4_stage(I4Ctx& c, int g, int ng, float16v (&acc)[2][2]) {
+__device__ __forceinline__ void i4_stage(I4Ctx& c, int g, int ng, float16v (&acc)[kIFi][kIFj]) {
   if (!kChecked || g + 1 < ng) {
     INT4_WAIT_VMCNT(kILoads);     // stage g + 1's loads may stay in flight
   } else {
@@ -667,8 +672,8 @@ __global__ __launch_bounds__(64 * kIWaves, 1) void int4g_gemm_tiled_kernel(const
 
   I4Ctx c;
   c.lane = lane;
-  c.wm = wave >> 2;
-  c.wn = wave & 3;
+  c.wm = wave / (IT_N / 32 / kIFj);     // waves along n first
+  c.wn = wave % (IT_N / 32 / kIFj);
   // x: 4 fragments x 8 steps; wave w copies step w of every fragment.
   // Lane l of region (f, jj): row 32f + l%32, values 64(l/32) + 8jj .. +8.
   // Offsets are relative to the tile's first row (at most 128 x 2K bytes of
@@ -692,13 +697,14 @@ __global__ __launch_bounds__(64 * kIWaves, 1) void int4g_gemm_tiled_kernel(const
     c.lds_q[i] = kXBytes + qd * 1024;
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) c.gsc[j] = s + (int64_t)min(n0 + 64 * c.wn + 32 * j + (lane & 31), N - 1) * ng;
+  for (int j = 0; j < kIFj; ++j)
+    c.gsc[j] = s + (int64_t)min(n0 + 32 * kIFj * c.wn + 32 * j + (lane & 31), N - 1) * ng;
 
-  float16v acc[2][2];
+  float16v acc[kIFi][kIFj];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kIFi; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = float16v{};
+    for (int j = 0; j < kIFj; ++j) acc[i][j] = float16v{};
 
   // Prologue: stages 0 and 1 in flight.  With a single group slot 1 gets
   // group 0 again (never read): no branch here, so the compiler's count of
@@ -725,14 +731,14 @@ __global__ __launch_bounds__(64 * kIWaves, 1) void int4g_gemm_tiled_kernel(const
   // D[m][n] of each 32 x 32 tile: lane n + 32((m/4)%2), register (m%4) + 4(m/8).
   const int wm = c.wm, wn = c.wn, h = lane >> 5, r32 = lane & 31;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + 64 * wn + 32 * j + r32;
+  for (int j = 0; j < kIFj; ++j) {
+    const int n = n0 + 32 * kIFj * wn + 32 * j + r32;
     if (n >= N) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kIFi; ++i) {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const int m = m0 + 64 * wm + 32 * i + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        const int m = m0 + 32 * kIFi * wm + 32 * i + 8 * (rr >> 2) + 4 * h + (rr & 3);
         if (m < M) out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(acc[i][j][rr]);
       }
     }
