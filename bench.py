@@ -727,6 +727,12 @@ def run_int4(torch, q, iters=64, copies=8):
                       "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                       "traffic_bytes": t["fetch_bytes"] + t["write_bytes"] if t else None}
     log(f"int4 asym M=1: {us:.2f} us, {out['asym_M1']['GBps']:.0f} GB/s")
+    # M = 2048 on the tile kernel (group sums of x on the matrix cores)
+    xa = dev_bf16(torch, x_bits)
+    ya = torch.empty((2048, N), dtype=torch.bfloat16, device="cuda:0")
+    ms = _event_ms(torch, lambda: q.int4g_asym_gemv(xa, *rot[0], out=ya), 5)
+    out["asym_M2048"] = {"ms": ms, "tflops": 2.0 * 2048 * N * K / (ms * 1e-3) / 1e12}
+    log(f"int4 asym M=2048: {ms:.3f} ms")
     del rot
     return out
 

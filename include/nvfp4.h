@@ -342,8 +342,11 @@ nvfp4_status int4g_asym_quantize(const void* w_bf16, int64_t N, int64_t K, int64
 /*
  * out[M, N] (bf16) = bf16_RNE( sum_k x[m, k] * s16[n, k/128] * (q[n, k] -
  * z[n, k/128]) ), x bf16 [M, K] (the same passage; weight-only).  M <= 2
- * (K <= 32768) runs the row-slot GEMV that streams q once; other shapes a
- * one-output-per-thread kernel.  algo: NVFP4_ALGO_AUTO, _DECODE or _SIMPLE.
+ * (K <= 32768) runs the row-slot GEMV that streams q once; other shapes
+ * with K < 2^22 the LDS-staged MFMA tile kernel (per group, s16 (sum x q -
+ * z sum x), the group sums of x taken on the matrix cores), the rest a
+ * one-output-per-thread kernel.  algo: NVFP4_ALGO_AUTO, _TILED (K < 2^22,
+ * else NVFP4_ERR_UNSUPPORTED), _DECODE (M <= 2, K <= 32768) or _SIMPLE.
  */
 nvfp4_status int4g_asym_gemv(const void* x_bf16, const uint8_t* q, const void* scales_fp16,
                              const uint8_t* zeros, void* out_bf16, int64_t M, int64_t N, int64_t K,

@@ -581,8 +581,7 @@ nvfp4_status int4g_asym_gemv_ex(const void* x_bf16, const uint8_t* q, const void
   if (nvfp4_status s = check_products(M, N, K)) return s;
   if (group != 128) return fail(NVFP4_ERR_UNSUPPORTED, "group=%lld; only 128 is supported", (long long)group);
   if (K % 128 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of the group (128)", (long long)K);
-  if (algo != NVFP4_ALGO_AUTO && algo != NVFP4_ALGO_DECODE && algo != NVFP4_ALGO_SIMPLE)
-    return fail(NVFP4_ERR_INVALID_ARG, "algo %d is not available for the asymmetric INT4 GEMV", algo);
+  if (algo < NVFP4_ALGO_AUTO || algo > NVFP4_ALGO_SIMPLE) return fail(NVFP4_ERR_INVALID_ARG, "unknown algo %d", algo);
   REQUIRE_ALIGN(x_bf16, 16);
   REQUIRE_ALIGN(q, 16);
   REQUIRE_ALIGN(scales_fp16, 16);
@@ -593,8 +592,15 @@ nvfp4_status int4g_asym_gemv_ex(const void* x_bf16, const uint8_t* q, const void
   if (M == 0 || N == 0) return ok();
   if (nvfp4_status s = check_disjoint(outs, 1, ins, 4)) return s;
   const bool decode_ok = nvfp4k::int4g_asym_decode_supported(M, K);
-  if (algo == NVFP4_ALGO_AUTO) algo = decode_ok ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE;
+  if (algo == NVFP4_ALGO_AUTO)
+    algo = decode_ok ? NVFP4_ALGO_DECODE : (K < kInt4TiledKLimit ? NVFP4_ALGO_TILED : NVFP4_ALGO_SIMPLE);
   hipStream_t st = (hipStream_t)stream;
+  if (algo == NVFP4_ALGO_TILED) {
+    if (K >= kInt4TiledKLimit)
+      return fail(NVFP4_ERR_UNSUPPORTED, "tiled kernel needs 0 < K < 2^22 (K=%lld)", (long long)K);
+    return hip_status(nvfp4k::launch_int4g_asym_tiled(x_bf16, q, scales_fp16, zeros, out_bf16, M, N, K, st),
+                      "int4g_asym_gemv tiled launch");
+  }
   if (algo == NVFP4_ALGO_DECODE) {
     if (!decode_ok)
       return fail(NVFP4_ERR_UNSUPPORTED, "asymmetric decode kernel needs M <= 2 and 0 < K <= 32768 (M=%lld, K=%lld)",

@@ -70,7 +70,24 @@ __device__ __forceinline__ short8v int4x8_signed_bf16(uint32_t w) {
   return short8v{s0.x, s0.y, s1.x, s1.y, s2.x, s2.y, s3.x, s3.y};
 }
 
+// 8 unsigned nibbles (the zero-point form) -> 8 bf16 values q in element
+// order: a byte 0x00..0x0F read as E4M3 is exactly q * 2^-9.
+__device__ __forceinline__ short8v uint4x8_bf16(uint32_t w) {
+  const uint32_t ev = w & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
+  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+  const uint32_t lo = __builtin_amdgcn_perm(od, ev, 0x05010400u);   // e0 e1 e2 e3
+  const uint32_t hi = __builtin_amdgcn_perm(od, ev, 0x07030602u);   // e4 e5 e6 e7
+  const bf16x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false);
+  const bf16x2v p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true);
+  const bf16x2v p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false);
+  const bf16x2v p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true);
+  const short2v s0 = __builtin_bit_cast(short2v, p0), s1 = __builtin_bit_cast(short2v, p1);
+  const short2v s2 = __builtin_bit_cast(short2v, p2), s3 = __builtin_bit_cast(short2v, p3);
+  return short8v{s0.x, s0.y, s1.x, s1.y, s2.x, s2.y, s3.x, s3.y};
+}
+
 constexpr short kMinus8Bf16 = (short)0xC100;    // -8.0 in bf16
+constexpr short kOneBf16 = (short)0x3F80;       // 1.0 in bf16
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
@@ -551,8 +568,15 @@ constexpr int kQBytes = IT_N * IT_K / 2;        // 16 KB
 constexpr int kIStage = kXBytes + kQBytes;
 constexpr int kIRing = 3;
 constexpr int kIWaves = 8;
-constexpr int kIFi = 4, kIFj = 1;              // 32 x 32 tiles per wave along m and n
-constexpr int kILoads = 8;                      // vector memory instructions per wave per stage
+constexpr int kIDma = 6;                        // LDS-DMA copies per wave per stage (4 of x, 2 of codes)
+// 32 x 32 tiles per wave along m and n: 4 x 1 for the symmetric kernel
+// (every weight fragment decoded by one wave); 2 x 2 for the zero-point
+// kernel, whose extra accumulators (the group sums of x) would not fit
+// beside 4 x 1 at two waves per SIMD.
+template <bool kAsym> struct I4Shape {
+  static constexpr int Fi = kAsym ? 2 : 4, Fj = kAsym ? 2 : 1;
+  static constexpr int RegLoads = Fj * (kAsym ? 2 : 1);   // scales (and zero points) per stage
+};
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 #define INT4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
@@ -583,14 +607,18 @@ struct I4Ctx {
   int lds_x[4];
   uint32_t oq[2];          // weight copy offsets
   int lds_q[2];
-  const uint16_t* gsc[kIFj];  // group-scale rows of this lane's output columns
-  uint32_t scr[kIRing][kIFj]; // group scales per ring slot (raw fp16)
+  // (sized for the larger wave width, 2 columns of tiles; the symmetric
+  // kernel uses the first)
+  const uint16_t* gsc[2];     // group-scale rows of this lane's output columns
+  const uint8_t* gzp[2];      // and their zero points (zero-point kernel)
+  uint32_t scr[kIRing][2];    // group scales per ring slot (raw fp16)
+  uint32_t zr[kIRing][2];     // zero points per ring slot
   int wm, wn, lane;
 };
 
-// Copies of stage (group) g into slot B, and its group scales: kILoads
-// vector memory instructions per wave.
-template <int B>
+// Copies of stage (group) g into slot B (kIDma instructions per wave), then
+// its group scales and zero points (I4Shape::RegLoads loads into registers).
+template <int B, bool kAsym>
 __device__ __forceinline__ void i4_issue(I4Ctx& c, int g) {
   uint8_t* base = i4_slot<B>();
 #pragma unroll
@@ -600,67 +628,96 @@ __device__ __forceinline__ void i4_issue(I4Ctx& c, int g) {
   for (int i = 0; i < 2; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rq, (lds_void_t)(base + c.lds_q[i]), 16, c.oq[i] + 64u * g, 0, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kIFj; ++j) c.scr[B][j] = c.gsc[j][g];
+  for (int j = 0; j < I4Shape<kAsym>::Fj; ++j) {
+    c.scr[B][j] = c.gsc[j][g];
+    if (kAsym) c.zr[B][j] = c.gzp[j][g];
+  }
 }
 
-template <int B>
-__device__ __forceinline__ void i4_compute(I4Ctx& c, float16v (&acc)[kIFi][kIFj]) {
+// Group g from slot B into acc.  Symmetric: q decoded signed, acc += s16
+// sum x q.  Zero point: q decoded unsigned, and the group sums of x taken on
+// the matrix cores against a constant 1: acc += s16 (sum x q - z sum x).
+template <int B, bool kAsym>
+__device__ __forceinline__ void i4_compute(I4Ctx& c,
+                                           float16v (&acc)[I4Shape<kAsym>::Fi][I4Shape<kAsym>::Fj]) {
+  constexpr int Fi = I4Shape<kAsym>::Fi, Fj = I4Shape<kAsym>::Fj;
   const uint8_t* base = i4_slot<B>();
   const int lane = c.lane, wm = c.wm, wn = c.wn;
-  float sc[kIFj];
+  float sc[Fj], sz[Fj];
 #pragma unroll
-  for (int j = 0; j < kIFj; ++j) sc[j] = f16_bits_to_f32(c.scr[B][j]);
-  uint4 cq[kIFj][2];
+  for (int j = 0; j < Fj; ++j) {
+    sc[j] = f16_bits_to_f32(c.scr[B][j]);
+    sz[j] = kAsym ? sc[j] * (float)c.zr[B][j] : 0.f;
+  }
+  uint4 cq[Fj][2];
 #pragma unroll
-  for (int j = 0; j < kIFj; ++j)
+  for (int j = 0; j < Fj; ++j)
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
-      cq[j][hs] = *(const uint4*)(base + kXBytes + ((kIFj * wn + j) * 2 + hs) * 1024 + lane * 16);
-  float16v tmp[kIFi][kIFj];
+      cq[j][hs] = *(const uint4*)(base + kXBytes + ((Fj * wn + j) * 2 + hs) * 1024 + lane * 16);
+  const short8v c1 = {kOneBf16, kOneBf16, kOneBf16, kOneBf16, kOneBf16, kOneBf16, kOneBf16, kOneBf16};
+  float16v tmp[Fi][Fj], xs[kAsym ? Fi : 1];
 #pragma unroll
-  for (int i = 0; i < kIFi; ++i)
+  for (int i = 0; i < Fi; ++i) {
+    if (kAsym) xs[i] = float16v{};
 #pragma unroll
-    for (int j = 0; j < kIFj; ++j) tmp[i][j] = float16v{};
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    short8v xa[kIFi], wb[kIFj];
-#pragma unroll
-    for (int i = 0; i < kIFi; ++i)
-      xa[i] = as_short8(*(const uint4*)(base + ((kIFi * wm + i) * 8 + jj) * 1024 + lane * 16));
-#pragma unroll
-    for (int j = 0; j < kIFj; ++j) wb[j] = int4x8_signed_bf16(word_of(cq[j][jj >> 2], jj & 3));
-#pragma unroll
-    for (int i = 0; i < kIFi; ++i)
-#pragma unroll
-      for (int j = 0; j < kIFj; ++j)
-        tmp[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], wb[j], tmp[i][j], 0, 0, 0);
+    for (int j = 0; j < Fj; ++j) tmp[i][j] = float16v{};
   }
 #pragma unroll
-  for (int i = 0; i < kIFi; ++i)
+  for (int jj = 0; jj < 8; ++jj) {
+    short8v xa[Fi], wb[Fj];
 #pragma unroll
-    for (int j = 0; j < kIFj; ++j) acc[i][j] += sc[j] * tmp[i][j];
+    for (int i = 0; i < Fi; ++i)
+      xa[i] = as_short8(*(const uint4*)(base + ((Fi * wm + i) * 8 + jj) * 1024 + lane * 16));
+#pragma unroll
+    for (int j = 0; j < Fj; ++j)
+      wb[j] = kAsym ? uint4x8_bf16(word_of(cq[j][jj >> 2], jj & 3)) : int4x8_signed_bf16(word_of(cq[j][jj >> 2], jj & 3));
+#pragma unroll
+    for (int i = 0; i < Fi; ++i) {
+      if (kAsym) xs[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], c1, xs[i], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < Fj; ++j)
+        tmp[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], wb[j], tmp[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < Fi; ++i)
+#pragma unroll
+    for (int j = 0; j < Fj; ++j) {
+      if (kAsym)
+        acc[i][j] += sc[j] * tmp[i][j] - sz[j] * xs[i];
+      else
+        acc[i][j] += sc[j] * tmp[i][j];
+    }
 }
 
 // Stage g in slot B.  kChecked: near the end, where stage g + 1 or g + 2
 // may not exist (all conditions are uniform).
-template <int B, bool kChecked>
-__device__ __forceinline__ void i4_stage(I4Ctx& c, int g, int ng, float16v (&acc)[kIFi][kIFj]) {
+template <int B, bool kChecked, bool kAsym>
+__device__ __forceinline__ void i4_stage(I4Ctx& c, int g, int ng,
+                                         float16v (&acc)[I4Shape<kAsym>::Fi][I4Shape<kAsym>::Fj]) {
+  // Newer than stage g's copies: its own register loads and all of stage
+  // g + 1's, which may stay in flight.
+  constexpr int kAfter = kIDma + 2 * I4Shape<kAsym>::RegLoads;
   if (!kChecked || g + 1 < ng) {
-    INT4_WAIT_VMCNT(kILoads);     // stage g + 1's loads may stay in flight
+    INT4_WAIT_VMCNT(kAfter);
   } else {
     INT4_WAIT_VMCNT(0);
   }
   i4_barrier();                   // stage g landed for every wave; slot (B + 2) % 3 is free
-  if (!kChecked || g + 2 < ng) i4_issue<(B + 2) % kIRing>(c, g + 2);
-  i4_compute<B>(c, acc);
+  if (!kChecked || g + 2 < ng) i4_issue<(B + 2) % kIRing, kAsym>(c, g + 2);
+  i4_compute<B, kAsym>(c, acc);
 }
 }  // namespace
 
+template <bool kAsym>
 __global__ __launch_bounds__(64 * kIWaves, 1) void int4g_gemm_tiled_kernel(const uint16_t* __restrict__ x,
                                                                   const uint8_t* __restrict__ q,
                                                                   const uint16_t* __restrict__ s,
+                                                                  const uint8_t* __restrict__ zp,
                                                                   uint16_t* __restrict__ out, int M, int N, int K,
                                                                   int tiles_m, int tiles_n) {
+  constexpr int kIFi = I4Shape<kAsym>::Fi, kIFj = I4Shape<kAsym>::Fj;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // XCD-aware order: each XCD gets a contiguous run of tiles, n fastest.
   const int total = tiles_m * tiles_n;
@@ -697,8 +754,11 @@ __global__ __launch_bounds__(64 * kIWaves, 1) void int4g_gemm_tiled_kernel(const
     c.lds_q[i] = kXBytes + qd * 1024;
   }
 #pragma unroll
-  for (int j = 0; j < kIFj; ++j)
-    c.gsc[j] = s + (int64_t)min(n0 + 32 * kIFj * c.wn + 32 * j + (lane & 31), N - 1) * ng;
+  for (int j = 0; j < kIFj; ++j) {
+    const int64_t col = min(n0 + 32 * kIFj * c.wn + 32 * j + (lane & 31), N - 1);
+    c.gsc[j] = s + col * ng;
+    c.gzp[j] = kAsym ? zp + col * ng : nullptr;
+  }
 
   float16v acc[kIFi][kIFj];
 #pragma unroll
@@ -710,21 +770,21 @@ __global__ __launch_bounds__(64 * kIWaves, 1) void int4g_gemm_tiled_kernel(const
   // group 0 again (never read): no branch here, so the compiler's count of
   // copies in flight is the same on every path into the stage loop (a
   // branch made it wait for all copies before each group's first stage).
-  i4_issue<0>(c, 0);
-  i4_issue<1>(c, ng > 1 ? 1 : 0);
+  i4_issue<0, kAsym>(c, 0);
+  i4_issue<1, kAsym>(c, ng > 1 ? 1 : 0);
   int g = 0;
   // Whole groups of three stages while every wait and copy of the group is
   // in range (the last stage issued is g + 4).
   for (; g + 5 <= ng; g += 3) {
-    i4_stage<0, false>(c, g, ng, acc);
-    i4_stage<1, false>(c, g + 1, ng, acc);
-    i4_stage<2, false>(c, g + 2, ng, acc);
+    i4_stage<0, false, kAsym>(c, g, ng, acc);
+    i4_stage<1, false, kAsym>(c, g + 1, ng, acc);
+    i4_stage<2, false, kAsym>(c, g + 2, ng, acc);
   }
   // The last (up to 5) stages; g % 3 == 0 here.
   for (; g < ng; g += 3) {
-    i4_stage<0, true>(c, g, ng, acc);
-    if (g + 1 < ng) i4_stage<1, true>(c, g + 1, ng, acc);
-    if (g + 2 < ng) i4_stage<2, true>(c, g + 2, ng, acc);
+    i4_stage<0, true, kAsym>(c, g, ng, acc);
+    if (g + 1 < ng) i4_stage<1, true, kAsym>(c, g + 1, ng, acc);
+    if (g + 2 < ng) i4_stage<2, true, kAsym>(c, g + 2, ng, acc);
   }
   INT4_WAIT_VMCNT(0);      // no copy may land in LDS after the workgroup ends
 
@@ -799,9 +859,18 @@ hipError_t launch_int4g_gemm_decode(const void* x, const uint8_t* q, const void*
 hipError_t launch_int4g_gemm_tiled(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,
                                    int64_t N, int64_t K, hipStream_t stream) {
   const int tiles_m = (int)((M + IT_M - 1) / IT_M), tiles_n = (int)((N + IT_N - 1) / IT_N);
-  hipLaunchKernelGGL(int4g_gemm_tiled_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kIWaves), 0, stream,
-                     (const uint16_t*)x, q, (const uint16_t*)s, (uint16_t*)out, (int)M, (int)N, (int)K, tiles_m,
-                     tiles_n);
+  hipLaunchKernelGGL(int4g_gemm_tiled_kernel<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kIWaves), 0,
+                     stream, (const uint16_t*)x, q, (const uint16_t*)s, (const uint8_t*)nullptr, (uint16_t*)out,
+                     (int)M, (int)N, (int)K, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_int4g_asym_tiled(const void* x, const uint8_t* q, const void* s, const uint8_t* z, void* out,
+                                   int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int tiles_m = (int)((M + IT_M - 1) / IT_M), tiles_n = (int)((N + IT_N - 1) / IT_N);
+  hipLaunchKernelGGL(int4g_gemm_tiled_kernel<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kIWaves), 0,
+                     stream, (const uint16_t*)x, q, (const uint16_t*)s, z, (uint16_t*)out, (int)M, (int)N, (int)K,
+                     tiles_m, tiles_n);
   return hipGetLastError();
 }
 

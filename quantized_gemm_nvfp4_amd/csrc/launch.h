@@ -135,6 +135,9 @@ hipError_t launch_int4g_asym_quantize(const void* w, int64_t N, int64_t K, uint8
 bool int4g_asym_decode_supported(int64_t M, int64_t K);
 hipError_t launch_int4g_asym_decode(const void* x, const uint8_t* q, const void* s, const uint8_t* z, void* out,
                                     int64_t M, int64_t N, int64_t K, hipStream_t stream);
+// Zero-point INT4 on the LDS-staged MFMA tiles of the symmetric kernel (K < 2^22).
+hipError_t launch_int4g_asym_tiled(const void* x, const uint8_t* q, const void* s, const uint8_t* z, void* out,
+                                   int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_int4g_asym_simple(const void* x, const uint8_t* q, const void* s, const uint8_t* z, void* out,
                                     int64_t M, int64_t N, int64_t K, hipStream_t stream);
 

@@ -176,6 +176,12 @@ def test_int4_validation():
     big = (1 << 31) - 1
     assert g(A, B, C, D, big, big, 256, 128, 0, None) == UNSUP and "2^40" in _err()
     assert lib.int4g_asym_gemv_ex(A, B, C, D, E, big, big, 256, 128, 0, None) == UNSUP and "2^40" in _err()
+    a = lib.int4g_asym_gemv_ex
+    assert a(A, B, C, D, E, 4, 8, 256, 128, 9, None) == INVALID                       # unknown algo
+    assert a(A, B, C, D, E, 3, 8, 256, 128, q.ALGO_DECODE, None) == UNSUP             # decode needs M <= 2
+    far = [P(k << 40) for k in range(1, 6)]     # 1 TiB apart: the ranges of K = 2^22 cannot overlap
+    assert a(*far, 64, 8, 1 << 22, 128, q.ALGO_TILED, None) == UNSUP and "2^22" in _err()   # tiled needs K < 2^22
+    assert a(A, B, C, D, E, 0, 8, 256, 128, q.ALGO_TILED, None) == OK
     assert lib.nvfp4_gemm_w4a16_ex(A, B, C, D, E, big, big, 256, 0, None) == UNSUP and "2^40" in _err()
 
 

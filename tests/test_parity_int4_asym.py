@@ -93,8 +93,18 @@ def check_gemv(x_bits, w_bits, algos=(0,), label=""):
 def test_gemv_shapes(M, N, K):
     x = workloads.random_bf16(M + K + 7, (M, K), outlier_frac=0.01, outlier_mul=20)
     w = workloads.random_bf16(N + K + 8, (N, K), sigma=0.02, outlier_frac=0.005, outlier_mul=10)
-    algos = (0, 3) + ((2,) if M <= 2 and K <= 32768 else ())
+    algos = (0, 1, 3) + ((2,) if M <= 2 and K <= 32768 else ())
     check_gemv(x, w, algos=algos, label=f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 40, 256), (130, 257, 1024), (256, 512, 256), (16, 300, 8192),
+                                   (64, 1000, 4224), (200, 37, 128)])
+def test_tiled_shapes(M, N, K):
+    # M >= 3 runs the tile kernel: 128 x 256 tiles, ragged in both (M = 130,
+    # 200; N = 257, 300, 37), one group (K = 128), an odd group count (4224)
+    x = workloads.random_bf16(M * 5 + K, (M, K), outlier_frac=0.01, outlier_mul=20)
+    w = workloads.random_bf16(N * 7 + K, (N, K), sigma=0.02, outlier_frac=0.005, outlier_mul=10)
+    check_gemv(x, w, algos=(0, 1), label=f"tiled {M}x{N}x{K}")
 
 
 def test_config_sampled():
@@ -113,3 +123,11 @@ def test_config_sampled():
         ok, rl, rr = Mx.check_output(yv, I.int4g_asym_gemm(x[:M], op, osb, oz))
         log(f"int4 asym M={M} (64 sampled columns): rel_l2={rl:.3e} row_ratio={rr:.3e}")
         assert ok
+    # M = 2048 on the tile kernel: 16 sampled rows of x against the 64 columns
+    xr = np.sort(np.random.default_rng(13).choice(2048, 16, replace=False))
+    y = q.int4g_asym_gemv(dev_bf16(x), qt, st, zt)
+    torch.cuda.synchronize()
+    yv = F.bf16_from_bits(host_bits(y)).astype(np.float64)[xr][:, rows]
+    ok, rl, rr = Mx.check_output(yv, I.int4g_asym_gemm(x[xr], op, osb, oz))
+    log(f"int4 asym M=2048 (16 x 64 sampled): rel_l2={rl:.3e} row_ratio={rr:.3e}")
+    assert ok
