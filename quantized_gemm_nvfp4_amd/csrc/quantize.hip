@@ -122,9 +122,8 @@ __device__ __forceinline__ float block_error(const uint32_t (&w)[8], uint32_t sc
 // One 16-value block b of x: its scale under rule kRule (given g) and its
 // codes, stored at codes[b] and scales[b].
 template <int kRule>
-__device__ __forceinline__ void quantize_block(const uint4* __restrict__ x, int64_t b, float g,
-                                               uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const uint4 v0 = x[2 * b], v1 = x[2 * b + 1];
+__device__ __forceinline__ void quantize_block_words(const uint4 v0, const uint4 v1, int64_t b, float g,
+                                                     uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
   const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   uint32_t amax_bits = 0;
 #pragma unroll
@@ -155,6 +154,12 @@ __device__ __forceinline__ void quantize_block(const uint4* __restrict__ x, int6
   const float d = e4m3_to_f32(sc) * g;
   codes[b] = quot_fast(d) ? encode_block<true>(w, d, 1.0f / d) : encode_block<false>(w, d, 0.0f);
   scales[b] = (uint8_t)sc;
+}
+
+template <int kRule>
+__device__ __forceinline__ void quantize_block(const uint4* __restrict__ x, int64_t b, float g,
+                                               uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
+  quantize_block_words<kRule>(x[2 * b], x[2 * b + 1], b, g, codes, scales);
 }
 
 // x: bf16 [nblocks * 16]; codes: 8 bytes per block; scales: 1 byte per block.
@@ -218,13 +223,17 @@ __global__ __launch_bounds__(1024) void nvfp4_quant_small_kernel(const uint4* __
                                                                 float* __restrict__ gscale, int use_given) {
   __shared__ float s_g;
   __shared__ uint32_t s_max[16];
+  // the thread's own block, loaded once for the maximum and the codes
+  // (offsets past x read zero)
+  const int64_t b = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  const uint32_t nbytes = (uint32_t)nblocks * 32u;
+  const auto xr = buffer_of(x, nbytes);
+  const uint4 own0 = buffer_load16(xr, 32u * (uint32_t)b), own1 = buffer_load16(xr, 32u * (uint32_t)b + 16u);
   if (use_given) {
     if (threadIdx.x == 0) s_g = *gscale;
   } else {
     // eight 16-byte loads per thread in flight (offsets past x read zero)
     uint32_t m = 0;
-    const uint32_t nbytes = (uint32_t)nblocks * 32u;
-    const auto xr = buffer_of(x, nbytes);
     for (uint32_t i = 16u * threadIdx.x; i < nbytes; i += 8u * 16384u) {
       uint4 v[8];
 #pragma unroll
@@ -247,8 +256,7 @@ __global__ __launch_bounds__(1024) void nvfp4_quant_small_kernel(const uint4* __
   }
   __syncthreads();
   const float g = s_g;
-  const int64_t b = (int64_t)blockIdx.x * 1024 + threadIdx.x;
-  if (b < nblocks) quantize_block<kRule>(x, b, g, codes, scales);
+  if (b < nblocks) quantize_block_words<kRule>(own0, own1, b, g, codes, scales);
 }
 
 // ---- INT4 per-group (128) quantization ------------------------------------
