@@ -274,9 +274,13 @@ nvfp4_status nvfp4_quantize_amax(const void* x_bf16, int64_t rows, int64_t cols,
  * at M = 1, per row and slice of up to 768 values at 2 <= M <= 16 with
  * K <= 6144, per row and 512-value piece otherwise.  Elements within 2^32
  * of their slice's maximum are exact, smaller ones are truncated to the
- * fp16 subnormal grid.  Other shapes run a one-output-per-thread kernel in
- * fp32.
- * algo: NVFP4_ALGO_AUTO, _DECODE or _SIMPLE; others return
+ * fp16 subnormal grid.  Larger M (and decode-sized M the decode kernels do
+ * not take) with K % 128 == 0 and K < 2^22 run MFMA tiles in bf16: x as
+ * given and W decoded exactly to bf16, so every product is exact and only
+ * the fp32 summation rounds.  Other shapes run a one-output-per-thread
+ * kernel in fp32.
+ * algo: NVFP4_ALGO_AUTO, _TILED, _DECODE or _SIMPLE (a kernel that cannot
+ * take the shape returns NVFP4_ERR_UNSUPPORTED); other values return
  * NVFP4_ERR_INVALID_ARG.  out must not overlap any input.
  */
 nvfp4_status nvfp4_gemm_w4a16(const void* x_bf16, const uint8_t* w_codes, const uint8_t* w_scales,

@@ -60,8 +60,8 @@ nvfp4_status check_disjoint(const Range* outs, int nout, const Range* ins, int n
 }
 
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
-// The INT4 tiled kernel addresses a tile's rows of x (128 x 2K bytes) with
-// 32-bit buffer offsets.
+// The INT4 and weight-only NVFP4 tiled kernels address a tile's rows of x
+// (128 x 2K bytes) with 32-bit buffer offsets.
 constexpr int64_t kInt4TiledKLimit = (int64_t)1 << 22;
 // The weight-streaming kernels address at most kDecodeMaxRows packed weight
 // rows (the 112-row workgroup of the INT4 decode kernel is the largest) and
@@ -451,8 +451,7 @@ nvfp4_status nvfp4_gemm_w4a16_ex(const void* x_bf16, const uint8_t* w_codes, con
   REQUIRE_PTR(w_gscale);
   REQUIRE_PTR(out_bf16);
   if (K % 16 != 0) return fail(NVFP4_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
-  if (algo != NVFP4_ALGO_AUTO && algo != NVFP4_ALGO_DECODE && algo != NVFP4_ALGO_SIMPLE)
-    return fail(NVFP4_ERR_INVALID_ARG, "algo %d is not available for the weight-only GEMM", algo);
+  if (algo < NVFP4_ALGO_AUTO || algo > NVFP4_ALGO_SIMPLE) return fail(NVFP4_ERR_INVALID_ARG, "unknown algo %d", algo);
   REQUIRE_ALIGN(x_bf16, 16);
   REQUIRE_ALIGN(w_codes, 16);
   REQUIRE_ALIGN(w_scales, 16);
@@ -464,8 +463,19 @@ nvfp4_status nvfp4_gemm_w4a16_ex(const void* x_bf16, const uint8_t* w_codes, con
   if (M == 0 || N == 0) return ok();
   if (nvfp4_status s = check_disjoint(outs, 1, ins, 4)) return s;
   const bool decode_ok = nvfp4k::nvfp4_w4a16_decode_supported(M, K);
-  if (algo == NVFP4_ALGO_AUTO) algo = decode_ok ? NVFP4_ALGO_DECODE : NVFP4_ALGO_SIMPLE;
+  // the tiled kernel stages 128 values per step and addresses a tile's rows
+  // of x (128 x 2K bytes) with 32-bit buffer offsets
+  const bool tiled_ok = K > 0 && K % 128 == 0 && K < kInt4TiledKLimit;
+  if (algo == NVFP4_ALGO_AUTO)
+    algo = decode_ok ? NVFP4_ALGO_DECODE : (tiled_ok ? NVFP4_ALGO_TILED : NVFP4_ALGO_SIMPLE);
   hipStream_t st = (hipStream_t)stream;
+  if (algo == NVFP4_ALGO_TILED) {
+    if (!tiled_ok)
+      return fail(NVFP4_ERR_UNSUPPORTED, "weight-only tiled kernel needs K %% 128 == 0 and 0 < K < 2^22 (K=%lld)",
+                  (long long)K);
+    return hip_status(nvfp4k::launch_nvfp4_w4a16_tiled(x_bf16, w_codes, w_scales, w_gscale, out_bf16, M, N, K, st),
+                      "nvfp4_gemm_w4a16 tiled launch");
+  }
   if (algo == NVFP4_ALGO_DECODE) {
     if (!decode_ok)
       return fail(NVFP4_ERR_UNSUPPORTED, "weight-only decode kernel needs M <= 16, K %% 128 == 0 and K <= 32768 "

@@ -561,6 +561,15 @@ __global__ __launch_bounds__(1024) void int4g_gemv_rowslot_kernel(const uint16_t
 // copies in flight never alias the slot being read.  Per group: tmp tiles
 // start from zero, collect 8 steps, and are added to the accumulators times
 // the lane's column scale (read from global memory with the stage's copies).
+//
+// The same tiles serve the weight-only NVFP4 GEMM (bf16 x times the NVFP4
+// weight of nvfp4_gemm) at M > 16: the codes are copied the same way, and a
+// lane reads its four E4M3 block scales of the stage (the 16-value blocks of
+// its 64 K positions) with the stage's copies.  Each 8-value weight piece is
+// decoded exactly to bf16 (E2M1 -> fp32, times the block's fp32 scale, both
+// exact, an at most 6-bit product whose low 16 bits are zero, so the bf16 is
+// its high half) and goes straight into the accumulators; g_w scales the
+// stored result.
 namespace {
 constexpr int IT_M = 128, IT_N = 256, IT_K = 128;
 constexpr int kXBytes = IT_M * IT_K * 2;        // 32 KB
@@ -569,11 +578,14 @@ constexpr int kIStage = kXBytes + kQBytes;
 constexpr int kIRing = 3;
 constexpr int kIWaves = 8;
 constexpr int kIDma = 6;                        // LDS-DMA copies per wave per stage (4 of x, 2 of codes)
-// 32 x 32 tiles per wave along m and n: 4 x 1 for the symmetric kernel
-// (every weight fragment decoded by one wave); 2 x 2 for the zero-point
-// kernel, whose extra accumulators (the group sums of x) would not fit
-// beside 4 x 1 at two waves per SIMD.
-template <bool kAsym> struct I4Shape {
+// Weight kinds of the tiled kernel.
+constexpr int kWInt4 = 0, kWInt4Zp = 1, kWNvfp4 = 2;
+// 32 x 32 tiles per wave along m and n: 4 x 1 for the symmetric and NVFP4
+// kernels (every weight fragment decoded by one wave); 2 x 2 for the
+// zero-point kernel, whose extra accumulators (the group sums of x) would
+// not fit beside 4 x 1 at two waves per SIMD.
+template <int kKind> struct I4Shape {
+  static constexpr bool kAsym = kKind == kWInt4Zp;
   static constexpr int Fi = kAsym ? 2 : 4, Fj = kAsym ? 2 : 1;
   static constexpr int RegLoads = Fj * (kAsym ? 2 : 1);   // scales (and zero points) per stage
 };
@@ -611,15 +623,17 @@ struct I4Ctx {
   // kernel uses the first)
   const uint16_t* gsc[2];     // group-scale rows of this lane's output columns
   const uint8_t* gzp[2];      // and their zero points (zero-point kernel)
-  uint32_t scr[kIRing][2];    // group scales per ring slot (raw fp16)
+  const uint8_t* gsb[2];      // NVFP4: this lane's block scales of stage 0
+  uint32_t scr[kIRing][2];    // per ring slot: group scale (raw fp16) or 4 E4M3 block scales
   uint32_t zr[kIRing][2];     // zero points per ring slot
   int wm, wn, lane;
 };
 
 // Copies of stage (group) g into slot B (kIDma instructions per wave), then
 // its group scales and zero points (I4Shape::RegLoads loads into registers).
-template <int B, bool kAsym>
+template <int B, int kKind>
 __device__ __forceinline__ void i4_issue(I4Ctx& c, int g) {
+  constexpr bool kAsym = I4Shape<kKind>::kAsym;
   uint8_t* base = i4_slot<B>();
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -628,21 +642,72 @@ __device__ __forceinline__ void i4_issue(I4Ctx& c, int g) {
   for (int i = 0; i < 2; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rq, (lds_void_t)(base + c.lds_q[i]), 16, c.oq[i] + 64u * g, 0, 0, 0);
 #pragma unroll
-  for (int j = 0; j < I4Shape<kAsym>::Fj; ++j) {
-    c.scr[B][j] = c.gsc[j][g];
-    if (kAsym) c.zr[B][j] = c.gzp[j][g];
+  for (int j = 0; j < I4Shape<kKind>::Fj; ++j) {
+    if (kKind == kWNvfp4) {
+      c.scr[B][j] = *(const uint32_t*)(c.gsb[j] + 8 * g);
+    } else {
+      c.scr[B][j] = c.gsc[j][g];
+      if (kAsym) c.zr[B][j] = c.gzp[j][g];
+    }
   }
+}
+
+// 8 E2M1 codes (dword w, element 2j in the low nibble of byte j) times the
+// block scale s -> 8 bf16 in element order, exact: each product has at most
+// 6 significant bits, so its fp32 pattern ends in 16 zero bits.
+__device__ __forceinline__ uint32_t e2m1x2_scaled_bf16(float2v f, float s) {
+  return __builtin_amdgcn_perm(__float_as_uint(f[1] * s), __float_as_uint(f[0] * s), 0x07060302u);
+}
+__device__ __forceinline__ short8v e2m1x8_scaled_bf16(uint32_t w, float s) {
+  const uint32_t o0 = e2m1x2_scaled_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0), s);
+  const uint32_t o1 = e2m1x2_scaled_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1), s);
+  const uint32_t o2 = e2m1x2_scaled_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2), s);
+  const uint32_t o3 = e2m1x2_scaled_bf16(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3), s);
+  return __builtin_bit_cast(short8v, make_uint4(o0, o1, o2, o3));
 }
 
 // Group g from slot B into acc.  Symmetric: q decoded signed, acc += s16
 // sum x q.  Zero point: q decoded unsigned, and the group sums of x taken on
 // the matrix cores against a constant 1: acc += s16 (sum x q - z sum x).
-template <int B, bool kAsym>
+template <int B, int kKind>
 __device__ __forceinline__ void i4_compute(I4Ctx& c,
-                                           float16v (&acc)[I4Shape<kAsym>::Fi][I4Shape<kAsym>::Fj]) {
-  constexpr int Fi = I4Shape<kAsym>::Fi, Fj = I4Shape<kAsym>::Fj;
+                                           float16v (&acc)[I4Shape<kKind>::Fi][I4Shape<kKind>::Fj]) {
+  constexpr bool kAsym = I4Shape<kKind>::kAsym;
+  constexpr int Fi = I4Shape<kKind>::Fi, Fj = I4Shape<kKind>::Fj;
   const uint8_t* base = i4_slot<B>();
   const int lane = c.lane, wm = c.wm, wn = c.wn;
+  if constexpr (kKind == kWNvfp4) {
+    // NVFP4 weight: step jj holds K positions 64 (lane / 32) + 8 jj .. + 8 of
+    // the stage, block 4 (lane / 32) + jj / 2, whose scale is byte jj / 2.
+    float sb[Fj][4];
+#pragma unroll
+    for (int j = 0; j < Fj; ++j) {
+      const float2v lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.scr[B][j], 1.0f, false);
+      const float2v hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.scr[B][j], 1.0f, true);
+      sb[j][0] = lo[0], sb[j][1] = lo[1], sb[j][2] = hi[0], sb[j][3] = hi[1];
+    }
+    uint4 cq[Fj][2];
+#pragma unroll
+    for (int j = 0; j < Fj; ++j)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+        cq[j][hs] = *(const uint4*)(base + kXBytes + ((Fj * wn + j) * 2 + hs) * 1024 + lane * 16);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      short8v xa[Fi], wb[Fj];
+#pragma unroll
+      for (int i = 0; i < Fi; ++i)
+        xa[i] = as_short8(*(const uint4*)(base + ((Fi * wm + i) * 8 + jj) * 1024 + lane * 16));
+#pragma unroll
+      for (int j = 0; j < Fj; ++j) wb[j] = e2m1x8_scaled_bf16(word_of(cq[j][jj >> 2], jj & 3), sb[j][jj >> 1]);
+#pragma unroll
+      for (int i = 0; i < Fi; ++i)
+#pragma unroll
+        for (int j = 0; j < Fj; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], wb[j], acc[i][j], 0, 0, 0);
+    }
+    return;
+  }
   float sc[Fj], sz[Fj];
 #pragma unroll
   for (int j = 0; j < Fj; ++j) {
@@ -693,31 +758,35 @@ __device__ __forceinline__ void i4_compute(I4Ctx& c,
 
 // Stage g in slot B.  kChecked: near the end, where stage g + 1 or g + 2
 // may not exist (all conditions are uniform).
-template <int B, bool kChecked, bool kAsym>
+template <int B, bool kChecked, int kKind>
 __device__ __forceinline__ void i4_stage(I4Ctx& c, int g, int ng,
-                                         float16v (&acc)[I4Shape<kAsym>::Fi][I4Shape<kAsym>::Fj]) {
+                                         float16v (&acc)[I4Shape<kKind>::Fi][I4Shape<kKind>::Fj]) {
   // Newer than stage g's copies: its own register loads and all of stage
   // g + 1's, which may stay in flight.
-  constexpr int kAfter = kIDma + 2 * I4Shape<kAsym>::RegLoads;
+  constexpr int kAfter = kIDma + 2 * I4Shape<kKind>::RegLoads;
   if (!kChecked || g + 1 < ng) {
     INT4_WAIT_VMCNT(kAfter);
   } else {
     INT4_WAIT_VMCNT(0);
   }
   i4_barrier();                   // stage g landed for every wave; slot (B + 2) % 3 is free
-  if (!kChecked || g + 2 < ng) i4_issue<(B + 2) % kIRing, kAsym>(c, g + 2);
-  i4_compute<B, kAsym>(c, acc);
+  if (!kChecked || g + 2 < ng) i4_issue<(B + 2) % kIRing, kKind>(c, g + 2);
+  i4_compute<B, kKind>(c, acc);
 }
 }  // namespace
 
-template <bool kAsym>
+// s: the fp16 group scales (INT4) or the E4M3 block scales (NVFP4); zp: the
+// zero points (kWInt4Zp); w_g: the NVFP4 weight's global scale.
+template <int kKind>
 __global__ __launch_bounds__(64 * kIWaves, 1) void int4g_gemm_tiled_kernel(const uint16_t* __restrict__ x,
                                                                   const uint8_t* __restrict__ q,
-                                                                  const uint16_t* __restrict__ s,
+                                                                  const void* __restrict__ s,
                                                                   const uint8_t* __restrict__ zp,
+                                                                  const float* __restrict__ w_g,
                                                                   uint16_t* __restrict__ out, int M, int N, int K,
                                                                   int tiles_m, int tiles_n) {
-  constexpr int kIFi = I4Shape<kAsym>::Fi, kIFj = I4Shape<kAsym>::Fj;
+  constexpr bool kAsym = I4Shape<kKind>::kAsym;
+  constexpr int kIFi = I4Shape<kKind>::Fi, kIFj = I4Shape<kKind>::Fj;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // XCD-aware order: each XCD gets a contiguous run of tiles, n fastest.
   const int total = tiles_m * tiles_n;
@@ -756,8 +825,11 @@ __global__ __launch_bounds__(64 * kIWaves, 1) void int4g_gemm_tiled_kernel(const
 #pragma unroll
   for (int j = 0; j < kIFj; ++j) {
     const int64_t col = min(n0 + 32 * kIFj * c.wn + 32 * j + (lane & 31), N - 1);
-    c.gsc[j] = s + col * ng;
+    c.gsc[j] = (const uint16_t*)s + col * ng;
     c.gzp[j] = kAsym ? zp + col * ng : nullptr;
+    // NVFP4: the row's 8 scale bytes per stage, of which this lane's four
+    // start at 4 (lane / 32)
+    c.gsb[j] = (const uint8_t*)s + col * (K / 16) + 4 * (lane >> 5);
   }
 
   float16v acc[kIFi][kIFj];
@@ -770,26 +842,27 @@ __global__ __launch_bounds__(64 * kIWaves, 1) void int4g_gemm_tiled_kernel(const
   // group 0 again (never read): no branch here, so the compiler's count of
   // copies in flight is the same on every path into the stage loop (a
   // branch made it wait for all copies before each group's first stage).
-  i4_issue<0, kAsym>(c, 0);
-  i4_issue<1, kAsym>(c, ng > 1 ? 1 : 0);
+  i4_issue<0, kKind>(c, 0);
+  i4_issue<1, kKind>(c, ng > 1 ? 1 : 0);
   int g = 0;
   // Whole groups of three stages while every wait and copy of the group is
   // in range (the last stage issued is g + 4).
   for (; g + 5 <= ng; g += 3) {
-    i4_stage<0, false, kAsym>(c, g, ng, acc);
-    i4_stage<1, false, kAsym>(c, g + 1, ng, acc);
-    i4_stage<2, false, kAsym>(c, g + 2, ng, acc);
+    i4_stage<0, false, kKind>(c, g, ng, acc);
+    i4_stage<1, false, kKind>(c, g + 1, ng, acc);
+    i4_stage<2, false, kKind>(c, g + 2, ng, acc);
   }
   // The last (up to 5) stages; g % 3 == 0 here.
   for (; g < ng; g += 3) {
-    i4_stage<0, true, kAsym>(c, g, ng, acc);
-    if (g + 1 < ng) i4_stage<1, true, kAsym>(c, g + 1, ng, acc);
-    if (g + 2 < ng) i4_stage<2, true, kAsym>(c, g + 2, ng, acc);
+    i4_stage<0, true, kKind>(c, g, ng, acc);
+    if (g + 1 < ng) i4_stage<1, true, kKind>(c, g + 1, ng, acc);
+    if (g + 2 < ng) i4_stage<2, true, kKind>(c, g + 2, ng, acc);
   }
   INT4_WAIT_VMCNT(0);      // no copy may land in LDS after the workgroup ends
 
   // D[m][n] of each 32 x 32 tile: lane n + 32((m/4)%2), register (m%4) + 4(m/8).
   const int wm = c.wm, wn = c.wn, h = lane >> 5, r32 = lane & 31;
+  const float gw = kKind == kWNvfp4 ? *w_g : 1.0f;
 #pragma unroll
   for (int j = 0; j < kIFj; ++j) {
     const int n = n0 + 32 * kIFj * wn + 32 * j + r32;
@@ -799,7 +872,7 @@ __global__ __launch_bounds__(64 * kIWaves, 1) void int4g_gemm_tiled_kernel(const
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int m = m0 + 32 * kIFi * wm + 32 * i + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        if (m < M) out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(acc[i][j][rr]);
+        if (m < M) out[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(kKind == kWNvfp4 ? acc[i][j][rr] * gw : acc[i][j][rr]);
       }
     }
   }
@@ -859,18 +932,27 @@ hipError_t launch_int4g_gemm_decode(const void* x, const uint8_t* q, const void*
 hipError_t launch_int4g_gemm_tiled(const void* x, const uint8_t* q, const void* s, void* out, int64_t M,
                                    int64_t N, int64_t K, hipStream_t stream) {
   const int tiles_m = (int)((M + IT_M - 1) / IT_M), tiles_n = (int)((N + IT_N - 1) / IT_N);
-  hipLaunchKernelGGL(int4g_gemm_tiled_kernel<false>, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kIWaves), 0,
-                     stream, (const uint16_t*)x, q, (const uint16_t*)s, (const uint8_t*)nullptr, (uint16_t*)out,
-                     (int)M, (int)N, (int)K, tiles_m, tiles_n);
+  hipLaunchKernelGGL(int4g_gemm_tiled_kernel<kWInt4>, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kIWaves), 0,
+                     stream, (const uint16_t*)x, q, s, (const uint8_t*)nullptr, (const float*)nullptr,
+                     (uint16_t*)out, (int)M, (int)N, (int)K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_int4g_asym_tiled(const void* x, const uint8_t* q, const void* s, const uint8_t* z, void* out,
                                    int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const int tiles_m = (int)((M + IT_M - 1) / IT_M), tiles_n = (int)((N + IT_N - 1) / IT_N);
-  hipLaunchKernelGGL(int4g_gemm_tiled_kernel<true>, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kIWaves), 0,
-                     stream, (const uint16_t*)x, q, (const uint16_t*)s, z, (uint16_t*)out, (int)M, (int)N, (int)K,
-                     tiles_m, tiles_n);
+  hipLaunchKernelGGL(int4g_gemm_tiled_kernel<kWInt4Zp>, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kIWaves), 0,
+                     stream, (const uint16_t*)x, q, s, z, (const float*)nullptr, (uint16_t*)out, (int)M, (int)N,
+                     (int)K, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_w4a16_tiled(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
+                                    int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int tiles_m = (int)((M + IT_M - 1) / IT_M), tiles_n = (int)((N + IT_N - 1) / IT_N);
+  hipLaunchKernelGGL(int4g_gemm_tiled_kernel<kWNvfp4>, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kIWaves), 0,
+                     stream, (const uint16_t*)x, wc, (const void*)ws, (const uint8_t*)nullptr, wg, (uint16_t*)out,
+                     (int)M, (int)N, (int)K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -101,6 +101,10 @@ hipError_t launch_nvfp4_w4a16_decode(const void* x, const uint8_t* wc, const uin
                                      int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_nvfp4_w4a16_simple(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
                                      int64_t M, int64_t N, int64_t K, hipStream_t stream);
+// tiled (any M; K % 128 == 0, K < 2^22): the INT4 kernel's LDS-staged MFMA
+// tiles with the NVFP4 weight decoded exactly to bf16.
+hipError_t launch_nvfp4_w4a16_tiled(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
+                                    int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // The same NVFP4 GEMMs plus the low-rank branch T L_up^T (T fp32 [M, r],
 // L_up bf16 [N, r]) added before the bf16 rounding.

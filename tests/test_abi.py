@@ -185,6 +185,17 @@ def test_int4_validation():
     assert lib.nvfp4_gemm_w4a16_ex(A, B, C, D, E, big, big, 256, 0, None) == UNSUP and "2^40" in _err()
 
 
+def test_w4a16_algo_validation():
+    lib = q.lib()
+    w = lib.nvfp4_gemm_w4a16_ex
+    assert w(A, B, C, D, E, 4, 8, 256, 9, None) == INVALID                          # unknown algo
+    assert w(A, B, C, D, E, 17, 8, 256, q.ALGO_DECODE, None) == UNSUP              # decode needs M <= 16
+    assert w(A, B, C, D, E, 32, 8, 144, q.ALGO_TILED, None) == UNSUP               # tiled needs K % 128 == 0
+    far = [P(k << 40) for k in range(1, 6)]     # 1 TiB apart: the ranges of K = 2^22 cannot overlap
+    assert w(*far, 64, 8, 1 << 22, q.ALGO_TILED, None) == UNSUP and "2^22" in _err()
+    assert w(A, B, C, D, E, 0, 8, 256, q.ALGO_TILED, None) == OK
+
+
 def test_quantize_noalloc_validation():
     lib = q.lib()
     f = lib.nvfp4_quantize_noalloc

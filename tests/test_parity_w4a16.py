@@ -110,3 +110,29 @@ def test_decode_config():
     w_bits = workloads.decode_w()
     for M in (1, 2, 3, 4, 16):
         check(x_bits[:M], w_bits, algos=(0,), label=f"decode M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 37, 128), (64, 256, 1024), (130, 300, 2176), (300, 513, 384),
+                                   (33, 20, 6272), (2048, 512, 5376)])
+def test_tiled_shapes(M, N, K):
+    # M > 16 with K % 128 == 0 runs the LDS-staged MFMA tiles (128 x 256,
+    # one 128-value stage per step): partial tiles along M and N, one to 49
+    # stages (the unrolled stage loop and its checked tail), several rows of
+    # tiles at M = 2048.  bf16 x goes to the matrix cores as it is, so the
+    # products are exact whatever its range.
+    x = workloads.random_bf16(M * 19 + K, (M, K), outlier_frac=0.01, outlier_mul=20)
+    w = workloads.random_bf16(N * 23 + K, (N, K), sigma=0.02, zero_frac=0.05)
+    check(x, w, algos=(0, 1, 3), label=f"tiled {M}x{N}x{K}")
+
+
+def test_tiled_wide_range():
+    # activations 2^60 and 2^-60 apart in one row, all-zero weight rows and
+    # a weight row of one repeated block: the tiled path needs no rescaling
+    M, N, K = 40, 96, 512
+    x = workloads.random_bf16(7, (M, K))
+    x[0, ::7] = 0x5D80          # 2^60 (sign clear)
+    x[1, 3::5] = 0x2180         # 2^-60
+    w = workloads.random_bf16(8, (N, K), sigma=0.02)
+    w[5] = 0
+    w[6] = np.tile(w[7, :16], K // 16)
+    check(x, w, algos=(1, 3), label="tiled wide range")
