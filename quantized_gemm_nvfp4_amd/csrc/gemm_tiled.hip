@@ -929,9 +929,18 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
   if (bid < full_tiles) {
     tile_id = (full_tiles & 7) == 0 ? (bid & 7) * (full_tiles >> 3) + (bid >> 3) : bid;
   } else {
-    unit = bid - full_tiles;
-    const int p = unit % splits;
-    tile_id = full_tiles + unit / splits;
+    // K part p of leftover tile t is dispatched as u = p * left + t, and
+    // each XCD takes a contiguous range of u (when the counts divide by 8):
+    // the parts that run together on an XCD then read the same K range of
+    // neighbouring tiles and share their operand panels in its L2.  `unit`
+    // = t * splits + p is where the part's sums go (the reduce kernel's
+    // order), so the results do not depend on this order.
+    const int nunits = (int)gridDim.x - full_tiles, left = nunits / splits;
+    const int uo = bid - full_tiles;
+    const int u = ((full_tiles | nunits) & 7) == 0 ? (uo & 7) * (nunits >> 3) + (uo >> 3) : uo;
+    const int p = u / left, t = u % left;
+    unit = t * splits + p;
+    tile_id = full_tiles + t;
     if (kGroups) {
       const int ng = nst_all / kGroupStages;
       st0 = kGroupStages * (p * ng / splits);
