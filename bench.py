@@ -529,7 +529,14 @@ def run_decode(torch, q, iters=64, copies=16):
         out[f"w4a16_M{M}"] = {"us": us, "GBps": alg_bytes / (us * 1e-6) / 1e9,
                               "frac_hbm": alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "alg_bytes": alg_bytes}
         log(f"decode W4A16 M={M}: {us:.2f} us, {out[f'w4a16_M{M}']['GBps']:.0f} GB/s")
-    del ws
+    # weight-only past decode sizes: the prefill activation through the MFMA tiles
+    Mp = 4096
+    x = dev_bf16(torch, workloads.normal_bf16("prefill", 0, (4096, 5376)))   # the prefill x_up
+    y = torch.empty((Mp, N), dtype=torch.bfloat16, device="cuda:0")
+    ms = min(_event_ms(torch, lambda: q.nvfp4_gemm_w4a16(x, ws[0], out=y), 3) for _ in range(3))
+    out[f"w4a16_M{Mp}"] = {"ms": ms, "tflops": 2 * Mp * N * K / (ms * 1e-3) / 1e12}
+    log(f"W4A16 M={Mp} (tiled): {ms:.3f} ms, {out[f'w4a16_M{Mp}']['tflops']:.0f} TFLOP/s")
+    del ws, x, y
     # HBM bytes per call from committed rocprofv3 counters (None once the
     # kernels have changed since they were taken)
     tr = load_decode_traffic()
