@@ -761,6 +761,7 @@ def run_peaks(torch, iters=64, copies=16):
     lib.peak_out_elems.restype = ctypes.c_int
     lib.peak_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
     lib.peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.peak_read_lds.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     out = torch.empty(lib.peak_out_elems(), dtype=torch.float32, device="cuda:0")
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -785,6 +786,11 @@ def run_peaks(torch, iters=64, copies=16):
                                          for _ in range(reps)], 1) / reps
         if big.numel() / (ms_r * 1e-3) / 1e9 > read:
             read, read_wgs = big.numel() / (ms_r * 1e-3) / 1e9, wgs
+    # the same stream through LDS by DMA (how the GEMM kernels copy operands)
+    ms_l = _event_ms(torch, lambda: [check(lib.peak_read_lds(ctypes.c_void_p(big.data_ptr()), big.numel(),
+                                                             ctypes.c_void_p(out.data_ptr()), stream), "peak_read_lds")
+                                     for _ in range(reps)], 1) / reps
+    read_lds = big.numel() / (ms_l * 1e-3) / 1e9
     del big
     nb = 65074136
     bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda:0") for _ in range(copies)]
@@ -800,10 +806,11 @@ def run_peaks(torch, iters=64, copies=16):
     del bufs
     res = {"mfma_f16_tflops": mfma, "mfma_frac_of_spec": mfma / PEAK_MFMA_TFLOPS,
            "hbm_read_gbs": read, "hbm_frac_of_spec": read / PEAK_HBM_GBS, "read_wgs_per_cu": read_wgs,
+           "hbm_read_lds_dma_gbs": read_lds,
            "decode_read_floor_us": floor_us, "decode_read_floor_gbs": nb / (floor_us * 1e-6) / 1e9,
            "floor_wgs_per_cu": floor_wgs}
     log(f"peaks: MFMA fp16 loop {mfma:.0f} TFLOP/s ({mfma / PEAK_MFMA_TFLOPS:.3f} of spec), 1 GiB read "
-        f"{read:.0f} GB/s, 65 MB read per call (graph) {floor_us:.2f} us")
+        f"{read:.0f} GB/s ({read_lds:.0f} GB/s through LDS by DMA), 65 MB read per call (graph) {floor_us:.2f} us")
     return res
 
 

@@ -98,6 +98,38 @@ __global__ __launch_bounds__(kReadThreads) void peak_read_kernel(const void* __r
   out[blockIdx.x * kReadThreads + threadIdx.x] = x;
 }
 
+// The same stream of 1 KB chunks as peak_read_kernel, but each chunk goes
+// to LDS by DMA (buffer_load_dwordx4 ... lds, as the GEMM kernels copy their
+// operands): wave w keeps kReadDepth chunks in flight in a ring of
+// kReadDepth 1 KB slots of its own, waiting (vmcnt) only for the oldest
+// before reusing its slot.  Four waves per workgroup, one workgroup per CU
+// (the ring takes 32 KB of LDS).  Offsets past the end read zero.
+constexpr int kLdsWaves = 4;
+__shared__ __attribute__((aligned(1024))) uint8_t g_read_ring[kLdsWaves * kReadDepth * 1024];
+typedef __attribute__((address_space(3))) void* lds_void_t;
+__device__ __forceinline__ void read_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)dst, 16, off, 0, 0, 0);
+}
+__global__ __launch_bounds__(64 * kLdsWaves) void peak_read_lds_kernel(const void* __restrict__ src, uint32_t bytes,
+                                                                        uint32_t* __restrict__ out) {
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), 0, (int)bytes, 0x00020000);
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t w = blockIdx.x * kLdsWaves + wave, W = gridDim.x * kLdsWaves;
+  const uint32_t nch = (bytes + 1023u) / 1024u;
+  uint8_t* ring = g_read_ring + wave * kReadDepth * 1024;
+  uint32_t slot = 0;
+  for (uint32_t c = w; c < nch; c += W) {
+    read_to_lds(r, 1024u * c + 16u * lane, ring + slot * 1024);
+    slot = slot + 1 == kReadDepth ? 0 : slot + 1;
+    // vmcnt(kReadDepth - 1): the chunk issued kReadDepth chunks ago has
+    // landed, so its slot may be written again
+    __builtin_amdgcn_s_waitcnt(((kReadDepth - 1) & 0xF) | (((kReadDepth - 1) >> 4) << 14) | 0x70 | 0xF00);
+  }
+  __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);   // vmcnt(0): nothing lands after the workgroup ends
+  __syncthreads();
+  out[blockIdx.x * 64 * kLdsWaves + threadIdx.x] = ring[lane];
+}
+
 int cus() {
   static int n = 0;
   if (n == 0) {
@@ -138,6 +170,18 @@ int peak_read(const void* src, int64_t bytes, int wgs_per_cu, uint32_t* out, voi
       wgs_per_cu < 1 || wgs_per_cu > kReadMaxWgsPerCu || (reinterpret_cast<uintptr_t>(src) & 15) != 0)
     return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(peak_read_kernel, dim3(cus() * wgs_per_cu), dim3(kReadThreads), 0, (hipStream_t)stream, src,
+                     (uint32_t)bytes, out);
+  return (int)hipGetLastError();
+}
+
+// Launches one read of `bytes` (0 < bytes < 2^31, 16-byte aligned src)
+// through LDS by DMA on `stream`, one workgroup of 4 waves per compute unit.
+// Returns a hipError_t value.
+int peak_read_lds(const void* src, int64_t bytes, uint32_t* out, void* stream) {
+  if (src == nullptr || out == nullptr || bytes <= 0 || bytes >= (int64_t(1) << 31) || cus() <= 0 ||
+      (reinterpret_cast<uintptr_t>(src) & 15) != 0)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(peak_read_lds_kernel, dim3(cus()), dim3(64 * kLdsWaves), 0, (hipStream_t)stream, src,
                      (uint32_t)bytes, out);
   return (int)hipGetLastError();
 }
