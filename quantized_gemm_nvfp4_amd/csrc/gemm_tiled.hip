@@ -923,7 +923,16 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
   using Ctx = TiledCtx<kW>;
   constexpr int kFr = Ctx::kFr, kJ = Ctx::kJ;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bid = blockIdx.x;
+  // Dispatch order when the last round is split: half of the K parts first,
+  // then the whole tiles, then the other half of the parts.  The CUs that
+  // start with a part run a fraction of a tile ahead of the others from then
+  // on, so the rounds' boundaries (a tile's output stores and the next
+  // tile's first copies) fall at two different times instead of one.
+  int bid = blockIdx.x;
+  {
+    const int nunits = (int)gridDim.x - full_tiles, first = (nunits / 2) & ~7;
+    if (full_tiles > 0 && first > 0) bid = bid < first ? full_tiles + bid : (bid < first + full_tiles ? bid - first : bid);
+  }
   const int nst_all = K / TK;
   int tile_id, st0 = 0, st1 = nst_all, unit = -1;
   if (bid < full_tiles) {
