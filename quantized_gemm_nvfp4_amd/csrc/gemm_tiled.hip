@@ -897,7 +897,8 @@ __device__ __forceinline__ void lora_branch_n64(float16v (&acc)[2][8], float tsc
   }
 }
 
-// Grid: full_tiles whole tiles, then (tiles - full_tiles) x splits K parts.
+// Grid: full_tiles whole tiles and (tiles - full_tiles) x splits K parts
+// (half of the parts dispatched before the whole tiles, half after).
 // Whole tiles are visited in an XCD-aware order when full_tiles % 8 == 0.
 // Part p of leftover tile t takes stages [p nst / S, (p + 1) nst / S) and
 // stores its unscaled fp32 accumulators to part[(t S + p)] in lane order
