@@ -650,17 +650,38 @@ __device__ __forceinline__ void tiled_stage_n64(const TiledCtx<4>& c, int ls, fl
   }
 }
 
-// bf16 stores of one 32 x 32 fragment times gmul: rows m, columns
-// nb + 8 rq + 4 h + (0..3) from registers 4 rq .. 4 rq + 3.  D[n][m] of a
+// bf16 stores of one 32 x 32 fragment times gmul, row m.  D[n][m] of a
 // fragment sits at lane m + 32((n/4)%2), register (n%4) + 4(n/8): four
-// consecutive n per register quad.  Returns the largest |bf16| bit pattern
+// consecutive n per register quad.  With N % 8 == 0 and the fragment's 32
+// columns inside N, lanes m and m + 32 swap halves (v_permlane32_swap) and
+// each stores 8 consecutive columns nb + 16 k + 8 h .. + 7 (k = 0, 1) as
+// 16 bytes; otherwise each lane stores columns nb + 8 rq + 4 h + (0..3)
+// from registers 4 rq .. 4 rq + 3.  Returns the largest |bf16| bit pattern
 // (sign cleared) among the values stored (0 if none).
 __device__ __forceinline__ uint32_t store_frag(const float16v& a, float gmul, uint16_t* __restrict__ out, int M,
                                                int N, int m, int nb, int h) {
   if (m >= M) return 0u;
   uint16_t* orow = out + (int64_t)m * N;
-  const bool vec_ok = (N & 3) == 0;
   uint32_t mx = 0u;
+  if ((N & 7) == 0 && nb + 31 < N) {
+    // 16 bytes per lane: lanes m and m + 32 (the same row) swap halves so
+    // that each holds 8 consecutive columns, nb + 16 k + 8 h .. + 7.
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t a01 = f32x2_to_bf16x2_rne(a[8 * k + 0] * gmul, a[8 * k + 1] * gmul);
+      const uint32_t a23 = f32x2_to_bf16x2_rne(a[8 * k + 2] * gmul, a[8 * k + 3] * gmul);
+      const uint32_t b01 = f32x2_to_bf16x2_rne(a[8 * k + 4] * gmul, a[8 * k + 5] * gmul);
+      const uint32_t b23 = f32x2_to_bf16x2_rne(a[8 * k + 6] * gmul, a[8 * k + 7] * gmul);
+      mx = max(mx, max(max(bf16x2_absmax_bits(a01), bf16x2_absmax_bits(a23)),
+                       max(bf16x2_absmax_bits(b01), bf16x2_absmax_bits(b23))));
+      // lanes 32..63 of the first operand trade with lanes 0..31 of the second
+      const auto s01 = __builtin_amdgcn_permlane32_swap(a01, b01, false, false);
+      const auto s23 = __builtin_amdgcn_permlane32_swap(a23, b23, false, false);
+      *(uint4*)(orow + nb + 16 * k + 8 * h) = make_uint4(s01[0], s23[0], s01[1], s23[1]);
+    }
+    return mx;
+  }
+  const bool vec_ok = (N & 3) == 0;
 #pragma unroll
   for (int rq = 0; rq < 4; ++rq) {
     const int n = nb + 8 * rq + 4 * h;
@@ -687,9 +708,11 @@ __device__ __noinline__ void add_branch_frag(const float* __restrict__ lora_t, c
   if (m >= M) return;
   uint16_t* orow = out + (int64_t)m * N;
   const float* trow = lora_t + (int64_t)m * r;
+  // the columns this lane stored (store_frag's two layouts)
+  const bool swapped = (N & 7) == 0 && nb + 31 < N;
 #pragma unroll 1
   for (int q = 0; q < 16; ++q) {
-    const int n = nb + 8 * (q >> 2) + 4 * h + (q & 3);
+    const int n = swapped ? nb + 16 * (q >> 3) + 8 * h + (q & 7) : nb + 8 * (q >> 2) + 4 * h + (q & 3);
     if (n >= N) continue;
     const uint16_t* urow = lora_up + (int64_t)n * r;
     float v = 0.f;
