@@ -948,10 +948,11 @@ __global__ __launch_bounds__(64 * kW, 1) void nvfp4_gemm_tiled_kernel(
   constexpr int kFr = Ctx::kFr, kJ = Ctx::kJ;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Dispatch order when the last round is split: half of the K parts first,
-  // then the whole tiles, then the other half of the parts.  The CUs that
-  // start with a part run a fraction of a tile ahead of the others from then
-  // on, so the rounds' boundaries (a tile's output stores and the next
-  // tile's first copies) fall at two different times instead of one.
+  // then the whole tiles, then the other half of the parts.  On every XCD
+  // the CUs that start with a part run a fraction of a tile ahead of the
+  // others from then on, so the tiles of one XCD do not all request the
+  // same lines at the same moment (measured faster than every tile in step,
+  // though the XCD's L2 then re-fetches more of their shared panels).
   int bid = blockIdx.x;
   {
     const int nunits = (int)gridDim.x - full_tiles, first = (nunits / 2) & ~7;
