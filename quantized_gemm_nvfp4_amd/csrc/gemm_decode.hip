@@ -429,7 +429,8 @@ __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_gemv_stream_kernel(
 namespace {
 constexpr int kNxWaves = 8;
 constexpr int kNxPiece = 512;                     // K values per wave per pass
-constexpr int kNxDepth = 4;                       // stages in flight per wave
+constexpr int kNxDepth = 4;                       // stage slots per wave (one LDS object each)
+constexpr int kNxAhead = 2;                       // stages copied ahead (as in the INT4 kernel)
 constexpr int kNxRegion = 1024 + 64;              // one code copy (4 rows x 256 B) + bank padding
 constexpr int kNxScaleOff = 4 * kNxRegion;        // 16 rows x 32 scale bytes
 constexpr int kNxStage = kNxScaleOff + 512;
@@ -488,12 +489,12 @@ __device__ __forceinline__ void nx_issue(const NxCtx& c, int t_in) {
 }
 
 // Stage t from slot S: wait for its copies, read and decode the 16 rows'
-// piece in MFMA order, refill the slot with stage t + kNxDepth, 16 MFMAs.
+// piece in MFMA order, copy stage t + kNxAhead into its slot, 16 MFMAs.
 template <int kRG, int S>
 __device__ __forceinline__ void nx_stage(const NxCtx& c, int t, int lane, const half8v (&xv)[4][4],
                                          const float4v& unscale, float4v& acc) {
   const int n16 = lane & 15, g4 = lane >> 4;
-  wait_vmcnt<(kNxDepth - 1) * kNxStageLoads>();   // later stages' copies may stay in flight
+  wait_vmcnt<(kNxAhead - 1) * kNxStageLoads>();   // later stages' copies may stay in flight
   const uint8_t* src = nx_slot<S>(c.wave);
   const uint32_t a_w = lds_addr(src + (n16 >> 2) * kNxRegion + 16 * (4 * g4 + (n16 & 3)));
   const uint32_t a_s = lds_addr(src + kNxScaleOff + 32 * n16 + 2 * g4);
@@ -514,7 +515,7 @@ __device__ __forceinline__ void nx_stage(const NxCtx& c, int t, int lane, const 
       : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
       : "v"(a_w), "v"(a_s)
       : "memory");
-  nx_issue<kRG, S>(c, t + kNxDepth);              // the slot may be overwritten now
+  nx_issue<kRG, (S + kNxAhead) % kNxDepth>(c, t + kNxAhead);   // read by stage t + kNxAhead - kNxDepth
   const uint4 w[4] = {make_uint4(w0[0], w0[1], w0[2], w0[3]), make_uint4(w1[0], w1[1], w1[2], w1[3]),
                       make_uint4(w2[0], w2[1], w2[2], w2[3]), make_uint4(w3[0], w3[1], w3[2], w3[3])};
   const uint32_t sb[4] = {s0, s1, s2, s3};
@@ -567,10 +568,9 @@ __global__ __launch_bounds__(64 * kNxWaves) void nvfp4_w4a16_xs_kernel(
 
   for (int bt = 0; bt < nbatch; ++bt) {
     c.bt = bt;
+    static_assert(kNxAhead == 2 && kNxAhead < kNxDepth, "the prologue copies kNxAhead stages");
     nx_issue<kRG, 0>(c, 0);
     nx_issue<kRG, 1>(c, 1);
-    nx_issue<kRG, 2>(c, 2);
-    nx_issue<kRG, 3>(c, 3);
     float4v acc[kRG];
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) acc[rg] = float4v{0.f, 0.f, 0.f, 0.f};

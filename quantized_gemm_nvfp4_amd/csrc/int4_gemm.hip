@@ -219,8 +219,8 @@ __global__ __launch_bounds__(64 * kI4Waves) void int4g_gemm_decode_kernel(const 
 //    piece (16 rows x 256 bytes) with four LDS-DMA instructions, each 4 rows
 //    x 256 contiguous bytes (global memory serves 4-row bands nearly as fast
 //    as whole rows), and the 16 x 4 group scales with a fifth, into a
-//    private ring of kXsDepth stages, so no barrier is needed until the
-//    epilogue.  Lane 4 c + r of a code copy takes bytes [16 c, 16 c + 16) of
+//    private ring of kXsDepth stage slots, kXsAhead stages ahead of the one
+//    it multiplies, so no barrier is needed until the epilogue.  Lane 4 c + r of a code copy takes bytes [16 c, 16 c + 16) of
 //    band row r, and each 1 KB copy region is padded by 64 bytes, so the
 //    MFMA-order reads below hit 16 different banks.
 //  - Lane (n, g) then reads row n's bytes [64 G + 16 g, +16) for group G:
@@ -236,7 +236,12 @@ namespace {
 constexpr int kXsWaves = 8;
 constexpr int kXsPiece = 512;                     // K values per wave per pass
 constexpr int kXsPass = kXsWaves * kXsPiece;      // K values per pass
-constexpr int kXsDepth = 4;                       // stages in flight per wave (one LDS object each)
+constexpr int kXsDepth = 4;                       // stage slots per wave (one LDS object each)
+// Stages copied ahead.  Fewer copies in flight wait less: with the whole
+// chip's waves each keeping 3 stages in flight (~23 MB) a copy took ~7 us to
+// land and 28672 x 8192 at M = 4 / 16 took 34.9 / 42.0 us; 2 ahead: 33.0 /
+// 40.2 us (3 ahead: 33.7 / 41.0).
+constexpr int kXsAhead = 2;
 constexpr int kXsRegion = 1024 + 64;              // one code copy (4 rows x 256 B) + bank padding
 constexpr int kXsScaleOff = 4 * kXsRegion;        // 16 rows x 4 fp16 scales (256 B copied)
 constexpr int kXsStage = kXsScaleOff + 256;
@@ -294,13 +299,14 @@ __device__ __forceinline__ void xs_issue(const XsCtx& c, int t_in) {
 }
 
 // Stage t from slot S into acc: wait for its copies, read the 16 rows' bytes
-// in MFMA order and their scales, refill the slot with stage t + kXsDepth,
-// then four groups of (offset term + 4 MFMAs) * scale.
+// in MFMA order and their scales, copy stage t + kXsAhead into its slot
+// (read by stage t + kXsAhead - kXsDepth, long done), then four groups of
+// (offset term + 4 MFMAs) * scale.
 template <int kRG, int S>
 __device__ __forceinline__ void xs_stage(const XsCtx& c, int t, int lane, const uint4 (&xv)[4][4],
                                          const float4v (&off)[4], float4v& acc) {
   const int n16 = lane & 15, g4 = lane >> 4;
-  wait_vmcnt<(kXsDepth - 1) * kXsStageLoads>();   // later stages' copies may stay in flight
+  wait_vmcnt<(kXsAhead - 1) * kXsStageLoads>();   // later stages' copies may stay in flight
   const uint8_t* src = xs_slot<S>(c.wave);
   // The four code reads (groups G at +256 G) and the scale read, written as
   // one asm block that also waits for them: the compiler's own tracking of
@@ -324,7 +330,7 @@ __device__ __forceinline__ void xs_stage(const XsCtx& c, int t, int lane, const 
   const uint4 w[4] = {make_uint4(w0[0], w0[1], w0[2], w0[3]), make_uint4(w1[0], w1[1], w1[2], w1[3]),
                       make_uint4(w2[0], w2[1], w2[2], w2[3]), make_uint4(w3[0], w3[1], w3[2], w3[3])};
   const uint2 sb = make_uint2(sbv[0], sbv[1]);
-  xs_issue<kRG, S>(c, t + kXsDepth);                     // the slot may be overwritten now
+  xs_issue<kRG, (S + kXsAhead) % kXsDepth>(c, t + kXsAhead);
   const float sc[4] = {f16_bits_to_f32(sb.x & 0xFFFFu), f16_bits_to_f32(sb.x >> 16), f16_bits_to_f32(sb.y & 0xFFFFu),
                        f16_bits_to_f32(sb.y >> 16)};
 #pragma unroll
@@ -378,10 +384,9 @@ __global__ __launch_bounds__(64 * kXsWaves) void int4g_gemm_xs_kernel(const uint
 
   for (int bt = 0; bt < nbatch; ++bt) {
     c.bt = bt;
+    static_assert(kXsAhead == 2 && kXsAhead < kXsDepth, "the prologue copies kXsAhead stages");
     xs_issue<kRG, 0>(c, 0);
     xs_issue<kRG, 1>(c, 1);
-    xs_issue<kRG, 2>(c, 2);
-    xs_issue<kRG, 3>(c, 3);
     float4v acc[kRG];
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) acc[rg] = float4v{0.f, 0.f, 0.f, 0.f};
