@@ -136,3 +136,25 @@ def test_tiled_wide_range():
     w[5] = 0
     w[6] = np.tile(w[7, :16], K // 16)
     check(x, w, algos=(1, 3), label="tiled wide range")
+
+
+def test_tiled_prefill_shape_sampled():
+    # The weight-only call bench.py times past decode sizes: the prefill
+    # activation [4096 x 5376] times the 21504 x 5376 decode weight, through
+    # the MFMA tiles; 32 sampled rows against the oracle (x is not quantized,
+    # so a row of the output depends only on that row of x).
+    q = _q()
+    import torch
+    x_bits = workloads.normal_bf16("prefill", 0, (4096, 5376))
+    w_bits = workloads.decode_w()
+    w = q.nvfp4_quantize(dev_bf16(w_bits))
+    out = Guarded((4096, 21504), torch.bfloat16)
+    q.nvfp4_gemm_w4a16(dev_bf16(x_bits), w, out=out.t)
+    torch.cuda.synchronize()
+    assert out.intact(), "wrote outside its output"
+    rows = np.sort(np.random.default_rng(11).choice(4096, 32, replace=False))
+    ref = O.gemm_w4a16(x_bits[rows], *O.quantize(w_bits))
+    y = F.bf16_from_bits(host_bits(out.t)).astype(np.float64)[rows]
+    ok, rl, rr = Mx.check_output(y, ref)
+    log(f"w4a16 tiled prefill shape (sampled): rel_l2={rl:.3e} row_ratio={rr:.3e}")
+    assert ok, f"rel_l2={rl:.3e} row_ratio={rr:.3e}"
