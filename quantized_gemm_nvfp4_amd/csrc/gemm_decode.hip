@@ -288,6 +288,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_gemv_stream_kernel(
 #pragma unroll
     for (int w = 0; w < kStreamWaves; ++w) mx = max(mx, s_mx[w]);
     gq = bf16_bits_to_f32(mx) / 2688.0f;   // amax / (6 * 448)
+    const float rq = scale_recip(gq);
     const bool store = blockIdx.x == 0;     // workgroup 0 also returns x's NVFP4 form
     if (store && q_g != nullptr && threadIdx.x == 0) *q_g = gq;
 #pragma unroll
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_gemv_stream_kernel(
       const uint32_t b = threadIdx.x + 256u * u;
       if (b < nblk) {
         uint32_t sc;
-        const uint2 c = absmax_block(xw[u], gq, sc);
+        const uint2 c = absmax_block(xw[u], gq, rq, sc);
         if (store && q_codes != nullptr) {
           *(uint2*)(q_codes + 8u * b) = c;
           q_scales[b] = (uint8_t)sc;

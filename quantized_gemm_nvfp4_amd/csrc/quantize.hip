@@ -122,18 +122,18 @@ __device__ __forceinline__ float block_error(const uint32_t (&w)[8], uint32_t sc
 // One 16-value block b of x: its scale under rule kRule (given g) and its
 // codes, stored at codes[b] and scales[b].
 template <int kRule>
-__device__ __forceinline__ void quantize_block_words(const uint4 v0, const uint4 v1, int64_t b, float g,
+__device__ __forceinline__ void quantize_block_words(const uint4 v0, const uint4 v1, int64_t b, float g, float rg,
                                                      uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
   const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   uint32_t amax_bits = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, bf16x2_absmax_bits(w[i]));
   const float amax_b = bf16_bits_to_f32(amax_bits);
-  uint32_t sc = scale_code(amax_b, 6.0f, g);
+  uint32_t sc = scale_code(amax_b, 6.0f, g, rg);
   if (kRule != kRuleAbsmax) {
     float best = block_error(w, sc, g);
     if (kRule == kRuleFourOverSix) {
-      const uint32_t c4 = scale_code(amax_b, 4.0f, g);
+      const uint32_t c4 = scale_code(amax_b, 4.0f, g, rg);
       if (block_error(w, c4, g) < best) sc = c4;
     } else {
       const int c6 = (int)sc;
@@ -157,9 +157,9 @@ __device__ __forceinline__ void quantize_block_words(const uint4 v0, const uint4
 }
 
 template <int kRule>
-__device__ __forceinline__ void quantize_block(const uint4* __restrict__ x, int64_t b, float g,
+__device__ __forceinline__ void quantize_block(const uint4* __restrict__ x, int64_t b, float g, float rg,
                                                uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
-  quantize_block_words<kRule>(x[2 * b], x[2 * b + 1], b, g, codes, scales);
+  quantize_block_words<kRule>(x[2 * b], x[2 * b + 1], b, g, rg, codes, scales);
 }
 
 // x: bf16 [nblocks * 16]; codes: 8 bytes per block; scales: 1 byte per block.
@@ -170,10 +170,13 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
                                                           const uint32_t* __restrict__ partial, int npartial,
                                                           int use_given, const float* __restrict__ t_part,
                                                           int t_splits, float* __restrict__ t_out, int64_t t_n) {
-  __shared__ float s_g;
+  __shared__ float s_g, s_rg;
   __shared__ uint32_t s_max[4];
   if (use_given) {
-    if (threadIdx.x == 0) s_g = *gscale;
+    if (threadIdx.x == 0) {
+      s_g = *gscale;
+      s_rg = scale_recip(s_g);
+    }
   } else {
     // All 256 threads load their partials four at a time before using any,
     // so a workgroup waits for about one memory latency, not one per load.
@@ -194,10 +197,11 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
       const float g = bf16_bits_to_f32(m) / 2688.0f;   // amax / (6 * 448)
       if (blockIdx.x == 0) *gscale = g;
       s_g = g;
+      s_rg = scale_recip(g);
     }
   }
   __syncthreads();
-  const float g = s_g;
+  const float g = s_g, rg = s_rg;
 
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   // Side job for a split low-rank down projection: T = the sum of its K
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint4* __restric
     t_out[e] = v;
   }
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride)
-    quantize_block<kRule>(x, b, g, codes, scales);
+    quantize_block<kRule>(x, b, g, rg, codes, scales);
 }
 
 // Small tensors (decode activations, at most kSmallQuantBlocks blocks): a
@@ -221,7 +225,7 @@ template <int kRule>
 __global__ __launch_bounds__(1024) void nvfp4_quant_small_kernel(const uint4* __restrict__ x, int64_t nblocks,
                                                                 uint2* __restrict__ codes, uint8_t* __restrict__ scales,
                                                                 float* __restrict__ gscale, int use_given) {
-  __shared__ float s_g;
+  __shared__ float s_g, s_rg;
   __shared__ uint32_t s_max[16];
   // the thread's own block, loaded once for the maximum and the codes
   // (offsets past x read zero)
@@ -230,7 +234,10 @@ __global__ __launch_bounds__(1024) void nvfp4_quant_small_kernel(const uint4* __
   const auto xr = buffer_of(x, nbytes);
   const uint4 own0 = buffer_load16(xr, 32u * (uint32_t)b), own1 = buffer_load16(xr, 32u * (uint32_t)b + 16u);
   if (use_given) {
-    if (threadIdx.x == 0) s_g = *gscale;
+    if (threadIdx.x == 0) {
+      s_g = *gscale;
+      s_rg = scale_recip(s_g);
+    }
   } else {
     // eight 16-byte loads per thread in flight (offsets past x read zero)
     uint32_t m = 0;
@@ -252,11 +259,12 @@ __global__ __launch_bounds__(1024) void nvfp4_quant_small_kernel(const uint4* __
       const float g = bf16_bits_to_f32(m) / 2688.0f;   // amax / (6 * 448)
       if (blockIdx.x == 0) *gscale = g;
       s_g = g;
+      s_rg = scale_recip(g);
     }
   }
   __syncthreads();
-  const float g = s_g;
-  if (b < nblocks) quantize_block_words<kRule>(own0, own1, b, g, codes, scales);
+  const float g = s_g, rg = s_rg;
+  if (b < nblocks) quantize_block_words<kRule>(own0, own1, b, g, rg, codes, scales);
 }
 
 // ---- INT4 per-group (128) quantization ------------------------------------

@@ -1,8 +1,9 @@
-"""The quantizer's element division (|x| / d with one rounding) is taken as
-q = |x| r, then q + (|x| - q d) r with two fmas, r = 1/d once per block.
-tests/quotient_check.c compares that with the correctly rounded division
-on the host; here it runs on every bf16 significand against every 61st fp32
-significand (the full 2^30-pair run takes a few seconds more: STEP=1)."""
+"""The quantizer's element division (|x| / d with one rounding, x's sign
+kept) is taken as q = x r, then q - (q d - x) r with two fmas, r = 1/d once
+per block.  tests/quotient_check.c compares that, for x and -x, with the
+correctly rounded division on the host; here it runs on every bf16
+significand against every 61st fp32 significand (the full 2^30-pair run
+takes about 20 s: QUOTIENT_CHECK_STEP=1)."""
 import os
 import shutil
 import subprocess
