@@ -67,18 +67,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// E2M1 magnitude code (0..7) of y >= 0, RNE with ties to the even code,
-// saturating at 6.  Below 1 the grid is the subnormal step 0.5, so the code
-// is rint(2y); from 1 up, E2M1 keeps one mantissa bit, so the fp32 pattern is
-// rounded to one mantissa bit and rebased from exponent bias 127 to 1.
-__device__ __forceinline__ uint32_t e2m1_code_from_f32(float y) {
-  if (y < 1.0f) return (uint32_t)__builtin_rintf(y * 2.0f);    // 0, 1, 2
-  uint32_t b = __float_as_uint(y);
-  uint32_t r = (b + 0x1FFFFFu + ((b >> 22) & 1u)) >> 22;        // exp8:1 | man1
-  r -= (126u << 1);
-  return r < 7u ? r : 7u;
-}
-
 // fp32 -> fp16 bits, RNE, gradual underflow, overflow -> inf.
 __device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -71,42 +71,31 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const uint4* __restri
 // multiply-add: d = s * g, x_hat = v * d (v the signed E2M1 value of the
 // element's code), e = x - x_hat, err = sum of e * e in element order.
 namespace {
-// Signed E2M1 value of code c (0..15), exact: codes 0/1 are 0 and 0.5, then
-// (1 + m/2) * 2^(e - 1) with e = c >> 1, m = c & 1.
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t mag = c & 7u;
-  const float v = mag < 2u ? 0.5f * (float)mag : __uint_as_float((((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22));
-  return (c & 8u) ? -v : v;
+// Signed E2M1 values of elements 2J and 2J + 1 of a code word (byte J),
+// exact (the conversion's scale 1.0 leaves them unscaled).
+template <int J>
+__device__ __forceinline__ float2v e2m1x2_values(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, J);
 }
 
-// Element code of the bf16 pattern h under d (the quantizer's rule); with
-// kFast, r = 1/d and quot_fast(d).
-template <bool kFast>
-__device__ __forceinline__ uint32_t element_code(uint32_t h, float d, float r) {
-#pragma clang fp contract(off)
-  const float ax = bf16_bits_to_f32(h & 0x7FFFu);
-  float y;
-  if (kFast) {
-    const float q = ax * r;
-    y = __builtin_fmaf(__builtin_fmaf(-q, d, ax), r, q);
-  } else {
-    y = (d != 0.0f) ? ax / d : 0.0f;
-  }
-  return e2m1_code_from_f32(y) | ((h >> 12) & 8u);
-}
-
+// The block's codes under d come from encode_block, as when they are
+// stored, and go back to their E2M1 values through the matching conversion.
 template <bool kFast>
 __device__ __forceinline__ float block_error_d(const uint32_t (&w)[8], float d, float r) {
 #pragma clang fp contract(off)
+  const uint2 c = encode_block<kFast>(w, d, r);
+  const float2v v[8] = {e2m1x2_values<0>(c.x), e2m1x2_values<1>(c.x), e2m1x2_values<2>(c.x),
+                        e2m1x2_values<3>(c.x), e2m1x2_values<0>(c.y), e2m1x2_values<1>(c.y),
+                        e2m1x2_values<2>(c.y), e2m1x2_values<3>(c.y)};
   float acc = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-    const float x = bf16_bits_to_f32(h);
-    const float xhat = e2m1_value(element_code<kFast>(h, d, r)) * d;
-    const float e = x - xhat;
-    const float sq = e * e;
-    acc = acc + sq;
+  for (int i = 0; i < 8; ++i) {
+    const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xFFFF0000u);
+    const float h0 = v[i][0] * d, h1 = v[i][1] * d;
+    const float e0 = x0 - h0, e1 = x1 - h1;
+    const float s0 = e0 * e0, s1 = e1 * e1;
+    acc = acc + s0;
+    acc = acc + s1;
   }
   return acc;
 }
