@@ -26,8 +26,8 @@ constexpr float kQuotLo = 0x1p-64f, kQuotHi = 0x1p100f;
 
 __device__ __forceinline__ bool quot_fast(float d) { return d >= kQuotLo && d < kQuotHi; }
 
-// |x| / d (one rounding: the element step above) with the sign of x put
-// back, for x given as the fp32 pattern of a bf16 value.
+// |x| / d (one rounding: the element step above) carrying the sign of x,
+// for x given as the fp32 pattern of a bf16 value.
 template <bool kFast>
 __device__ __forceinline__ float signed_quotient(uint32_t xbits, float d, float r) {
 #pragma clang fp contract(off)

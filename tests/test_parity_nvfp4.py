@@ -120,6 +120,48 @@ def test_quantize_rounding_boundaries():
         assert np.array_equal(host_u8(codes), oc), f"j={j}: codes {host_u8(codes)} vs {oc}"
 
 
+def test_quantize_block_scale_boundaries():
+    # The block scale s = (amax / 6) / g (two fp32 divisions, each rounded
+    # once) is rounded to E4M3.  With g stepped one ulp at a time around
+    # (amax / 6) / t for E4M3 midpoints t (normal, subnormal and next to the
+    # largest value), s crosses each midpoint; amax / 6 is exact for amax =
+    # 6 and inexact for 7 and 0.625.  Scales and codes must equal the
+    # oracle's for every step.
+    q = _q()
+    import torch
+    for amax in (6.0, 7.0, 0.625):
+        vals = [amax, -0.5 * amax, 0.375 * amax, -0.75 * amax] + [0.0] * 12
+        bits = F.bf16_bits(np.array([vals], dtype=np.float32))
+        assert F.bf16_from_bits(bits)[0, 0] == amax
+        for t in (1.0625, 1.4375, 17.0, 432.0, 1.5 * 2.0 ** -9, 2.0 ** -7 + 2.0 ** -10):
+            g0 = np.float32(np.float32(amax / 6.0) / np.float32(t))
+            for j in range(-24, 25):
+                gj = g0
+                step = np.float32(np.inf) if j > 0 else np.float32(-np.inf)
+                for _ in range(abs(j)):
+                    gj = np.nextafter(gj, step, dtype=np.float32)
+                gt = torch.tensor([float(gj)], dtype=torch.float32, device="cuda:0")
+                codes, scales, _ = q.nvfp4_quantize(dev_bf16(bits), global_scale=gt)
+                torch.cuda.synchronize()
+                oc, osc, _ = O.quantize(bits, g=gj)
+                assert host_u8(scales)[0, 0] == osc[0, 0], \
+                    f"amax={amax} t={t} j={j}: scale {host_u8(scales)[0, 0]:#x} vs {osc[0, 0]:#x}"
+                assert np.array_equal(host_u8(codes), oc), f"amax={amax} t={t} j={j}: codes"
+
+
+@pytest.mark.parametrize("g", [2.0 ** -60, float(np.nextafter(np.float32(2.0 ** -60), np.float32(0))),
+                               2.0 ** 60, float(np.nextafter(np.float32(2.0 ** 60), np.float32(np.inf)))])
+def test_quantize_block_scale_range(g):
+    # The block-scale step takes reciprocals while g is in [2^-60, 2^60] and
+    # the block's amax is 0 or in [2^-60, 2^60], and divides otherwise.  At
+    # and just past the bounds of g, blocks whose scale ratio (amax / 6) / g
+    # is spread log-uniformly over [2^-12, 2^11] have amax on both sides of
+    # the amax bounds; scales and codes must equal the oracle's.
+    seed = {2.0 ** -60: 1, 2.0 ** 60: 2}.get(g, 3 if g < 1 else 4)
+    bits = workloads.blocks_at_scale_ratio(seed, g, 4096, -12.0, 11.0)
+    assert_quant_equal(bits, g=np.float32(g), label=f"g={g!r}")
+
+
 def test_quantize_given_global_scale():
     bits = workloads.random_bf16(8, (33, 128))
     for g in (1.0, 0.003, 1e-30, 0.0):

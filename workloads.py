@@ -142,3 +142,15 @@ def random_bf16(seed, shape, sigma=1.0, outlier_frac=0.0, outlier_mul=1.0, zero_
     if zero_frac:
         a[rng.random(shape) < zero_frac] = 0.0
     return _to_bf16_bits(a)
+
+
+def blocks_at_scale_ratio(seed, g, nblk, log2_lo, log2_hi, cols=1024):
+    """bf16 bits of nblk 16-value blocks (rows of `cols` values) whose
+    largest magnitude is about r * 6 * g, log2 r uniform in [log2_lo,
+    log2_hi]: one element of each block at +-that magnitude, the others
+    uniform in [-1, 1] times it."""
+    rng = np.random.default_rng([101, seed])
+    amax = 2.0 ** rng.uniform(log2_lo, log2_hi, size=nblk) * 6.0 * float(g)
+    u = rng.uniform(-1.0, 1.0, size=(nblk, 16))
+    u[:, 0] = np.where(rng.random(nblk) < 0.5, 1.0, -1.0)
+    return _to_bf16_bits((u * amax[:, None]).astype(np.float32).reshape(-1, cols))
