@@ -211,6 +211,7 @@ def summarize_traffic(fetch_csv, write_csv):
 DECODE_TRAFFIC = [
     ("nvfp4_w4a4_M1", "nvfp4", 1), ("nvfp4_w4a4_M2", "nvfp4", 2), ("nvfp4_w4a4_M4", "nvfp4", 4),
     ("nvfp4_w4a4_M16", "nvfp4", 16), ("nvfp4_linear_M1", "nvfp4", 1), ("nvfp4_linear_M2", "nvfp4", 2),
+    ("nvfp4_linear_M4", "nvfp4", 4),
     ("nvfp4_w4a16_M1", "nvfp4", 1), ("nvfp4_w4a16_M2", "nvfp4", 2), ("nvfp4_w4a16_M4", "nvfp4", 4),
     ("nvfp4_w4a16_M16", "nvfp4", 16), ("int4_M1", "int4", 1), ("int4_M4", "int4", 4), ("int4_M16", "int4", 16),
     ("int4_asym_M1", "int4_asym", 1)]

@@ -210,11 +210,12 @@ nvfp4_status nvfp4_gemm_ws(const uint8_t* a_codes, const uint8_t* a_scales, cons
  * nvfp4_quantize(x) (absmax rule, g from max|x|) followed by nvfp4_gemm on
  * its codes: out [M, N] bf16, and x's codes [M, K/2], scales [M, K/16] and
  * g (one fp32) in x_codes, x_scales, x_gscale, which the caller provides.
- * 1 <= M <= 2 with K % 128 == 0 and K <= 8192 (a decode step) runs one
- * kernel: each wave of the weight-streaming GEMV quantizes the activation
- * values it needs itself, with the quantizer's arithmetic; one wave also
- * stores them to x_codes / x_scales / x_gscale.  Other shapes run the
- * quantizer and then the GEMM.
+ * Decode steps run one kernel, which quantizes x itself with the
+ * quantizer's arithmetic and also stores x_codes / x_scales / x_gscale:
+ * 1 <= M <= 2 with K % 128 == 0 and K <= 8192 (the weight-streaming GEMV),
+ * and 3 <= M <= 16 with K % 128 == 0 and M * K / 16 <= 3072 (the row-block
+ * GEMM, each workgroup quantizing all of x into LDS first).  Other shapes
+ * run the quantizer and then the GEMM.
  * K > 0, K % 16 == 0 (else NVFP4_ERR_SHAPE); M == 0 does nothing; N == 0
  * only quantizes x.  x, out, x_codes, x_scales: 16-byte aligned.
  * workspace: >= nvfp4_linear_workspace_bytes(M, N, K) bytes of device

@@ -278,7 +278,8 @@ def nvfp4_linear(x, w, out=None, x_out=None, workspace=None):
     """Quantize bf16 x [M, K] (absmax rule, g from max|x|) and multiply by
     the NVFP4 weight w: bit-identical to nvfp4_gemm(nvfp4_quantize(x), w).
 
-    At M <= 2, K % 128 == 0, K <= 8192 one kernel does both.  x_out:
+    One kernel does both when K % 128 == 0 and either M <= 2, K <= 8192 or
+    3 <= M <= 16, M * K / 16 <= 3072.  x_out:
     optional (codes, scales, global_scale) buffers for x's NVFP4 form.
     Returns (out bf16 [M, N], (codes, scales, global_scale)).
     """

@@ -1014,14 +1014,29 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_w4a16_rowslot_kernel(
 namespace {
 constexpr int kRbGroups = 3;   // 48 W rows per workgroup
 constexpr int kRbWaves = 8;    // waves splitting K
+constexpr int kRbPad = 16;     // bytes after each activation row in LDS (kQ)
 }  // namespace
 
-template <bool kLora>
+// With kQ (nvfp4_linear, 3 <= M <= 16 with at most 512 kQB blocks of x) the
+// activation arrives as bf16 x [M, K] and every workgroup quantizes all of
+// it into LDS first, as the streaming GEMV's prologue does: thread t loads
+// blocks t + 512 u (u < kQB) into registers, the workgroup's integer max of
+// the |bf16| patterns is the quantizer's global amax, and each block then
+// goes through the quantizer's own per-block function (csrc/quant_block.h),
+// so codes, scales and g, and with them the output, equal those of
+// nvfp4_quantize followed by this kernel; workgroup 0 also stores them
+// (q_codes, q_scales, q_g).  The main loop then reads the activation's
+// codes and scales from LDS (rows K/2 + kRbPad and K/16 + kRbPad bytes)
+// instead of from global memory.
+template <bool kLora, int kQB = 0>
 __global__ __launch_bounds__(64 * kRbWaves) void nvfp4_gemm_rowblock_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, const float* __restrict__ w_g,
     uint16_t* __restrict__ out, int M, int N, int K, const float* __restrict__ lora_t,
-    const uint16_t* __restrict__ lora_up, int rank) {
+    const uint16_t* __restrict__ lora_up, int rank, const uint16_t* __restrict__ x_bf16 = nullptr,
+    uint8_t* __restrict__ q_codes = nullptr, uint8_t* __restrict__ q_scales = nullptr,
+    float* __restrict__ q_g = nullptr) {
+  constexpr bool kQ = kQB > 0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t row_bytes = (uint32_t)K / 2, row_scales = (uint32_t)K / 16;
@@ -1033,6 +1048,53 @@ __global__ __launch_bounds__(64 * kRbWaves) void nvfp4_gemm_rowblock_kernel(
   const auto asr = buffer_of(a_scales, (uint32_t)M * row_scales);
   const int i = lane & 15, g = lane >> 4;
   const uint32_t nsteps = (row_bytes + 127u) / 128u;
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_xq[];   // kQ: [M][K/2 + pad] codes, [M][K/16 + pad] scales
+  const uint32_t xq_row = row_bytes + kRbPad, xq_srow = row_scales + kRbPad;
+  uint8_t* const s_xs = s_xq + (uint32_t)M * xq_row;
+  float gq = 0.f;
+  if (kQ) {
+    __shared__ uint32_t s_mx[kRbWaves];
+    const uint32_t nblk = (uint32_t)M * row_scales;
+    const auto xr = buffer_of(x_bf16, nblk * 32u);          // blocks past x read zero
+    uint32_t xw[kQ ? kQB : 1][8];
+#pragma unroll
+    for (int u = 0; u < kQB; ++u) {
+      const uint32_t b = threadIdx.x + 64u * kRbWaves * u;
+      const uint4 v0 = buffer_load16(xr, 32u * b), v1 = buffer_load16(xr, 32u * b + 16u);
+      xw[u][0] = v0.x, xw[u][1] = v0.y, xw[u][2] = v0.z, xw[u][3] = v0.w;
+      xw[u][4] = v1.x, xw[u][5] = v1.y, xw[u][6] = v1.z, xw[u][7] = v1.w;
+    }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int u = 0; u < kQB; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = max(mx, bf16x2_absmax_bits(xw[u][j]));
+    mx = wave_max_u32(mx);
+    if (lane == 0) s_mx[wave] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kRbWaves; ++w) mx = max(mx, s_mx[w]);
+    gq = bf16_bits_to_f32(mx) / 2688.0f;   // amax / (6 * 448)
+    const float rq = scale_recip(gq);
+    const bool store = blockIdx.x == 0;    // workgroup 0 also returns x's NVFP4 form
+    if (store && q_g != nullptr && threadIdx.x == 0) *q_g = gq;
+#pragma unroll
+    for (int u = 0; u < kQB; ++u) {
+      const uint32_t b = threadIdx.x + 64u * kRbWaves * u;
+      if (b < nblk) {
+        uint32_t sc;
+        const uint2 c = absmax_block(xw[u], gq, rq, sc);
+        if (store && q_codes != nullptr) {
+          *(uint2*)(q_codes + 8u * b) = c;
+          q_scales[b] = (uint8_t)sc;
+        }
+        const uint32_t m = b / row_scales, kb = b - m * row_scales;
+        *(uint2*)(s_xq + m * xq_row + 8u * kb) = c;
+        s_xs[m * xq_srow + kb] = (uint8_t)sc;
+      }
+    }
+    __syncthreads();
+  }
 
   float4v acc[kRbGroups];
 #pragma unroll
@@ -1049,9 +1111,18 @@ __global__ __launch_bounds__(64 * kRbWaves) void nvfp4_gemm_rowblock_kernel(
       wc[rg][1] = buffer_load16(wr, in ? row * row_bytes + off + 16u : kOob);
       ws[rg] = buffer_load4(wsr, in ? row * row_scales + off / 8u : kOob);
     }
-    xc[0] = buffer_load16(ar, in ? (uint32_t)i * row_bytes + off : kOob);
-    xc[1] = buffer_load16(ar, in ? (uint32_t)i * row_bytes + off + 16u : kOob);
-    xs = buffer_load4(asr, in ? (uint32_t)i * row_scales + off / 8u : kOob);
+    if (kQ) {
+      // from the workgroup's quantized copy (rows past M and steps past K: zero)
+      const bool xin = in && i < M;
+      const uint8_t* xrow = s_xq + (uint32_t)(xin ? i : 0) * xq_row + (xin ? off : 0u);
+      xc[0] = xin ? *(const uint4*)xrow : make_uint4(0u, 0u, 0u, 0u);
+      xc[1] = xin ? *(const uint4*)(xrow + 16) : make_uint4(0u, 0u, 0u, 0u);
+      xs = xin ? *(const uint32_t*)(s_xs + (uint32_t)i * xq_srow + off / 8u) : 0u;
+    } else {
+      xc[0] = buffer_load16(ar, in ? (uint32_t)i * row_bytes + off : kOob);
+      xc[1] = buffer_load16(ar, in ? (uint32_t)i * row_bytes + off + 16u : kOob);
+      xs = buffer_load4(asr, in ? (uint32_t)i * row_scales + off / 8u : kOob);
+    }
     // all of the step's loads issue before any decoding (left to itself the
     // compiler interleaves them with the math and waits earlier: ~18% slower)
     __builtin_amdgcn_sched_barrier(0);
@@ -1078,7 +1149,7 @@ __global__ __launch_bounds__(64 * kRbWaves) void nvfp4_gemm_rowblock_kernel(
 #pragma unroll
   for (int rg = 0; rg < kRbGroups; ++rg) red[wave][rg][lane] = acc[rg];
   __syncthreads();
-  const float gg = (*a_g) * (*w_g);
+  const float gg = (kQ ? gq : *a_g) * (*w_g);
   // D[n][m] (16 x 16) of row group rg: lane m + 16 (n / 4), register n % 4.
   for (int e = threadIdx.x; e < kRbGroups * 64; e += 64 * kRbWaves) {
     const int rg = e >> 6, ln = e & 63;
@@ -1225,17 +1296,53 @@ hipError_t launch_nvfp4_gemm_decode_lora(const uint8_t* ac, const uint8_t* as, c
   return hipGetLastError();
 }
 
+namespace {
+// 3 <= M <= 16: x's blocks in registers, at most 6 per thread of the
+// row-block kernel's 512 (and its codes in at most 3072 * 9 = 27 KB of LDS).
+constexpr int kRbQMaxPerThread = 6;
+constexpr int64_t kRbQMaxBlocks = (int64_t)kRbQMaxPerThread * 64 * kRbWaves;
+
+template <int kQB>
+void launch_rowblock_q(const uint16_t* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out, int M,
+                       int N, int K, uint8_t* q_codes, uint8_t* q_scales, float* q_g, hipStream_t stream) {
+  const dim3 grid((unsigned)((N + 16 * kRbGroups - 1) / (16 * kRbGroups))), block(64 * kRbWaves);
+  const size_t lds = (size_t)M * ((size_t)K / 2 + kRbPad + (size_t)K / 16 + kRbPad);
+  hipLaunchKernelGGL((nvfp4_gemm_rowblock_kernel<false, kQB>), grid, block, lds, stream, (const uint8_t*)nullptr,
+                     (const uint8_t*)nullptr, (const float*)nullptr, wc, ws, wg, (uint16_t*)out, M, N, K,
+                     (const float*)nullptr, (const uint16_t*)nullptr, 0, x, q_codes, q_scales, q_g);
+}
+}  // namespace
+
 bool nvfp4_linear_fused_supported(int64_t M, int64_t K) {
-  return M >= 1 && M <= 2 && K > 0 && K % 128 == 0 && K <= (int64_t)kStreamMaxSlots * 2048;
+  if (K <= 0 || K % 128 != 0) return false;
+  if (M >= 1 && M <= 2) return K <= (int64_t)kStreamMaxSlots * 2048;
+  return M >= 3 && M <= 16 && M * (K / 16) <= kRbQMaxBlocks;
 }
 
 hipError_t launch_nvfp4_linear_fused(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
                                      int64_t M, int64_t N, int64_t K, uint8_t* q_codes, uint8_t* q_scales,
                                      float* q_g, hipStream_t stream) {
-  const StreamX a = {nullptr, nullptr, nullptr, (const uint16_t*)x, q_codes, q_scales, q_g};
-  const bool done = M == 1 ? launch_stream_k<1, true>(a, wc, ws, wg, out, (int)M, (int)N, (int)K, stream)
-                           : launch_stream_k<2, true>(a, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
-  return done ? hipGetLastError() : hipErrorInvalidValue;
+  if (M <= 2) {
+    const StreamX a = {nullptr, nullptr, nullptr, (const uint16_t*)x, q_codes, q_scales, q_g};
+    const bool done = M == 1 ? launch_stream_k<1, true>(a, wc, ws, wg, out, (int)M, (int)N, (int)K, stream)
+                             : launch_stream_k<2, true>(a, wc, ws, wg, out, (int)M, (int)N, (int)K, stream);
+    return done ? hipGetLastError() : hipErrorInvalidValue;
+  }
+  const int64_t per = (M * (K / 16) + 64 * kRbWaves - 1) / (64 * kRbWaves);   // blocks per thread
+  const uint16_t* xb = (const uint16_t*)x;
+  if (per <= 1)
+    launch_rowblock_q<1>(xb, wc, ws, wg, out, (int)M, (int)N, (int)K, q_codes, q_scales, q_g, stream);
+  else if (per <= 2)
+    launch_rowblock_q<2>(xb, wc, ws, wg, out, (int)M, (int)N, (int)K, q_codes, q_scales, q_g, stream);
+  else if (per <= 3)
+    launch_rowblock_q<3>(xb, wc, ws, wg, out, (int)M, (int)N, (int)K, q_codes, q_scales, q_g, stream);
+  else if (per <= 4)
+    launch_rowblock_q<4>(xb, wc, ws, wg, out, (int)M, (int)N, (int)K, q_codes, q_scales, q_g, stream);
+  else if (per <= kRbQMaxPerThread)
+    launch_rowblock_q<kRbQMaxPerThread>(xb, wc, ws, wg, out, (int)M, (int)N, (int)K, q_codes, q_scales, q_g, stream);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_gemm_decode(const uint8_t* ac, const uint8_t* as, const float* ag, const uint8_t* wc,

@@ -85,10 +85,12 @@ hipError_t launch_nvfp4_gemm_simple(const uint8_t* ac, const uint8_t* as, const 
                                     const uint8_t* ws, const float* wg, void* out, int64_t M, int64_t N,
                                     int64_t K, hipStream_t stream);
 
-// Quantize bf16 x and multiply in one launch (the streaming GEMV, each wave
-// quantizing the values it needs); bit-identical to launch_nvfp4_quantize
-// followed by the decode GEMM.  q_codes / q_scales / q_g (optional) receive
-// x's codes, scales and g.  Needs nvfp4_linear_fused_supported(M, K).
+// Quantize bf16 x and multiply in one launch (M <= 2: the streaming GEMV,
+// each workgroup quantizing x in its prologue; 3 <= M <= 16 with M K / 16 <=
+// 3072: the row-block GEMM, each workgroup quantizing x into LDS first);
+// bit-identical to launch_nvfp4_quantize followed by the decode GEMM.
+// q_codes / q_scales / q_g (optional) receive x's codes, scales and g.
+// Needs nvfp4_linear_fused_supported(M, K).
 bool nvfp4_linear_fused_supported(int64_t M, int64_t K);
 hipError_t launch_nvfp4_linear_fused(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out,
                                      int64_t M, int64_t N, int64_t K, uint8_t* q_codes, uint8_t* q_scales,

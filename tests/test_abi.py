@@ -229,12 +229,15 @@ def test_linear_validation():
     assert lib.nvfp4_linear_workspace_bytes(1, 21504, 5376) == 0
     assert lib.nvfp4_linear_workspace_bytes(2, 64, 8192) == 0
     assert lib.nvfp4_linear_workspace_bytes(1, 64, 8192 + 128) == 4096
-    assert lib.nvfp4_linear_workspace_bytes(3, 64, 128) == 4096
+    assert lib.nvfp4_linear_workspace_bytes(3, 64, 128) == 0
+    assert lib.nvfp4_linear_workspace_bytes(16, 64, 3072) == 0                 # M K / 16 = 3072
+    assert lib.nvfp4_linear_workspace_bytes(16, 64, 3072 + 128) == 4096
+    assert lib.nvfp4_linear_workspace_bytes(17, 64, 128) == 4096
     assert lib.nvfp4_linear_workspace_bytes(2, 64, 48) == 4096
     assert lib.nvfp4_linear_workspace_bytes(4096, 4096, 4096) >= 4096
-    assert f(*good, 3, 64, 128, *xo, None, 0, None) == INVALID and "workspace" in _err()
-    assert f(*good, 3, 64, 128, *xo, P(0x100010), 4096, None) == ALIGN
-    assert f(*good, 3, 64, 128, *xo, W, 4095, None) == INVALID
+    assert f(*good, 17, 64, 128, *xo, None, 0, None) == INVALID and "workspace" in _err()
+    assert f(*good, 17, 64, 128, *xo, P(0x100010), 4096, None) == ALIGN
+    assert f(*good, 17, 64, 128, *xo, W, 4095, None) == INVALID
     assert f(*good, 0, 64, 128, *xo, None, 0, None) == OK
     assert f(*good, 1 << 30, 1 << 30, 128, *xo, None, 0, None) == UNSUP
 

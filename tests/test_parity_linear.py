@@ -2,9 +2,10 @@
 
 x's codes, scales and g must equal the oracle's quantization byte for byte,
 and the output must be bit-identical to nvfp4_quantize followed by
-nvfp4_gemm on the same device (the one-kernel path at M <= 2 repeats the
-quantizer's arithmetic inside the GEMV), and within the GEMM tolerance of
-the oracle's fp64 product rounded to bf16."""
+nvfp4_gemm on the same device (the one-kernel paths, the GEMV at M <= 2 and
+the row-block GEMM at 3 <= M <= 16 for small x, repeat the quantizer's
+arithmetic in their prologues), and within the GEMM tolerance of the
+oracle's fp64 product rounded to bf16."""
 import numpy as np
 import pytest
 
@@ -63,9 +64,24 @@ def test_linear_one_kernel_shapes(M, N, K):
     _run(x_bits, w_bits, f"fused {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 33, 8192 + 128), (3, 50, 2176), (16, 64, 5376), (40, 300, 1024), (2, 21, 48)])
+@pytest.mark.parametrize("M,N,K", [
+    (3, 50, 2176), (4, 97, 5376), (5, 1, 128), (8, 48, 6144), (9, 200, 5376), (12, 130, 4096), (16, 30, 3072),
+    (3, 20000, 256)])
+def test_linear_one_kernel_rowblock_shapes(M, N, K):
+    # 3 <= M <= 16, K % 128 == 0 and M K / 16 <= 3072: every workgroup of
+    # the row-block GEMM quantizes all of x into LDS (one to six blocks per
+    # thread; 8 x 6144 and 12 x 4096 and 16 x 3072 fill all six), workgroup 0
+    # also stores x's codes; N not a multiple of the 48 rows per workgroup
+    x_bits = workloads.random_bf16(M * 59 + K, (M, K), outlier_frac=0.01, outlier_mul=30)
+    w_bits = workloads.random_bf16(N * 61 + K, (N, K), sigma=0.02, zero_frac=0.05)
+    _run(x_bits, w_bits, f"fused row-block {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 33, 8192 + 128), (10, 50, 5376), (16, 64, 5376), (40, 300, 1024),
+                                   (2, 21, 48), (4, 30, 1040)])
 def test_linear_two_kernel_shapes(M, N, K):
-    # K past 8192, M >= 3 and K % 128 != 0 quantize first, then multiply
+    # K past 8192 at M <= 2, M K / 16 past 3072 at 3 <= M <= 16, M > 16 and
+    # K % 128 != 0 quantize first, then multiply
     x_bits = workloads.random_bf16(M * 47 + K, (M, K), outlier_frac=0.01, outlier_mul=30)
     w_bits = workloads.random_bf16(N * 53 + K, (N, K), sigma=0.02, zero_frac=0.05)
     _run(x_bits, w_bits, f"two-kernel {M}x{N}x{K}")
@@ -76,6 +92,7 @@ def test_linear_degenerate_activations():
     # nonzero value, and values 2^97 next to bf16 subnormals
     w_bits = workloads.random_bf16(5, (96, 1024), sigma=0.02)
     _run(np.zeros((1, 1024), np.uint16), w_bits, "zero x")
+    _run(np.zeros((4, 1024), np.uint16), w_bits, "zero x, M = 4")
     one = np.zeros((2, 1024), np.uint16)
     one[1, 517] = 0xC2F6                        # -123.0
     _run(one, w_bits, "one value")
@@ -83,12 +100,16 @@ def test_linear_degenerate_activations():
     wide[0, ::16] = 0x7000                      # 2^97
     wide[1, 3::16] = 0x0001                     # the smallest subnormal
     _run(wide, w_bits, "wide range")
+    wide5 = workloads.random_bf16(7, (5, 1024))
+    wide5[0, ::16] = 0x7000
+    wide5[3, 3::16] = 0x0001
+    _run(wide5, w_bits, "wide range, M = 5")
 
 
 def test_linear_decode_config():
-    # the 21504 x 5376 decode weight with the first one and two rows of the
-    # decode activation
+    # the 21504 x 5376 decode weight with the first 1, 2, 4 and 8 rows of
+    # the decode activation (one kernel each)
     x_bits, _ = workloads.decode_x()
     w_bits = workloads.decode_w()
-    for M in (1, 2):
+    for M in (1, 2, 4, 8):
         _run(x_bits[:M], w_bits, f"decode M={M}")
