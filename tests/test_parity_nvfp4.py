@@ -442,3 +442,7 @@ def test_gemm_subnormal_and_zero_scales():
     assert sub(oa[1]) > 0 and sub(ow[1]) > 0, "case must contain subnormal scales"
     check_gemm(a_bits, w_bits, algos=(0, 1, 2, 3) if a_bits.shape[0] <= 16 else (0, 1, 3), label="subnormal scales")
     check_gemm(a_bits[:16], w_bits, algos=(2,), label="subnormal scales decode")
+    # M = 1 runs the streaming GEMV: subnormal and zero block scales through
+    # its exact 2^-8 scale conversion
+    check_gemm(a_bits[:1], w_bits, algos=(0, 2), label="subnormal scales M=1")
+    check_gemm(a_bits[20:21], w_bits, algos=(0, 2), label="subnormal scales M=1, small row")
