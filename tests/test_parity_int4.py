@@ -123,9 +123,12 @@ def test_int4_stationary_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(2, 28672, 8192), (16, 140001, 256), (5, 3000, 12288 + 128), (4, 9, 128),
-                                   (2, 300, 65536)])
+                                   (2, 300, 65536), (1, 140001, 256), (1, 300, 6144 + 128), (1, 5000, 8192)])
 def test_int4_more_decode_shapes(M, N, K):
-    # the row-slot GEMV at the decode weight's shape with M = 2; the
+    # M = 1 on the row-slot GEMV: 17501 workgroups of 8 rows (N = 140001,
+    # the last one partial), a partial last slot (K = 6272), four whole
+    # slots (K = 8192); the row-slot GEMV at the decode weight's shape with
+    # M = 2; the
     # row-block kernel (K % 512 != 0) with 1250 workgroups of 112 rows (N =
     # 140001), an odd group count (K = 12416: a half step at the end) and a
     # lone group (K = 128); K past the row-slot GEMV's limit at M = 2
