@@ -25,6 +25,9 @@
  *    0-3 of byte j, element 2j+1 in bits 4-7.  A code is sign<<3 | E2M1
  *    magnitude code (0..7 = 0, .5, 1, 1.5, 2, 3, 4, 6).
  *  - NVFP4 scales: uint8 [rows, cols/16], E4M3 (OCP "fn") bit patterns.
+ *    The GEMM entry points take the scale bytes the quantizers write:
+ *    non-negative and finite (sign bit clear, not 0x7F).  For other bytes
+ *    (negative scales, NaN) the decode kernels' results are unspecified.
  *  - NVFP4 global scale: one fp32 in device memory.  The value of element
  *    (r, c) is E2M1(code) * E4M3(scale[r][c/16]) * global_scale.
  *  - INT4 codes: uint8 [N, K/2], two's-complement nibbles in [-7, 7],
