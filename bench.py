@@ -751,7 +751,9 @@ PEAK_LIB = os.path.join(ROOT, "peak", "libpeak.so")
 
 def run_peaks(torch, iters=64, copies=16):
     """Measured roofline denominators (peak/peak.hip): the dense fp16 MFMA
-    issue loop over the whole chip (TFLOP/s), a 1 GiB non-temporal read
+    issue loop over the whole chip (TFLOP/s), the tiled GEMM's 32x32x16 MFMA
+    with operand data of three kinds and with vector instructions between
+    the MFMAs, a 1 GiB non-temporal read
     (GB/s), and the per-call time of a plain read of the decode weight's
     bytes (65,074,136) over 16 rotated buffers, replayed from a HIP graph as
     the decode calls are (the floor a decode call could reach)."""
@@ -777,6 +779,21 @@ def run_peaks(torch, iters=64, copies=16):
     ms = _event_ms(torch, lambda: [check(lib.peak_mfma(4096, ctypes.c_void_p(out.data_ptr()), ctypes.byref(flops),
                                                        stream), "peak_mfma") for _ in range(reps)], 1) / reps
     mfma = flops.value / (ms * 1e-3) / 1e12
+    # the tiled GEMM's v_mfma_f32_32x32x16_f16 at one wave per SIMD, operands
+    # changing every instruction: zeros / E2M1 x E4M3 products / random fp16,
+    # and with 2 or 4 vector instructions after every MFMA (products data)
+    lib.peak_mfma_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    mix = {}
+    for mode, name in ((0, "zeros"), (1, "e2m1_x_e4m3"), (2, "random_f16")):
+        for valu in ((0, 2, 4) if mode == 1 else (0,)):
+            def run_mix(mode=mode, valu=valu):
+                check(lib.peak_mfma_mix(16384, mode, valu, ctypes.c_void_p(out.data_ptr()), ctypes.byref(flops),
+                                        stream), "peak_mfma_mix")
+            for _ in range(2):
+                run_mix()
+            ms_m = _event_ms(torch, lambda: [run_mix() for _ in range(5)], 1) / 5
+            mix[f"{name}_valu{valu}"] = flops.value / (ms_m * 1e-3) / 1e12
     # reads: the best of three grid sizes (2, 4, 8 workgroups per CU)
     big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     big.fill_(1)
@@ -809,9 +826,12 @@ def run_peaks(torch, iters=64, copies=16):
            "hbm_read_gbs": read, "hbm_frac_of_spec": read / PEAK_HBM_GBS, "read_wgs_per_cu": read_wgs,
            "hbm_read_lds_dma_gbs": read_lds,
            "decode_read_floor_us": floor_us, "decode_read_floor_gbs": nb / (floor_us * 1e-6) / 1e9,
-           "floor_wgs_per_cu": floor_wgs}
+           "floor_wgs_per_cu": floor_wgs,
+           "mfma_32x32x16_f16_one_wave_per_simd_tflops": mix}
     log(f"peaks: MFMA fp16 loop {mfma:.0f} TFLOP/s ({mfma / PEAK_MFMA_TFLOPS:.3f} of spec), 1 GiB read "
         f"{read:.0f} GB/s ({read_lds:.0f} GB/s through LDS by DMA), 65 MB read per call (graph) {floor_us:.2f} us")
+    log("peaks: 32x32x16 MFMA loop, one wave per SIMD (TFLOP/s): " +
+        ", ".join(f"{k} {v:.0f}" for k, v in mix.items()))
     return res
 
 
@@ -1002,8 +1022,16 @@ def main():
                      "kernel": "nvfp4_gemm_tiled_kernel (+ nvfp4_gemm_tiled_reduce_kernel: one GEMM call)",
                      "avg_launch_ms": round(pre["gemm_avg_ms"], 4),
                      "peak_measured": round(peaks["mfma_f16_tflops"], 1),
-                     "frac_measured": round(achieved / peaks["mfma_f16_tflops"], 4)},
-        "peaks": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in peaks.items()},
+                     "frac_measured": round(achieved / peaks["mfma_f16_tflops"], 4),
+                     # the same instruction on the operand values the GEMM feeds it (decoded
+                     # E2M1 x E4M3 products) with 2 vector instructions per MFMA, as in its loop
+                     "peak_measured_products": round(peaks["mfma_32x32x16_f16_one_wave_per_simd_tflops"]
+                                                     ["e2m1_x_e4m3_valu2"], 1),
+                     "frac_measured_products": round(achieved / peaks["mfma_32x32x16_f16_one_wave_per_simd_tflops"]
+                                                     ["e2m1_x_e4m3_valu2"], 4)},
+        "peaks": {k: (round(v, 4) if isinstance(v, float) else
+                      ({kk: round(vv, 1) for kk, vv in v.items()} if isinstance(v, dict) else v))
+                  for k, v in peaks.items()},
         "cpu_baseline": cpu,
         "prefill": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in pre.items()},
     }

@@ -130,6 +130,99 @@ __global__ __launch_bounds__(64 * kLdsWaves) void peak_read_lds_kernel(const voi
   out[blockIdx.x * 64 * kLdsWaves + threadIdx.x] = ring[lane];
 }
 
+// The tiled GEMM's matrix instruction, v_mfma_f32_32x32x16_f16, at one
+// wave per SIMD (one 4-wave workgroup per CU, as the GEMM runs), with
+// operands that change every instruction: each wave holds four A and four B
+// operands and issues 16 MFMAs per trip over four independent accumulators,
+// each pairing a different (A, B).  The operand values are drawn in the
+// prologue from a per-lane hash (no memory access inside the loop):
+//   mode 0: zeros;
+//   mode 1: E2M1 value x E4M3 scale products, the values the GEMM feeds the
+//           matrix cores (signed codes from {0.5, 1, 1.5, 2, 3, 4, 6}, block
+//           scales 2^[-4, 3] x (1 + j/8));
+//   mode 2: random fp16 (random sign and 10-bit mantissa, exponent in
+//           [-4, 3]).
+// kV independent vector instructions (v_xor_b32 on registers no MFMA reads)
+// follow every MFMA, so the loop measures what issuing vector work between
+// the MFMAs costs.  The matrix cores' rate depends on the operand bits
+// (power), which is why the three modes differ.
+typedef float float16v __attribute__((ext_vector_type(16)));
+constexpr int kMixThreads = 256;
+
+__device__ __forceinline__ uint32_t mix_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+__device__ __forceinline__ _Float16 mix_value(int mode, uint32_t h) {
+  if (mode == 0) return (_Float16)0.0f;
+  const float sign = (h & 1u) ? -1.0f : 1.0f;
+  if (mode == 1) {
+    const float e2m1[7] = {0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    const float c = e2m1[(h >> 1) % 7u];
+    const float scale = __builtin_ldexpf(1.0f + 0.125f * (float)((h >> 4) & 7u), (int)((h >> 7) & 7u) - 4);
+    return (_Float16)(sign * c * scale);
+  }
+  const float m = 1.0f + (float)((h >> 1) & 1023u) / 1024.0f;
+  return (_Float16)(sign * __builtin_ldexpf(m, (int)((h >> 11) & 7u) - 4));
+}
+
+#define PK_MF(C, A, B) "v_mfma_f32_32x32x16_f16 %" #C ", %" #A ", %" #B ", %" #C "\n\t"
+#define PK_VX(U) "v_xor_b32 %" #U ", %" #U ", %16\n\t"
+#define PK_BODY(V)                                                                                        \
+  PK_MF(0, 8, 12) V PK_MF(1, 9, 13) V PK_MF(2, 10, 14) V PK_MF(3, 11, 15) V PK_MF(0, 9, 14) V              \
+  PK_MF(1, 10, 15) V PK_MF(2, 11, 12) V PK_MF(3, 8, 13) V PK_MF(0, 10, 12) V PK_MF(1, 11, 13) V           \
+  PK_MF(2, 8, 14) V PK_MF(3, 9, 15) V PK_MF(0, 11, 14) V PK_MF(1, 8, 15) V PK_MF(2, 9, 12) V              \
+  PK_MF(3, 10, 13) V
+
+template <int kV>
+__global__ __launch_bounds__(kMixThreads) void peak_mfma_mix_kernel(int iters, int mode, float* __restrict__ out) {
+  const uint32_t t = blockIdx.x * kMixThreads + threadIdx.x;
+  half8v a[4], b[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[r][i] = mix_value(mode, mix_hash(t * 64u + r * 8u + i));
+      b[r][i] = mix_value(mode, mix_hash(t * 64u + 32u + r * 8u + i));
+    }
+  float16v acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
+  uint32_t u0 = t, u1 = t + 1u, u2 = t + 2u, u3 = t + 3u;
+  const uint32_t k = mix_hash(t);
+  for (int it = 0; it < iters; it += 16) {
+    if (kV == 0) {
+      asm volatile(PK_BODY("")
+                   : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+v"(u0), "+v"(u1), "+v"(u2), "+v"(u3)
+                   : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(k));
+    } else if (kV == 2) {
+      asm volatile(PK_BODY(PK_VX(4) PK_VX(5))
+                   : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+v"(u0), "+v"(u1), "+v"(u2), "+v"(u3)
+                   : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(k));
+    } else {
+      asm volatile(PK_BODY(PK_VX(4) PK_VX(5) PK_VX(6) PK_VX(7))
+                   : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+v"(u0), "+v"(u1), "+v"(u2), "+v"(u3)
+                   : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(k));
+    }
+  }
+  float s = (float)(u0 ^ u1 ^ u2 ^ u3) * 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[c][i];
+  out[t] = s;
+}
+#undef PK_BODY
+#undef PK_VX
+#undef PK_MF
+
 int cus() {
   static int n = 0;
   if (n == 0) {
@@ -159,6 +252,26 @@ int peak_mfma(int iters, float* out, double* flops, void* stream) {
   const int grid = cus() * kMfmaWgsPerCu;
   *flops = (double)grid * (kMfmaThreads / 64) * iters * kChains * 16384.0;
   hipLaunchKernelGGL(peak_mfma_kernel, dim3(grid), dim3(kMfmaThreads), 0, (hipStream_t)stream, iters, out);
+  return (int)hipGetLastError();
+}
+
+// Launches the 32x32x16 MFMA loop (one 4-wave workgroup per CU) with
+// operand data `mode` (0 zeros, 1 E2M1 x E4M3 products, 2 random fp16) and
+// `valu` (0, 2 or 4) vector instructions after every MFMA; iters a multiple
+// of 16.  *flops receives the flops it performs.  Returns a hipError_t value.
+int peak_mfma_mix(int iters, int mode, int valu, float* out, double* flops, void* stream) {
+  if (iters <= 0 || iters % 16 != 0 || mode < 0 || mode > 2 || (valu != 0 && valu != 2 && valu != 4) ||
+      out == nullptr || flops == nullptr || cus() <= 0)
+    return (int)hipErrorInvalidValue;
+  const int grid = cus();
+  *flops = (double)grid * (kMixThreads / 64) * iters * 32768.0;
+  const hipStream_t st = (hipStream_t)stream;
+  if (valu == 0)
+    hipLaunchKernelGGL(peak_mfma_mix_kernel<0>, dim3(grid), dim3(kMixThreads), 0, st, iters, mode, out);
+  else if (valu == 2)
+    hipLaunchKernelGGL(peak_mfma_mix_kernel<2>, dim3(grid), dim3(kMixThreads), 0, st, iters, mode, out);
+  else
+    hipLaunchKernelGGL(peak_mfma_mix_kernel<4>, dim3(grid), dim3(kMixThreads), 0, st, iters, mode, out);
   return (int)hipGetLastError();
 }
 
