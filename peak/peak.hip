@@ -173,13 +173,25 @@ __device__ __forceinline__ _Float16 mix_value(int mode, uint32_t h) {
 
 #define PK_MF(C, A, B) "v_mfma_f32_32x32x16_f16 %" #C ", %" #A ", %" #B ", %" #C "\n\t"
 #define PK_VX(U) "v_xor_b32 %" #U ", %" #U ", %16\n\t"
+// kP = 0: both operands change with every MFMA; kP = 1: the GEMM's order,
+// the first operand (a weight fragment) held for eight MFMAs while the second
+// (an activation fragment) changes with every one.
 #define PK_BODY(V)                                                                                        \
   PK_MF(0, 8, 12) V PK_MF(1, 9, 13) V PK_MF(2, 10, 14) V PK_MF(3, 11, 15) V PK_MF(0, 9, 14) V              \
   PK_MF(1, 10, 15) V PK_MF(2, 11, 12) V PK_MF(3, 8, 13) V PK_MF(0, 10, 12) V PK_MF(1, 11, 13) V           \
   PK_MF(2, 8, 14) V PK_MF(3, 9, 15) V PK_MF(0, 11, 14) V PK_MF(1, 8, 15) V PK_MF(2, 9, 12) V              \
   PK_MF(3, 10, 13) V
+#define PK_BODY_HOLD(V)                                                                                   \
+  PK_MF(0, 8, 12) V PK_MF(1, 8, 13) V PK_MF(2, 8, 14) V PK_MF(3, 8, 15) V PK_MF(0, 8, 12) V                \
+  PK_MF(1, 8, 13) V PK_MF(2, 8, 14) V PK_MF(3, 8, 15) V PK_MF(0, 9, 12) V PK_MF(1, 9, 13) V               \
+  PK_MF(2, 9, 14) V PK_MF(3, 9, 15) V PK_MF(0, 9, 12) V PK_MF(1, 9, 13) V PK_MF(2, 9, 14) V               \
+  PK_MF(3, 9, 15) V
+#define PK_ASM(BODY)                                                                                     \
+  asm volatile(BODY                                                                                      \
+               : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+v"(u0), "+v"(u1), "+v"(u2), "+v"(u3) \
+               : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(k))
 
-template <int kV>
+template <int kV, int kP>
 __global__ __launch_bounds__(kMixThreads) void peak_mfma_mix_kernel(int iters, int mode, float* __restrict__ out) {
   const uint32_t t = blockIdx.x * kMixThreads + threadIdx.x;
   half8v a[4], b[4];
@@ -198,18 +210,14 @@ __global__ __launch_bounds__(kMixThreads) void peak_mfma_mix_kernel(int iters, i
   uint32_t u0 = t, u1 = t + 1u, u2 = t + 2u, u3 = t + 3u;
   const uint32_t k = mix_hash(t);
   for (int it = 0; it < iters; it += 16) {
-    if (kV == 0) {
-      asm volatile(PK_BODY("")
-                   : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+v"(u0), "+v"(u1), "+v"(u2), "+v"(u3)
-                   : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(k));
-    } else if (kV == 2) {
-      asm volatile(PK_BODY(PK_VX(4) PK_VX(5))
-                   : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+v"(u0), "+v"(u1), "+v"(u2), "+v"(u3)
-                   : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(k));
+    if (kP == 0) {
+      if (kV == 0) PK_ASM(PK_BODY(""));
+      else if (kV == 2) PK_ASM(PK_BODY(PK_VX(4) PK_VX(5)));
+      else PK_ASM(PK_BODY(PK_VX(4) PK_VX(5) PK_VX(6) PK_VX(7)));
     } else {
-      asm volatile(PK_BODY(PK_VX(4) PK_VX(5) PK_VX(6) PK_VX(7))
-                   : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+v"(u0), "+v"(u1), "+v"(u2), "+v"(u3)
-                   : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(k));
+      if (kV == 0) PK_ASM(PK_BODY_HOLD(""));
+      else if (kV == 2) PK_ASM(PK_BODY_HOLD(PK_VX(4) PK_VX(5)));
+      else PK_ASM(PK_BODY_HOLD(PK_VX(4) PK_VX(5) PK_VX(6) PK_VX(7)));
     }
   }
   float s = (float)(u0 ^ u1 ^ u2 ^ u3) * 0.0f;
@@ -219,6 +227,8 @@ __global__ __launch_bounds__(kMixThreads) void peak_mfma_mix_kernel(int iters, i
     for (int i = 0; i < 16; ++i) s += acc[c][i];
   out[t] = s;
 }
+#undef PK_ASM
+#undef PK_BODY_HOLD
 #undef PK_BODY
 #undef PK_VX
 #undef PK_MF
@@ -256,22 +266,28 @@ int peak_mfma(int iters, float* out, double* flops, void* stream) {
 }
 
 // Launches the 32x32x16 MFMA loop (one 4-wave workgroup per CU) with
-// operand data `mode` (0 zeros, 1 E2M1 x E4M3 products, 2 random fp16) and
-// `valu` (0, 2 or 4) vector instructions after every MFMA; iters a multiple
-// of 16.  *flops receives the flops it performs.  Returns a hipError_t value.
-int peak_mfma_mix(int iters, int mode, int valu, float* out, double* flops, void* stream) {
+// operand data `mode` (0 zeros, 1 E2M1 x E4M3 products, 2 random fp16),
+// `valu` (0, 2 or 4) vector instructions after every MFMA and operand order
+// `hold` (0: both operands change every MFMA; 1: the first held for eight
+// MFMAs, as in the GEMM); iters a multiple of 16.  *flops receives the flops
+// it performs.  Returns a hipError_t value.
+int peak_mfma_mix(int iters, int mode, int valu, int hold, float* out, double* flops, void* stream) {
   if (iters <= 0 || iters % 16 != 0 || mode < 0 || mode > 2 || (valu != 0 && valu != 2 && valu != 4) ||
-      out == nullptr || flops == nullptr || cus() <= 0)
+      (hold != 0 && hold != 1) || out == nullptr || flops == nullptr || cus() <= 0)
     return (int)hipErrorInvalidValue;
   const int grid = cus();
   *flops = (double)grid * (kMixThreads / 64) * iters * 32768.0;
   const hipStream_t st = (hipStream_t)stream;
-  if (valu == 0)
-    hipLaunchKernelGGL(peak_mfma_mix_kernel<0>, dim3(grid), dim3(kMixThreads), 0, st, iters, mode, out);
-  else if (valu == 2)
-    hipLaunchKernelGGL(peak_mfma_mix_kernel<2>, dim3(grid), dim3(kMixThreads), 0, st, iters, mode, out);
-  else
-    hipLaunchKernelGGL(peak_mfma_mix_kernel<4>, dim3(grid), dim3(kMixThreads), 0, st, iters, mode, out);
+  const dim3 g(grid), b(kMixThreads);
+  if (hold == 0) {
+    if (valu == 0) hipLaunchKernelGGL((peak_mfma_mix_kernel<0, 0>), g, b, 0, st, iters, mode, out);
+    else if (valu == 2) hipLaunchKernelGGL((peak_mfma_mix_kernel<2, 0>), g, b, 0, st, iters, mode, out);
+    else hipLaunchKernelGGL((peak_mfma_mix_kernel<4, 0>), g, b, 0, st, iters, mode, out);
+  } else {
+    if (valu == 0) hipLaunchKernelGGL((peak_mfma_mix_kernel<0, 1>), g, b, 0, st, iters, mode, out);
+    else if (valu == 2) hipLaunchKernelGGL((peak_mfma_mix_kernel<2, 1>), g, b, 0, st, iters, mode, out);
+    else hipLaunchKernelGGL((peak_mfma_mix_kernel<4, 1>), g, b, 0, st, iters, mode, out);
+  }
   return (int)hipGetLastError();
 }
 
