@@ -993,7 +993,8 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_w4a16_rowslot_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Weight-only streaming GEMV (bf16 x, M = 1, K <= 8192).
+// Weight-only streaming GEMV (bf16 x, M = 1, K <= 8192; the template also
+// takes M = 2 with K <= 6144, which measured no faster than the row band).
 //
 // The streaming GEMV's schedule (a persistent grid, whole rows per wave, the
 // next kStreamDepth rows in flight) with the weight-only row-slot kernel's
@@ -1004,13 +1005,13 @@ __global__ __launch_bounds__(1024) void nvfp4_gemv_w4a16_rowslot_kernel(
 // each row's 16 diagonal entries in the row-slot kernel's pairwise order.
 // Every step repeats the row-slot kernel's, in the same order, so the
 // outputs are the same bit for bit.
-template <int kS>
+template <int kM, int kS>
 __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_w4a16_stream_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
-    const float* __restrict__ w_g, uint16_t* __restrict__ out, int N, int K) {
+    const float* __restrict__ w_g, uint16_t* __restrict__ out, int M, int N, int K) {
 #pragma clang fp contract(off)
   constexpr int kD = kStreamDepth;
-  __shared__ __attribute__((aligned(16))) float s_part[kStreamWaves][kStreamBatch * 16];
+  __shared__ __attribute__((aligned(16))) float s_part[kStreamWaves][kStreamBatch * kM * 16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * kStreamWaves + wave, TW = gridDim.x * kStreamWaves;
@@ -1024,16 +1025,20 @@ __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_w4a16_stream_kernel(
     const bool valid = row < N;
     return buffer_of(w_scales + (int64_t)(valid ? row : 0) * row_scales, valid ? row_scales : 0u);
   };
-  // the lane's 32 values of each slot: x first, then the first kD rows
-  const auto xr = buffer_of(x, (uint32_t)K * 2u);
-  uint4 xb[kS][4];
+  // the lane's 32 values of each slot (rows >= M read as zero): x first,
+  // then the first kD rows
+  const auto xr = buffer_of(x, (uint32_t)M * (uint32_t)K * 2u);
+  uint4 xb[kM][kS][4];
 #pragma unroll
-  for (int s = 0; s < kS; ++s) {
-    const uint32_t off = 1024u * s + 16u * lane;
-    const bool in = off < row_bytes;
+  for (int m = 0; m < kM; ++m)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) xb[s][jj] = buffer_load16(xr, in ? 2u * (2u * off + 8u * jj) : kOob);
-  }
+    for (int s = 0; s < kS; ++s) {
+      const uint32_t off = 1024u * s + 16u * lane;
+      const bool in = off < row_bytes;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        xb[m][s][jj] = buffer_load16(xr, in ? 2u * ((uint32_t)m * K + 2u * off + 8u * jj) : kOob);
+    }
   uint4 wc[kD][kS];
   uint32_t ws[kD][kS];
 #pragma unroll
@@ -1049,34 +1054,36 @@ __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_w4a16_stream_kernel(
 
   // slot s of x in fp16 after 2^-k_s, k_s = (biased exponent of the slot's
   // largest magnitude) - 127 - 15, kept where 2^-k and 2^k are normal
-  half8v xv[kS][4];
-  float unscale[kS];
+  half8v xv[kM][kS][4];
+  float unscale[kM][kS];
 #pragma unroll
-  for (int s = 0; s < kS; ++s) {
-    uint32_t mx = 0;
+  for (int m = 0; m < kM; ++m)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      mx = max(max(max(mx, bf16x2_absmax_bits(xb[s][jj].x)), bf16x2_absmax_bits(xb[s][jj].y)),
-               max(bf16x2_absmax_bits(xb[s][jj].z), bf16x2_absmax_bits(xb[s][jj].w)));
-    mx = wave_max_u32(mx);
-    const int k = min(max((int)(mx >> 7) - 142, -126), 126);
-    const float pre = __uint_as_float((uint32_t)(127 - k) << 23);
-    unscale[s] = __uint_as_float((uint32_t)(127 + k) << 23);
+    for (int s = 0; s < kS; ++s) {
+      uint32_t mx = 0;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const uint32_t wv[4] = {xb[s][jj].x, xb[s][jj].y, xb[s][jj].z, xb[s][jj].w};
-      half8v h;
+      for (int jj = 0; jj < 4; ++jj)
+        mx = max(max(max(mx, bf16x2_absmax_bits(xb[m][s][jj].x)), bf16x2_absmax_bits(xb[m][s][jj].y)),
+                 max(bf16x2_absmax_bits(xb[m][s][jj].z), bf16x2_absmax_bits(xb[m][s][jj].w)));
+      mx = wave_max_u32(mx);
+      const int k = min(max((int)(mx >> 7) - 142, -126), 126);
+      const float pre = __uint_as_float((uint32_t)(127 - k) << 23);
+      unscale[m][s] = __uint_as_float((uint32_t)(127 + k) << 23);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float lo = __uint_as_float(wv[t] << 16) * pre;
-        const float hi = __uint_as_float(wv[t] & 0xFFFF0000u) * pre;
-        const half2v p = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-        h[2 * t] = p.x;
-        h[2 * t + 1] = p.y;
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t wv[4] = {xb[m][s][jj].x, xb[m][s][jj].y, xb[m][s][jj].z, xb[m][s][jj].w};
+        half8v h;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float lo = __uint_as_float(wv[t] << 16) * pre;
+          const float hi = __uint_as_float(wv[t] & 0xFFFF0000u) * pre;
+          const half2v p = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+          h[2 * t] = p.x;
+          h[2 * t + 1] = p.y;
+        }
+        xv[m][s][jj] = h;
       }
-      xv[s][jj] = h;
     }
-  }
 
   const int i = lane & 15;
   const bool diag_lane = (i >> 2) == (lane >> 4);
@@ -1086,11 +1093,14 @@ __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_w4a16_stream_kernel(
   auto flush = [&]() {
     // lane l < nbat: row row0 + l TW, its 16 diagonal entries added pairwise
     if (lane < nbat) {
-      const float4v* p = (const float4v*)(part + lane * 16);
-      const float4v a = p[0], b = p[1], c = p[2], e = p[3];
-      const float t0 = (a[0] + a[1]) + (a[2] + a[3]), t1 = (b[0] + b[1]) + (b[2] + b[3]);
-      const float t2 = (c[0] + c[1]) + (c[2] + c[3]), t3 = (e[0] + e[1]) + (e[2] + e[3]);
-      out[row0 + lane * TW] = (uint16_t)f32_to_bf16_rne(((t0 + t1) + (t2 + t3)) * gwt);
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        const float4v* p = (const float4v*)(part + (lane * kM + m) * 16);
+        const float4v a = p[0], b = p[1], c = p[2], e = p[3];
+        const float t0 = (a[0] + a[1]) + (a[2] + a[3]), t1 = (b[0] + b[1]) + (b[2] + b[3]);
+        const float t2 = (c[0] + c[1]) + (c[2] + c[3]), t3 = (e[0] + e[1]) + (e[2] + e[3]);
+        if (m < M) out[(int64_t)m * N + row0 + lane * TW] = (uint16_t)f32_to_bf16_rne(((t0 + t1) + (t2 + t3)) * gwt);
+      }
     }
   };
   for (int row = gw; row < N; row += kD * TW) {
@@ -1098,7 +1108,9 @@ __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_w4a16_stream_kernel(
     for (int d = 0; d < kD; ++d) {
       const int r = row + d * TW;
       const auto wr = row_codes(r + kD * TW), wsr = row_scl(r + kD * TW);
-      float4v dsum = float4v{0.f, 0.f, 0.f, 0.f};
+      float4v dsum[kM];
+#pragma unroll
+      for (int m = 0; m < kM; ++m) dsum[m] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < kS; ++s) {
         half8v wv[4];
@@ -1109,16 +1121,23 @@ __global__ __launch_bounds__(64 * kStreamWaves) void nvfp4_w4a16_stream_kernel(
         // slot s of row r + kD TW into the registers just decoded
         wc[d][s] = buffer_load16<kCachePolicyNT>(wr, 1024u * s + 16u * lane);
         ws[d][s] = buffer_load2<kCachePolicyNT>(wsr, 128u * s + 2u * lane);
-        float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[jj], xv[s][jj], acc, 0, 0, 0);
-        const float4v ps = acc * unscale[s];
-        dsum = dsum + ps;
+        for (int m = 0; m < kM; ++m) {
+          float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[jj], xv[m][s][jj], acc, 0, 0, 0);
+          const float4v ps = acc * unscale[m][s];
+          dsum[m] = dsum[m] + ps;
+        }
       }
       if (r < N) {
         if (diag_lane) {
           const int c = i & 3;
-          part[nbat * 16 + i] = c == 0 ? dsum[0] : (c == 1 ? dsum[1] : (c == 2 ? dsum[2] : dsum[3]));
+#pragma unroll
+          for (int m = 0; m < kM; ++m)
+            part[(nbat * kM + m) * 16 + i] =
+                c == 0 ? dsum[m][0] : (c == 1 ? dsum[m][1] : (c == 2 ? dsum[m][2] : dsum[m][3]));
         }
         if (++nbat == kStreamBatch) {
           flush();
@@ -1363,14 +1382,31 @@ void launch_stream(const StreamX& a, const uint8_t* wc, const uint8_t* ws, const
   hipLaunchKernelGGL((nvfp4_gemv_stream_kernel<kM, kS, kQ>), dim3(grid), dim3(64 * kStreamWaves), 0, stream, a.codes,
                      a.scales, a.g, wc, ws, wg, (uint16_t*)out, M, N, K, a.x, a.q_codes, a.q_scales, a.q_g);
 }
-template <int kS>
-void launch_w4a16_stream(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out, int N, int K,
-                         hipStream_t stream) {
+template <int kM, int kS>
+void launch_w4a16_stream(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out, int M, int N,
+                         int K, hipStream_t stream) {
   const int64_t cap = (int64_t)device_cus() * kStreamWgsPerCu;
   const int64_t need = ((int64_t)N + kStreamWaves - 1) / kStreamWaves;
   const unsigned grid = (unsigned)(need < cap ? need : cap);
-  hipLaunchKernelGGL((nvfp4_w4a16_stream_kernel<kS>), dim3(grid), dim3(64 * kStreamWaves), 0, stream,
-                     (const uint16_t*)x, wc, ws, wg, (uint16_t*)out, N, K);
+  hipLaunchKernelGGL((nvfp4_w4a16_stream_kernel<kM, kS>), dim3(grid), dim3(64 * kStreamWaves), 0, stream,
+                     (const uint16_t*)x, wc, ws, wg, (uint16_t*)out, M, N, K);
+}
+// The weight-only streaming GEMV for M = 1 and K <= 8192 (kM = 2: K <= 6144,
+// since four slots of two rows need more registers than two waves per SIMD
+// allow); false otherwise.
+template <int kM>
+bool launch_w4a16_stream_k(const void* x, const uint8_t* wc, const uint8_t* ws, const float* wg, void* out, int M,
+                           int N, int K, hipStream_t stream) {
+  switch ((K + 2047) / 2048) {
+    case 1: launch_w4a16_stream<kM, 1>(x, wc, ws, wg, out, M, N, K, stream); return true;
+    case 2: launch_w4a16_stream<kM, 2>(x, wc, ws, wg, out, M, N, K, stream); return true;
+    case 3: launch_w4a16_stream<kM, 3>(x, wc, ws, wg, out, M, N, K, stream); return true;
+    case 4:
+      if (kM > 1) return false;
+      launch_w4a16_stream<1, 4>(x, wc, ws, wg, out, M, N, K, stream);
+      return true;
+    default: return false;
+  }
 }
 // Launches the streaming GEMV for M <= 2 and K <= kStreamMaxSlots * 2048;
 // false if the shape is outside that range.
@@ -1399,6 +1435,9 @@ hipError_t launch_nvfp4_w4a16_decode(const void* x, const uint8_t* wc, const uin
   // weight once for all rows.  M = 1 and the remaining M = 2: the row-slot
   // GEMV, 8 rows per workgroup (at M = 2, 8 rows took 19.4 us per call
   // against 21.5 us for 4 and 20.5 us for 6; 12 and more spill registers).
+  // M = 1, K <= 8192: the streaming GEMV (at M = 2 it measured no faster
+  // than the row band: 19.9-20.2 against 20.1-20.2 us, alternating runs).
+  if (M == 1 && launch_w4a16_stream_k<1>(x, wc, ws, wg, out, 1, (int)N, (int)K, stream)) return hipGetLastError();
   if (M >= 2 && launch_w4a16_band(x, wc, ws, wg, out, M, N, K, stream)) return hipGetLastError();
   if (M >= 3) {
     if (!launch_w4a16_xs(x, wc, ws, wg, out, M, N, K, stream)) return hipErrorInvalidValue;
@@ -1407,13 +1446,7 @@ hipError_t launch_nvfp4_w4a16_decode(const void* x, const uint8_t* wc, const uin
   if (M == 2)
     launch_w4a16_rowslot<2, 8>(x, wc, ws, wg, out, 2, (int)N, (int)K, stream);
   else
-    switch ((K + 2047) / 2048) {   // M = 1: the streaming form while K <= 8192 (same outputs)
-      case 1: launch_w4a16_stream<1>(x, wc, ws, wg, out, (int)N, (int)K, stream); break;
-      case 2: launch_w4a16_stream<2>(x, wc, ws, wg, out, (int)N, (int)K, stream); break;
-      case 3: launch_w4a16_stream<3>(x, wc, ws, wg, out, (int)N, (int)K, stream); break;
-      case 4: launch_w4a16_stream<4>(x, wc, ws, wg, out, (int)N, (int)K, stream); break;
-      default: launch_w4a16_rowslot<1, 8>(x, wc, ws, wg, out, 1, (int)N, (int)K, stream); break;
-    }
+    launch_w4a16_rowslot<1, 8>(x, wc, ws, wg, out, 1, (int)N, (int)K, stream);
   return hipGetLastError();
 }
 

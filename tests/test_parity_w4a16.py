@@ -39,11 +39,11 @@ def check(x_bits, w_bits, algos=(0,), label=""):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (2, 37, 256), (1, 33, 4224), (2, 8, 6144), (1, 9, 32768),
                                    (3, 37, 256), (5, 20, 2176), (16, 41, 1024), (1, 140001, 256),
-                                   (1, 300, 6144 + 128), (1, 5000, 8192)])
+                                   (1, 300, 6144 + 128), (1, 5000, 8192), (2, 140001, 256), (2, 300, 6144 + 128)])
 def test_decode_shapes(M, N, K):
     # M = 1 with K <= 8192 runs the streaming GEMV (N = 140001: each wave
     # takes more than 64 rows; K = 6272: a partial last slot), larger K the
-    # row-slot GEMV
+    # row-slot GEMV; M = 2 the row band, past its K the row-slot GEMV
     x = workloads.random_bf16(M * 3 + K, (M, K), outlier_frac=0.01, outlier_mul=20)
     w = workloads.random_bf16(N * 5 + K, (N, K), sigma=0.02, zero_frac=0.05)
     check(x, w, algos=(0, 2, 3), label=f"{M}x{N}x{K}")
