@@ -21,6 +21,8 @@
 //    128-byte lines.
 //  - weight-only GEMM (bf16 x, 3 <= M <= 16): activation-stationary, W
 //    streamed through LDS by DMA, so W is read once for all M rows.
+// The weight-only (bf16 x) forms of the row-slot and streaming GEMVs and a
+// row-band kernel (2 <= M <= 16, K <= 6144) follow the same patterns.
 #include "common.h"
 #include "launch.h"
 #include "quant_block.h"
